@@ -1,0 +1,297 @@
+"""Benchmark of the ternary BitLinear hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Headline (the JSON `value`): decode GEMV packed-weight GB/s on the
+BitNet-2B-like layer at batch 1 (hidden 2560, k/v 640, FFN 6912). One step =
+one pass of the per-token hot path over that layer: for each of the 7
+projections (q, k, v, o, gate, up, down) the per-token absmax int8
+quantization of its bf16 input and the I2_S GEMV with the bf16 dequant fused
+into the store. Weight packing is the offline conversion and is done once
+before timing. Steps rotate over R distinct copies of the layer's packed
+weights (R * 17.4 MB > the 256 MB Infinity Cache), so every step streams its
+weights from HBM. Steps are replayed from HIP graphs (captured through
+torch.cuda.CUDAGraph) so host launch cost is not timed.
+
+Also reported on the same JSON line:
+  roofline      the GEMV kernel alone: algorithmic packed bytes per launch over
+                its average launch duration (HIP events around graph replays of
+                GEMV launches only), against 8 TB/s;
+  gemm          prefill on the 100B-class layer (2048 tokens, hidden 8192,
+                FFN 28672, k/v 1024): 2*M*N*K int8 ops per second over the 7
+                projections (quantize + GEMM), against 5.0 POP/s dense int8;
+  cpu_baseline  the CPU oracle on a bounded sample of the decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=640)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--rotate", type=int, default=32, help="distinct layer copies")
+    p.add_argument("--gemm-steps", type=int, default=5)
+    p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mpgemm_token_absmax_amd as bl
+    import workloads as W
+
+    bl.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ----------------------------------------------------------------- decode
+    cfg = W.CONFIGS[2]
+    M = 1
+    R = max(1, args.rotate)
+    log(f"setup decode: {cfg.name}, {R} layer copies")
+    layers = []        # layers[r][p] = packed tensor
+    gammas, xs, qs, ds, ys = [], [], [], [], []
+    base = []
+    for proj in cfg.projs:
+        inp = W.proj_inputs(cfg, proj, M)
+        packed = bl.pack_i2s(to_dev(inp.w_tern))
+        base.append(packed)
+        gammas.append(to_dev(np.array([inp.gamma], np.float32)))
+        xs.append(to_dev(inp.x_bf16.view(np.int16)).view(torch.bfloat16))
+        qs.append(torch.empty((M, proj.K), dtype=torch.int8, device=dev))
+        ds.append(torch.empty((M,), dtype=torch.float32, device=dev))
+        ys.append(torch.empty((M, proj.N), dtype=torch.bfloat16, device=dev))
+    for r in range(R):
+        layers.append([b.clone() for b in base])
+    torch.cuda.synchronize()
+    step_bytes = cfg.packed_bytes
+
+    def step(r):
+        for p in range(len(cfg.projs)):
+            bl.quantize_act(xs[p], qs[p], ds[p])
+            bl.gemv(layers[r][p], gammas[p], qs[p], ds[p], out_dtype="bf16", out=ys[p])
+
+    def gemv_only(r):
+        for p in range(len(cfg.projs)):
+            bl.gemv(layers[r][p], gammas[p], qs[p], ds[p], out_dtype="bf16", out=ys[p])
+
+    # eager warm-up (also loads the code objects) before capture
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all, stream=stream):
+        for r in range(R):
+            step(r)
+    g_one = []
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step(r)
+        g_one.append(g)
+    g_gemv = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_gemv, stream=stream):
+        for r in range(R):
+            gemv_only(r)
+    torch.cuda.synchronize()
+
+    def run_steps(n):
+        full, rem = divmod(n, R)
+        for _ in range(full):
+            g_all.replay()
+        for r in range(rem):
+            g_one[r].replay()
+
+    log(f"warmup {args.warmup} steps")
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    run_steps(args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"decode: {ms_step * 1e3:.2f} us/step, {gbs:.1f} GB/s packed")
+
+    # GEMV kernel alone: graph replays on the capture stream, events on that stream
+    reps = max(4, args.steps // R)
+    with torch.cuda.stream(stream):
+        g_gemv.replay()
+        k0 = torch.cuda.Event(enable_timing=True)
+        k1 = torch.cuda.Event(enable_timing=True)
+        k0.record(stream)
+        for _ in range(reps):
+            g_gemv.replay()
+        k1.record(stream)
+    torch.cuda.synchronize()
+    launches = reps * R * len(cfg.projs)
+    us_launch = k0.elapsed_time(k1) * 1e3 / launches
+    bytes_launch = step_bytes / len(cfg.projs)
+    gemv_gbs = bytes_launch / (us_launch * 1e-6) / 1e9
+    log(f"gemv kernel: {us_launch:.2f} us/launch avg, {gemv_gbs:.1f} GB/s")
+
+    result = {
+        "metric": "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM int8 TOPS (% peak)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": M, "hidden": 2560, "ffn": 6912, "kv": 640,
+                   "layer_copies": R, "packed_bytes_per_step": step_bytes,
+                   "step": "7x (quantize bf16 -> int8 + I2_S GEMV -> bf16)",
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_gemv_i2s", "us_per_launch": round(us_launch, 3),
+                     "bytes_per_launch": bytes_launch},
+    }
+    del layers, g_all, g_one, g_gemv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # ----------------------------------------------------------------- prefill
+    if not args.no_gemm:
+        cfg5 = W.CONFIGS[5]
+        M5 = 2048
+        log(f"setup prefill: {cfg5.name}")
+        P = []
+        for proj in cfg5.projs:
+            inp = W.proj_inputs(cfg5, proj, M5)
+            packed = bl.pack_i2s(to_dev(inp.w_tern))
+            x = to_dev(inp.x_bf16.view(np.int16)).view(torch.bfloat16)
+            P.append(dict(packed=packed, gamma=to_dev(np.array([inp.gamma], np.float32)), x=x,
+                          q=torch.empty((M5, proj.K), dtype=torch.int8, device=dev),
+                          d=torch.empty((M5,), dtype=torch.float32, device=dev),
+                          y=torch.empty((M5, proj.N), dtype=torch.bfloat16, device=dev)))
+            del inp
+        torch.cuda.synchronize()
+
+        def layer(gemm_only=False):
+            for e in P:
+                if not gemm_only:
+                    bl.quantize_act(e["x"], e["q"], e["d"])
+                bl.gemm(e["packed"], e["gamma"], e["q"], e["d"], out_dtype="bf16", out=e["y"])
+
+        layer()
+        layer()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(args.gemm_steps):
+            layer()
+        a1.record()
+        torch.cuda.synchronize()
+        ms_layer = a0.elapsed_time(a1) / args.gemm_steps
+        ops = cfg5.ops(M5)
+        tops = ops / (ms_layer * 1e-3) / 1e12
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(args.gemm_steps):
+            layer(gemm_only=True)
+        b1.record()
+        torch.cuda.synchronize()
+        ms_gemm = b0.elapsed_time(b1) / args.gemm_steps
+        gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
+        per_proj = {}
+        for proj, e in zip(cfg5.projs, P):
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record()
+            for _ in range(3):
+                bl.gemm(e["packed"], e["gamma"], e["q"], e["d"], out_dtype="bf16", out=e["y"])
+            c1.record()
+            torch.cuda.synchronize()
+            ms = c0.elapsed_time(c1) / 3
+            per_proj[proj.name] = round(2 * M5 * proj.N * proj.K / (ms * 1e-3) / 1e12, 1)
+        log(f"prefill: {ms_layer:.3f} ms/layer ({tops:.1f} TOPS incl. quantize), "
+            f"GEMM only {gemm_tops:.1f} TOPS; per projection {per_proj}")
+        result["gemm"] = {"workload": cfg5.name, "tokens": M5, "ops_per_layer": ops,
+                          "ms_per_layer": round(ms_layer, 4), "tops": round(tops, 1),
+                          "gemm_only_tops": round(gemm_tops, 1), "peak_tops": INT8_PEAK_TOPS,
+                          "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                          "tops_per_projection": per_proj}
+        del P
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU oracle
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline: oracle on the decode layer")
+        inputs = []
+        for proj in cfg.projs:
+            inp = W.proj_inputs(cfg, proj, M)
+            inputs.append((inp, oracle.pack_i2s(inp.w_tern)))
+
+        def oracle_step():
+            for inp, packed in inputs:
+                q, d = oracle.quantize_act_absmax(inp.x_bf16)
+                t = oracle.unpack_i2s(packed, inp.proj.K)
+                acc = oracle.mpgemm_acc(q, t)
+                oracle.round_f64_to_bf16_bits(oracle.dequant_f64(acc, inp.gamma, d))
+
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle_step()
+            n += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        cpu_gbs = step_bytes * n / dt / 1e9
+        result["cpu_baseline"] = {
+            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} decode steps of the same layer (7 projections: quantize, unpack, "
+                      f"int64 dot, dequant, bf16) in {dt:.1f} s; numpy, single thread; "
+                      f"host has {len(os.sched_getaffinity(0))} cores"}
+        log(f"cpu oracle: {cpu_gbs:.4f} GB/s ({n} steps in {dt:.1f} s)")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * bitlinear.h -- C ABI of the ternary BitLinear mpGEMM library (libbitlinear.so).
+ *
+ * The library computes a BitNet b1.58 linear layer on an AMD Instinct MI355X
+ * (gfx950): ternary weights {-1, 0, +1} stored as 2-bit I2_S codes with one
+ * per-tensor absmean scale, contracted against int8 activations quantized per
+ * token by absmax, with exact int32 accumulation, then dequantized.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [BN]  "Bitnet.cpp: Efficient Edge Inference for Ternary LLMs" reading
+ *         notes (arXiv 2502.11880): Part A 2.3 (I2_S: element-wise,
+ *         multiply-add based, 2.0 bits per weight, ternary weights with one
+ *         scale and int8 activations), 4.1 (lossless: no re-quantized partial
+ *         sums), Part B "方法公式化".
+ *   [FF]  FairyFuse article: "三元量化方案" (threshold at +-0.5 of a per-layer
+ *         scale), "融合内核设计" (codes 00/01/10 = 0/+1/-1; add or subtract
+ *         activations; fused unpack-accumulate-store).
+ *   [HB]  bitnet.cpp how-to blog: 1.1 (decode streams every weight once per
+ *         token, so it is memory-bandwidth bound), 1.2 (ternary weights turn
+ *         multiply-adds into adds and subtracts).
+ *
+ * Conventions (all calls):
+ *   - Every array argument is a DEVICE pointer owned by the caller. The
+ *     library never allocates, frees or keeps global mutable state.
+ *     Outputs must not alias inputs.
+ *   - Base pointers of x, q, packed, w and y must be 16-byte aligned; d and
+ *     gamma 4-byte aligned (BL_ERR_ALIGN otherwise). Allocations from
+ *     hipMalloc / PyTorch satisfy this.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on `stream` and returns; arguments are validated before
+ *     anything is enqueued, and a rejected call enqueues nothing. A launch
+ *     failure returns BL_ERR_HIP. Faults during execution surface at the
+ *     caller's next synchronization of the stream. No call synchronizes.
+ *   - M (tokens), N (output features) and K (input features) are counts;
+ *     negative values are BL_ERR_SHAPE. K must be a multiple of 4.
+ *     A call with M == 0 or N == 0 does nothing and returns BL_OK.
+ *   - Calls are thread-safe (no shared state); results are deterministic and
+ *     do not depend on the launch configuration.
+ *
+ * I2_S packed layout (the pages fix the code table [FF] and the 2-bit width
+ * [BN], not the bit order; this layout is the library's choice):
+ *   packed is uint8 [N][K/4], row n at byte offset n*(K/4). Each row is cut
+ *   into groups of 16 weights (4 bytes); the last group of a row may hold
+ *   4, 8 or 12 weights (b = 1, 2 or 3 bytes). Within a group of b bytes,
+ *   weight o (0 <= o < 4b) is stored in byte (o mod b) at bits
+ *   2*(o div b) .. 2*(o div b)+1. Code 00 = 0, 01 = +1, 10 = -1; 11 is never
+ *   written (it decodes as 0). For a full group, shifting its little-endian
+ *   32-bit word right by 2i and masking 0x03030303 yields the codes of
+ *   weights 4i .. 4i+3 in byte order.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BL_ABI_VERSION 1
+
+/* Status codes returned by every call. */
+enum {
+  BL_OK = 0,
+  BL_ERR_NULL = -1,      /* a required pointer is NULL                        */
+  BL_ERR_SHAPE = -2,     /* negative size, K % 4 != 0, ldx < K, M > 16 (gemv) */
+  BL_ERR_ALIGN = -3,     /* a pointer or stride breaks the alignment rules    */
+  BL_ERR_DTYPE = -4,     /* unknown weight or output type enum                */
+  BL_ERR_WORKSPACE = -5, /* workspace missing or smaller than required        */
+  BL_ERR_HIP = -6        /* the HIP runtime refused a launch                  */
+};
+
+/* Weight input type of bl_pack_i2s. */
+enum {
+  BL_W_F32 = 0,         /* fp32 [N][K]: absmean-ternarize, write *gamma      */
+  BL_W_TERNARY_I8 = 1   /* int8 [N][K] ternary values: pack only             */
+};
+
+/* Output type of bl_gemv / bl_gemm. */
+enum {
+  BL_OUT_I32 = 0,   /* raw exact accumulator acc[t][n] (int32)               */
+  BL_OUT_F32 = 1,   /* y = fl32(fl32(acc) * fl32(gamma * d_t))               */
+  BL_OUT_BF16 = 2   /* the fp32 y rounded to nearest-even bf16 (uint16 bits) */
+};
+
+/* BL_ABI_VERSION of the loaded library. */
+int bl_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *bl_status_string(int status);
+
+/*
+ * bl_quantize_act -- per-token absmax int8 quantization of activations.
+ * Defines: [BN] Part A 2.3 / 4.1 (int8 activations with one scale per
+ * vector, not per block); applied per token (row of x).
+ *   m_t = max_k |x[t][k]|;   if m_t == 0: q[t][:] = 0, d[t] = 0;  else
+ *   s_t = fl32(127 / m_t),   q[t][k] = clamp(rne(fl32(x[t][k] * s_t)), -127, 127),
+ *   d[t] = fl32(m_t / 127)   (the dequantization multiplier).
+ * x:   bf16 bit patterns, [M] rows of K values, row stride ldx elements
+ *      (ldx >= K, ldx % 4 == 0).
+ * q:   int8 [M][K], row stride K.     d: fp32 [M].
+ * Inputs must be finite; rows whose absmax is below 2^-120 (where 127/m
+ * overflows fp32) give unspecified q. K == 0 writes d[:] = 0.
+ */
+int bl_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                    int8_t *q, float *d, void *stream);
+
+/*
+ * bl_pack_i2s_workspace -- bytes of workspace bl_pack_i2s needs for an
+ * N x K fp32 matrix (BL_W_F32). BL_W_TERNARY_I8 needs none.
+ */
+size_t bl_pack_i2s_workspace(int64_t N, int64_t K);
+
+/*
+ * bl_pack_i2s -- ternarize (optionally) and pack weights into I2_S.
+ * Defines: [BN] Part A 2.3 (2-bit I2_S with one per-tensor scale),
+ * [FF] "三元量化方案" (w > 0.5*alpha -> +1, w < -0.5*alpha -> -1, else 0),
+ * with alpha read as BitNet b1.58's absmean scale gamma = mean |W|.
+ *   BL_W_F32: w is fp32 [N][K] (finite). gamma = fl32(fl64(exact sum |w|) /
+ *     (N*K)) is written to *gamma (device, 1 float); t = fl32(0.5*gamma);
+ *     weight -> +1 if w > t, -1 if w < -t, else 0. The exact sum is order
+ *     independent, so gamma and the codes are bit-reproducible.
+ *     1 <= N*K < 2^38. Needs ws_bytes >= bl_pack_i2s_workspace(N, K) (16-byte aligned).
+ *   BL_W_TERNARY_I8: w is int8 [N][K] ternary values; each is taken by its
+ *     sign (> 0 -> +1, < 0 -> -1, 0 -> 0). *gamma is neither read nor
+ *     written (the caller keeps the scale); gamma and ws may be NULL.
+ * packed: uint8 [N][K/4] in the layout above.
+ */
+int bl_pack_i2s(const void *w, int wtype, int64_t N, int64_t K, uint8_t *packed,
+                float *gamma, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * bl_gemv -- decode-time BitLinear for 1 <= M <= 16 tokens.
+ * Defines: [BN] Part A 2.3 / 4.1 (I2_S multiply-add with exact sums),
+ * [HB] 1.1-1.2, [FF] "融合内核设计" (unpack and accumulate in one pass).
+ *   acc[t][n] = sum_k q[t][k] * w[n][k]  (exact int32; |acc| <= 127*K)
+ *   y[t][n]   = acc[t][n] (BL_OUT_I32) or its dequantized value (BL_OUT_F32 /
+ *               BL_OUT_BF16, see the output enum), y row stride N.
+ * packed: uint8 [N][K/4]; gamma: device fp32 (1 value); q: int8 [M][K];
+ * d: fp32 [M]. M > 16 is BL_ERR_SHAPE (use bl_gemm). For BL_OUT_F32 and
+ * BL_OUT_BF16, K must satisfy 127*K < 2^24 (fp32-exact accumulator).
+ * Results are bit-identical to bl_gemm's for the same inputs.
+ */
+int bl_gemv(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
+            const int8_t *q, const float *d, int64_t M, void *y, int ytype,
+            void *stream);
+
+/* bl_gemm_workspace -- bytes of workspace bl_gemm needs (currently 0). */
+size_t bl_gemm_workspace(int64_t M, int64_t N, int64_t K);
+
+/*
+ * bl_gemm -- prefill BitLinear for any M >= 1 (int8 MFMA path).
+ * Defines: as bl_gemv ([BN] Part A 2.3 / 4.1); the pages leave prefill
+ * unoptimized ([BN] 4.4), so this is the dense contraction on matrix cores.
+ * Same arguments and results as bl_gemv, plus a workspace of ws_bytes
+ * (>= bl_gemm_workspace(M, N, K); may be NULL when that is 0).
+ */
+int bl_gemm(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
+            const int8_t *q, const float *d, int64_t M, void *y, int ytype,
+            void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

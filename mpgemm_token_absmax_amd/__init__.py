@@ -1,0 +1,139 @@
+"""Ternary BitLinear mpGEMM on AMD Instinct MI355X (gfx950).
+
+Python binding of libbitlinear.so (C ABI: include/bitlinear.h). The functions
+here take and return torch tensors on the GPU, pass their device pointers and
+torch's current stream to the library, and do nothing else: every step of the
+computation runs in the library's HIP kernels. PyTorch provides device memory
+and streams only.
+
+    q, d        = quantize_act(x_bf16)              # per-token absmax int8
+    packed, g   = pack_i2s(w_fp32)                  # absmean ternary -> 2-bit I2_S
+    packed      = pack_i2s(w_ternary_int8)          # pack only (caller keeps gamma)
+    y           = gemv(packed, g, q, d)             # M <= 16 tokens
+    y           = gemm(packed, g, q, d)             # any M (int8 MFMA)
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I8,
+                   BitLinearError, check, lib, status_string)
+
+__all__ = ["quantize_act", "pack_i2s", "pack_i2s_workspace", "gemv", "gemm",
+           "gemm_workspace", "BitLinearError", "status_string", "lib", "OUT_TYPES"]
+
+OUT_TYPES = {"i32": (BL_OUT_I32, torch.int32), "f32": (BL_OUT_F32, torch.float32),
+             "bf16": (BL_OUT_BF16, torch.bfloat16)}
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+
+
+def quantize_act(x: torch.Tensor, q: torch.Tensor | None = None, d: torch.Tensor | None = None):
+    """x: bf16 [M][K] (row stride x.stride(0)) -> (q int8 [M][K], d fp32 [M])."""
+    _need(x, "x", torch.bfloat16, 2)
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((M,), dtype=torch.float32, device=x.device)
+    check("bl_quantize_act", lib().bl_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d),
+                                                   _stream(x.device)))
+    return q, d
+
+
+def pack_i2s_workspace(N: int, K: int) -> int:
+    return int(lib().bl_pack_i2s_workspace(N, K))
+
+
+def pack_i2s(w: torch.Tensor, packed: torch.Tensor | None = None,
+             gamma: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """fp32 [N][K] -> (packed uint8 [N][K/4], gamma fp32 [1]) (absmean ternarize + pack);
+    int8 ternary [N][K] -> packed uint8 [N][K/4] (pack only)."""
+    if not isinstance(w, torch.Tensor) or not w.is_cuda or w.dim() != 2:
+        raise TypeError("w must be a 2-D CUDA tensor")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    N, K = w.shape
+    if K % 4:
+        raise ValueError("K must be a multiple of 4")
+    if packed is None:
+        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=w.device)
+    s = _stream(w.device)
+    if w.dtype == torch.float32:
+        if gamma is None:
+            gamma = torch.empty((1,), dtype=torch.float32, device=w.device)
+        nws = pack_i2s_workspace(N, K)
+        if workspace is None:
+            workspace = torch.empty((max(nws, 16),), dtype=torch.uint8, device=w.device)
+        check("bl_pack_i2s", lib().bl_pack_i2s(_ptr(w), BL_W_F32, N, K, _ptr(packed),
+                                               _ptr(gamma), _ptr(workspace),
+                                               workspace.numel(), s))
+        return packed, gamma
+    if w.dtype == torch.int8:
+        check("bl_pack_i2s", lib().bl_pack_i2s(_ptr(w), BL_W_TERNARY_I8, N, K, _ptr(packed),
+                                               None, None, 0, s))
+        return packed
+    raise TypeError("w must be float32 or int8")
+
+
+def _matmul_args(packed, gamma, q, d, out, out_dtype):
+    _need(packed, "packed", torch.uint8, 2)
+    _need(q, "q", torch.int8, 2)
+    N, KB = packed.shape
+    M, K = q.shape
+    if KB * 4 != K:
+        raise ValueError(f"packed [{N}][{KB}] does not match q [{M}][{K}]")
+    ytype, tdt = OUT_TYPES[out_dtype]
+    if ytype != BL_OUT_I32:
+        _need(gamma, "gamma", torch.float32, 1)
+        _need(d, "d", torch.float32, 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=tdt, device=q.device)
+    elif out.dtype != tdt or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out has the wrong dtype, shape or layout")
+    return N, K, M, ytype, out
+
+
+def gemv(packed: torch.Tensor, gamma: torch.Tensor, q: torch.Tensor, d: torch.Tensor,
+         out_dtype: str = "bf16", out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M][N] for M <= 16 tokens (decode path)."""
+    N, K, M, ytype, out = _matmul_args(packed, gamma, q, d, out, out_dtype)
+    check("bl_gemv", lib().bl_gemv(_ptr(packed), _ptr(gamma), N, K, _ptr(q), _ptr(d), M,
+                                   _ptr(out), ytype, _stream(q.device)))
+    return out
+
+
+def gemm_workspace(M: int, N: int, K: int) -> int:
+    return int(lib().bl_gemm_workspace(M, N, K))
+
+
+def gemm(packed: torch.Tensor, gamma: torch.Tensor, q: torch.Tensor, d: torch.Tensor,
+         out_dtype: str = "bf16", out: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M][N] for any M (prefill path, int8 MFMA)."""
+    N, K, M, ytype, out = _matmul_args(packed, gamma, q, d, out, out_dtype)
+    nws = gemm_workspace(M, N, K)
+    if nws and workspace is None:
+        workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
+    check("bl_gemm", lib().bl_gemm(_ptr(packed), _ptr(gamma), N, K, _ptr(q), _ptr(d), M,
+                                   _ptr(out), ytype, _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(),
+                                   _stream(q.device)))
+    return out

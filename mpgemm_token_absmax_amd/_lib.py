@@ -1,0 +1,83 @@
+"""ctypes loader for libbitlinear.so (the C ABI in include/bitlinear.h).
+
+Argument marshalling only: no computation happens here. The library must have
+been built in-tree (mpgemm_token_absmax_amd/build.py); loading fails loudly
+otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbitlinear.so")
+
+BL_OK = 0
+BL_ERR_NULL = -1
+BL_ERR_SHAPE = -2
+BL_ERR_ALIGN = -3
+BL_ERR_DTYPE = -4
+BL_ERR_WORKSPACE = -5
+BL_ERR_HIP = -6
+
+BL_W_F32 = 0
+BL_W_TERNARY_I8 = 1
+
+BL_OUT_I32 = 0
+BL_OUT_F32 = 1
+BL_OUT_BF16 = 2
+
+EXPORTS = ("bl_abi_version", "bl_status_string", "bl_quantize_act", "bl_pack_i2s_workspace",
+           "bl_pack_i2s", "bl_gemv", "bl_gemm_workspace", "bl_gemm")
+
+_lib = None
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+
+
+def _declare(lib):
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    INT = ctypes.c_int
+    SZ = ctypes.c_size_t
+    lib.bl_abi_version.restype = INT
+    lib.bl_abi_version.argtypes = []
+    lib.bl_status_string.restype = ctypes.c_char_p
+    lib.bl_status_string.argtypes = [INT]
+    lib.bl_quantize_act.restype = INT
+    lib.bl_quantize_act.argtypes = [P, I64, I64, I64, P, P, P]
+    lib.bl_pack_i2s_workspace.restype = SZ
+    lib.bl_pack_i2s_workspace.argtypes = [I64, I64]
+    lib.bl_pack_i2s.restype = INT
+    lib.bl_pack_i2s.argtypes = [P, INT, I64, I64, P, P, P, SZ, P]
+    lib.bl_gemv.restype = INT
+    lib.bl_gemv.argtypes = [P, P, I64, I64, P, P, I64, P, INT, P]
+    lib.bl_gemm_workspace.restype = SZ
+    lib.bl_gemm_workspace.argtypes = [I64, I64, I64]
+    lib.bl_gemm.restype = INT
+    lib.bl_gemm.argtypes = [P, P, I64, I64, P, P, I64, P, INT, P, SZ, P]
+    return lib
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m mpgemm_token_absmax_amd.build`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().bl_status_string(int(status)).decode()
+
+
+def check(fn: str, status: int):
+    if status != BL_OK:
+        raise BitLinearError(fn, status)

@@ -1,0 +1,121 @@
+// C ABI of the ternary BitLinear library: argument validation and dispatch.
+// Declarations, argument meaning, layouts, ownership and errors: the public
+// header bitlinear.h. Validation touches no HIP API, so every error path runs
+// (and is tested) on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include "../../include/bitlinear.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kGemvMaxM = 16;
+constexpr int64_t kFp32ExactK = ((int64_t)1 << 24) / 127;   // 127*K < 2^24
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int check_matmul(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
+                 const int8_t* q, const float* d, int64_t M, const void* y, int ytype) {
+  if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return BL_ERR_SHAPE;
+  if (ytype < BL_OUT_I32 || ytype > BL_OUT_BF16) return BL_ERR_DTYPE;
+  if (M == 0 || N == 0) return BL_OK;
+  if (!y) return BL_ERR_NULL;
+  if (K > 0 && (!packed || !q)) return BL_ERR_NULL;
+  if (ytype != BL_OUT_I32 && (!gamma || !d)) return BL_ERR_NULL;
+  if (127 * K > INT32_MAX) return BL_ERR_SHAPE;
+  if (ytype != BL_OUT_I32 && K > kFp32ExactK) return BL_ERR_SHAPE;
+  if (!aligned(y, 16)) return BL_ERR_ALIGN;
+  if (K > 0 && (!aligned(packed, 16) || !aligned(q, 16))) return BL_ERR_ALIGN;
+  if ((gamma && !aligned(gamma, 4)) || (d && !aligned(d, 4))) return BL_ERR_ALIGN;
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bl_abi_version(void) { return BL_ABI_VERSION; }
+
+const char* bl_status_string(int status) {
+  switch (status) {
+    case BL_OK: return "ok";
+    case BL_ERR_NULL: return "a required pointer is NULL";
+    case BL_ERR_SHAPE: return "invalid shape (negative size, K % 4 != 0, ldx < K, M > 16 for gemv, or K too large)";
+    case BL_ERR_ALIGN: return "misaligned pointer or stride";
+    case BL_ERR_DTYPE: return "unknown weight or output type";
+    case BL_ERR_WORKSPACE: return "workspace missing or too small";
+    case BL_ERR_HIP: return "HIP runtime error while launching";
+    default: return "unknown status";
+  }
+}
+
+int bl_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* d,
+                    void* stream) {
+  if (M < 0 || K < 0 || K % 4 != 0 || ldx < K) return BL_ERR_SHAPE;
+  if (M == 0) return BL_OK;
+  if (!d || (K > 0 && (!x || !q))) return BL_ERR_NULL;
+  if (ldx % 4 != 0) return BL_ERR_ALIGN;
+  if (!aligned(d, 4)) return BL_ERR_ALIGN;
+  if (K > 0 && (!aligned(x, 16) || !aligned(q, 16))) return BL_ERR_ALIGN;
+  if (M > INT32_MAX) return BL_ERR_SHAPE;
+  return hip_status(bl::launch_quantize_act(x, M, K, ldx, q, d, as_stream(stream)));
+}
+
+size_t bl_pack_i2s_workspace(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return bl::pack_workspace_bytes(N, K);
+}
+
+int bl_pack_i2s(const void* w, int wtype, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                void* ws, size_t ws_bytes, void* stream) {
+  if (N < 0 || K < 0 || K % 4 != 0) return BL_ERR_SHAPE;
+  if (wtype != BL_W_F32 && wtype != BL_W_TERNARY_I8) return BL_ERR_DTYPE;
+  if (wtype == BL_W_F32) {
+    if (N == 0 || K == 0) return BL_ERR_SHAPE;     // gamma of an empty matrix is undefined
+    if (N > ((int64_t)1 << 38) / K) return BL_ERR_SHAPE;   // exact-sum bins: n < 2^38
+    if (!w || !packed || !gamma) return BL_ERR_NULL;
+    if (!ws) return BL_ERR_WORKSPACE;
+    if (ws_bytes < bl::pack_workspace_bytes(N, K)) return BL_ERR_WORKSPACE;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(ws, 16))
+      return BL_ERR_ALIGN;
+    return hip_status(bl::launch_pack_f32(static_cast<const float*>(w), N, K, packed, gamma, ws,
+                                          as_stream(stream)));
+  }
+  if (N == 0 || K == 0) return BL_OK;
+  if (!w || !packed) return BL_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(packed, 16)) return BL_ERR_ALIGN;
+  return hip_status(bl::launch_pack_ternary(static_cast<const int8_t*>(w), N, K, packed,
+                                            as_stream(stream)));
+}
+
+int bl_gemv(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, const int8_t* q,
+            const float* d, int64_t M, void* y, int ytype, void* stream) {
+  if (M > kGemvMaxM) return BL_ERR_SHAPE;
+  const int st = check_matmul(packed, gamma, N, K, q, d, M, y, ytype);
+  if (st != BL_OK || M == 0 || N == 0) return st;
+  return hip_status(bl::launch_gemv(packed, gamma, N, K, q, d, M, y, ytype, as_stream(stream)));
+}
+
+size_t bl_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+int bl_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, const int8_t* q,
+            const float* d, int64_t M, void* y, int ytype, void* ws, size_t ws_bytes,
+            void* stream) {
+  const int st = check_matmul(packed, gamma, N, K, q, d, M, y, ytype);
+  if (st != BL_OK || M == 0 || N == 0) return st;
+  if (ws_bytes < bl_gemm_workspace(M, N, K)) return BL_ERR_WORKSPACE;
+  (void)ws;
+  if (N > (int64_t)UINT32_MAX * 64 || M > (int64_t)65535 * 128) return BL_ERR_SHAPE;
+  return hip_status(bl::launch_gemm(packed, gamma, N, K, q, d, M, y, ytype, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// Per-token absmax int8 activation quantization (gfx950).
+//
+// Source: "Bitnet.cpp: Efficient Edge Inference for Ternary LLMs" reading
+// notes, Part A 2.3 / 4.1: the ternary weights meet int8 activations that
+// carry one scale per vector (not per block). Per token t (one row of x):
+//   m = max |x[t][:]|, s = fl32(127/m), q = clamp(rne(fl32(x*s)), -127, 127),
+//   d[t] = fl32(m/127); an all-zero row gives q = 0, d = 0.
+//
+// One workgroup of 256 threads per token. Each thread reads 4 bf16 (8 bytes)
+// per chunk; for K <= 256*4*NC the row stays in registers between the max
+// and the quantize pass, otherwise the second pass re-reads it (an L2 hit).
+// The max is taken on the magnitude bits: for finite values the ordering of
+// the bit patterns of |x| is the ordering of the values.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bl {
+namespace {
+
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ uint32_t absmax4(uint2 v) {
+  const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
+  return max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16));
+}
+
+__device__ __forceinline__ int8_t quant1(uint32_t bf16bits, float s) {
+  const float x = __uint_as_float(bf16bits << 16);
+  float r = rintf(__fmul_rn(x, s));
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int8_t)(int)r;
+}
+
+__device__ __forceinline__ uint32_t quant4(uint2 v, float s) {
+  const uint32_t b0 = (uint8_t)quant1(v.x & 0xFFFFu, s);
+  const uint32_t b1 = (uint8_t)quant1(v.x >> 16, s);
+  const uint32_t b2 = (uint8_t)quant1(v.y & 0xFFFFu, s);
+  const uint32_t b3 = (uint8_t)quant1(v.y >> 16, s);
+  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
+  __syncthreads();
+  uint32_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < kQThreads / kWave; ++w) m = max(m, red[w]);
+  return m;
+}
+
+// NC > 0: row cached in registers (K <= 1024*NC). NC == 0: two passes over x.
+template <int NC>
+__global__ __launch_bounds__(kQThreads) void k_quant_absmax(
+    const uint16_t* __restrict__ x, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    float* __restrict__ d) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  const int64_t t = blockIdx.x;
+  const uint2* xr = reinterpret_cast<const uint2*>(x + t * ldx);
+  uint32_t* qr = reinterpret_cast<uint32_t*>(q + t * K);
+  const int64_t nchunk = K / 4;
+  uint32_t mb = 0;
+  if constexpr (NC > 0) {
+    uint2 v[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t c = threadIdx.x + (int64_t)i * kQThreads;
+      v[i] = c < nchunk ? xr[c] : make_uint2(0u, 0u);
+      mb = max(mb, absmax4(v[i]));
+    }
+    mb = block_max_u32(mb, red);
+    const float m = __uint_as_float(mb << 16);
+    const float s = mb ? 127.0f / m : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t c = threadIdx.x + (int64_t)i * kQThreads;
+      if (c < nchunk) qr[c] = mb ? quant4(v[i], s) : 0u;
+    }
+    if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
+  } else {
+    for (int64_t c = threadIdx.x; c < nchunk; c += kQThreads) mb = max(mb, absmax4(xr[c]));
+    mb = block_max_u32(mb, red);
+    const float m = __uint_as_float(mb << 16);
+    const float s = mb ? 127.0f / m : 0.0f;
+    for (int64_t c = threadIdx.x; c < nchunk; c += kQThreads) qr[c] = mb ? quant4(xr[c], s) : 0u;
+    if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
+  }
+}
+
+__global__ void k_fill_zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+template <int NC>
+hipError_t launch_nc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* d,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(k_quant_absmax<NC>, dim3((unsigned)M), dim3(kQThreads), 0, s, x, K, ldx, q,
+                     d);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                               float* d, hipStream_t s) {
+  if (K == 0) {
+    hipLaunchKernelGGL(k_fill_zero_f32, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, d, M);
+    return hipGetLastError();
+  }
+  const int64_t per_thread = (K / 4 + kQThreads - 1) / kQThreads;
+  if (per_thread <= 1) return launch_nc<1>(x, M, K, ldx, q, d, s);
+  if (per_thread <= 2) return launch_nc<2>(x, M, K, ldx, q, d, s);
+  if (per_thread <= 4) return launch_nc<4>(x, M, K, ldx, q, d, s);
+  if (per_thread <= 8) return launch_nc<8>(x, M, K, ldx, q, d, s);
+  if (per_thread <= 16) return launch_nc<16>(x, M, K, ldx, q, d, s);
+  if (per_thread <= 32) return launch_nc<32>(x, M, K, ldx, q, d, s);
+  return launch_nc<0>(x, M, K, ldx, q, d, s);
+}
+
+}  // namespace bl

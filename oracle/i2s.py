@@ -7,11 +7,15 @@ Sources:
   * FairyFuse article, "融合内核设计": ternary indices are stored bit-packed
     with the codes 00, 01, 10 standing for 0, +1, -1.
 
-The code table is the FairyFuse one; the pages give no bit layout, so the
-plainest one is taken: row-major [N][K/4] bytes, weight k of row n sits in
-byte n*(K/4) + k//4 at bits 2*(k%4) .. 2*(k%4)+1 (first weight in the low
-bits). Code 11 is never written; unpacking rejects it. K must be a multiple
-of 4 (no padding rule exists).
+The code table is the FairyFuse one. The pages give no bit order; the
+library's layout is:
+  packed is uint8 [N][K/4]; each row is cut into groups of 16 weights
+  (4 bytes), the last group of a row possibly shorter (4, 8 or 12 weights,
+  i.e. b = 1, 2 or 3 bytes); inside a group of b bytes, weight o is stored in
+  byte (o mod b) at bits 2*(o div b) .. 2*(o div b) + 1.
+For a full group this puts weights 4i .. 4i+3 in field i of bytes 0..3, so a
+shift by 2i and a mask of the group's 32-bit word gives them in byte order.
+Code 11 is never written; unpacking rejects it. K must be a multiple of 4.
 """
 from __future__ import annotations
 
@@ -20,13 +24,23 @@ import numpy as np
 CODE_ZERO = 0b00
 CODE_POS = 0b01
 CODE_NEG = 0b10
-FIELDS_PER_BYTE = 4
+WEIGHTS_PER_BYTE = 4
+GROUP = 16          # weights per full group (one 32-bit word)
 FIELD_BITS = 2
 
 
-def _field_shift(j: int) -> int:
-    """Bit offset of the j-th weight (0..3) within its byte."""
-    return FIELD_BITS * j
+def _field_shift(i: int) -> int:
+    """Bit offset of field i (0..3) within a byte."""
+    return FIELD_BITS * i
+
+
+def _groups(K: int):
+    """(first weight, number of bytes b) of each group of a row of K weights."""
+    out = []
+    for k0 in range(0, K, GROUP):
+        L = min(GROUP, K - k0)
+        out.append((k0, L // WEIGHTS_PER_BYTE))
+    return out
 
 
 def pack_i2s(tern: np.ndarray) -> np.ndarray:
@@ -35,30 +49,35 @@ def pack_i2s(tern: np.ndarray) -> np.ndarray:
     if t.ndim != 2:
         raise ValueError("ternary weights must be 2-D [N][K]")
     N, K = t.shape
-    if K % FIELDS_PER_BYTE:
+    if K % WEIGHTS_PER_BYTE:
         raise ValueError("K must be a multiple of 4")
     if not np.all((t == -1) | (t == 0) | (t == 1)):
         raise ValueError("weights must be in {-1, 0, +1}")
     codes = np.full(t.shape, CODE_ZERO, dtype=np.uint8)
     codes[t == 1] = CODE_POS
     codes[t == -1] = CODE_NEG
-    c = codes.reshape(N, K // FIELDS_PER_BYTE, FIELDS_PER_BYTE)
-    out = np.zeros((N, K // FIELDS_PER_BYTE), dtype=np.uint8)
-    for j in range(FIELDS_PER_BYTE):
-        out |= (c[:, :, j] << np.uint8(_field_shift(j))).astype(np.uint8)
+    out = np.zeros((N, K // WEIGHTS_PER_BYTE), dtype=np.uint8)
+    for k0, b in _groups(K):
+        g = codes[:, k0:k0 + 4 * b].reshape(N, 4, b)   # [row][field i][byte j], o = i*b + j
+        byte0 = k0 // WEIGHTS_PER_BYTE
+        for i in range(4):
+            out[:, byte0:byte0 + b] |= (g[:, i, :] << np.uint8(_field_shift(i))).astype(np.uint8)
     return out
 
 
 def unpack_i2s(packed: np.ndarray, K: int) -> np.ndarray:
     """uint8 [N][K/4] -> int8 {-1,0,+1} [N][K]; raises on the unused code 11."""
     p = np.asarray(packed, dtype=np.uint8)
-    if p.ndim != 2 or p.shape[1] * FIELDS_PER_BYTE != K:
+    if K % WEIGHTS_PER_BYTE or p.ndim != 2 or p.shape[1] * WEIGHTS_PER_BYTE != K:
         raise ValueError("packed shape does not match K")
     N = p.shape[0]
-    out = np.zeros((N, K // FIELDS_PER_BYTE, FIELDS_PER_BYTE), dtype=np.int8)
-    for j in range(FIELDS_PER_BYTE):
-        f = (p >> np.uint8(_field_shift(j))) & np.uint8(0b11)
-        if np.any(f == 0b11):
-            raise ValueError("invalid I2_S code 11")
-        out[:, :, j] = np.where(f == CODE_POS, 1, np.where(f == CODE_NEG, -1, 0))
-    return out.reshape(N, K)
+    out = np.zeros((N, K), dtype=np.int8)
+    for k0, b in _groups(K):
+        byte0 = k0 // WEIGHTS_PER_BYTE
+        for i in range(4):
+            f = (p[:, byte0:byte0 + b] >> np.uint8(_field_shift(i))) & np.uint8(0b11)
+            if np.any(f == 0b11):
+                raise ValueError("invalid I2_S code 11")
+            vals = np.where(f == CODE_POS, 1, np.where(f == CODE_NEG, -1, 0))
+            out[:, k0 + i * b:k0 + (i + 1) * b] = vals
+    return out

@@ -1,0 +1,120 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/bitlinear.h declares, and rejects bad arguments before launching
+anything (every call below fails validation, so no kernel is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mpgemm_token_absmax_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+A16 = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
+B16 = 0x20000
+C16 = 0x30000
+D16 = 0x40000
+E16 = 0x50000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bl_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libbitlinear.so not built (run __graft_entry__.build())")
+    return L.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(L.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bl_abi_version() == 1
+    for s in (L.BL_OK, L.BL_ERR_NULL, L.BL_ERR_SHAPE, L.BL_ERR_ALIGN, L.BL_ERR_DTYPE,
+              L.BL_ERR_WORKSPACE, L.BL_ERR_HIP):
+        assert lib.bl_status_string(s)
+    assert lib.bl_status_string(12345) == b"unknown status"
+
+
+def test_quantize_validation(lib):
+    f = lib.bl_quantize_act
+    assert f(A16, 2, 6, 6, B16, C16, None) == L.BL_ERR_SHAPE        # K % 4
+    assert f(A16, -1, 8, 8, B16, C16, None) == L.BL_ERR_SHAPE
+    assert f(A16, 2, 8, 4, B16, C16, None) == L.BL_ERR_SHAPE        # ldx < K
+    assert f(None, 2, 8, 8, B16, C16, None) == L.BL_ERR_NULL
+    assert f(A16, 2, 8, 8, None, C16, None) == L.BL_ERR_NULL
+    assert f(A16, 2, 8, 8, B16, None, None) == L.BL_ERR_NULL
+    assert f(A16 + 8, 2, 8, 8, B16, C16, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 8, 8, B16 + 4, C16, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 8, 8, B16, C16 + 2, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 8, 10, B16, C16, None) == L.BL_ERR_ALIGN       # ldx % 4
+    assert f(None, 0, 8, 8, None, None, None) == L.BL_OK            # M == 0: nothing to do
+
+
+def test_pack_validation(lib):
+    f = lib.bl_pack_i2s
+    ws = lib.bl_pack_i2s_workspace(64, 64)
+    assert ws > 0 and ws % 16 == 0
+    assert lib.bl_pack_i2s_workspace(0, 64) == 0
+    assert f(A16, 0, 4, 6, B16, C16, D16, ws, None) == L.BL_ERR_SHAPE
+    assert f(A16, 7, 4, 8, B16, C16, D16, ws, None) == L.BL_ERR_DTYPE
+    assert f(A16, 0, 0, 8, B16, C16, D16, ws, None) == L.BL_ERR_SHAPE   # empty fp32: no gamma
+    assert f(None, 0, 64, 64, B16, C16, D16, ws, None) == L.BL_ERR_NULL
+    assert f(A16, 0, 64, 64, B16, None, D16, ws, None) == L.BL_ERR_NULL
+    assert f(A16, 0, 64, 64, B16, C16, None, ws, None) == L.BL_ERR_WORKSPACE
+    assert f(A16, 0, 64, 64, B16, C16, D16, ws - 1, None) == L.BL_ERR_WORKSPACE
+    assert f(A16 + 4, 0, 64, 64, B16, C16, D16, ws, None) == L.BL_ERR_ALIGN
+    assert f(A16, 0, 64, 64, B16 + 1, C16, D16, ws, None) == L.BL_ERR_ALIGN
+    assert f(A16, 0, 1 << 30, 1 << 10, B16, C16, D16, 1 << 40, None) == L.BL_ERR_SHAPE
+    assert f(None, 1, 64, 64, B16, None, None, 0, None) == L.BL_ERR_NULL
+    assert f(A16, 1, 64, 64, B16 + 8, None, None, 0, None) == L.BL_ERR_ALIGN
+    assert f(None, 1, 0, 64, None, None, None, 0, None) == L.BL_OK     # empty ternary pack
+
+
+@pytest.mark.parametrize("name", ["bl_gemv", "bl_gemm"])
+def test_matmul_validation(lib, name):
+    fn = getattr(lib, name)
+
+    def call(packed=A16, gamma=B16, N=64, K=64, q=C16, d=D16, M=2, y=E16, yt=1):
+        if name == "bl_gemv":
+            return fn(packed, gamma, N, K, q, d, M, y, yt, None)
+        return fn(packed, gamma, N, K, q, d, M, y, yt, None, 0, None)
+
+    assert call(K=6) == L.BL_ERR_SHAPE
+    assert call(N=-1) == L.BL_ERR_SHAPE
+    assert call(M=-3) == L.BL_ERR_SHAPE
+    assert call(yt=3) == L.BL_ERR_DTYPE
+    assert call(y=None) == L.BL_ERR_NULL
+    assert call(packed=None) == L.BL_ERR_NULL
+    assert call(q=None) == L.BL_ERR_NULL
+    assert call(gamma=None) == L.BL_ERR_NULL
+    assert call(d=None) == L.BL_ERR_NULL
+    assert call(packed=A16 + 4) == L.BL_ERR_ALIGN
+    assert call(q=C16 + 1) == L.BL_ERR_ALIGN
+    assert call(y=E16 + 8) == L.BL_ERR_ALIGN
+    assert call(gamma=B16 + 2) == L.BL_ERR_ALIGN
+    assert call(K=132108) == L.BL_ERR_SHAPE           # 127*K >= 2^24 with a float output
+    assert call(M=0) == L.BL_OK and call(N=0) == L.BL_OK
+    assert call(M=0, y=None, packed=None, q=None) == L.BL_OK
+    if name == "bl_gemv":
+        assert call(M=17) == L.BL_ERR_SHAPE           # gemv covers M <= 16 only
+    else:
+        assert lib.bl_gemm_workspace(2048, 8192, 8192) == 0
+
+
+def test_status_to_exception(lib):
+    with pytest.raises(L.BitLinearError) as e:
+        L.check("bl_gemv", L.BL_ERR_SHAPE)
+    assert e.value.status == L.BL_ERR_SHAPE
+    assert "shape" in str(e.value)

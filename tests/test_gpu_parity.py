@@ -1,0 +1,385 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: bit-exact packed bytes, gamma, quantized activations, int32 accumulators
+and fp32 outputs (the fp32 epilogue fl32(fl32(acc) * fl32(gamma*d)) is a
+defined single-rounding formula); fp32 also within 1e-6 relative of the fp64
+y_ref = acc*gamma*d; bf16 bit-exact to the round-to-nearest-even of that fp32
+value and within 1 bf16 ulp of y_ref rounded directly from fp64.
+
+Inputs come from the seeded generators in workloads.py, never from the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GAMMA = np.float32(W.GAMMA_DRAWN)
+
+
+def _bl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mpgemm_token_absmax_amd as bl
+    bl.lib()                   # fails loudly if the library is missing
+    return bl
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def check_outputs(acc_ref, gamma, d, y_i32=None, y_f32=None, y_bf16=None, rows=None, cols=None):
+    """Compare GPU outputs (the full [M][N] arrays, or the entries (rows, cols))
+    with the oracle's accumulators acc_ref ([M][N], or [S] at the entries)."""
+    if rows is None:
+        A, D = np.asarray(acc_ref), np.asarray(d)
+        sel = (lambda a: a)
+    else:
+        A, D = np.asarray(acc_ref)[:, None], np.asarray(d)[rows]
+        sel = (lambda a: a[rows, cols][:, None])
+    if y_i32 is not None:
+        assert np.array_equal(sel(y_i32).astype(np.int64), A), "int32 accumulators differ"
+    y32_ref = oracle.dequant_f32(A, gamma, D)
+    y64_ref = oracle.dequant_f64(A, gamma, D)
+    if y_f32 is not None:
+        got = sel(y_f32)
+        assert np.array_equal(got.view(np.uint32), y32_ref.view(np.uint32)), "fp32 outputs differ"
+        assert np.array_equal(y64_ref == 0, got == 0)
+        nz = y64_ref != 0
+        rel = np.abs(got.astype(np.float64)[nz] - y64_ref[nz]) / np.abs(y64_ref[nz])
+        assert rel.size == 0 or rel.max() <= 1e-6, rel.max()
+    if y_bf16 is not None:
+        got = sel(y_bf16)
+        exp = oracle.round_f64_to_bf16_bits(y32_ref.astype(np.float64))
+        assert np.array_equal(got, exp), "bf16 outputs differ from RNE(fp32)"
+        direct = oracle.round_f64_to_bf16_bits(y64_ref)
+        g_i = got.astype(np.int32)
+        r_i = direct.astype(np.int32)
+        same_sign = (g_i & 0x8000) == (r_i & 0x8000)
+        within = np.abs((g_i & 0x7FFF) - (r_i & 0x7FFF)) <= 1
+        assert np.all((g_i == r_i) | (same_sign & within)), "bf16 more than 1 ulp from y_ref"
+
+
+def run_all_outputs(bl, fn, packed_d, gamma_d, q_d, d_d):
+    outs = {}
+    for name in ("i32", "f32", "bf16"):
+        outs[name] = host(fn(packed_d, gamma_d, q_d, d_d, out_dtype=name))
+    return outs
+
+
+# ---------------------------------------------------------------------------
+# quantize_act
+# ---------------------------------------------------------------------------
+
+QUANT_SHAPES = [(1, 4), (1, 64), (3, 260), (16, 1024), (17, 2560), (5, 6912), (4, 11008),
+                (2, 28672), (3, 36000), (64, 4096), (1, 8)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES, ids=[f"M{m}K{k}" for m, k in QUANT_SHAPES])
+def test_quantize_parity(M, K):
+    bl = _bl()
+    say(f"quantize M={M} K={K}")
+    x = W.activations_bf16(100 + M * 7 + K, M, K, outlier_frac=0.01, outlier_scale=20.0)
+    q_ref, d_ref = oracle.quantize_act_absmax(x)
+    q, d = bl.quantize_act(dev_bf16(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+
+
+def test_quantize_special_rows_and_stride():
+    bl = _bl()
+    say("quantize special rows + ldx > K")
+    import pins
+    rows = []
+    for name in ("e1_quant_basic.json", "e2_quant_ties.json"):
+        g = pins.golden(name)
+        r = np.zeros(8, dtype=np.float32)
+        r[:len(g["x"][0])] = g["x"][0]
+        rows.append(r)
+    rows += [np.zeros(8, np.float32), np.full(8, -3.0, np.float32),
+             np.array([0, 0, 0, 0, 0, 9, 0, 0], np.float32), np.full(8, 2.0**-100, np.float32),
+             np.array([1e30, -1e30, 1, -1, 0, 2, 3, 4], np.float32)]
+    x = W.f32_to_bf16_bits(np.stack(rows))
+    # embed in a wider buffer: row stride 24 elements
+    wide = np.zeros((x.shape[0], 24), dtype=np.uint16)
+    wide[:, 8:16] = x
+    q_ref, d_ref = oracle.quantize_act_absmax(x)
+    xd = dev_bf16(wide)[:, 8:16]            # base 16-byte aligned, rows 8-byte aligned
+    assert xd.stride(0) == 24
+    q, d = bl.quantize_act(xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+    # the golden q values themselves
+    assert host(q)[0, :4].tolist() == [-127, 32, 16, 95]
+    assert host(q)[1, :6].tolist() == [127, 62, -62, 0, 2, -2]
+
+
+def test_quantize_empty():
+    bl = _bl()
+    say("quantize empty")
+    q, d = bl.quantize_act(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"))
+    assert q.shape == (0, 64) and d.shape == (0,)
+    q, d = bl.quantize_act(torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert host(d).tolist() == [0.0, 0.0, 0.0]
+
+
+# ---------------------------------------------------------------------------
+# pack_i2s
+# ---------------------------------------------------------------------------
+
+PACK_SHAPES = [(1, 4), (3, 12), (2, 20), (16, 64), (17, 260), (640, 2560), (1024, 1024),
+               (33, 4096)]
+
+
+@pytest.mark.parametrize("N,K", PACK_SHAPES, ids=[f"N{n}K{k}" for n, k in PACK_SHAPES])
+def test_pack_f32_parity(N, K):
+    bl = _bl()
+    say(f"pack f32 N={N} K={K}")
+    w = W.weights_f32_normal(200 + N + K, N, K)
+    t_ref, g_ref = oracle.ternarize_absmean(w)
+    p_ref = oracle.pack_i2s(t_ref)
+    packed, gamma = bl.pack_i2s(dev(w))
+    torch.cuda.synchronize()
+    assert host(gamma).view(np.uint32)[0] == np.float32(g_ref).view(np.uint32)
+    assert np.array_equal(host(packed), p_ref)
+
+
+def _tiles_with_ties(N, K, seed):
+    """Rows whose |w| values are a permutation of a pattern with mean exactly 1,
+    so gamma = 1, t = 0.5 and every +-0.5 sits exactly on the threshold."""
+    base = np.array([2.0, 0.5, 0.5, 1.0, 0.0, 0.5, 1.5, 2.0], dtype=np.float32)  # mean 1
+    r = W.rng(seed)
+    w = np.empty((N, K), dtype=np.float32)
+    for n in range(N):
+        row = np.resize(base, K)
+        w[n] = r.permutation(row) * np.where(r.random(K) < 0.5, -1, 1)
+    return w
+
+
+@pytest.mark.parametrize("case", ["ties", "huge_small", "subnormal", "spread", "golden_e3",
+                                  "golden_e4"])
+def test_pack_f32_adversarial(case):
+    bl = _bl()
+    say(f"pack f32 adversarial {case}")
+    r = W.rng(31)
+    if case == "ties":
+        w = _tiles_with_ties(12, 64, 5)
+    elif case == "huge_small":
+        w = np.array([[2.0**60] + [1.0] * 1023 + [2.0**-20] * 64], dtype=np.float32)
+    elif case == "subnormal":
+        w = np.array([[1e-45, 3e-45, 1.0, 2.0**-126, 2.0**-130, 0.1, 0.3, 0.0]], np.float32)
+    elif case == "spread":
+        w = (r.standard_normal((4, 500)) * np.exp2(r.integers(-60, 60, (4, 500)))).astype(
+            np.float32)
+    elif case == "golden_e3":
+        w = np.array([[7.0, 1.0, 0.0, 0.0]], np.float32)
+    else:  # e4's 12 weights laid out as 3 x 4
+        w = np.array([[0.75, -0.25, 0.125, -1.0], [0.0, 0.375, -0.75, 0.25],
+                      [-0.125, 1.0, 0.0, -0.375]], np.float32)
+    t_ref, g_ref = oracle.ternarize_absmean(w)
+    packed, gamma = bl.pack_i2s(dev(w))
+    torch.cuda.synchronize()
+    assert host(gamma).view(np.uint32)[0] == np.float32(g_ref).view(np.uint32), (
+        host(gamma)[0], g_ref)
+    assert np.array_equal(host(packed), oracle.pack_i2s(t_ref))
+    if case == "ties":
+        assert g_ref == 1.0 and np.any(np.abs(w) == 0.5)
+
+
+@pytest.mark.parametrize("N,K", [(1, 4), (5, 12), (7, 36), (64, 256), (300, 2560)])
+def test_pack_ternary_parity(N, K):
+    bl = _bl()
+    say(f"pack ternary N={N} K={K}")
+    t = W.ternary_drawn(300 + N, N, K, 0.4)
+    packed = bl.pack_i2s(dev(t))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(packed), oracle.pack_i2s(t))
+    # values outside {-1, 0, 1} are taken by their sign
+    wide = (t.astype(np.int16) * W.rng(7).integers(1, 100, t.shape)).clip(-128, 127).astype(
+        np.int8)
+    packed2 = bl.pack_i2s(dev(wide))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(packed2), oracle.pack_i2s(np.sign(wide).astype(np.int8)))
+
+
+# ---------------------------------------------------------------------------
+# gemv / gemm on generated int8 activations
+# ---------------------------------------------------------------------------
+
+def _mm_case(M, N, K, seed, zero_rows=()):
+    q = W.int8_codes(seed, M, K, zero_rows)
+    q[0, :min(K, 8)] = 127              # extremes
+    if M > 1:
+        q[1, :min(K, 8)] = -127
+    t = W.ternary_drawn(seed + 1, N, K, 0.35)
+    if N > 2:
+        t[2, :] = 1                       # all +1 row: acc = sum of q
+    d = W.positive_scales(seed + 2, M, zero_rows)
+    return q, t, d
+
+
+def _run_mm(bl, fn_name, M, N, K, seed, zero_rows=()):
+    say(f"{fn_name} M={M} N={N} K={K} seed={seed}")
+    q, t, d = _mm_case(M, N, K, seed, zero_rows)
+    acc = oracle.mpgemm_acc(q, t)
+    packed = bl.pack_i2s(dev(t))
+    gd = dev(np.array([GAMMA], np.float32))
+    fn = getattr(bl, fn_name)
+    outs = run_all_outputs(bl, fn, packed, gd, dev(q), dev(d))
+    torch.cuda.synchronize()
+    check_outputs(acc, GAMMA, d, outs["i32"], outs["f32"], outs["bf16"])
+    return outs
+
+
+GEMV_CASES = [(1, 1, 64), (1, 5, 4), (1, 17, 12), (1, 100, 320), (1, 640, 2560), (2, 33, 256),
+              (3, 16, 1024), (4, 129, 576), (5, 64, 2560), (8, 300, 260), (15, 17, 6912),
+              (16, 128, 4096), (16, 3, 64), (1, 2049, 256), (16, 2100, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_CASES, ids=[f"M{m}N{n}K{k}" for m, n, k in GEMV_CASES])
+def test_gemv_parity(M, N, K):
+    bl = _bl()
+    _run_mm(bl, "gemv", M, N, K, seed=1000 + M * 31 + N * 7 + K, zero_rows=(M - 1,) if M > 2
+            else ())
+
+
+GEMM_CASES = [(17, 1, 64), (17, 130, 256), (33, 17, 4), (64, 64, 2560), (100, 640, 320),
+              (128, 128, 256), (129, 257, 576), (300, 100, 1024), (512, 640, 2560),
+              (65, 48, 6912), (1, 40, 256), (16, 40, 256), (200, 33, 260)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES, ids=[f"M{m}N{n}K{k}" for m, n, k in GEMM_CASES])
+def test_gemm_parity(M, N, K):
+    bl = _bl()
+    _run_mm(bl, "gemm", M, N, K, seed=2000 + M * 31 + N * 7 + K, zero_rows=(M - 2,) if M > 3
+            else ())
+
+
+def test_gemv_equals_gemm_and_deterministic():
+    bl = _bl()
+    say("gemv == gemm, repeat determinism")
+    for M in (1, 4, 16):
+        q, t, d = _mm_case(M, 333, 1024, 77)
+        packed = bl.pack_i2s(dev(t))
+        gd = dev(np.array([GAMMA], np.float32))
+        a = host(bl.gemv(packed, gd, dev(q), dev(d), out_dtype="f32"))
+        b = host(bl.gemm(packed, gd, dev(q), dev(d), out_dtype="f32"))
+        torch.cuda.synchronize()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    q, t, d = _mm_case(300, 700, 2560, 78)
+    packed = bl.pack_i2s(dev(t))
+    gd = dev(np.array([GAMMA], np.float32))
+    y1 = host(bl.gemm(packed, gd, dev(q), dev(d), out_dtype="bf16"))
+    y2 = host(bl.gemm(packed, gd, dev(q), dev(d), out_dtype="bf16"))
+    assert np.array_equal(y1, y2)
+
+
+def test_k_zero_and_empty():
+    bl = _bl()
+    say("K == 0 and empty M/N")
+    q = torch.zeros((3, 0), dtype=torch.int8, device="cuda")
+    packed = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    gd = dev(np.array([GAMMA], np.float32))
+    dd = dev(np.ones(3, np.float32))
+    for fn in (bl.gemv, bl.gemm):
+        y = fn(packed, gd, q, dd, out_dtype="f32")
+        torch.cuda.synchronize()
+        assert np.all(host(y) == 0) and y.shape == (3, 5)
+    y = bl.gemm(torch.zeros((0, 16), dtype=torch.uint8, device="cuda"), gd,
+                torch.zeros((4, 64), dtype=torch.int8, device="cuda"), dd[:1].repeat(4))
+    assert y.shape == (4, 0)
+
+
+# ---------------------------------------------------------------------------
+# full pipelines at the layer shapes
+# ---------------------------------------------------------------------------
+
+def _pipeline(bl, cfg, proj, M, p_zero_override=None, sample=None):
+    """x -> quantize -> (pack) -> gemv/gemm, each stage checked against the oracle."""
+    inp = W.proj_inputs(cfg, proj, M, p_zero_override=p_zero_override)
+    say(f"config {cfg.cid} {proj.name} M={M} K={proj.K} N={proj.N}")
+    q_ref, d_ref = oracle.quantize_act_absmax(inp.x_bf16)
+    q, d = bl.quantize_act(dev_bf16(inp.x_bf16))
+    if inp.w_f32 is not None:
+        t_ref, g_ref = oracle.ternarize_absmean(inp.w_f32)
+        packed, gd = bl.pack_i2s(dev(inp.w_f32))
+    else:
+        t_ref, g_ref = inp.w_tern, np.float32(inp.gamma)
+        packed = bl.pack_i2s(dev(inp.w_tern))
+        gd = dev(np.array([g_ref], np.float32))
+    fn = bl.gemv if M <= 16 else bl.gemm
+    y = fn(packed, gd, q, d, out_dtype="bf16")
+    y32 = fn(packed, gd, q, d, out_dtype="f32")
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+    if inp.w_f32 is not None:
+        assert host(gd).view(np.uint32)[0] == np.float32(g_ref).view(np.uint32)
+        assert np.array_equal(host(packed), oracle.pack_i2s(t_ref))
+    if sample is None:
+        acc = oracle.mpgemm_acc(q_ref, t_ref) if M * proj.N * proj.K < 4e8 else \
+            oracle.mpgemm_acc_f64blas(q_ref, t_ref)
+        check_outputs(acc, g_ref, d_ref, None, host(y32), host(y))
+    else:
+        r = W.rng(sample)
+        rows = np.concatenate([r.integers(0, M, 256), [0, M - 1]])
+        cols = np.concatenate([r.integers(0, proj.N, 256), [proj.N - 1, 0]])
+        acc = oracle.mpgemm_acc_entries(q_ref, t_ref, rows, cols)
+        check_outputs(acc, g_ref, d_ref, None, host(y32), host(y), rows=rows, cols=cols)
+        # two full tokens and two full output features
+        yb = host(y32)
+        for tok in (0, M // 2):
+            acc_row = oracle.mpgemm_acc(q_ref[tok:tok + 1], t_ref)
+            check_outputs(acc_row, g_ref, d_ref[tok:tok + 1], None, yb[tok:tok + 1])
+        for n in (1, proj.N // 3):
+            acc_col = oracle.mpgemm_acc(q_ref, t_ref[n:n + 1])
+            check_outputs(acc_col, g_ref, d_ref, None, yb[:, n:n + 1])
+
+
+@pytest.mark.parametrize("cid,M", [(1, 1), (2, 1), (4, 1), (4, 4), (4, 16), (3, 512)])
+def test_layer_configs(cid, M):
+    bl = _bl()
+    cfg = W.CONFIGS[cid]
+    for proj in cfg.projs:
+        _pipeline(bl, cfg, proj, M)
+
+
+def test_config4_sparse_variant():
+    """7B layer with ternary weights drawn at P(0) = 0.65."""
+    bl = _bl()
+    cfg = W.CONFIGS[4]
+    for proj in cfg.projs:
+        _pipeline(bl, cfg, proj, 1, p_zero_override=0.65)
+
+
+def test_config5_sampled():
+    """100B-class layer at 2048 tokens: every stage at full size; the GEMM checked
+    on sampled entries, two full tokens and two full output features."""
+    bl = _bl()
+    cfg = W.CONFIGS[5]
+    for proj in cfg.projs:
+        _pipeline(bl, cfg, proj, 2048, sample=5000 + proj.index)

@@ -23,6 +23,7 @@ MUTATIONS = {
                             lambda w: abs(float(np.sum(w.astype(np.float64))))),
     "pack_swap_codes": (oracle.i2s, "CODE_POS", 0b10),
     "pack_bit_order_reversed": (oracle.i2s, "_field_shift", lambda j: 2 * (3 - j)),
+    "pack_plain_byte_order": (oracle.i2s, "GROUP", 4),
     "dot_missing_transpose": (oracle.dot, "_as_columns", lambda w: w.astype(np.int64)),
     "dot_drops_last_k": (oracle.dot, "_as_columns",
                          lambda w: np.concatenate([w[:, :-1], 0 * w[:, -1:]], axis=1)

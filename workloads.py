@@ -165,3 +165,20 @@ def small_case(seed: int, M: int, N: int, K: int, kind: str = "f32_normal",
     if kind == "f32_normal":
         return x, weights_f32_normal(2 * seed, N, K)
     return x, ternary_drawn(2 * seed, N, K, p_zero)
+
+
+def int8_codes(seed: int, M: int, K: int, zero_rows=()) -> np.ndarray:
+    """int8 [M][K] uniform in [-127, 127] (stand-in quantized activations)."""
+    q = rng(seed).integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    for t in zero_rows:
+        q[t] = 0
+    return q
+
+
+def positive_scales(seed: int, M: int, zero_rows=()) -> np.ndarray:
+    """fp32 [M] per-token scales in [0.004, 0.06) (zero for the listed rows)."""
+    d = (rng(seed).random(M, dtype=np.float32) * np.float32(0.056) + np.float32(0.004))
+    d = d.astype(np.float32)
+    for t in zero_rows:
+        d[t] = 0
+    return d
