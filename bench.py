@@ -7,16 +7,17 @@ BitNet-2B-like layer at batch 1 (hidden 2560, k/v 640, FFN 6912). One step =
 one pass of the per-token hot path over that layer: for each of the 7
 projections (q, k, v, o, gate, up, down) the per-token absmax int8
 quantization of its bf16 input and the I2_S GEMV with the bf16 dequant fused
-into the store. Weight packing is the offline conversion and is done once
-before timing. Steps rotate over R distinct copies of the layer's packed
+into the store, issued as one fused launch per group of projections that do
+not depend on each other in a decoder layer: {q,k,v}, {o}, {gate,up}, {down}.
+Weight packing is the offline conversion and is done once before timing. Steps rotate over R distinct copies of the layer's packed
 weights (R * 17.4 MB > the 256 MB Infinity Cache), so every step streams its
 weights from HBM. Steps are replayed from HIP graphs (captured through
 torch.cuda.CUDAGraph) so host launch cost is not timed.
 
 Also reported on the same JSON line:
-  roofline      the GEMV kernel alone: algorithmic packed bytes per launch over
-                its average launch duration (HIP events around graph replays of
-                GEMV launches only), against 8 TB/s;
+  roofline      the fused decode kernel: algorithmic packed bytes per launch
+                over its average launch duration (HIP events around graph
+                replays on the replay stream), against 8 TB/s;
   gemm          prefill on the 100B-class layer (2048 tokens, hidden 8192,
                 FFN 28672, k/v 1024): 2*M*N*K int8 ops per second over the 7
                 projections (quantize + GEMM), against 5.0 POP/s dense int8;
@@ -78,52 +79,61 @@ def main():
     M = 1
     R = max(1, args.rotate)
     log(f"setup decode: {cfg.name}, {R} layer copies")
-    layers = []        # layers[r][p] = packed tensor
-    gammas, xs, qs, ds, ys = [], [], [], [], []
-    base = []
+    inputs = {}
     for proj in cfg.projs:
         inp = W.proj_inputs(cfg, proj, M)
-        packed = bl.pack_i2s(to_dev(inp.w_tern))
-        base.append(packed)
-        gammas.append(to_dev(np.array([inp.gamma], np.float32)))
-        xs.append(to_dev(inp.x_bf16.view(np.int16)).view(torch.bfloat16))
-        qs.append(torch.empty((M, proj.K), dtype=torch.int8, device=dev))
-        ds.append(torch.empty((M,), dtype=torch.float32, device=dev))
-        ys.append(torch.empty((M, proj.N), dtype=torch.bfloat16, device=dev))
-    for r in range(R):
-        layers.append([b.clone() for b in base])
+        inputs[proj.name] = dict(
+            packed=bl.pack_i2s(to_dev(inp.w_tern)),
+            gamma=to_dev(np.array([inp.gamma], np.float32)),
+            x=to_dev(inp.x_bf16.view(np.int16)).view(torch.bfloat16),
+            y=torch.empty((M, proj.N), dtype=torch.bfloat16, device=dev),
+            q=torch.empty((M, proj.K), dtype=torch.int8, device=dev),
+            d=torch.empty((M,), dtype=torch.float32, device=dev))
     torch.cuda.synchronize()
     step_bytes = cfg.packed_bytes
+    # the projections of a decoder layer that do not depend on each other
+    GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    layers = []            # layers[r] = fused decode launches of layer copy r
+    for r in range(R):
+        launches = []
+        for names in GROUPS:
+            probs = []
+            for nm in names:
+                e = inputs[nm]
+                packed = e["packed"] if r == 0 else e["packed"].clone()
+                probs.append(dict(packed=packed, gamma=e["gamma"], x=e["x"], y=e["y"], name=nm))
+            launches.append(bl.DecodeGroup(probs))
+        layers.append(launches)
+    torch.cuda.synchronize()
 
     def step(r):
-        for p in range(len(cfg.projs)):
-            bl.quantize_act(xs[p], qs[p], ds[p])
-            bl.gemv(layers[r][p], gammas[p], qs[p], ds[p], out_dtype="bf16", out=ys[p])
+        for launch in layers[r]:
+            launch()
 
-    def gemv_only(r):
-        for p in range(len(cfg.projs)):
-            bl.gemv(layers[r][p], gammas[p], qs[p], ds[p], out_dtype="bf16", out=ys[p])
+    def step_unfused(r):        # 7 x (bl_quantize_act + bl_gemv), for comparison
+        for launch in layers[r]:
+            for p in launch.problems:
+                e = inputs[p["name"]]
+                bl.quantize_act(p["x"], e["q"], e["d"])
+                bl.gemv(p["packed"], p["gamma"], e["q"], e["d"], out_dtype="bf16", out=p["y"])
 
-    # eager warm-up (also loads the code objects) before capture
-    for r in range(R):
+    for r in range(R):          # eager warm-up (loads the code objects) before capture
         step(r)
+        step_unfused(r)
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all, stream=stream):
-        for r in range(R):
-            step(r)
-    g_one = []
-    for r in range(R):
+
+    def capture(fn, rs):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            step(r)
-        g_one.append(g)
-    g_gemv = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_gemv, stream=stream):
-        for r in range(R):
-            gemv_only(r)
+            for r in rs:
+                fn(r)
+        return g
+
+    g_all = capture(step, range(R))
+    g_one = [capture(step, [r]) for r in range(R)]
+    g_unfused = capture(step_unfused, range(R))
     torch.cuda.synchronize()
 
     def run_steps(n):
@@ -149,22 +159,32 @@ def main():
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"decode: {ms_step * 1e3:.2f} us/step, {gbs:.1f} GB/s packed")
 
-    # GEMV kernel alone: graph replays on the capture stream, events on that stream
+    # The dominant kernel is the fused decode kernel itself (the step is made of
+    # its launches): average launch duration from events on the replay stream.
     reps = max(4, args.steps // R)
     with torch.cuda.stream(stream):
-        g_gemv.replay()
+        g_all.replay()
         k0 = torch.cuda.Event(enable_timing=True)
         k1 = torch.cuda.Event(enable_timing=True)
         k0.record(stream)
         for _ in range(reps):
-            g_gemv.replay()
+            g_all.replay()
         k1.record(stream)
+        u0 = torch.cuda.Event(enable_timing=True)
+        u1 = torch.cuda.Event(enable_timing=True)
+        g_unfused.replay()
+        u0.record(stream)
+        for _ in range(reps):
+            g_unfused.replay()
+        u1.record(stream)
     torch.cuda.synchronize()
-    launches = reps * R * len(cfg.projs)
+    launches = reps * R * len(GROUPS)
     us_launch = k0.elapsed_time(k1) * 1e3 / launches
-    bytes_launch = step_bytes / len(cfg.projs)
+    bytes_launch = step_bytes / len(GROUPS)
     gemv_gbs = bytes_launch / (us_launch * 1e-6) / 1e9
-    log(f"gemv kernel: {us_launch:.2f} us/launch avg, {gemv_gbs:.1f} GB/s")
+    us_unfused = u0.elapsed_time(u1) * 1e3 / (reps * R)
+    log(f"fused decode kernel: {us_launch:.2f} us/launch avg, {gemv_gbs:.1f} GB/s; "
+        f"unfused 7x(quantize+gemv): {us_unfused:.2f} us/step")
 
     result = {
         "metric": "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM int8 TOPS (% peak)",
@@ -181,14 +201,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": M, "hidden": 2560, "ffn": 6912, "kv": 640,
                    "layer_copies": R, "packed_bytes_per_step": step_bytes,
-                   "step": "7x (quantize bf16 -> int8 + I2_S GEMV -> bf16)",
-                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+                   "step": "4 fused launches {q,k,v},{o},{gate,up},{down}: per-token absmax "
+                           "int8 quantize + I2_S GEMV + bf16 dequant",
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "unfused_us_per_step": round(us_unfused, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_gemv_i2s", "us_per_launch": round(us_launch, 3),
-                     "bytes_per_launch": bytes_launch},
+                     "kernel": "k_gemv_i2s (fused decode group)",
+                     "us_per_launch": round(us_launch, 3), "bytes_per_launch": bytes_launch},
     }
-    del layers, g_all, g_one, g_gemv
+    del layers, g_all, g_one, g_unfused
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
@@ -262,13 +284,13 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         log("cpu baseline: oracle on the decode layer")
-        inputs = []
+        host_inputs = []
         for proj in cfg.projs:
             inp = W.proj_inputs(cfg, proj, M)
-            inputs.append((inp, oracle.pack_i2s(inp.w_tern)))
+            host_inputs.append((inp, oracle.pack_i2s(inp.w_tern)))
 
         def oracle_step():
-            for inp, packed in inputs:
+            for inp, packed in host_inputs:
                 q, d = oracle.quantize_act_absmax(inp.x_bf16)
                 t = oracle.unpack_i2s(packed, inp.proj.K)
                 acc = oracle.mpgemm_acc(q, t)

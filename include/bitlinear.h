@@ -160,6 +160,41 @@ int bl_gemm(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
             const int8_t *q, const float *d, int64_t M, void *y, int ytype,
             void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * bl_decode_problem / bl_decode_group -- fused decode BitLinear for a group
+ * of independent projections in ONE launch: per-token absmax int8
+ * quantization of bf16 activations, the I2_S GEMV and the dequant.
+ * Defines: the composition of bl_quantize_act and bl_gemv ([BN] Part A 2.3 /
+ * 4.1, [HB] 1.1-1.2), fused as in [FF] "融合内核设计" (activations loaded,
+ * codes walked, sums accumulated and written in one pass). Results (y, and q
+ * and d when requested) are bit-identical to bl_quantize_act followed by
+ * bl_gemv on the same inputs. Meant for the projections of one decoder layer
+ * that do not depend on each other (e.g. q/k/v, or gate/up).
+ *   problems: HOST array of `count` descriptors (1 <= count <= 8), read during
+ *     the call only; every pointer inside is a device pointer.
+ *   M: tokens, 1 <= M <= 16, shared by all problems.
+ *   per problem: packed uint8 [N][K/4], gamma (device, 1 float), x bf16 [M]
+ *     rows of K values with row stride ldx (ldx >= K, ldx % 4 == 0), y [M][N]
+ *     of type ytype; q (int8 [M][K]) and d (fp32 [M]) are optional outputs
+ *     (NULL: not written). K % 64 == 0 is required (BL_ERR_SHAPE otherwise);
+ *     N == 0 problems are skipped. Outputs must not alias any input or each
+ *     other.
+ */
+typedef struct bl_decode_problem {
+  const uint8_t *packed;
+  const float *gamma;
+  int64_t N;
+  int64_t K;
+  const uint16_t *x;
+  int64_t ldx;
+  int8_t *q;
+  float *d;
+  void *y;
+  int ytype;
+} bl_decode_problem;
+
+int bl_decode_group(const bl_decode_problem *problems, int count, int64_t M, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

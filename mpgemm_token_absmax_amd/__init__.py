@@ -11,16 +11,19 @@ and streams only.
     packed      = pack_i2s(w_ternary_int8)          # pack only (caller keeps gamma)
     y           = gemv(packed, g, q, d)             # M <= 16 tokens
     y           = gemm(packed, g, q, d)             # any M (int8 MFMA)
+    ys          = decode_group([dict(packed=.., gamma=.., x=..), ...])
+                                                    # fused quantize + GEMV, one launch
 """
 from __future__ import annotations
 
 import torch
 
-from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I8,
-                   BitLinearError, check, lib, status_string)
+from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I8, MAX_GROUP,
+                   BitLinearError, DecodeProblem, check, lib, status_string)
 
 __all__ = ["quantize_act", "pack_i2s", "pack_i2s_workspace", "gemv", "gemm",
-           "gemm_workspace", "BitLinearError", "status_string", "lib", "OUT_TYPES"]
+           "gemm_workspace", "decode_group", "DecodeGroup", "BitLinearError", "status_string",
+           "lib", "OUT_TYPES"]
 
 OUT_TYPES = {"i32": (BL_OUT_I32, torch.int32), "f32": (BL_OUT_F32, torch.float32),
              "bf16": (BL_OUT_BF16, torch.bfloat16)}
@@ -137,3 +140,60 @@ def gemm(packed: torch.Tensor, gamma: torch.Tensor, q: torch.Tensor, d: torch.Te
                                    0 if workspace is None else workspace.numel(),
                                    _stream(q.device)))
     return out
+
+
+class DecodeGroup:
+    """A prepared bl_decode_group call: the descriptor array is built once, so
+    repeated calls (or a graph capture) only pass pointers.
+
+    problems: list of dicts with keys packed (uint8 [N][K/4]), gamma (fp32 [1]),
+    x (bf16 [M][K]), and optional y (output), q (int8 [M][K]) and d (fp32 [M])
+    buffers; out_dtype applies to every y that is allocated here."""
+
+    def __init__(self, problems, out_dtype: str = "bf16"):
+        if not 1 <= len(problems) <= MAX_GROUP:
+            raise ValueError(f"1..{MAX_GROUP} problems per group")
+        self.problems = []
+        arr = (DecodeProblem * len(problems))()
+        M = None
+        for i, p in enumerate(problems):
+            packed, x = p["packed"], p["x"]
+            _need(packed, "packed", torch.uint8, 2)
+            _need(x, "x", torch.bfloat16, 2)
+            if x.stride(1) != 1:
+                raise ValueError("x rows must be contiguous")
+            N, KB = packed.shape
+            Mi, K = x.shape
+            if KB * 4 != K:
+                raise ValueError("packed does not match x")
+            M = Mi if M is None else M
+            if Mi != M:
+                raise ValueError("all problems of a group share M")
+            ytype, tdt = OUT_TYPES[p.get("out_dtype", out_dtype)]
+            y = p.get("y")
+            if y is None:
+                y = torch.empty((M, N), dtype=tdt, device=x.device)
+            elif y.dtype != tdt or tuple(y.shape) != (M, N) or not y.is_contiguous():
+                raise ValueError("y has the wrong dtype, shape or layout")
+            q, d, gamma = p.get("q"), p.get("d"), p.get("gamma")
+            arr[i] = DecodeProblem(packed.data_ptr(), _ptr(gamma), N, K, x.data_ptr(),
+                                   x.stride(0), _ptr(q), _ptr(d), y.data_ptr(), ytype)
+            self.problems.append(dict(p, y=y))
+        self.M = M
+        self._arr = arr
+        self._device = problems[0]["x"].device
+
+    @property
+    def outputs(self):
+        return [p["y"] for p in self.problems]
+
+    def __call__(self):
+        check("bl_decode_group", lib().bl_decode_group(self._arr, len(self.problems), self.M,
+                                                       _stream(self._device)))
+        return self.outputs
+
+
+def decode_group(problems, out_dtype: str = "bf16"):
+    """One fused launch: quantize each problem's bf16 x per token, GEMV, dequant.
+    Returns the list of outputs y."""
+    return DecodeGroup(problems, out_dtype)()

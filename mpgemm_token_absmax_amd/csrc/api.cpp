@@ -58,7 +58,7 @@ int bl_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t
   if (M < 0 || K < 0 || K % 4 != 0 || ldx < K) return BL_ERR_SHAPE;
   if (M == 0) return BL_OK;
   if (!d || (K > 0 && (!x || !q))) return BL_ERR_NULL;
-  if (ldx % 4 != 0) return BL_ERR_ALIGN;
+  if (K > 0 && ldx % 4 != 0) return BL_ERR_ALIGN;
   if (!aligned(d, 4)) return BL_ERR_ALIGN;
   if (K > 0 && (!aligned(x, 16) || !aligned(q, 16))) return BL_ERR_ALIGN;
   if (M > INT32_MAX) return BL_ERR_SHAPE;
@@ -116,6 +116,42 @@ int bl_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, con
   (void)ws;
   if (N > (int64_t)UINT32_MAX * 64 || M > (int64_t)65535 * 128) return BL_ERR_SHAPE;
   return hip_status(bl::launch_gemm(packed, gamma, N, K, q, d, M, y, ytype, as_stream(stream)));
+}
+
+int bl_decode_group(const bl_decode_problem* problems, int count, int64_t M, void* stream) {
+  if (count < 0 || count > bl::kMaxGroup || M < 0 || M > kGemvMaxM) return BL_ERR_SHAPE;
+  if (count == 0 || M == 0) return BL_OK;
+  if (!problems) return BL_ERR_NULL;
+  bl::DecodeGroup g{};
+  g.M = (int)M;
+  for (int i = 0; i < count; ++i) {
+    const bl_decode_problem& p = problems[i];
+    if (p.N < 0 || p.K < 0 || p.K % 64 != 0 || p.ldx < p.K) return BL_ERR_SHAPE;
+    if (p.ytype < BL_OUT_I32 || p.ytype > BL_OUT_BF16) return BL_ERR_DTYPE;
+    if (p.ytype != BL_OUT_I32 && p.K > kFp32ExactK) return BL_ERR_SHAPE;
+    if (127 * p.K > INT32_MAX) return BL_ERR_SHAPE;
+    if (p.N == 0) continue;
+    if (!p.y || (p.K > 0 && (!p.packed || !p.x)) || (p.ytype != BL_OUT_I32 && !p.gamma))
+      return BL_ERR_NULL;
+    if (p.ldx % 4 != 0 || !aligned(p.y, 16)) return BL_ERR_ALIGN;
+    if (p.K > 0 && (!aligned(p.packed, 16) || !aligned(p.x, 16))) return BL_ERR_ALIGN;
+    if ((p.q && !aligned(p.q, 16)) || (p.d && !aligned(p.d, 4)) ||
+        (p.gamma && !aligned(p.gamma, 4)))
+      return BL_ERR_ALIGN;
+    bl::DecodeProblem& d = g.p[g.count++];
+    d.packed = p.packed;
+    d.gamma = p.gamma;
+    d.N = p.N;
+    d.K = p.K;
+    d.x = p.x;
+    d.ldx = p.ldx;
+    d.q = p.q;
+    d.d = p.d;
+    d.y = p.y;
+    d.ytype = p.ytype;
+  }
+  if (g.count == 0) return BL_OK;
+  return hip_status(bl::launch_decode_group(g, as_stream(stream)));
 }
 
 }  // extern "C"

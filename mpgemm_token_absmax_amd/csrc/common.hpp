@@ -54,6 +54,28 @@ __device__ __forceinline__ float dequant(int acc, float c) {
   return __fmul_rn((float)acc, c);
 }
 
+// Per-token absmax int8 quantization arithmetic, shared by bl_quantize_act and
+// the fused decode kernel so both produce identical codes:
+//   max of |x| taken on bf16 magnitude bits (for finite values the bit order of
+//   |x| is the value order); s = fl32(127 / m); q = clamp(rne(fl32(x * s)), +-127).
+__device__ __forceinline__ uint32_t absmax4_bf16(uint2 v) {
+  const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
+  return max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16));
+}
+
+__device__ __forceinline__ uint32_t quant1_bf16(uint32_t bf16bits, float s) {
+  const float x = __uint_as_float(bf16bits << 16);
+  float r = rintf(__fmul_rn(x, s));
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (uint32_t)(uint8_t)(int8_t)(int)r;
+}
+
+// 4 bf16 -> 4 int8 packed little-endian in a 32-bit word.
+__device__ __forceinline__ uint32_t quant4_bf16(uint2 v, float s) {
+  return quant1_bf16(v.x & 0xFFFFu, s) | (quant1_bf16(v.x >> 16, s) << 8) |
+         (quant1_bf16(v.y & 0xFFFFu, s) << 16) | (quant1_bf16(v.y >> 16, s) << 24);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));

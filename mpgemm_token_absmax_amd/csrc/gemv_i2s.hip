@@ -1,25 +1,36 @@
-// Decode-time ternary GEMV (1 <= M <= 16 tokens) on gfx950, plus the generic
-// kernel for shapes off the fast paths.
+// Decode-time ternary GEMV (1 <= M <= 16 tokens) on gfx950: the plain GEMV
+// (int8 activations in) and the fused decode group (bf16 activations in:
+// per-token absmax quantization, GEMV and dequant in one launch for up to
+// kMaxGroup independent projections), plus the generic kernel for shapes off
+// the fast paths.
 //
 // Sources: "Bitnet.cpp: Efficient Edge Inference for Ternary LLMs" reading
-// notes, Part A 2.3 / 4.1 (I2_S: element-wise multiply-add over 2-bit
-// ternary codes and int8 activations, exact sums); bitnet.cpp how-to blog 1.1
-// (decode streams every weight once per token: memory-bandwidth bound) and
-// 1.2 (ternary weights make the products adds and subtracts); FairyFuse
-// "融合内核设计" (unpack, accumulate and write in one pass, no intermediate
-// stores).
+// notes, Part A 2.3 / 4.1 (I2_S: element-wise multiply-add over 2-bit ternary
+// codes and int8 activations quantized with one scale per vector, exact
+// sums); bitnet.cpp how-to blog 1.1 (decode streams every weight once per
+// token: memory-bandwidth bound) and 1.2 (ternary weights make the products
+// adds and subtracts); FairyFuse "融合内核设计" (load activations, walk the
+// 2-bit codes, accumulate and write in one pass with no intermediate stores).
 //
-// Design (HBM-bound): the packed weights are the only large stream. Each wave
-// owns RTW tiles of 16 output rows and a K-slice; lane (r = lane%16,
-// h = lane/16) streams 16 bytes (64 weights) of row r per 256-weight step with
-// one 128-bit load, so the 4 lanes of a row read 64 contiguous bytes. Each
-// 32-bit group word decodes in registers (shift, mask, v_perm_b32 through the
-// code table) to 16 int8 weights in k order, which feed one
-// v_mfma_i32_16x16x64_i8 against the matching 16 activation bytes of token r
-// (zero for r >= M). The int8 x ternary products are therefore exact int32
-// adds; the MFMA sums 64 of them per lane group. Waves that split K combine
-// their int32 tiles through LDS (exact, order free), and the dequant epilogue
-// (acc * fl32(gamma * d_t)) is fused into the store.
+// Design (HBM-bound: the packed weights are the only large stream):
+//  * a launch covers one or more problems; blocks are dealt to problems by a
+//    prefix table in the kernel arguments;
+//  * each block first issues its first batch of weight loads, then builds the
+//    int8 activations of all M tokens in LDS: copied from q (plain GEMV) or
+//    quantized from bf16 x with the same arithmetic as bl_quantize_act
+//    (fused decode; block 0 of a problem also writes q and d);
+//  * each wave owns RTW tiles of 16 output rows and every WK-th 256-weight
+//    step of K. Lane (r = lane%16, h = lane/16) streams 16 bytes (64 weights)
+//    of row r per step with one 128-bit load (the 4 lanes of a row read 64
+//    contiguous bytes); loads of the next U steps are in flight while the
+//    current ones are consumed;
+//  * each 32-bit group word decodes in registers (9 VALU ops: shift, masks,
+//    v_perm_b32 through the code table) to 16 int8 weights in k order and
+//    feeds one v_mfma_i32_16x16x64_i8 against the 16 matching activation
+//    bytes of token r read from LDS (zero for r >= M): the ternary x int8
+//    products are exact int32 adds;
+//  * waves that split K add their int32 tiles through LDS (exact, order
+//    free) and the dequant acc * fl32(gamma * d_t) is fused into the store.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,6 +39,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kActLds = 48 * 1024;      // LDS bytes for activations (M * K chunk)
+constexpr int kXReg = 8;                // bf16 x chunks (4 values) per thread kept in registers
+constexpr int kQReg = 2;                // int8 q chunks (16 values) per thread kept in registers
 
 __device__ __forceinline__ void store_out(void* y, int ytype, int64_t idx, int acc, float c) {
   if (ytype == 0) {
@@ -39,8 +53,8 @@ __device__ __forceinline__ void store_out(void* y, int ytype, int64_t idx, int a
   }
 }
 
-// Store 4 consecutive outputs y[t][n .. n+3] of one token (vector store when
-// the 4 columns exist and are aligned).
+// Store y[t][n .. n+3] of one token (vector store when the 4 columns exist and
+// are aligned).
 __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_t t, int64_t n,
                                            v4i acc, float c) {
   const int64_t base = t * N + n;
@@ -48,9 +62,8 @@ __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_
     if (ytype == 0) {
       *reinterpret_cast<v4i*>(static_cast<int*>(y) + base) = acc;
     } else if (ytype == 1) {
-      float4 f = make_float4(dequant(acc.x, c), dequant(acc.y, c), dequant(acc.z, c),
-                             dequant(acc.w, c));
-      *reinterpret_cast<float4*>(static_cast<float*>(y) + base) = f;
+      *reinterpret_cast<float4*>(static_cast<float*>(y) + base) =
+          make_float4(dequant(acc.x, c), dequant(acc.y, c), dequant(acc.z, c), dequant(acc.w, c));
     } else {
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(dequant(acc.x, c)) |
                           ((uint32_t)f32_to_bf16_rne(dequant(acc.y, c)) << 16);
@@ -65,67 +78,182 @@ __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_
   }
 }
 
-// RTW: 16-row tiles per wave. WK: waves splitting K (the block's other
-// kWavesPerBlock / WK waves take further row tiles). U: 256-weight steps whose
-// loads are issued together.
 template <int RTW, int WK, int U>
-__global__ __launch_bounds__(kThreads) void k_gemv_i2s(
-    const uint8_t* __restrict__ packed, const float* __restrict__ gamma, int64_t N, int64_t K,
-    const int8_t* __restrict__ q, const float* __restrict__ d, int64_t M, void* __restrict__ y,
-    int ytype) {
+__global__ __launch_bounds__(kThreads) void k_gemv_i2s(DecodeGroup grp) {
   constexpr int WR = kWavesPerBlock / WK;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
+  extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [M][kc] int8
+  __shared__ v4i red[WK > 1 ? WK - 1 : 1][WR][RTW][kWave];
+  __shared__ uint32_t mred[kWavesPerBlock][kMaxDecodeM];
+  __shared__ float sc[kMaxDecodeM];
+  __shared__ float dsh[kMaxDecodeM];
+
+  // problem of this block (uniform scan over a short prefix table)
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i) pi += (i < grp.count && (int)blockIdx.x >= grp.block0[i]);
+  const DecodeProblem& P = grp.p[pi];
+  const int64_t N = P.N, K = P.K;
+  const int M = grp.M;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
   const int wr = wv / WK, wk = wv % WK;
   const int r = lane & 15, h = lane >> 4;
   const int64_t RB = K / 4;                       // packed bytes per row
-  const int64_t nss = (RB + 63) / 64;             // 256-weight steps per row
-  const int64_t n0 = ((int64_t)blockIdx.x * WR + wr) * RTW * 16;
+  const int64_t n0 = ((int64_t)(blockIdx.x - grp.block0[pi]) * WR + wr) * RTW * 16;
+  const bool first_block = (int)blockIdx.x == grp.block0[pi];
+  const uint8_t* __restrict__ packed = P.packed;
+  const uint16_t* __restrict__ xg = P.x;
+  const int64_t kq = K / 4;                       // 4-element chunks per token row
+
+  // K is processed in chunks of kc weights whose int8 activations fit in LDS.
+  const int64_t kc_max = ((int64_t)(kActLds / M) / 256) * 256;
+  const int64_t kc = K < kc_max ? K : kc_max;
+
+  v4i wa[U][RTW], wb[U][RTW];   // two batches of weight loads
+  // loads of the steps [j, min(j + U, jend)) of this wave into dst
+  auto load_w = [&](v4i (&dst)[U][RTW], int64_t j, int64_t jend) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = (j + u) * 64 + 16 * h;
+      const bool kv = j + u < jend && off < RB;
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) {
+        const int64_t row = n0 + rt * 16 + r;
+        dst[u][rt] = (kv && row < N)
+                         ? __builtin_nontemporal_load(
+                               reinterpret_cast<const v4i*>(packed + row * RB + off))
+                         : v4i{0, 0, 0, 0};
+      }
+    }
+  };
+  // this wave's contiguous range of 256-weight steps inside a chunk
+  auto wave_range = [&](int64_t k0, int64_t kn, int64_t& ja, int64_t& jb) {
+    const int64_t js0 = k0 / 256, jend = (k0 + kn + 255) / 256;
+    const int64_t len = (jend - js0 + WK - 1) / WK;
+    ja = js0 + wk * len;
+    jb = ja + len < jend ? ja + len : jend;
+  };
+
+  int64_t ja, jb;
+  wave_range(0, kc, ja, jb);
+  load_w(wa, ja, jb);                             // weights in flight during the prologue
+
+  // ---- per-token scales (fused path: absmax of bf16 x, same arithmetic as
+  // bl_quantize_act); rows of M*K <= kThreads*4*kXReg stay in registers.
+  const bool x_in_regs = xg && M * kq <= (int64_t)kThreads * kXReg;
+  uint2 xv[kXReg];
+  if (xg) {
+    for (int t = 0; t < M; ++t) {
+      uint32_t m = 0u;
+      if (x_in_regs) {
+#pragma unroll
+        for (int u = 0; u < kXReg; ++u) {
+          const int64_t i = tid + (int64_t)u * kThreads;
+          if (t == 0) {
+            xv[u] = make_uint2(0u, 0u);
+            if (i < M * kq) xv[u] = *reinterpret_cast<const uint2*>(xg + (i / kq) * P.ldx +
+                                                                   (i % kq) * 4);
+          }
+          if (i < M * kq && i / kq == t) m = max(m, absmax4_bf16(xv[u]));
+        }
+      } else {
+        const uint2* xr = reinterpret_cast<const uint2*>(xg + (int64_t)t * P.ldx);
+        for (int64_t c = tid; c < kq; c += kThreads) m = max(m, absmax4_bf16(xr[c]));
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, kWave));
+      if (lane == 0) mred[wv][t] = m;
+    }
+    __syncthreads();
+    if (tid < M) {
+      uint32_t mb = mred[0][tid];
+#pragma unroll
+      for (int w = 1; w < kWavesPerBlock; ++w) mb = max(mb, mred[w][tid]);
+      const float m = __uint_as_float(mb << 16);
+      sc[tid] = mb ? 127.0f / m : 0.0f;
+      const float dd = mb ? m / 127.0f : 0.0f;
+      dsh[tid] = dd;
+      if (first_block && P.d) P.d[tid] = dd;
+    }
+    __syncthreads();
+  }
 
   v4i acc[RTW];
 #pragma unroll
   for (int i = 0; i < RTW; ++i) acc[i] = v4i{0, 0, 0, 0};
 
-  const bool tok_ok = r < M;
-  const int8_t* qrow = q + (int64_t)r * K;
-
-  for (int64_t js = wk; js < nss; js += (int64_t)WK * U) {
-    uint4 wq[U][RTW];
-    v4i b[U][4];
+  for (int64_t k0 = 0; k0 < K; k0 += kc) {
+    const int64_t kn = (K - k0) < kc ? (K - k0) : kc;      // multiple of 64
+    if (k0 > 0) {
+      wave_range(k0, kn, ja, jb);
+      load_w(wa, ja, jb);
+      __syncthreads();                                     // previous chunk consumed
+    }
+    // stage the int8 activations [M][kn] of this chunk into LDS
+    if (x_in_regs) {                                       // single chunk (kn == K)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = js + (int64_t)u * WK;
-      const int64_t off = j * 64 + 16 * h;
-      const bool kv = j < nss && off < RB;
-#pragma unroll
-      for (int rt = 0; rt < RTW; ++rt) {
-        const int64_t row = n0 + rt * 16 + r;
-        wq[u][rt] = (kv && row < N)
-                        ? *reinterpret_cast<const uint4*>(packed + row * RB + off)
-                        : make_uint4(0u, 0u, 0u, 0u);
+      for (int u = 0; u < kXReg; ++u) {
+        const int64_t i = tid + (int64_t)u * kThreads;
+        if (i < M * kq) {
+          const int64_t t = i / kq;
+          const float s = sc[t];
+          const uint32_t v = s != 0.0f ? quant4_bf16(xv[u], s) : 0u;
+          reinterpret_cast<uint32_t*>(act)[i] = v;
+          if (first_block && P.q) reinterpret_cast<uint32_t*>(P.q)[i] = v;
+        }
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int64_t k = j * 256 + 64 * h + 16 * s;
-        b[u][s] = (kv && tok_ok && k < K) ? *reinterpret_cast<const v4i*>(qrow + k)
-                                         : v4i{0, 0, 0, 0};
+    } else if (xg) {
+      const int64_t nq = kn / 4;
+      for (int64_t i = tid; i < M * nq; i += kThreads) {
+        const int64_t t = i / nq, c = i % nq;
+        const float s = sc[t];
+        const uint2 v2 = *reinterpret_cast<const uint2*>(xg + t * P.ldx + k0 + 4 * c);
+        const uint32_t v = s != 0.0f ? quant4_bf16(v2, s) : 0u;
+        reinterpret_cast<uint32_t*>(act)[i] = v;
+        if (first_block && P.q)
+          *reinterpret_cast<uint32_t*>(P.q + t * K + k0 + 4 * c) = v;
+      }
+    } else {
+      const int64_t n16 = kn / 16;
+      for (int64_t i = tid; i < M * n16; i += kThreads) {
+        const int64_t t = i / n16, c = i % n16;
+        reinterpret_cast<v4i*>(act)[i] =
+            *reinterpret_cast<const v4i*>(P.qin + t * K + k0 + 16 * c);
       }
     }
+    __syncthreads();
+
+    const int8_t* arow = act + (int64_t)r * kn + 64 * h;
+    const bool tok_ok = r < M;
+    const int64_t js0 = k0 / 256;
+    auto compute = [&](const v4i (&w)[U][RTW], int64_t j) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U; ++u) {
+        if (j + u >= jb) break;
+        const int64_t kk = (j + u - js0) * 256;            // offset inside the chunk
 #pragma unroll
-      for (int rt = 0; rt < RTW; ++rt) {
-        const uint32_t wds[4] = {wq[u][rt].x, wq[u][rt].y, wq[u][rt].z, wq[u][rt].w};
+        for (int s = 0; s < 4; ++s) {
+          v4i b = v4i{0, 0, 0, 0};
+          if (tok_ok && kk + 64 * h + 16 * s < kn)
+            b = *reinterpret_cast<const v4i*>(arow + kk + 16 * s);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word(wds[s]), b[u][s], acc[rt],
-                                                          0, 0, 0);
+          for (int rt = 0; rt < RTW; ++rt)
+            acc[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]),
+                                                            b, acc[rt], 0, 0, 0);
+        }
       }
+    };
+    // two batches of U steps in flight: compute one while the next loads
+    for (int64_t j = ja; j < jb; j += 2 * U) {
+      if (j + U < jb) load_w(wb, j + U, jb);
+      compute(wa, j);
+      if (j + 2 * U < jb) load_w(wa, j + 2 * U, jb);
+      if (j + U < jb) compute(wb, j + U);
     }
   }
 
   if constexpr (WK > 1) {
-    __shared__ v4i red[WK > 1 ? WK - 1 : 1][WR][RTW][kWave];
     if (wk > 0) {
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt) red[wk - 1][wr][rt][lane] = acc[rt];
@@ -138,14 +266,247 @@ __global__ __launch_bounds__(kThreads) void k_gemv_i2s(
       for (int rt = 0; rt < RTW; ++rt) acc[rt] += red[w][wr][rt][lane];
   }
 
-  // D[i][j] layout of the 16x16 MFMA: lane holds column j = lane%16 (token)
-  // and rows i = 4*(lane/16) + v (output features), v = 0..3.
-  if (!tok_ok) return;
-  const float c = ytype ? gamma[0] * d[r] : 0.0f;
+  // D[i][j] of the 16x16 MFMA: lane holds column j = lane%16 (token) and rows
+  // i = 4*(lane/16) + v (output features), v = 0..3.
+  if (r >= M) return;
+  float c = 0.0f;
+  if (P.ytype) c = P.gamma[0] * (xg ? dsh[r] : P.din[r]);
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const int64_t n = n0 + rt * 16 + 4 * h;
-    if (n < N) store_quad(y, ytype, N, r, n, acc[rt], c);
+    if (n < N) store_quad(P.y, P.ytype, N, r, n, acc[rt], c);
+  }
+}
+
+// Fast decode kernel (every problem's per-wave activation slice fits in LDS):
+// each wave owns a contiguous range of 256-weight steps and builds the int8
+// activations of exactly that range in a wave-private LDS region, so the only
+// block barriers are the per-token absmax exchange (fused path) and the final
+// K-split reduction. The activation work overlaps the weight loads, which are
+// issued first. Wave-uniform quantities are forced into scalar registers so
+// the step loop has no per-lane control flow: rows past N load a valid row
+// (their outputs are never stored) and lanes past the end of K load a valid
+// address whose products meet zero activations (the LDS tail is zero-filled).
+template <int RTW, int WK, int U>
+__global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int len_max) {
+  constexpr int WR = kWavesPerBlock / WK;
+  extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][M][len_max*256]
+  __shared__ v4i red[WK > 1 ? WK - 1 : 1][WR][RTW][kWave];
+  __shared__ uint32_t smax[kMaxDecodeM];
+
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i) pi += (i < grp.count && (int)blockIdx.x >= grp.block0[i]);
+  const DecodeProblem& P = grp.p[pi];
+  const int64_t N = P.N;
+  const int K = (int)P.K;
+  const int M = grp.M;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wv / WK, wk = wv % WK;
+  const int r = lane & 15, h = lane >> 4;
+  const int RB = K / 4;
+  const int64_t n0 = ((int64_t)(blockIdx.x - grp.block0[pi]) * WR + wr) * RTW * 16;
+  const bool first_block = (int)blockIdx.x == grp.block0[pi];
+  const uint16_t* __restrict__ xg = P.x;
+  if (K < 64) return;         // the launcher routes K == 0 problems to k_zero_outputs
+
+  // this wave's steps [ja, jb) and weights [klo, khi)
+  const int nsteps = (K + 255) / 256;
+  const int len = (nsteps + WK - 1) / WK;
+  const int ja = min(wk * len, nsteps);
+  const int jb = min(ja + len, nsteps);
+  const int klo = min(ja * 256, K);
+  const int khi = min(jb * 256, K);
+  const int kw = khi - klo;                           // multiple of 64 (may be 0)
+  const int region = len_max * 256;                   // bytes per token row in LDS
+  int8_t* wact = act + wv * M * region;
+
+  // per-lane row pointers (rows past N read row N-1; never stored)
+  const uint8_t* wrow[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    int64_t row = n0 + rt * 16 + r;
+    row = row < N ? row : N - 1;
+    wrow[rt] = P.packed + row * RB;
+  }
+  v4i wa[U][RTW], wb[U][RTW];
+  // Loads are unconditional (so the compiler can count outstanding loads and
+  // wait for older ones only): slots past the wave's range re-read its last
+  // step (never used), lanes past K read a valid address whose products meet
+  // zero activations.
+  auto load_w = [&](v4i (&dst)[U][RTW], int j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int step = max(min(j + u, jb - 1), 0);
+      int off = step * 64 + 16 * h;
+      off = off < RB ? off : RB - 16;
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+        dst[u][rt] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow[rt] + off));
+    }
+  };
+
+  // Vector loads retire in issue order, so the activation loads (small, L2
+  // resident) are issued before the weight loads: waiting for them then does
+  // not wait for the weights, and the activation work overlaps the HBM stream.
+  const int cpt = kw / 4;                             // 4-element chunks per token
+  const bool cache = xg && M == 1 && cpt <= kXReg * kWave;
+  const int c16 = kw / 16;
+  const bool qcache = !xg && M == 1 && c16 <= kQReg * kWave;
+  uint2 xv[kXReg];
+  v4i qv[kQReg];
+  if (cache && cpt > 0) {
+#pragma unroll
+    for (int u = 0; u < kXReg; ++u) {                 // clamped: lanes past the range reload
+      const int c = min(lane + u * kWave, cpt - 1);   // the last chunk (masked when used)
+      xv[u] = *reinterpret_cast<const uint2*>(xg + klo + 4 * c);
+    }
+  }
+  if (qcache && c16 > 0) {
+#pragma unroll
+    for (int u = 0; u < kQReg; ++u) {
+      const int c = min(lane + u * kWave, c16 - 1);
+      qv[u] = *reinterpret_cast<const v4i*>(P.qin + klo + 16 * c);
+    }
+  }
+  const float gam = P.ytype ? P.gamma[0] : 0.0f;      // epilogue operands, fetched early
+  const float din_r = (!xg && P.ytype) ? P.din[r < M ? r : 0] : 0.0f;
+  __builtin_amdgcn_sched_barrier(0);
+  if (xg && tid < M) smax[tid] = 0u;
+  load_w(wa, ja);                                     // weights in flight from here on
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- activations of this wave's range -> int8 in the wave's LDS region
+  float s_lane = 0.0f, d_lane = 0.0f;                 // lane t < M: token t's scales
+  if (xg) {
+    __syncthreads();                                  // smax initialised
+    for (int t = 0; t < M; ++t) {
+      uint32_t m = 0u;
+      if (cache) {
+#pragma unroll
+        for (int u = 0; u < kXReg; ++u)
+          m = max(m, lane + u * kWave < cpt ? absmax4_bf16(xv[u]) : 0u);
+      } else {
+        const uint16_t* xr = xg + (int64_t)t * P.ldx + klo;
+        for (int c = lane; c < cpt; c += kWave)
+          m = max(m, absmax4_bf16(*reinterpret_cast<const uint2*>(xr + 4 * c)));
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, kWave));
+      if (lane == 0 && m) atomicMax(&smax[t], m);
+    }
+    __syncthreads();                                  // all maxima in
+    if (lane < M) {
+      const uint32_t mb = smax[lane];
+      const float m = __uint_as_float(mb << 16);
+      s_lane = mb ? 127.0f / m : 0.0f;
+      d_lane = mb ? m / 127.0f : 0.0f;
+      if (first_block && wv == 0 && P.d) P.d[lane] = d_lane;
+    }
+    const bool write_q = first_block && wr == 0 && P.q;
+    for (int t = 0; t < M; ++t) {
+      const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                    __builtin_bit_cast(int, s_lane), t));
+      uint32_t* dst = reinterpret_cast<uint32_t*>(wact + t * region);
+      uint32_t* qo = write_q ? reinterpret_cast<uint32_t*>(P.q + (int64_t)t * K + klo) : nullptr;
+      if (cache) {
+#pragma unroll
+        for (int u = 0; u < kXReg; ++u) {
+          const int c = lane + u * kWave;
+          if (c < cpt) {
+            const uint32_t v = s != 0.0f ? quant4_bf16(xv[u], s) : 0u;
+            dst[c] = v;
+            if (qo) qo[c] = v;
+          }
+        }
+      } else {
+        const uint16_t* xr = xg + (int64_t)t * P.ldx + klo;
+        for (int c = lane; c < cpt; c += kWave) {
+          const uint32_t v =
+              s != 0.0f ? quant4_bf16(*reinterpret_cast<const uint2*>(xr + 4 * c), s) : 0u;
+          dst[c] = v;
+          if (qo) qo[c] = v;
+        }
+      }
+    }
+  } else if (qcache) {
+    // plain GEMV, one token: the q range is already in registers
+    v4i* dst = reinterpret_cast<v4i*>(wact);
+#pragma unroll
+    for (int u = 0; u < kQReg; ++u) {
+      const int c = lane + u * kWave;
+      if (c < c16) dst[c] = qv[u];
+    }
+  } else {
+    // plain GEMV: copy this wave's q range into its region (16-byte chunks)
+    for (int t = 0; t < M; ++t) {
+      const v4i* src = reinterpret_cast<const v4i*>(P.qin + (int64_t)t * K + klo);
+      v4i* dst = reinterpret_cast<v4i*>(wact + t * region);
+      for (int c = lane; c < c16; c += kWave) dst[c] = src[c];
+    }
+  }
+  // zero the region tail [kw, len*256) that the last partial step reads
+  for (int t = 0; t < M; ++t) {
+    v4i* dst = reinterpret_cast<v4i*>(wact + t * region);
+    for (int c = kw / 16 + lane; c < len * 16; c += kWave) dst[c] = v4i{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  v4i acc[RTW];
+#pragma unroll
+  for (int i = 0; i < RTW; ++i) acc[i] = v4i{0, 0, 0, 0};
+  const bool tok_ok = r < M;
+  const int8_t* arow = wact + (tok_ok ? r : 0) * region + 64 * h;
+  auto compute = [&](const v4i (&w)[U][RTW], int j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j + u < jb) {
+        const int kk = (j + u - ja) * 256;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          v4i b = *reinterpret_cast<const v4i*>(arow + kk + 16 * s);
+          b = tok_ok ? b : v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int rt = 0; rt < RTW; ++rt)
+            acc[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]),
+                                                            b, acc[rt], 0, 0, 0);
+        }
+      }
+    }
+  };
+  for (int j = ja; j < jb; j += 2 * U) {
+    if (j + U < jb) load_w(wb, j + U);
+    compute(wa, j);
+    if (j + 2 * U < jb) load_w(wa, j + 2 * U);
+    if (j + U < jb) compute(wb, j + U);
+  }
+
+  if constexpr (WK > 1) {
+    if (wk > 0) {
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) red[wk - 1][wr][rt][lane] = acc[rt];
+    }
+    __syncthreads();
+    if (wk > 0) return;
+#pragma unroll
+    for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) acc[rt] += red[w][wr][rt][lane];
+  }
+
+  // D[i][j] of the 16x16 MFMA: lane holds column j = lane%16 (token) and rows
+  // i = 4*(lane/16) + v (output features), v = 0..3.
+  const float dr = xg ? __shfl(d_lane, tok_ok ? r : 0, kWave) : din_r;
+  if (!tok_ok) return;
+  const float c = gam * dr;
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    const int64_t n = n0 + rt * 16 + 4 * h;
+    if (n < N) store_quad(P.y, P.ytype, N, r, n, acc[rt], c);
   }
 }
 
@@ -171,14 +532,24 @@ __global__ void k_generic(const uint8_t* __restrict__ packed, const float* __res
 }
 
 template <int RTW, int WK, int U>
-hipError_t launch_cfg(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
-                      const int8_t* q, const float* d, int64_t M, void* y, int ytype,
-                      hipStream_t s) {
+hipError_t launch_cfg(DecodeGroup& g, hipStream_t s) {
   constexpr int WR = kWavesPerBlock / WK;
-  const int64_t rows_per_block = (int64_t)WR * RTW * 16;
-  const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((k_gemv_i2s<RTW, WK, U>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                     packed, gamma, N, K, q, d, M, y, ytype);
+  constexpr int64_t rows_per_block = (int64_t)WR * RTW * 16;
+  int blocks = 0;
+  for (int i = 0; i < g.count; ++i) {
+    g.block0[i] = blocks;
+    blocks += (int)((g.p[i].N + rows_per_block - 1) / rows_per_block);
+  }
+  if (blocks == 0) return hipSuccess;
+  // dynamic LDS: the largest [M][K chunk] activation tile of the group
+  size_t lds = 16;
+  for (int i = 0; i < g.count; ++i) {
+    const int64_t kc_max = ((int64_t)(kActLds / g.M) / 256) * 256;
+    const int64_t kc = g.p[i].K < kc_max ? g.p[i].K : kc_max;
+    const size_t b = (size_t)(g.M * kc);
+    if (b > lds) lds = b;
+  }
+  hipLaunchKernelGGL((k_gemv_i2s<RTW, WK, U>), dim3((unsigned)blocks), dim3(kThreads), lds, s, g);
   return hipGetLastError();
 }
 
@@ -194,17 +565,86 @@ hipError_t launch_generic(const uint8_t* packed, const float* gamma, int64_t N, 
   return hipGetLastError();
 }
 
+// K == 0: nothing to contract, every output is 0 (and every token's scale 0).
+__global__ void k_zero_outputs(void* __restrict__ y, int ytype, int64_t n, float* __restrict__ d,
+                               int M) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) store_out(y, ytype, i, 0, 0.0f);
+  if (d && i < M) d[i] = 0.0f;
+}
+
+hipError_t launch_zero_outputs(const DecodeProblem& p, int M, hipStream_t s) {
+  const int64_t n = (int64_t)M * p.N;
+  const int64_t cover = n > M ? n : M;
+  hipLaunchKernelGGL(k_zero_outputs, dim3((unsigned)((cover + 255) / 256)), dim3(256), 0, s, p.y,
+                     p.ytype, n, p.x ? p.d : nullptr, M);
+  return hipGetLastError();
+}
+
+template <int RTW, int WK, int U>
+hipError_t launch_fast(DecodeGroup& g, int len_max, hipStream_t s) {
+  constexpr int WR = kWavesPerBlock / WK;
+  constexpr int64_t rows_per_block = (int64_t)WR * RTW * 16;
+  int blocks = 0;
+  for (int i = 0; i < g.count; ++i) {
+    g.block0[i] = blocks;
+    blocks += (int)((g.p[i].N + rows_per_block - 1) / rows_per_block);
+  }
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = (size_t)kWavesPerBlock * g.M * len_max * 256;
+  hipLaunchKernelGGL((k_decode_fast<RTW, WK, U>), dim3((unsigned)blocks), dim3(kThreads),
+                     lds < 16 ? 16 : lds, s, g, len_max);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
+  // problems with K == 0 only need zero outputs; keep them away from the
+  // MFMA kernels (whose loads assume at least one 64-weight group per row)
+  int kept = 0;
+  for (int i = 0; i < g.count; ++i) {
+    if (g.p[i].K == 0) {
+      const hipError_t e = launch_zero_outputs(g.p[i], g.M, s);
+      if (e != hipSuccess) return e;
+    } else {
+      g.p[kept++] = g.p[i];
+    }
+  }
+  g.count = kept;
+  if (g.count == 0) return hipSuccess;
+  int64_t row_tiles = 0;
+  for (int i = 0; i < g.count; ++i) row_tiles += (g.p[i].N + 15) / 16;
+  // fast path: each wave's [M][steps * 256] int8 slice fits in LDS
+  constexpr int kFastWK = 4;
+  int len_max = 0;
+  for (int i = 0; i < g.count; ++i) {
+    const int64_t steps = (g.p[i].K + 255) / 256;
+    const int len = (int)((steps + kFastWK - 1) / kFastWK);
+    if (len > len_max) len_max = len;
+  }
+  if ((int64_t)kWavesPerBlock * g.M * len_max * 256 <= kActLds)
+    return len_max <= 4 ? launch_fast<1, kFastWK, 4>(g, len_max, s)
+                        : launch_fast<1, kFastWK, 8>(g, len_max, s);
+  if (row_tiles >= 2048) return launch_cfg<1, 2, 8>(g, s);
+  return launch_cfg<1, 4, 8>(g, s);
+}
+
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                        const int8_t* q, const float* d, int64_t M, void* y, int ytype,
                        hipStream_t s) {
   if (K % 64 != 0) return launch_generic(packed, gamma, N, K, q, d, M, y, ytype, s);
-  const int64_t row_tiles = (N + 15) / 16;
-  if (M > 4) {
-    if (row_tiles >= 1024) return launch_cfg<2, 2, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
-    return launch_cfg<2, 4, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
-  }
-  if (row_tiles >= 2048) return launch_cfg<1, 2, 4>(packed, gamma, N, K, q, d, M, y, ytype, s);
-  return launch_cfg<1, 4, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
+  DecodeGroup g{};
+  g.count = 1;
+  g.M = (int)M;
+  DecodeProblem& p = g.p[0];
+  p.packed = packed;
+  p.gamma = gamma;
+  p.N = N;
+  p.K = K;
+  p.qin = q;
+  p.din = d;
+  p.y = y;
+  p.ytype = ytype;
+  return launch_decode_group(g, s);
 }
 
 }  // namespace bl

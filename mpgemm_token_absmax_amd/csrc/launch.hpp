@@ -8,6 +8,39 @@
 
 namespace bl {
 
+constexpr int kMaxGroup = 8;        // problems per decode-group launch
+constexpr int kMaxDecodeM = 16;     // tokens of the decode kernels
+
+// One GEMV of a decode launch. Activations come either as bf16 x (quantized
+// in-kernel; q and d, when not NULL, receive the codes and scales) or as
+// int8 qin with scales din.
+struct DecodeProblem {
+  const uint8_t* packed;
+  const float* gamma;
+  const uint16_t* x;
+  int8_t* q;
+  float* d;
+  const int8_t* qin;
+  const float* din;
+  void* y;
+  int64_t N;
+  int64_t K;
+  int64_t ldx;
+  int ytype;
+};
+
+// Kernel argument of a decode launch. The header (count, M and each
+// problem's first block) comes first so one scalar load finds the problem of
+// a block.
+struct DecodeGroup {
+  int count;
+  int M;
+  int block0[kMaxGroup];      // first block of each problem (set by the launcher)
+  DecodeProblem p[kMaxGroup];
+};
+
+hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s);
+
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                float* d, hipStream_t s);
 

@@ -19,26 +19,6 @@ namespace {
 
 constexpr int kQThreads = 256;
 
-__device__ __forceinline__ uint32_t absmax4(uint2 v) {
-  const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu;
-  return max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16));
-}
-
-__device__ __forceinline__ int8_t quant1(uint32_t bf16bits, float s) {
-  const float x = __uint_as_float(bf16bits << 16);
-  float r = rintf(__fmul_rn(x, s));
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int8_t)(int)r;
-}
-
-__device__ __forceinline__ uint32_t quant4(uint2 v, float s) {
-  const uint32_t b0 = (uint8_t)quant1(v.x & 0xFFFFu, s);
-  const uint32_t b1 = (uint8_t)quant1(v.x >> 16, s);
-  const uint32_t b2 = (uint8_t)quant1(v.y & 0xFFFFu, s);
-  const uint32_t b3 = (uint8_t)quant1(v.y >> 16, s);
-  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-}
-
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
@@ -68,7 +48,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_absmax(
     for (int i = 0; i < NC; ++i) {
       const int64_t c = threadIdx.x + (int64_t)i * kQThreads;
       v[i] = c < nchunk ? xr[c] : make_uint2(0u, 0u);
-      mb = max(mb, absmax4(v[i]));
+      mb = max(mb, absmax4_bf16(v[i]));
     }
     mb = block_max_u32(mb, red);
     const float m = __uint_as_float(mb << 16);
@@ -76,15 +56,15 @@ __global__ __launch_bounds__(kQThreads) void k_quant_absmax(
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int64_t c = threadIdx.x + (int64_t)i * kQThreads;
-      if (c < nchunk) qr[c] = mb ? quant4(v[i], s) : 0u;
+      if (c < nchunk) qr[c] = mb ? quant4_bf16(v[i], s) : 0u;
     }
     if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
   } else {
-    for (int64_t c = threadIdx.x; c < nchunk; c += kQThreads) mb = max(mb, absmax4(xr[c]));
+    for (int64_t c = threadIdx.x; c < nchunk; c += kQThreads) mb = max(mb, absmax4_bf16(xr[c]));
     mb = block_max_u32(mb, red);
     const float m = __uint_as_float(mb << 16);
     const float s = mb ? 127.0f / m : 0.0f;
-    for (int64_t c = threadIdx.x; c < nchunk; c += kQThreads) qr[c] = mb ? quant4(xr[c], s) : 0u;
+    for (int64_t c = threadIdx.x; c < nchunk; c += kQThreads) qr[c] = mb ? quant4_bf16(xr[c], s) : 0u;
     if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
   }
 }

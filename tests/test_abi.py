@@ -118,3 +118,36 @@ def test_status_to_exception(lib):
         L.check("bl_gemv", L.BL_ERR_SHAPE)
     assert e.value.status == L.BL_ERR_SHAPE
     assert "shape" in str(e.value)
+
+
+def test_decode_group_validation(lib):
+    P = L.DecodeProblem
+
+    def prob(**kw):
+        base = dict(packed=A16, gamma=B16, N=64, K=256, x=C16, ldx=256, q=None, d=None, y=E16,
+                    ytype=2)
+        base.update(kw)
+        return P(**base)
+
+    def call(probs, M=1):
+        arr = (P * max(1, len(probs)))(*probs)
+        return lib.bl_decode_group(arr, len(probs), M, None)
+
+    assert call([prob()] * 9) == L.BL_ERR_SHAPE            # more than 8 problems
+    assert call([prob()], M=17) == L.BL_ERR_SHAPE           # more than 16 tokens
+    assert call([prob(K=260, ldx=260)]) == L.BL_ERR_SHAPE   # K % 64
+    assert call([prob(ldx=128)]) == L.BL_ERR_SHAPE          # ldx < K
+    assert call([prob(ytype=5)]) == L.BL_ERR_DTYPE
+    assert call([prob(packed=None)]) == L.BL_ERR_NULL
+    assert call([prob(x=None)]) == L.BL_ERR_NULL
+    assert call([prob(gamma=None)]) == L.BL_ERR_NULL
+    assert call([prob(), prob(y=None)]) == L.BL_ERR_NULL     # the second problem is checked too
+    assert call([prob(x=C16 + 8)]) == L.BL_ERR_ALIGN
+    assert call([prob(q=D16 + 4)]) == L.BL_ERR_ALIGN
+    assert call([prob(d=D16 + 2)]) == L.BL_ERR_ALIGN
+    assert call([prob(ldx=258)]) == L.BL_ERR_ALIGN
+    assert call([prob(K=132160, ldx=132160)]) == L.BL_ERR_SHAPE   # fp32-exact bound
+    assert call([], M=1) == L.BL_OK
+    assert call([prob()], M=0) == L.BL_OK
+    assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK      # nothing to compute
+    assert lib.bl_decode_group(None, 1, 1, None) == L.BL_ERR_NULL

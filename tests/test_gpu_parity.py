@@ -315,6 +315,103 @@ def test_k_zero_and_empty():
 
 
 # ---------------------------------------------------------------------------
+# fused decode group (quantize + GEMV + dequant in one launch)
+# ---------------------------------------------------------------------------
+
+def _decode_group_case(bl, M, shapes, seed, with_qd=True, out_types=None):
+    say(f"decode_group M={M} shapes={shapes} with_qd={with_qd}")
+    probs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x = W.activations_bf16(seed + 10 * i, M, K, outlier_frac=0.01, outlier_scale=20.0)
+        if M > 2:
+            x[M - 1] = 0                                  # an all-zero token
+        t = W.ternary_drawn(seed + 10 * i + 1, N, K, 0.4)
+        ot = (out_types or ["bf16", "f32", "i32"])[i % len(out_types or ["bf16", "f32", "i32"])]
+        p = dict(packed=bl.pack_i2s(dev(t)), gamma=dev(np.array([GAMMA], np.float32)),
+                 x=dev_bf16(x), out_dtype=ot)
+        if with_qd:
+            p["q"] = torch.empty((M, K), dtype=torch.int8, device="cuda")
+            p["d"] = torch.empty((M,), dtype=torch.float32, device="cuda")
+        probs.append(p)
+        refs.append((x, t, ot))
+    grp = bl.DecodeGroup(probs)
+    ys = grp()
+    torch.cuda.synchronize()
+    for p, y, (x, t, ot) in zip(probs, ys, refs):
+        q_ref, d_ref = oracle.quantize_act_absmax(x)
+        acc = oracle.mpgemm_acc(q_ref, t)
+        if with_qd:
+            assert np.array_equal(host(p["q"]), q_ref)
+            assert np.array_equal(host(p["d"]).view(np.uint32), d_ref.view(np.uint32))
+        kw = {"i32": "y_i32", "f32": "y_f32", "bf16": "y_bf16"}[ot]
+        check_outputs(acc, GAMMA, d_ref, **{kw: host(y)})
+        # identical to the unfused calls
+        q, d = bl.quantize_act(p["x"])
+        y2 = bl.gemv(p["packed"], p["gamma"], q, d, out_dtype=ot)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y2).view(np.uint8), host(y).view(np.uint8))
+    return grp
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 16])
+def test_decode_group_parity(M):
+    bl = _bl()
+    _decode_group_case(bl, M, [(100, 320), (640, 2560), (33, 64), (2049, 256), (5, 6912)],
+                       seed=40 + M)
+
+
+def test_decode_group_chunked_k_and_no_qd():
+    """K larger than one LDS chunk (several chunks per block), q/d not requested."""
+    bl = _bl()
+    _decode_group_case(bl, 16, [(300, 11008), (64, 4096)], seed=60)
+    _decode_group_case(bl, 4, [(130, 28672)], seed=61, with_qd=False)
+    _decode_group_case(bl, 1, [(17, 28672), (8, 64), (1, 128)], seed=62, out_types=["f32"])
+
+
+def test_decode_group_repeat_and_graph():
+    """Repeated calls and HIP-graph replays give the eager result every time."""
+    bl = _bl()
+    grp = _decode_group_case(bl, 1, [(2560, 2560), (640, 2560)], seed=63)
+    ref = [host(y).copy() for y in grp.outputs]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        grp()
+    for _ in range(3):
+        for y in grp.outputs:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, r in zip(grp.outputs, ref):
+            assert np.array_equal(host(y), r)
+
+
+def test_config2_layer_decode_groups():
+    """BitNet-2B-like layer at batch 1 through the fused decode groups of a real
+    decoder layer: {q, k, v}, {o}, {gate, up}, {down}."""
+    bl = _bl()
+    cfg = W.CONFIGS[2]
+    groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    by_name = {p.name: p for p in cfg.projs}
+    for names in groups:
+        probs, refs = [], []
+        for nm in names:
+            inp = W.proj_inputs(cfg, by_name[nm], 1)
+            probs.append(dict(packed=bl.pack_i2s(dev(inp.w_tern)),
+                              gamma=dev(np.array([inp.gamma], np.float32)),
+                              x=dev_bf16(inp.x_bf16), out_dtype="bf16"))
+            refs.append(inp)
+        say(f"config 2 decode group {names}")
+        ys = bl.decode_group(probs)
+        torch.cuda.synchronize()
+        for y, inp in zip(ys, refs):
+            q_ref, d_ref = oracle.quantize_act_absmax(inp.x_bf16)
+            acc = oracle.mpgemm_acc(q_ref, inp.w_tern)
+            check_outputs(acc, np.float32(inp.gamma), d_ref, y_bf16=host(y))
+
+
+# ---------------------------------------------------------------------------
 # full pipelines at the layer shapes
 # ---------------------------------------------------------------------------
 

@@ -1,0 +1,118 @@
+"""Host-side model of the decode and GEMM kernels' global-memory addressing.
+
+The kernels' loads are made unconditional (clamped) so the compiler can
+overlap them; this model recomputes, for every block, wave, lane and
+unrolled slot, the byte ranges those loads touch and checks they stay inside
+the buffers, for the shapes the GPU tests and the benchmark use plus edge
+cases. It mirrors the index arithmetic of k_decode_fast (gemv_i2s.hip) and
+k_gemm_i2s (gemm_i2s.hip); it runs on the CPU and launches nothing.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+WAVE = 64
+LANES = np.arange(WAVE)
+R_OF = LANES & 15
+H_OF = LANES >> 4
+
+
+def decode_fast_ranges(N, K, M, WK=4, U=None, ldx=None):
+    """Yield (buffer, lo, hi) byte ranges of every load of one decode problem."""
+    assert K % 64 == 0
+    if K == 0:                      # routed to the zero-output kernel: no loads
+        return
+    ldx = K if ldx is None else ldx
+    RB = K // 4
+    nsteps = (K + 255) // 256
+    length = (nsteps + WK - 1) // WK
+    if U is None:
+        U = 4 if length <= 4 else 8
+    WR = 4 // WK
+    blocks = (N + 16 * WR - 1) // (16 * WR)
+    XREG, QREG = 8, 2
+    for b, wv in itertools.product(range(blocks), range(4)):
+        wr, wk = wv // WK, wv % WK
+        n0 = (b * WR + wr) * 16
+        ja = min(wk * length, nsteps)
+        jb = min(ja + length, nsteps)
+        klo, khi = min(ja * 256, K), min(jb * 256, K)
+        kw = khi - klo
+        rows = np.minimum(n0 + R_OF, N - 1)
+        starts = list(range(ja, jb, 2 * U)) or [ja]
+        for j in starts:
+            for base in (j, j + U, j + 2 * U):
+                for u in range(U):
+                    step = max(min(base + u, jb - 1), 0)
+                    off = np.minimum(step * 64 + 16 * H_OF, RB - 16)
+                    lo = rows * RB + off
+                    yield "packed", lo.min(), (lo + 16).max(), N * RB
+        cpt = kw // 4
+        if M == 1 and 0 < cpt <= XREG * WAVE:          # x chunks kept in registers
+            for u in range(XREG):
+                c = np.minimum(LANES + u * WAVE, cpt - 1)
+                lo = 2 * (klo + 4 * c)
+                yield "x", lo.min(), (lo + 8).max(), 2 * ((M - 1) * ldx + K)
+        c16 = kw // 16
+        if M == 1 and 0 < c16 <= QREG * WAVE:          # q chunks kept in registers
+            for u in range(QREG):
+                c = np.minimum(LANES + u * WAVE, c16 - 1)
+                lo = klo + 16 * c
+                yield "q", lo.min(), (lo + 16).max(), M * K
+
+
+def gemm_ranges(N, K, M, RT=4, TT=4, BK=256):
+    """Yield byte ranges of every load of k_gemm_i2s (guarded loads only)."""
+    BN, BM = 2 * RT * 16, 2 * TT * 16
+    RB = K // 4
+    chunks = BM * BK // 16 // 256
+    nks = (K + BK - 1) // BK
+    tid = np.arange(256)
+    for bx, by, ks in itertools.product(range((N + BN - 1) // BN), range((M + BM - 1) // BM),
+                                        range(nks)):
+        m0 = by * BM
+        for u in range(chunks):
+            c = tid + u * 256
+            tok = m0 + c // 16
+            k = ks * BK + (c % 16) * 16
+            ok = (tok < M) & (k < K)
+            if ok.any():
+                lo = (tok * K + k)[ok]
+                yield "q", lo.min(), (lo + 16).max(), M * K
+        for wv in range(4):
+            wr = wv >> 1
+            n0 = bx * BN + wr * RT * 16
+            kw = ks * BK + 64 * H_OF
+            for rt in range(RT):
+                row = n0 + rt * 16 + R_OF
+                ok = (row < N) & (kw < K)
+                if ok.any():
+                    lo = (row * RB + kw // 4)[ok]
+                    yield "packed", lo.min(), (lo + 16).max(), N * RB
+
+
+DECODE_SHAPES = [(1, 64, 1), (5, 64, 1), (17, 128, 1), (640, 2560, 1), (2560, 6912, 1),
+                 (100, 320, 4), (33, 64, 16), (2049, 256, 2), (5, 6912, 1), (300, 11008, 1),
+                 (8, 64, 1), (1, 128, 1), (3, 0, 1), (130, 1024, 4), (7, 4096, 1)]
+
+
+@pytest.mark.parametrize("N,K,M", DECODE_SHAPES, ids=[f"N{n}K{k}M{m}" for n, k, m in DECODE_SHAPES])
+def test_decode_loads_in_bounds(N, K, M):
+    for U in (4, 8):
+        for buf, lo, hi, size in decode_fast_ranges(N, K, M, U=U):
+            assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_decode_zero_k_launches_no_loads():
+    assert list(decode_fast_ranges(5, 0, 3)) == []
+
+
+GEMM_SHAPES = [(1, 64, 17), (130, 256, 17), (64, 2560, 64), (640, 320, 100), (257, 576, 129),
+               (48, 6912, 65), (40, 256, 200), (7, 0, 20)]
+
+
+@pytest.mark.parametrize("N,K,M", GEMM_SHAPES, ids=[f"N{n}K{k}M{m}" for n, k, m in GEMM_SHAPES])
+def test_gemm_loads_in_bounds(N, K, M):
+    for buf, lo, hi, size in gemm_ranges(N, K, M):
+        assert 0 <= lo and hi <= size, (buf, lo, hi, size)
