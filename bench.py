@@ -39,6 +39,29 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fast_traffic.json")
+DECODE_SOURCES = ("mpgemm_token_absmax_amd/csrc/gemv_i2s.hip",
+                  "mpgemm_token_absmax_amd/csrc/common.hpp",
+                  "mpgemm_token_absmax_amd/csrc/launch.hpp")
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain-kernel calibration), or
+    None when the decode kernel's sources changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for rel in DECODE_SOURCES:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def parse():
@@ -51,6 +74,9 @@ def parse():
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--traffic", action="store_true",
+                   help="counter-collection mode: a 256 MiB plain copy (calibration) and "
+                        "eager decode launches over distinct weight copies; no JSON line")
     return p.parse_args()
 
 
@@ -109,6 +135,19 @@ def main():
     def step(r):
         for launch in layers[r]:
             launch()
+
+    if args.traffic:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src).fill_(0)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)       # calibration kernel: 256 MiB read, 256 MiB written
+        torch.cuda.synchronize()
+        for r in range(R):                    # each launch reads weights no earlier launch read
+            step(r)
+        torch.cuda.synchronize()
+        log(f"traffic mode: 1 calibration kernel over {src.numel()} B, {R * len(GROUPS)} decode launches "
+            f"({step_bytes // len(GROUPS)} packed bytes per launch on average)")
+        return
 
     def step_unfused(r):        # 7 x (bl_quantize_act + bl_gemv), for comparison
         for launch in layers[r]:
@@ -206,7 +245,8 @@ def main():
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                    "unfused_us_per_step": round(us_unfused, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
                      "kernel": "k_gemv_i2s (fused decode group)",
                      "us_per_launch": round(us_launch, 3), "bytes_per_launch": bytes_launch},
     }
