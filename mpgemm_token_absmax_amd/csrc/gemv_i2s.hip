@@ -278,21 +278,26 @@ __global__ __launch_bounds__(kThreads) void k_gemv_i2s(DecodeGroup grp) {
   }
 }
 
-// Fast decode kernel (every problem's per-wave activation slice fits in LDS):
-// each wave owns a contiguous range of 256-weight steps and builds the int8
-// activations of exactly that range in a wave-private LDS region, so the only
-// block barriers are the per-token absmax exchange (fused path) and the final
-// K-split reduction. The activation work overlaps the weight loads, which are
-// issued first. Wave-uniform quantities are forced into scalar registers so
-// the step loop has no per-lane control flow: rows past N load a valid row
-// (their outputs are never stored) and lanes past the end of K load a valid
-// address whose products meet zero activations (the LDS tail is zero-filled).
-template <int RTW, int WK, int U>
+// Fast decode kernel (every problem's per-wave activation slice fits in LDS).
+// Each wave owns a contiguous range of 256-weight steps and builds the int8
+// activations of exactly that range in a wave-private LDS region.
+//  * Vector loads retire in issue order, so the activation loads are issued
+//    before the weight loads: waiting for them never waits for the HBM stream.
+//  * XF > 0 (fused, one token, K <= XF*512): every wave reads the whole bf16
+//    row and takes its absmax itself, so no block barrier precedes the MFMA
+//    loop; otherwise the waves exchange per-token maxima through LDS (one
+//    barrier).
+//  * Wave-uniform values live in scalar registers and loads are unconditional
+//    with clamped, always-valid addresses (rows past N read row N-1 and are
+//    never stored; lanes past K meet zero activations), so the step loop has
+//    no per-lane control flow and the compiler waits only for the loads it
+//    needs.
+template <int RTW, int WK, int U, int XF>
 __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int len_max) {
   constexpr int WR = kWavesPerBlock / WK;
   extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][M][len_max*256]
   __shared__ v4i red[WK > 1 ? WK - 1 : 1][WR][RTW][kWave];
-  __shared__ uint32_t smax[kMaxDecodeM];
+  __shared__ uint32_t wmax[kWavesPerBlock][kMaxDecodeM];
 
   int pi = 0;
 #pragma unroll
@@ -323,7 +328,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
   const int region = len_max * 256;                   // bytes per token row in LDS
   int8_t* wact = act + wv * M * region;
 
-  // per-lane row pointers (rows past N read row N-1; never stored)
   const uint8_t* wrow[RTW];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
@@ -332,10 +336,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
     wrow[rt] = P.packed + row * RB;
   }
   v4i wa[U][RTW], wb[U][RTW];
-  // Loads are unconditional (so the compiler can count outstanding loads and
-  // wait for older ones only): slots past the wave's range re-read its last
-  // step (never used), lanes past K read a valid address whose products meet
-  // zero activations.
   auto load_w = [&](v4i (&dst)[U][RTW], int j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -348,22 +348,30 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
     }
   };
 
-  // Vector loads retire in issue order, so the activation loads (small, L2
-  // resident) are issued before the weight loads: waiting for them then does
-  // not wait for the weights, and the activation work overlaps the HBM stream.
-  const int cpt = kw / 4;                             // 4-element chunks per token
-  const bool cache = xg && M == 1 && cpt <= kXReg * kWave;
-  const int c16 = kw / 16;
-  const bool qcache = !xg && M == 1 && c16 <= kQReg * kWave;
+  // ---- 1. activation loads (before the weights) -------------------------
+  const bool full_row = XF > 0 && xg && M == 1 && K <= XF * 512;
+  const int nch8 = K / 8;                             // 8-value chunks of the row
+  uint4 xf[XF > 0 ? XF : 1];
+  if (full_row) {
+#pragma unroll
+    for (int u = 0; u < XF; ++u) {
+      const int c = min(lane + u * kWave, nch8 - 1);
+      xf[u] = *reinterpret_cast<const uint4*>(xg + 8 * c);
+    }
+  }
+  const int cpt = kw / 4;                             // 4-value chunks of this wave's range
+  const bool cache = xg && !full_row && M == 1 && cpt <= kXReg * kWave;
   uint2 xv[kXReg];
-  v4i qv[kQReg];
   if (cache && cpt > 0) {
 #pragma unroll
-    for (int u = 0; u < kXReg; ++u) {                 // clamped: lanes past the range reload
-      const int c = min(lane + u * kWave, cpt - 1);   // the last chunk (masked when used)
+    for (int u = 0; u < kXReg; ++u) {
+      const int c = min(lane + u * kWave, cpt - 1);
       xv[u] = *reinterpret_cast<const uint2*>(xg + klo + 4 * c);
     }
   }
+  const int c16 = kw / 16;
+  const bool qcache = !xg && M == 1 && c16 <= kQReg * kWave;
+  v4i qv[kQReg];
   if (qcache && c16 > 0) {
 #pragma unroll
     for (int u = 0; u < kQReg; ++u) {
@@ -374,14 +382,39 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
   const float gam = P.ytype ? P.gamma[0] : 0.0f;      // epilogue operands, fetched early
   const float din_r = (!xg && P.ytype) ? P.din[r < M ? r : 0] : 0.0f;
   __builtin_amdgcn_sched_barrier(0);
-  if (xg && tid < M) smax[tid] = 0u;
-  load_w(wa, ja);                                     // weights in flight from here on
+  // ---- 2. weight loads --------------------------------------------------
+  load_w(wa, ja);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- activations of this wave's range -> int8 in the wave's LDS region
-  float s_lane = 0.0f, d_lane = 0.0f;                 // lane t < M: token t's scales
-  if (xg) {
-    __syncthreads();                                  // smax initialised
+  // ---- 3. int8 activations of this wave's range -> its LDS region -------
+  float d_lane = 0.0f;                                // lane t < M: token t's d
+  const bool write_q = first_block && wr == 0 && P.q;
+  if (full_row) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int u = 0; u < XF; ++u)
+      if (lane + u * kWave < nch8)
+        m = max(m, max(absmax4_bf16(make_uint2(xf[u].x, xf[u].y)),
+                       absmax4_bf16(make_uint2(xf[u].z, xf[u].w))));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, kWave));
+    const float mf = __uint_as_float(m << 16);
+    const float s = m ? 127.0f / mf : 0.0f;
+    d_lane = m ? mf / 127.0f : 0.0f;
+    if (first_block && wv == 0 && lane == 0 && P.d) P.d[0] = d_lane;
+    const int c_lo = klo / 8, c_hi = khi / 8;
+#pragma unroll
+    for (int u = 0; u < XF; ++u) {
+      const int c = lane + u * kWave;
+      if (c >= c_lo && c < c_hi) {
+        const uint32_t lo = s != 0.0f ? quant4_bf16(make_uint2(xf[u].x, xf[u].y), s) : 0u;
+        const uint32_t hi = s != 0.0f ? quant4_bf16(make_uint2(xf[u].z, xf[u].w), s) : 0u;
+        *reinterpret_cast<uint2*>(wact + 8 * (c - c_lo)) = make_uint2(lo, hi);
+        if (write_q) *reinterpret_cast<uint2*>(P.q + 8 * c) = make_uint2(lo, hi);
+      }
+    }
+  } else if (xg) {
+    // per-token maxima of this wave's range, exchanged through LDS (1 barrier)
     for (int t = 0; t < M; ++t) {
       uint32_t m = 0u;
       if (cache) {
@@ -395,17 +428,19 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
       }
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, kWave));
-      if (lane == 0 && m) atomicMax(&smax[t], m);
+      if (lane == 0) wmax[wv][t] = m;
     }
-    __syncthreads();                                  // all maxima in
+    __syncthreads();
+    float s_lane = 0.0f;
     if (lane < M) {
-      const uint32_t mb = smax[lane];
+      uint32_t mb = wmax[0][lane];
+#pragma unroll
+      for (int w = 1; w < kWavesPerBlock; ++w) mb = max(mb, wmax[w][lane]);
       const float m = __uint_as_float(mb << 16);
       s_lane = mb ? 127.0f / m : 0.0f;
       d_lane = mb ? m / 127.0f : 0.0f;
       if (first_block && wv == 0 && P.d) P.d[lane] = d_lane;
     }
-    const bool write_q = first_block && wr == 0 && P.q;
     for (int t = 0; t < M; ++t) {
       const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                     __builtin_bit_cast(int, s_lane), t));
@@ -432,7 +467,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
       }
     }
   } else if (qcache) {
-    // plain GEMV, one token: the q range is already in registers
     v4i* dst = reinterpret_cast<v4i*>(wact);
 #pragma unroll
     for (int u = 0; u < kQReg; ++u) {
@@ -440,7 +474,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
       if (c < c16) dst[c] = qv[u];
     }
   } else {
-    // plain GEMV: copy this wave's q range into its region (16-byte chunks)
     for (int t = 0; t < M; ++t) {
       const v4i* src = reinterpret_cast<const v4i*>(P.qin + (int64_t)t * K + klo);
       v4i* dst = reinterpret_cast<v4i*>(wact + t * region);
@@ -452,29 +485,40 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
     v4i* dst = reinterpret_cast<v4i*>(wact + t * region);
     for (int c = kw / 16 + lane; c < len * 16; c += kWave) dst[c] = v4i{0, 0, 0, 0};
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  // The region is private to this wave and LDS serves a wave's accesses in
+  // order, so its reads below see these writes without a fence.
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  v4i acc[RTW];
+  // ---- 4. MFMA over this wave's steps -----------------------------------
+  v4i acc0[RTW], acc1[RTW];                           // two chains (even / odd s)
 #pragma unroll
-  for (int i = 0; i < RTW; ++i) acc[i] = v4i{0, 0, 0, 0};
+  for (int i = 0; i < RTW; ++i) acc0[i] = acc1[i] = v4i{0, 0, 0, 0};
   const bool tok_ok = r < M;
   const int8_t* arow = wact + (tok_ok ? r : 0) * region + 64 * h;
+  auto read_b = [&](v4i (&b)[4], int j) {             // activation fragments of step j
+    const int kk = (j - ja) * 256;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const v4i v = *reinterpret_cast<const v4i*>(arow + kk + 16 * s);
+      b[s] = tok_ok ? v : v4i{0, 0, 0, 0};
+    }
+  };
   auto compute = [&](const v4i (&w)[U][RTW], int j) {
+    v4i bn[4];
+    read_b(bn, j);                                    // issued before the weights are awaited
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j + u < jb) {
-        const int kk = (j + u - ja) * 256;
+        v4i b[4] = {bn[0], bn[1], bn[2], bn[3]};
+        if (u + 1 < U && j + u + 1 < jb) read_b(bn, j + u + 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          v4i b = *reinterpret_cast<const v4i*>(arow + kk + 16 * s);
-          b = tok_ok ? b : v4i{0, 0, 0, 0};
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int rt = 0; rt < RTW; ++rt)
-            acc[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]),
-                                                            b, acc[rt], 0, 0, 0);
-        }
+          for (int rt = 0; rt < RTW; ++rt) {
+            v4i& a = (s & 1) ? acc1[rt] : acc0[rt];
+            a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]), b[s], a,
+                                                      0, 0, 0);
+          }
       }
     }
   };
@@ -484,7 +528,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
     if (j + 2 * U < jb) load_w(wa, j + 2 * U);
     if (j + U < jb) compute(wb, j + U);
   }
+  v4i acc[RTW];
+#pragma unroll
+  for (int i = 0; i < RTW; ++i) acc[i] = acc0[i] + acc1[i];
 
+  // ---- 5. K-split reduction and the fused dequant store -----------------
   if constexpr (WK > 1) {
     if (wk > 0) {
 #pragma unroll
@@ -500,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_fast(DecodeGroup grp, int l
 
   // D[i][j] of the 16x16 MFMA: lane holds column j = lane%16 (token) and rows
   // i = 4*(lane/16) + v (output features), v = 0..3.
-  const float dr = xg ? __shfl(d_lane, tok_ok ? r : 0, kWave) : din_r;
+  const float dr = xg ? (full_row ? d_lane : __shfl(d_lane, tok_ok ? r : 0, kWave)) : din_r;
   if (!tok_ok) return;
   const float c = gam * dr;
 #pragma unroll
@@ -581,7 +629,7 @@ hipError_t launch_zero_outputs(const DecodeProblem& p, int M, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int RTW, int WK, int U>
+template <int RTW, int WK, int U, int XF>
 hipError_t launch_fast(DecodeGroup& g, int len_max, hipStream_t s) {
   constexpr int WR = kWavesPerBlock / WK;
   constexpr int64_t rows_per_block = (int64_t)WR * RTW * 16;
@@ -592,7 +640,7 @@ hipError_t launch_fast(DecodeGroup& g, int len_max, hipStream_t s) {
   }
   if (blocks == 0) return hipSuccess;
   const size_t lds = (size_t)kWavesPerBlock * g.M * len_max * 256;
-  hipLaunchKernelGGL((k_decode_fast<RTW, WK, U>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((k_decode_fast<RTW, WK, U, XF>), dim3((unsigned)blocks), dim3(kThreads),
                      lds < 16 ? 16 : lds, s, g, len_max);
   return hipGetLastError();
 }
@@ -621,9 +669,17 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
     const int len = (int)((steps + kFastWK - 1) / kFastWK);
     if (len > len_max) len_max = len;
   }
-  if ((int64_t)kWavesPerBlock * g.M * len_max * 256 <= kActLds)
-    return len_max <= 4 ? launch_fast<1, kFastWK, 4>(g, len_max, s)
-                        : launch_fast<1, kFastWK, 8>(g, len_max, s);
+  if ((int64_t)kWavesPerBlock * g.M * len_max * 256 <= kActLds) {
+    int64_t kmax = 0;
+    for (int i = 0; i < g.count; ++i) kmax = g.p[i].K > kmax ? g.p[i].K : kmax;
+    const bool fused1 = g.M == 1 && g.p[0].x != nullptr;   // whole-row absmax per wave
+    if (len_max <= 4) {
+      if (fused1 && kmax <= 8 * 512) return launch_fast<1, kFastWK, 4, 8>(g, len_max, s);
+      return launch_fast<1, kFastWK, 4, 0>(g, len_max, s);
+    }
+    if (fused1 && kmax <= 16 * 512) return launch_fast<1, kFastWK, 8, 16>(g, len_max, s);
+    return launch_fast<1, kFastWK, 8, 0>(g, len_max, s);
+  }
   if (row_tiles >= 2048) return launch_cfg<1, 2, 8>(g, s);
   return launch_cfg<1, 4, 8>(g, s);
 }

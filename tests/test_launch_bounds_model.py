@@ -48,8 +48,16 @@ def decode_fast_ranges(N, K, M, WK=4, U=None, ldx=None):
                     off = np.minimum(step * 64 + 16 * H_OF, RB - 16)
                     lo = rows * RB + off
                     yield "packed", lo.min(), (lo + 16).max(), N * RB
+        XF = (8 if length <= 4 else 16) if M == 1 else 0
+        full_row = XF > 0 and K <= XF * 512            # whole bf16 row per wave (fused, M = 1)
+        if full_row:
+            nch8 = K // 8
+            for u in range(XF):
+                c = np.minimum(LANES + u * WAVE, nch8 - 1)
+                lo = 16 * c
+                yield "x", lo.min(), (lo + 16).max(), 2 * K
         cpt = kw // 4
-        if M == 1 and 0 < cpt <= XREG * WAVE:          # x chunks kept in registers
+        if M == 1 and not full_row and 0 < cpt <= XREG * WAVE:   # x range kept in registers
             for u in range(XREG):
                 c = np.minimum(LANES + u * WAVE, cpt - 1)
                 lo = 2 * (klo + 4 * c)
