@@ -10,19 +10,25 @@
 // runs on v_mfma_i32_16x16x64_i8 with the ternary weights decoded to int8 in
 // registers just before the MFMA.
 //
-// Block = 4 waves as 2 (rows) x 2 (tokens); wave tile = RT*16 output features
-// x TT*16 tokens; K advances 256 weights per step (4 MFMA sub-steps of 64).
-//   * activations (int8, the large operand per byte of work) are staged per
-//     step into LDS as a [128 tokens][256 + 16 pad] byte tile, shared by the
-//     two waves of each token half; the next step's tile is prefetched into
-//     registers while the current one is consumed;
-//   * packed weights (2 bits, 4x smaller) go straight from global memory to
-//     registers: lane (r = lane%16, h = lane/16) loads 16 bytes of row r
-//     covering weights 64h .. 64h+63 of the step; its 32-bit word s decodes
-//     (9 VALU ops) to the 16 int8 weights 64h+16s .. +15, which the MFMA of
-//     sub-step s pairs with activation bytes 64h+16s .. +15 of token r. The
-//     same lane -> k assignment on both operands makes the MFMA's 64-term dot
-//     exactly the sum over those k.
+// Block = 4 waves as WRW (feature rows) x WTW (tokens); wave tile = RT*16
+// output features x TT*16 tokens; K advances 128 weights per step (two MFMA
+// sub-steps of 64).
+//  * Both operands of a step are staged in LDS by direct-to-LDS loads
+//    (global_load_lds_dwordx4: no register staging); STAGES steps are in
+//    flight, one barrier per step. Each 16-byte chunk of a 128-byte
+//    activation row is stored at chunk (c XOR t%8), which keeps the MFMA
+//    fragment reads free of bank conflicts.
+//  * Lane (r = lane%16, h = lane/16) of a sub-step s covers k = 32h + 16s ..
+//    +15 of the step on both operands: the 32-bit packed word of that k range
+//    decodes (9 VALU ops) to 16 int8 weights that the MFMA pairs with the 16
+//    activation bytes of the same k range, so the MFMA's 64-term dot is
+//    exactly the sum over those k.
+//  * Loads are unconditional with clamped addresses; out-of-range tokens and
+//    rows only reach outputs that are never stored, and weights past K are
+//    zeroed before the MFMA, so stale activations there add nothing.
+//  * Blocks are ordered so that consecutive blocks on one XCD (blocks are
+//    dealt to the 8 XCDs round robin) share a token tile, whose activations
+//    then stay in that XCD's L2.
 // Accumulation is exact int32; the dequant (acc * fl32(gamma * d_t)) is fused
 // into the store.
 #include "common.hpp"
@@ -32,8 +38,10 @@ namespace bl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 256;                 // weights (k) per step
-constexpr int kLdsStride = kBK + 16;     // padded bytes per token row in LDS
+constexpr int kBK = 128;                 // weights (k) per step
+constexpr int kXcds = 8;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_t t, int64_t n,
                                            v4i acc, float c) {
@@ -62,88 +70,149 @@ __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_
   }
 }
 
-template <int RT, int TT>
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] (15) | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+template <int RT, int TT, int WRW, int STAGES>
+struct GemmCfg {
+  static constexpr int WTW = 4 / WRW;
+  static constexpr int BN = WRW * RT * 16;            // output features per block
+  static constexpr int BM = WTW * TT * 16;            // tokens per block
+  static constexpr int kBBytes = BM * kBK;            // activation tile per stage
+  static constexpr int kABytes = BN * (kBK / 4);      // packed weight tile per stage
+  static constexpr int kStage = kBBytes + kABytes;
+  static constexpr int kLds = STAGES * kStage;
+  static constexpr int kBLoads = kBBytes / (16 * kThreads);   // per wave per stage
+  static constexpr int kALoads = (kABytes + 16 * kThreads - 1) / (16 * kThreads);
+  static constexpr int kLoads = kBLoads + kALoads;
+  static_assert(kBBytes % (16 * kThreads) == 0, "activation tile must split over the block");
+};
+
+// Direct-to-LDS loads of step ks into its stage (see k_gemm_i2s).
+template <int NB, int STAGES, int kStage, int kBBytes>
+__device__ __forceinline__ void issue_step(int8_t* smem, int ks, int wv, int lane,
+                                           const int8_t* const (&bsrc)[NB], int bchunk,
+                                           const uint8_t* asrc, bool has_a, int64_t K,
+                                           int64_t RB) {
+  int8_t* st = smem + (ks % STAGES) * kStage;
+  const int64_t kb = (int64_t)ks * kBK;
+  // chunks past K (the last step when K % 128 == 64) re-read a chunk 64
+  // weights earlier in the same row: valid memory, products with zeroed weights
+  int64_t boff = kb + bchunk;
+  if (boff >= K) boff -= 64;
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    __builtin_amdgcn_global_load_lds(bsrc[i] + boff, (lds_void*)(st + (i * 4 + wv) * 1024), 16,
+                                     0, 0);
+  if (has_a) {                                        // wave-uniform
+    int64_t aoff = kb / 4 + 16 * (lane & 1);
+    if (aoff >= RB) aoff -= 16;
+    __builtin_amdgcn_global_load_lds(asrc + aoff, (lds_void*)(st + kBBytes + wv * 1024), 16, 0,
+                                     0);
+  }
+}
+
+template <int RT, int TT, int WRW, int STAGES>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma, int64_t N, int64_t K,
     const int8_t* __restrict__ q, const float* __restrict__ d, int64_t M, void* __restrict__ y,
-    int ytype) {
-  constexpr int BN = 2 * RT * 16;       // output features per block
-  constexpr int BM = 2 * TT * 16;       // tokens per block
-  constexpr int kChunks = BM * kBK / 16 / kThreads;   // 16-byte activation chunks per thread
-  static_assert(kChunks * kThreads * 16 == BM * kBK, "tile/threads mismatch");
-  __shared__ __attribute__((aligned(16))) int8_t bs[BM * kLdsStride];
+    int ytype, int n_row_blocks, int n_tok_blocks) {
+  using C = GemmCfg<RT, TT, WRW, STAGES>;
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+
+  // XCD-aware order: block b runs on XCD b % 8; give each XCD a contiguous run
+  // of the tile sequence (token-tile major) so its blocks share activations.
+  const int nb = n_row_blocks * n_tok_blocks;
+  int lin = blockIdx.x;
+  if (nb % kXcds == 0) lin = (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds;
+  const int tb = lin / n_row_blocks, rb = lin % n_row_blocks;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
-  const int wr = wv >> 1, wt = wv & 1;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wv % WRW, wt = wv / WRW;
   const int r = lane & 15, h = lane >> 4;
   const int64_t RB = K / 4;
-  const int64_t n0 = (int64_t)blockIdx.x * BN + wr * RT * 16;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t nks = (K + kBK - 1) / kBK;
+  const int64_t n_blk = (int64_t)rb * C::BN;
+  const int64_t m_blk = (int64_t)tb * C::BM;
+  const int nks = (int)((K + kBK - 1) / kBK);
 
-  // activation staging: chunk c -> token c/16, 16-byte column c%16
-  uint4 stage[kChunks];
-  auto load_b = [&](int64_t ks) {
+  // ---- per-lane source addresses of the direct-to-LDS loads ---------------
+  // activations: wave instruction i covers tile rows (i*4 + wv)*8 .. +7; lane
+  // l -> row + l/8, LDS chunk p = l%8 holds global chunk p ^ (row%8)
+  const int8_t* bsrc[C::kBLoads];
+  const int bchunk = 16 * ((lane & 7) ^ (lane >> 3 & 7));   // t%8 == (lane>>3)%8 for every i
 #pragma unroll
-    for (int u = 0; u < kChunks; ++u) {
-      const int c = tid + u * kThreads;
-      const int64_t tok = m0 + c / 16;
-      const int64_t k = ks * kBK + (c % 16) * 16;
-      stage[u] = (tok < M && k < K) ? *reinterpret_cast<const uint4*>(q + tok * K + k)
-                                    : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_b = [&]() {
-#pragma unroll
-    for (int u = 0; u < kChunks; ++u) {
-      const int c = tid + u * kThreads;
-      *reinterpret_cast<uint4*>(bs + (c / 16) * kLdsStride + (c % 16) * 16) = stage[u];
-    }
-  };
-  uint4 wa[RT];
-  auto load_a = [&](int64_t ks) {
-    const int64_t kw = ks * kBK + 64 * h;       // first weight of this lane's chunk
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int64_t row = n0 + rt * 16 + r;
-      wa[rt] = (row < N && kw < K) ? *reinterpret_cast<const uint4*>(packed + row * RB + kw / 4)
-                                   : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-
+  for (int i = 0; i < C::kBLoads; ++i) {
+    const int t = (i * 4 + wv) * 8 + (lane >> 3);
+    int64_t tok = m_blk + t;
+    tok = tok < M ? tok : M - 1;
+    bsrc[i] = q + tok * K;
+  }
+  // packed weights: 32 bytes per row per step; wave instruction i covers rows
+  // (i*4 + wv)*32 + l/2, lane half l%2
+  static_assert(C::kALoads == 1, "one packed-weight load per wave and step");
+  const bool has_a = wv * 32 < C::BN;                 // waves past the tile's rows load nothing
+  const uint8_t* asrc[1];
+  {
+    const int row = wv * 32 + (lane >> 1);
+    int64_t n = n_blk + (row < C::BN ? row : C::BN - 1);
+    n = n < N ? n : N - 1;
+    asrc[0] = packed + n * RB;
+  }
   v4i acc[RT][TT];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < TT; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  load_a(0);
-  load_b(0);
-  for (int64_t ks = 0; ks < nks; ++ks) {
-    __syncthreads();                 // every wave is done reading the previous tile
-    store_b();
-    __syncthreads();
-    uint4 wcur[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) wcur[rt] = wa[rt];
-    if (ks + 1 < nks) {              // prefetch the next step while this one computes
-      load_a(ks + 1);
-      load_b(ks + 1);
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nks)
+      issue_step<C::kBLoads, STAGES, C::kStage, C::kBBytes>(smem, s, wv, lane, bsrc, bchunk,
+                                                            asrc[0], has_a, K, RB);
+
+  for (int ks = 0; ks < nks; ++ks) {
+    // this wave's loads of step ks are done once at most (STAGES-2) steps of
+    // loads are still outstanding behind them
+    if (ks + STAGES - 2 < nks) {
+      if (has_a) wait_vm<C::kLoads * (STAGES - 2)>();
+      else wait_vm<C::kBLoads * (STAGES - 2)>();
+    } else {
+      wait_vm<0>();
     }
-    const int8_t* bw = bs + (wt * TT * 16 + r) * kLdsStride + 64 * h;
+    __syncthreads();          // every wave's step-ks data is in LDS, step ks-1 is consumed
+    if (ks + STAGES - 1 < nks)
+      issue_step<C::kBLoads, STAGES, C::kStage, C::kBBytes>(smem, ks + STAGES - 1, wv, lane, bsrc,
+                                                            bchunk, asrc[0], has_a, K, RB);
+
+    const int8_t* st = smem + (ks % STAGES) * C::kStage;
+    const int8_t* sa = st + C::kBBytes;
+    const int64_t kb = (int64_t)ks * kBK;
+    // packed words of the two sub-steps: row rt*16 + r, bytes 8h .. 8h+7
+    uint2 aw[RT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int rt = 0; rt < RT; ++rt)
+      aw[rt] = *reinterpret_cast<const uint2*>(sa + (wr * RT * 16 + rt * 16 + r) * 32 + 8 * h);
+    const bool kin = kb + 32 * h < K;                 // this lane's 32 weights exist
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
       v4i bf[TT];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-        bf[tt] = *reinterpret_cast<const v4i*>(bw + tt * 16 * kLdsStride + 16 * s);
+      for (int tt = 0; tt < TT; ++tt) {
+        const int t = wt * TT * 16 + tt * 16 + r;
+        const int p = (2 * h + s) ^ (t & 7);
+        bf[tt] = *reinterpret_cast<const v4i*>(st + t * kBK + 16 * p);
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const uint32_t word = s == 0 ? wcur[rt].x : s == 1 ? wcur[rt].y : s == 2 ? wcur[rt].z
-                                                                                 : wcur[rt].w;
-        const v4i af = decode_word(word);
+        v4i af = decode_word(s == 0 ? aw[rt].x : aw[rt].y);
+        if (!kin) af = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
           acc[rt][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[tt], acc[rt][tt], 0, 0, 0);
@@ -154,25 +223,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
   // D layout: lane holds token (column) lane%16 and features 4*(lane/16) + v.
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
-    const int64_t tok = m0 + wt * TT * 16 + tt * 16 + r;
+    const int64_t tok = m_blk + wt * TT * 16 + tt * 16 + r;
     if (tok >= M) continue;
     const float c = ytype ? gamma[0] * d[tok] : 0.0f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int64_t n = n0 + rt * 16 + 4 * h;
+      const int64_t n = n_blk + wr * RT * 16 + rt * 16 + 4 * h;
       if (n < N) store_quad(y, ytype, N, tok, n, acc[rt][tt], c);
     }
   }
 }
 
-template <int RT, int TT>
+template <int RT, int TT, int WRW, int STAGES>
 hipError_t launch_cfg(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                       const int8_t* q, const float* d, int64_t M, void* y, int ytype,
                       hipStream_t s) {
-  constexpr int BN = 2 * RT * 16, BM = 2 * TT * 16;
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL((k_gemm_i2s<RT, TT>), grid, dim3(kThreads), 0, s, packed, gamma, N, K, q,
-                     d, M, y, ytype);
+  using C = GemmCfg<RT, TT, WRW, STAGES>;
+  const int nrb = (int)((N + C::BN - 1) / C::BN);
+  const int ntb = (int)((M + C::BM - 1) / C::BM);
+  if (C::kLds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_gemm_i2s<RT, TT, WRW, STAGES>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW, STAGES>), dim3((unsigned)(nrb * ntb)),
+                     dim3(kThreads), C::kLds, s, packed, gamma, N, K, q, d, M, y, ytype, nrb, ntb);
   return hipGetLastError();
 }
 
@@ -183,7 +259,10 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, int64_t N, int
                        hipStream_t s) {
   if (K % 64 != 0) return launch_generic(packed, gamma, N, K, q, d, M, y, ytype, s);
   if (M <= 16) return launch_gemv(packed, gamma, N, K, q, d, M, y, ytype, s);
-  return launch_cfg<4, 4>(packed, gamma, N, K, q, d, M, y, ytype, s);
+  // large tiles when they still give every CU work, smaller ones otherwise
+  const int64_t big = ((N + 127) / 128) * ((M + 255) / 256);
+  if (big >= 256) return launch_cfg<4, 8, 2, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
+  return launch_cfg<2, 4, 2, 3>(packed, gamma, N, K, q, d, M, y, ytype, s);
 }
 
 }  // namespace bl

@@ -70,34 +70,33 @@ def decode_fast_ranges(N, K, M, WK=4, U=None, ldx=None):
                 yield "q", lo.min(), (lo + 16).max(), M * K
 
 
-def gemm_ranges(N, K, M, RT=4, TT=4, BK=256):
-    """Yield byte ranges of every load of k_gemm_i2s (guarded loads only)."""
-    BN, BM = 2 * RT * 16, 2 * TT * 16
+def gemm_ranges(N, K, M, RT=4, TT=8, WRW=2):
+    """Yield byte ranges of every direct-to-LDS load of k_gemm_i2s."""
+    BK = 128
+    WTW = 4 // WRW
+    BN, BM = WRW * RT * 16, WTW * TT * 16
     RB = K // 4
-    chunks = BM * BK // 16 // 256
     nks = (K + BK - 1) // BK
-    tid = np.arange(256)
-    for bx, by, ks in itertools.product(range((N + BN - 1) // BN), range((M + BM - 1) // BM),
-                                        range(nks)):
-        m0 = by * BM
-        for u in range(chunks):
-            c = tid + u * 256
-            tok = m0 + c // 16
-            k = ks * BK + (c % 16) * 16
-            ok = (tok < M) & (k < K)
-            if ok.any():
-                lo = (tok * K + k)[ok]
+    n_b_loads = BM * BK // (16 * 256)
+    bchunk = 16 * ((LANES & 7) ^ ((LANES >> 3) & 7))
+    for rb, tb in itertools.product(range((N + BN - 1) // BN), range((M + BM - 1) // BM)):
+        n_blk, m_blk = rb * BN, tb * BM
+        for ks, wv in itertools.product(range(nks), range(4)):
+            kb = ks * BK
+            boff = kb + bchunk
+            boff = np.where(boff >= K, boff - 64, boff)
+            for i in range(n_b_loads):
+                t = (i * 4 + wv) * 8 + (LANES >> 3)
+                tok = np.minimum(m_blk + t, M - 1)
+                lo = tok * K + boff
                 yield "q", lo.min(), (lo + 16).max(), M * K
-        for wv in range(4):
-            wr = wv >> 1
-            n0 = bx * BN + wr * RT * 16
-            kw = ks * BK + 64 * H_OF
-            for rt in range(RT):
-                row = n0 + rt * 16 + R_OF
-                ok = (row < N) & (kw < K)
-                if ok.any():
-                    lo = (row * RB + kw // 4)[ok]
-                    yield "packed", lo.min(), (lo + 16).max(), N * RB
+            if wv * 32 < BN:
+                row = wv * 32 + (LANES >> 1)
+                n = np.minimum(n_blk + np.minimum(row, BN - 1), N - 1)
+                aoff = kb // 4 + 16 * (LANES & 1)
+                aoff = np.where(aoff >= RB, aoff - 16, aoff)
+                lo = n * RB + aoff
+                yield "packed", lo.min(), (lo + 16).max(), N * RB
 
 
 DECODE_SHAPES = [(1, 64, 1), (5, 64, 1), (17, 128, 1), (640, 2560, 1), (2560, 6912, 1),
@@ -117,10 +116,15 @@ def test_decode_zero_k_launches_no_loads():
 
 
 GEMM_SHAPES = [(1, 64, 17), (130, 256, 17), (64, 2560, 64), (640, 320, 100), (257, 576, 129),
-               (48, 6912, 65), (40, 256, 200), (7, 0, 20)]
+               (48, 6912, 65), (40, 256, 200), (7, 64, 20), (300, 192, 300)]
 
 
 @pytest.mark.parametrize("N,K,M", GEMM_SHAPES, ids=[f"N{n}K{k}M{m}" for n, k, m in GEMM_SHAPES])
-def test_gemm_loads_in_bounds(N, K, M):
-    for buf, lo, hi, size in gemm_ranges(N, K, M):
+@pytest.mark.parametrize("tile", [(4, 8, 2), (2, 4, 2)], ids=["128x256", "64x128"])
+def test_gemm_loads_in_bounds(N, K, M, tile):
+    for buf, lo, hi, size in gemm_ranges(N, K, M, *tile):
         assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_gemm_zero_k_issues_no_loads():
+    assert list(gemm_ranges(7, 0, 20)) == []
