@@ -14,10 +14,17 @@
 // output features x TT*16 tokens; K advances 128 weights per step (two MFMA
 // sub-steps of 64).
 //  * Both operands of a step are staged in LDS by direct-to-LDS loads
-//    (global_load_lds_dwordx4: no register staging); STAGES steps are in
-//    flight, one barrier per step. Each 16-byte chunk of a 128-byte
-//    activation row is stored at chunk (c XOR t%8), which keeps the MFMA
-//    fragment reads free of bank conflicts.
+//    (global_load_lds_dwordx4: no register staging) into two stage buffers,
+//    one barrier per step: a wave reads all of step ks's fragments into
+//    registers, then issues step ks+1's loads, which land while its MFMAs
+//    run. LDS has 64 4-byte banks; a 64-bit read serves lanes 0-31 in one
+//    cycle and 32-63 in the next, a 128-bit read serves 16 lanes a cycle,
+//    the lanes of a 32-lane half being split by the parity of lane bits
+//    2..4 (measured with the bank-conflict counter). Conflict-free layouts
+//    for the fragment reads under that rule: chunk c of activation row t
+//    (128 bytes) sits at chunk position c ^ swz(t) (swz below), and a
+//    16-row group of packed weights is stored as [bytes 0-15 of rows 0..15 |
+//    bytes 16-31 of rows 0..15].
 //  * Lane (r = lane%16, h = lane/16) of a sub-step s covers k = 32h + 16s ..
 //    +15 of the step on both operands: the 32-bit packed word of that k range
 //    decodes (9 VALU ops) to 16 int8 weights that the MFMA pairs with the 16
@@ -42,6 +49,14 @@ constexpr int kBK = 128;                 // weights (k) per step
 constexpr int kXcds = 8;
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l
+// writes dst + 16*l, dst is wave-uniform. A plain function, so that no kernel
+// template instantiates the device-only builtin itself (clang's host pass
+// rejects a second template instantiation that reaches it).
+__device__ __forceinline__ void lds_dma16(const void* src, int8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
 
 __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_t t, int64_t n,
                                            v4i acc, float c) {
@@ -70,6 +85,14 @@ __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_
   }
 }
 
+// Chunk swizzle of activation row t: u = (t/2) % 8 with bit 1 flipped when
+// bits 1 and 2 of u differ. Lanes served in one cycle of a 128-bit fragment
+// read then cover all 16 16-byte slots of a 256-byte bank row.
+__device__ __forceinline__ int swz(int t) {
+  const int u = (t >> 1) & 7;
+  return u ^ ((((u >> 1) ^ (u >> 2)) & 1) << 1);
+}
+
 // Wait until at most n vector-memory operations of this wave are outstanding.
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -78,7 +101,7 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-template <int RT, int TT, int WRW, int STAGES>
+template <int RT, int TT, int WRW>
 struct GemmCfg {
   static constexpr int WTW = 4 / WRW;
   static constexpr int BN = WRW * RT * 16;            // output features per block
@@ -86,20 +109,19 @@ struct GemmCfg {
   static constexpr int kBBytes = BM * kBK;            // activation tile per stage
   static constexpr int kABytes = BN * (kBK / 4);      // packed weight tile per stage
   static constexpr int kStage = kBBytes + kABytes;
-  static constexpr int kLds = STAGES * kStage;
+  static constexpr int kLds = 2 * kStage;              // double buffered
   static constexpr int kBLoads = kBBytes / (16 * kThreads);   // per wave per stage
   static constexpr int kALoads = (kABytes + 16 * kThreads - 1) / (16 * kThreads);
-  static constexpr int kLoads = kBLoads + kALoads;
   static_assert(kBBytes % (16 * kThreads) == 0, "activation tile must split over the block");
 };
 
 // Direct-to-LDS loads of step ks into its stage (see k_gemm_i2s).
-template <int NB, int STAGES, int kStage, int kBBytes>
+template <int NB, int NA, int kStage, int kBBytes, int BN>
 __device__ __forceinline__ void issue_step(int8_t* smem, int ks, int wv, int lane,
                                            const int8_t* const (&bsrc)[NB], int bchunk,
-                                           const uint8_t* asrc, bool has_a, int64_t K,
+                                           const uint8_t* const (&asrc)[NA], int64_t K,
                                            int64_t RB) {
-  int8_t* st = smem + (ks % STAGES) * kStage;
+  int8_t* st = smem + (ks & 1) * kStage;
   const int64_t kb = (int64_t)ks * kBK;
   // chunks past K (the last step when K % 128 == 64) re-read a chunk 64
   // weights earlier in the same row: valid memory, products with zeroed weights
@@ -107,22 +129,21 @@ __device__ __forceinline__ void issue_step(int8_t* smem, int ks, int wv, int lan
   if (boff >= K) boff -= 64;
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    __builtin_amdgcn_global_load_lds(bsrc[i] + boff, (lds_void*)(st + (i * 4 + wv) * 1024), 16,
-                                     0, 0);
-  if (has_a) {                                        // wave-uniform
-    int64_t aoff = kb / 4 + 16 * (lane & 1);
-    if (aoff >= RB) aoff -= 16;
-    __builtin_amdgcn_global_load_lds(asrc + aoff, (lds_void*)(st + kBBytes + wv * 1024), 16, 0,
-                                     0);
-  }
+    lds_dma16(bsrc[i] + boff, st + (i * 4 + wv) * 1024);
+  int64_t aoff = kb / 4 + 16 * (lane >> 4 & 1);
+  if (aoff >= RB) aoff -= 16;
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+    if ((i * 4 + wv) * 32 < BN)                       // wave-uniform: rows of the tile exist
+      lds_dma16(asrc[i] + aoff, st + kBBytes + (i * 4 + wv) * 1024);
 }
 
-template <int RT, int TT, int WRW, int STAGES>
+template <int RT, int TT, int WRW>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma, int64_t N, int64_t K,
     const int8_t* __restrict__ q, const float* __restrict__ d, int64_t M, void* __restrict__ y,
     int ytype, int n_row_blocks, int n_tok_blocks) {
-  using C = GemmCfg<RT, TT, WRW, STAGES>;
+  using C = GemmCfg<RT, TT, WRW>;
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
 
   // XCD-aware order: block b runs on XCD b % 8; give each XCD a contiguous run
@@ -134,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;   // 4 waves
   const int wr = wv % WRW, wt = wv / WRW;
   const int r = lane & 15, h = lane >> 4;
   const int64_t RB = K / 4;
@@ -143,10 +164,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
   const int nks = (int)((K + kBK - 1) / kBK);
 
   // ---- per-lane source addresses of the direct-to-LDS loads ---------------
-  // activations: wave instruction i covers tile rows (i*4 + wv)*8 .. +7; lane
-  // l -> row + l/8, LDS chunk p = l%8 holds global chunk p ^ (row%8)
+  // activations: wave instruction i covers tile rows t = (i*4 + wv)*8 + l/8;
+  // LDS chunk p = l%8 of row t holds global chunk p ^ swz(t), and swz(t)
+  // depends on (t/2) % 8 == (4*(wv%2) + l/16) % 8 only, the same for every i
   const int8_t* bsrc[C::kBLoads];
-  const int bchunk = 16 * ((lane & 7) ^ (lane >> 3 & 7));   // t%8 == (lane>>3)%8 for every i
+  const int bchunk = 16 * ((lane & 7) ^ swz(2 * (4 * (wv & 1) + (lane >> 4))));
 #pragma unroll
   for (int i = 0; i < C::kBLoads; ++i) {
     const int t = (i * 4 + wv) * 8 + (lane >> 3);
@@ -155,15 +177,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
     bsrc[i] = q + tok * K;
   }
   // packed weights: 32 bytes per row per step; wave instruction i covers rows
-  // (i*4 + wv)*32 + l/2, lane half l%2
-  static_assert(C::kALoads == 1, "one packed-weight load per wave and step");
-  const bool has_a = wv * 32 < C::BN;                 // waves past the tile's rows load nothing
-  const uint8_t* asrc[1];
-  {
-    const int row = wv * 32 + (lane >> 1);
+  // (i*4 + wv)*32 + 16*(l/32) + l%16, byte half (l/16)%2
+  const uint8_t* asrc[C::kALoads];
+#pragma unroll
+  for (int i = 0; i < C::kALoads; ++i) {
+    const int row = (i * 4 + wv) * 32 + 16 * (lane >> 5) + (lane & 15);
     int64_t n = n_blk + (row < C::BN ? row : C::BN - 1);
     n = n < N ? n : N - 1;
-    asrc[0] = packed + n * RB;
+    asrc[i] = packed + n * RB;
   }
   v4i acc[RT][TT];
 #pragma unroll
@@ -171,54 +192,56 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
 #pragma unroll
     for (int j = 0; j < TT; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nks)
-      issue_step<C::kBLoads, STAGES, C::kStage, C::kBBytes>(smem, s, wv, lane, bsrc, bchunk,
-                                                            asrc[0], has_a, K, RB);
+  if (nks > 0)
+    issue_step<C::kBLoads, C::kALoads, C::kStage, C::kBBytes, C::BN>(smem, 0, wv, lane, bsrc,
+                                                                     bchunk, asrc, K, RB);
 
   for (int ks = 0; ks < nks; ++ks) {
-    // this wave's loads of step ks are done once at most (STAGES-2) steps of
-    // loads are still outstanding behind them
-    if (ks + STAGES - 2 < nks) {
-      if (has_a) wait_vm<C::kLoads * (STAGES - 2)>();
-      else wait_vm<C::kBLoads * (STAGES - 2)>();
-    } else {
-      wait_vm<0>();
-    }
-    __syncthreads();          // every wave's step-ks data is in LDS, step ks-1 is consumed
-    if (ks + STAGES - 1 < nks)
-      issue_step<C::kBLoads, STAGES, C::kStage, C::kBBytes>(smem, ks + STAGES - 1, wv, lane, bsrc,
-                                                            bchunk, asrc[0], has_a, K, RB);
+    wait_vm<0>();             // this wave's loads of step ks have landed
+    __syncthreads();          // every wave's have; every wave is done reading step ks-1
 
-    const int8_t* st = smem + (ks % STAGES) * C::kStage;
+    // All fragments of step ks go to registers before step ks+1 is issued: the
+    // compiler cannot tell the two stages apart and would otherwise wait for
+    // the new loads before these reads, serialising load and compute.
+    const int8_t* st = smem + (ks & 1) * C::kStage;
     const int8_t* sa = st + C::kBBytes;
     const int64_t kb = (int64_t)ks * kBK;
     // packed words of the two sub-steps: row rt*16 + r, bytes 8h .. 8h+7
     uint2 aw[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
-      aw[rt] = *reinterpret_cast<const uint2*>(sa + (wr * RT * 16 + rt * 16 + r) * 32 + 8 * h);
-    const bool kin = kb + 32 * h < K;                 // this lane's 32 weights exist
+      aw[rt] = *reinterpret_cast<const uint2*>(sa + (wr * RT + rt) * 512 + (h >> 1) * 256 +
+                                               r * 16 + 8 * (h & 1));
+    v4i bf[2][TT];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v4i bf[TT];
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         const int t = wt * TT * 16 + tt * 16 + r;
-        const int p = (2 * h + s) ^ (t & 7);
-        bf[tt] = *reinterpret_cast<const v4i*>(st + t * kBK + 16 * p);
+        const int p = (2 * h + s) ^ swz(t);
+        bf[s][tt] = *reinterpret_cast<const v4i*>(st + t * kBK + 16 * p);
       }
+
+    // unconditional, so the wait counts stay exact across the loop: the last
+    // step re-loads itself into the idle buffer, which nothing reads again
+    issue_step<C::kBLoads, C::kALoads, C::kStage, C::kBBytes, C::BN>(
+        smem, ks + 1 < nks ? ks + 1 : ks, wv, lane, bsrc, bchunk, asrc, K, RB);
+
+    const bool kin = kb + 32 * h < K;                 // this lane's 32 weights exist
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         v4i af = decode_word(s == 0 ? aw[rt].x : aw[rt].y);
         if (!kin) af = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
-          acc[rt][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[tt], acc[rt][tt], 0, 0, 0);
+          acc[rt][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[s][tt], acc[rt][tt], 0, 0, 0);
       }
     }
   }
+
+  wait_vm<0>();                // no LDS write may still be in flight when the block ends
 
   // D layout: lane holds token (column) lane%16 and features 4*(lane/16) + v.
 #pragma unroll
@@ -234,20 +257,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
   }
 }
 
-template <int RT, int TT, int WRW, int STAGES>
+template <int RT, int TT, int WRW>
 hipError_t launch_cfg(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                       const int8_t* q, const float* d, int64_t M, void* y, int ytype,
                       hipStream_t s) {
-  using C = GemmCfg<RT, TT, WRW, STAGES>;
+  using C = GemmCfg<RT, TT, WRW>;
   const int nrb = (int)((N + C::BN - 1) / C::BN);
   const int ntb = (int)((M + C::BM - 1) / C::BM);
   if (C::kLds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_gemm_i2s<RT, TT, WRW, STAGES>),
+        reinterpret_cast<const void*>(&k_gemm_i2s<RT, TT, WRW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW, STAGES>), dim3((unsigned)(nrb * ntb)),
+  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW>), dim3((unsigned)(nrb * ntb)),
                      dim3(kThreads), C::kLds, s, packed, gamma, N, K, q, d, M, y, ytype, nrb, ntb);
   return hipGetLastError();
 }
@@ -261,8 +284,8 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, int64_t N, int
   if (M <= 16) return launch_gemv(packed, gamma, N, K, q, d, M, y, ytype, s);
   // large tiles when they still give every CU work, smaller ones otherwise
   const int64_t big = ((N + 127) / 128) * ((M + 255) / 256);
-  if (big >= 256) return launch_cfg<4, 8, 2, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
-  return launch_cfg<2, 4, 2, 3>(packed, gamma, N, K, q, d, M, y, ytype, s);
+  if (big >= 256) return launch_cfg<4, 8, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
+  return launch_cfg<2, 4, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
 }
 
 }  // namespace bl

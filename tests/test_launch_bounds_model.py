@@ -78,11 +78,12 @@ def gemm_ranges(N, K, M, RT=4, TT=8, WRW=2):
     RB = K // 4
     nks = (K + BK - 1) // BK
     n_b_loads = BM * BK // (16 * 256)
-    bchunk = 16 * ((LANES & 7) ^ ((LANES >> 3) & 7))
+    n_a_loads = -(-BN * (BK // 4) // (16 * 256))
     for rb, tb in itertools.product(range((N + BN - 1) // BN), range((M + BM - 1) // BM)):
         n_blk, m_blk = rb * BN, tb * BM
         for ks, wv in itertools.product(range(nks), range(4)):
             kb = ks * BK
+            bchunk = 16 * ((LANES & 7) ^ swz(2 * (4 * (wv & 1) + (LANES >> 4))))
             boff = kb + bchunk
             boff = np.where(boff >= K, boff - 64, boff)
             for i in range(n_b_loads):
@@ -90,11 +91,13 @@ def gemm_ranges(N, K, M, RT=4, TT=8, WRW=2):
                 tok = np.minimum(m_blk + t, M - 1)
                 lo = tok * K + boff
                 yield "q", lo.min(), (lo + 16).max(), M * K
-            if wv * 32 < BN:
-                row = wv * 32 + (LANES >> 1)
+            aoff = kb // 4 + 16 * ((LANES >> 4) & 1)
+            aoff = np.where(aoff >= RB, aoff - 16, aoff)
+            for i in range(n_a_loads):
+                if (i * 4 + wv) * 32 >= BN:
+                    continue
+                row = (i * 4 + wv) * 32 + 16 * (LANES >> 5) + (LANES & 15)
                 n = np.minimum(n_blk + np.minimum(row, BN - 1), N - 1)
-                aoff = kb // 4 + 16 * (LANES & 1)
-                aoff = np.where(aoff >= RB, aoff - 16, aoff)
                 lo = n * RB + aoff
                 yield "packed", lo.min(), (lo + 16).max(), N * RB
 
@@ -120,7 +123,8 @@ GEMM_SHAPES = [(1, 64, 17), (130, 256, 17), (64, 2560, 64), (640, 320, 100), (25
 
 
 @pytest.mark.parametrize("N,K,M", GEMM_SHAPES, ids=[f"N{n}K{k}M{m}" for n, k, m in GEMM_SHAPES])
-@pytest.mark.parametrize("tile", [(4, 8, 2), (2, 4, 2)], ids=["128x256", "64x128"])
+@pytest.mark.parametrize("tile", [(8, 4, 2), (4, 8, 2), (2, 4, 2), (2, 2, 2)],
+                         ids=["256x128", "128x256", "64x128", "64x64"])
 def test_gemm_loads_in_bounds(N, K, M, tile):
     for buf, lo, hi, size in gemm_ranges(N, K, M, *tile):
         assert 0 <= lo and hi <= size, (buf, lo, hi, size)
@@ -128,3 +132,92 @@ def test_gemm_loads_in_bounds(N, K, M, tile):
 
 def test_gemm_zero_k_issues_no_loads():
     assert list(gemm_ranges(7, 0, 20)) == []
+
+
+def gemm_lds_step(RT, TT, WRW):
+    """Simulate one step's direct-to-LDS writes of k_gemm_i2s: returns dicts
+    LDS byte -> (token, k byte) for activations and LDS byte -> (row, packed
+    byte) for weights, plus the block geometry."""
+    WTW = 4 // WRW
+    BN, BM = WRW * RT * 16, WTW * TT * 16
+    b_bytes = BM * 128
+    n_b, n_a = BM * 128 // 4096, -(-BN * 32 // 4096)
+    act, wts = {}, {}
+    for wv in range(4):
+        bchunk = 16 * ((LANES & 7) ^ swz(2 * (4 * (wv & 1) + (LANES >> 4))))
+        for i in range(n_b):
+            t = (i * 4 + wv) * 8 + (LANES >> 3)
+            for l in range(WAVE):
+                for b in range(16):
+                    act[(i * 4 + wv) * 1024 + 16 * l + b] = (t[l], bchunk[l] + b)
+        for i in range(n_a):
+            if (i * 4 + wv) * 32 >= BN:
+                continue
+            row = (i * 4 + wv) * 32 + 16 * (LANES >> 5) + (LANES & 15)
+            half = (LANES >> 4) & 1
+            for l in range(WAVE):
+                for b in range(16):
+                    wts[b_bytes + (i * 4 + wv) * 1024 + 16 * l + b] = (row[l], 16 * half[l] + b)
+    return act, wts, BN, BM, b_bytes
+
+
+def swz(t):
+    """Chunk swizzle of activation row t in k_gemm_i2s's LDS tile."""
+    u = (t >> 1) & 7
+    return u ^ ((((u >> 1) ^ (u >> 2)) & 1) << 1)
+
+
+def lds_cycles(width):
+    """Lane sets that one LDS cycle serves, as measured on gfx950 with the
+    bank-conflict counter (pairs of active lanes reading one bank): a 64-bit
+    read serves each 32-lane half at once, a 128-bit read each 32-lane half
+    in two cycles split by the parity of lane bits 2, 3 and 4."""
+    if width == 8:
+        return [LANES[:32], LANES[32:]]
+    par = ((LANES >> 2) ^ (LANES >> 3) ^ (LANES >> 4)) & 1
+    return [LANES[(LANES >> 5 == half) & (par == p)] for half in (0, 1) for p in (0, 1)]
+
+
+def banks_conflict_free(addrs, width):
+    """64 banks of 4 bytes: the lanes of one cycle touch every bank at most once."""
+    for lanes in lds_cycles(width):
+        banks = [((addrs[l] + o) // 4) % 64 for l in lanes for o in range(0, width, 4)]
+        if len(banks) != len(set(banks)):
+            return False
+    return True
+
+
+def test_lds_cycle_model_matches_measurements():
+    """The cycle model reproduces the probe outcomes it was fitted on: the
+    plain (t/2) % 8 swizzle conflicts, so do 8-byte reads of 32-byte rows."""
+    t = 16 + R_OF
+    assert not banks_conflict_free(t * 128 + 16 * ((2 * H_OF) ^ ((t >> 1) & 7)), 16)
+    assert not banks_conflict_free(t * 128 + 16 * ((2 * H_OF) ^ (t & 7)), 16)
+    assert banks_conflict_free(LANES * 16, 16) and banks_conflict_free(LANES * 8, 8)
+    assert not banks_conflict_free(R_OF * 32 + 8 * H_OF, 8)
+
+
+@pytest.mark.parametrize("tile", [(4, 8, 2), (2, 4, 2), (8, 4, 2), (2, 2, 2)])
+def test_gemm_lds_fragments(tile):
+    """Every MFMA fragment read of a step returns the intended operand bytes
+    and every read instruction is free of bank conflicts."""
+    RT, TT, WRW = tile
+    act, wts, BN, BM, b_bytes = gemm_lds_step(RT, TT, WRW)
+    for wv in range(4):
+        wr, wt = wv % WRW, wv // WRW
+        for s, tt in itertools.product(range(2), range(TT)):
+            t = wt * TT * 16 + tt * 16 + R_OF
+            p = (2 * H_OF + s) ^ swz(t)
+            addr = t * 128 + 16 * p
+            for l in range(WAVE):
+                got = [act[addr[l] + b] for b in range(16)]
+                want = [(t[l], 32 * H_OF[l] + 16 * s + b) for b in range(16)]
+                assert got == want
+            assert banks_conflict_free(addr, 16)
+        for rt in range(RT):
+            addr = b_bytes + (wr * RT + rt) * 512 + (H_OF >> 1) * 256 + R_OF * 16 + 8 * (H_OF & 1)
+            for l in range(WAVE):
+                got = [wts[addr[l] + b] for b in range(8)]
+                want = [(wr * RT * 16 + rt * 16 + R_OF[l], 8 * H_OF[l] + b) for b in range(8)]
+                assert got == want
+            assert banks_conflict_free(addr, 8)
