@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+PREFILL_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fast_traffic.json")
@@ -259,23 +260,30 @@ def main():
         cfg5 = W.CONFIGS[5]
         M5 = 2048
         log(f"setup prefill: {cfg5.name}")
-        P = []
-        for proj in cfg5.projs:
-            inp = W.proj_inputs(cfg5, proj, M5)
-            packed = bl.pack_i2s(to_dev(inp.w_tern))
-            x = to_dev(inp.x_bf16.view(np.int16)).view(torch.bfloat16)
-            P.append(dict(packed=packed, gamma=to_dev(np.array([inp.gamma], np.float32)), x=x,
-                          q=torch.empty((M5, proj.K), dtype=torch.int8, device=dev),
-                          d=torch.empty((M5,), dtype=torch.float32, device=dev),
-                          y=torch.empty((M5, proj.N), dtype=torch.bfloat16, device=dev)))
-            del inp
+        # one bf16 input per group of projections that read it; the group's
+        # GEMMs run through one bl_gemm_group call on its quantized codes
+        by = {proj.name: proj for proj in cfg5.projs}
+        G = []
+        for names in PREFILL_GROUPS:
+            inps = [W.proj_inputs(cfg5, by[n], M5) for n in names]
+            K = by[names[0]].K
+            x = to_dev(inps[0].x_bf16.view(np.int16)).view(torch.bfloat16)
+            q = torch.empty((M5, K), dtype=torch.int8, device=dev)
+            d = torch.empty((M5,), dtype=torch.float32, device=dev)
+            probs = [dict(packed=bl.pack_i2s(to_dev(inp.w_tern)),
+                          gamma=to_dev(np.array([inp.gamma], np.float32)),
+                          y=torch.empty((M5, by[n].N), dtype=torch.bfloat16, device=dev))
+                     for n, inp in zip(names, inps)]
+            G.append(dict(names=names, x=x, q=q, d=d, group=bl.GemmGroup(probs, q, d),
+                          ops=sum(2 * M5 * by[n].N * by[n].K for n in names)))
+            del inps
         torch.cuda.synchronize()
 
         def layer(gemm_only=False):
-            for e in P:
+            for e in G:
                 if not gemm_only:
                     bl.quantize_act(e["x"], e["q"], e["d"])
-                bl.gemm(e["packed"], e["gamma"], e["q"], e["d"], out_dtype="bf16", out=e["y"])
+                e["group"]()
 
         layer()
         layer()
@@ -299,25 +307,27 @@ def main():
         torch.cuda.synchronize()
         ms_gemm = b0.elapsed_time(b1) / args.gemm_steps
         gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
-        per_proj = {}
-        for proj, e in zip(cfg5.projs, P):
+        per_group = {}
+        for e in G:
             c0 = torch.cuda.Event(enable_timing=True)
             c1 = torch.cuda.Event(enable_timing=True)
             c0.record()
             for _ in range(3):
-                bl.gemm(e["packed"], e["gamma"], e["q"], e["d"], out_dtype="bf16", out=e["y"])
+                e["group"]()
             c1.record()
             torch.cuda.synchronize()
             ms = c0.elapsed_time(c1) / 3
-            per_proj[proj.name] = round(2 * M5 * proj.N * proj.K / (ms * 1e-3) / 1e12, 1)
+            per_group["+".join(e["names"])] = round(e["ops"] / (ms * 1e-3) / 1e12, 1)
         log(f"prefill: {ms_layer:.3f} ms/layer ({tops:.1f} TOPS incl. quantize), "
-            f"GEMM only {gemm_tops:.1f} TOPS; per projection {per_proj}")
+            f"GEMM only {gemm_tops:.1f} TOPS; per group {per_group}")
         result["gemm"] = {"workload": cfg5.name, "tokens": M5, "ops_per_layer": ops,
                           "ms_per_layer": round(ms_layer, 4), "tops": round(tops, 1),
                           "gemm_only_tops": round(gemm_tops, 1), "peak_tops": INT8_PEAK_TOPS,
                           "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                          "tops_per_projection": per_proj}
-        del P
+                          "step": "per input: bl_quantize_act, then one bl_gemm_group for "
+                                  "{q,k,v}, {o}, {gate,up}, {down}",
+                          "tops_per_group": per_group}
+        del G
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU oracle

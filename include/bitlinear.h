@@ -161,6 +161,31 @@ int bl_gemm(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
             void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * bl_gemm_problem / bl_gemm_group -- several BitLinear GEMMs over the SAME
+ * quantized activations, as few launches as the shapes allow.
+ * Defines: as bl_gemm, once per problem ([BN] Part A 2.3 / 4.1). Meant for
+ * the projections of a decoder layer that read one input (q/k/v; gate/up).
+ *   problems: HOST array of `count` descriptors (0 <= count <= 8), read during
+ *     the call only; every pointer inside is a device pointer.
+ *   per problem: packed uint8 [N][K/4], gamma (device, 1 float), y [M][N] of
+ *     type ytype (see the output enum), row stride N; N == 0 is skipped.
+ *   shared: K (K % 4 == 0), q int8 [M][K], d fp32 [M], M >= 0 tokens.
+ * Each y is bit-identical to what bl_gemm gives for that problem alone.
+ * Validation is bl_gemm's, problem by problem; nothing is launched when any
+ * problem fails it. Outputs must not alias any input or each other.
+ */
+typedef struct bl_gemm_problem {
+  const uint8_t *packed;
+  const float *gamma;
+  int64_t N;
+  void *y;
+  int ytype;
+} bl_gemm_problem;
+
+int bl_gemm_group(const bl_gemm_problem *problems, int count, int64_t K, const int8_t *q,
+                  const float *d, int64_t M, void *stream);
+
+/*
  * bl_decode_problem / bl_decode_group -- fused decode BitLinear for a group
  * of independent projections in ONE launch: per-token absmax int8
  * quantization of bf16 activations, the I2_S GEMV and the dequant.

@@ -11,6 +11,8 @@ and streams only.
     packed      = pack_i2s(w_ternary_int8)          # pack only (caller keeps gamma)
     y           = gemv(packed, g, q, d)             # M <= 16 tokens
     y           = gemm(packed, g, q, d)             # any M (int8 MFMA)
+    ys          = gemm_group([dict(packed=.., gamma=..), ...], q, d)
+                                                    # GEMMs sharing one q, fewest launches
     ys          = decode_group([dict(packed=.., gamma=.., x=..), ...])
                                                     # fused quantize + GEMV, one launch
 """
@@ -19,10 +21,11 @@ from __future__ import annotations
 import torch
 
 from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I8, MAX_GROUP,
-                   BitLinearError, DecodeProblem, check, lib, status_string)
+                   BitLinearError, DecodeProblem, GemmProblem, check, lib, status_string)
 
 __all__ = ["quantize_act", "pack_i2s", "pack_i2s_workspace", "gemv", "gemm",
-           "gemm_workspace", "decode_group", "DecodeGroup", "BitLinearError", "status_string",
+           "gemm_workspace", "gemm_group", "GemmGroup", "decode_group", "DecodeGroup",
+           "BitLinearError", "status_string",
            "lib", "OUT_TYPES"]
 
 OUT_TYPES = {"i32": (BL_OUT_I32, torch.int32), "f32": (BL_OUT_F32, torch.float32),
@@ -140,6 +143,59 @@ def gemm(packed: torch.Tensor, gamma: torch.Tensor, q: torch.Tensor, d: torch.Te
                                    0 if workspace is None else workspace.numel(),
                                    _stream(q.device)))
     return out
+
+
+class GemmGroup:
+    """A prepared bl_gemm_group call over one quantized input (q int8 [M][K],
+    d fp32 [M]): the descriptor array is built once, so repeated calls (or a
+    graph capture) only pass pointers.
+
+    problems: list of dicts with keys packed (uint8 [N][K/4]), gamma (fp32 [1])
+    and optional y (output [M][N]) and out_dtype."""
+
+    def __init__(self, problems, q: torch.Tensor, d: torch.Tensor, out_dtype: str = "bf16"):
+        if not 1 <= len(problems) <= MAX_GROUP:
+            raise ValueError(f"1..{MAX_GROUP} problems per group")
+        _need(q, "q", torch.int8, 2)
+        _need(d, "d", torch.float32, 1)
+        M, K = q.shape
+        arr = (GemmProblem * len(problems))()
+        self.problems = []
+        for i, p in enumerate(problems):
+            packed = p["packed"]
+            _need(packed, "packed", torch.uint8, 2)
+            N, KB = packed.shape
+            if KB * 4 != K:
+                raise ValueError(f"packed [{N}][{KB}] does not match q [{M}][{K}]")
+            ytype, tdt = OUT_TYPES[p.get("out_dtype", out_dtype)]
+            gamma = p.get("gamma")
+            if ytype != BL_OUT_I32:
+                _need(gamma, "gamma", torch.float32, 1)
+            y = p.get("y")
+            if y is None:
+                y = torch.empty((M, N), dtype=tdt, device=q.device)
+            elif y.dtype != tdt or tuple(y.shape) != (M, N) or not y.is_contiguous():
+                raise ValueError("y has the wrong dtype, shape or layout")
+            arr[i] = GemmProblem(packed.data_ptr(), _ptr(gamma), N, y.data_ptr(), ytype)
+            self.problems.append(dict(p, y=y))
+        self.q, self.d, self.M, self.K = q, d, M, K
+        self._arr = arr
+
+    @property
+    def outputs(self):
+        return [p["y"] for p in self.problems]
+
+    def __call__(self):
+        check("bl_gemm_group", lib().bl_gemm_group(self._arr, len(self.problems), self.K,
+                                                   self.q.data_ptr(), self.d.data_ptr(), self.M,
+                                                   _stream(self.q.device)))
+        return self.outputs
+
+
+def gemm_group(problems, q: torch.Tensor, d: torch.Tensor, out_dtype: str = "bf16"):
+    """GEMMs of several projections over the same quantized input q, d.
+    Returns the list of outputs y."""
+    return GemmGroup(problems, q, d, out_dtype)()
 
 
 class DecodeGroup:

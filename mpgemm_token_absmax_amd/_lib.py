@@ -28,7 +28,8 @@ BL_OUT_F32 = 1
 BL_OUT_BF16 = 2
 
 EXPORTS = ("bl_abi_version", "bl_status_string", "bl_quantize_act", "bl_pack_i2s_workspace",
-           "bl_pack_i2s", "bl_gemv", "bl_gemm_workspace", "bl_gemm", "bl_decode_group")
+           "bl_pack_i2s", "bl_gemv", "bl_gemm_workspace", "bl_gemm", "bl_gemm_group",
+           "bl_decode_group")
 
 MAX_GROUP = 8
 
@@ -40,6 +41,13 @@ class DecodeProblem(ctypes.Structure):
                 ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
                 ("q", ctypes.c_void_p), ("d", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("ytype", ctypes.c_int)]
+
+
+class GemmProblem(ctypes.Structure):
+    """Mirror of bl_gemm_problem (include/bitlinear.h)."""
+    _fields_ = [("packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("y", ctypes.c_void_p), ("ytype", ctypes.c_int)]
+
 
 _lib = None
 
@@ -71,6 +79,8 @@ def _declare(lib):
     lib.bl_gemm_workspace.argtypes = [I64, I64, I64]
     lib.bl_gemm.restype = INT
     lib.bl_gemm.argtypes = [P, P, I64, I64, P, P, I64, P, INT, P, SZ, P]
+    lib.bl_gemm_group.restype = INT
+    lib.bl_gemm_group.argtypes = [ctypes.POINTER(GemmProblem), INT, I64, P, P, I64, P]
     lib.bl_decode_group.restype = INT
     lib.bl_decode_group.argtypes = [ctypes.POINTER(DecodeProblem), INT, I64, P]
     return lib

@@ -118,6 +118,26 @@ int bl_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, con
   return hip_status(bl::launch_gemm(packed, gamma, N, K, q, d, M, y, ytype, as_stream(stream)));
 }
 
+int bl_gemm_group(const bl_gemm_problem* problems, int count, int64_t K, const int8_t* q,
+                  const float* d, int64_t M, void* stream) {
+  if (count < 0 || count > bl::kMaxGroup || M < 0 || K < 0 || K % 4 != 0) return BL_ERR_SHAPE;
+  if (count == 0 || M == 0) return BL_OK;
+  if (!problems) return BL_ERR_NULL;
+  if (M > (int64_t)65535 * 256) return BL_ERR_SHAPE;
+  bl::GemmProblem g[bl::kMaxGroup];
+  int n = 0;
+  for (int i = 0; i < count; ++i) {
+    const bl_gemm_problem& p = problems[i];
+    const int st = check_matmul(p.packed, p.gamma, p.N, K, q, d, M, p.y, p.ytype);
+    if (st != BL_OK) return st;
+    if (p.N > (int64_t)UINT32_MAX * 64) return BL_ERR_SHAPE;
+    if (p.N == 0) continue;
+    g[n++] = bl::GemmProblem{p.packed, p.gamma, p.y, p.N, p.ytype};
+  }
+  if (n == 0) return BL_OK;
+  return hip_status(bl::launch_gemm_group(g, n, K, q, d, M, as_stream(stream)));
+}
+
 int bl_decode_group(const bl_decode_problem* problems, int count, int64_t M, void* stream) {
   if (count < 0 || count > bl::kMaxGroup || M < 0 || M > kGemvMaxM) return BL_ERR_SHAPE;
   if (count == 0 || M == 0) return BL_OK;

@@ -101,6 +101,15 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// Kernel argument of a GEMM launch: the problems that share q, each owning
+// a contiguous range of row blocks [rb0[i], rb0[i+1]).
+struct GemmArgs {
+  int count;
+  int total_rb;
+  int rb0[kMaxGroup + 1];
+  GemmProblem p[kMaxGroup];
+};
+
 template <int RT, int TT, int WRW>
 struct GemmCfg {
   static constexpr int WTW = 4 / WRW;
@@ -139,19 +148,28 @@ __device__ __forceinline__ void issue_step(int8_t* smem, int ks, int wv, int lan
 }
 
 template <int RT, int TT, int WRW>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
-    const uint8_t* __restrict__ packed, const float* __restrict__ gamma, int64_t N, int64_t K,
-    const int8_t* __restrict__ q, const float* __restrict__ d, int64_t M, void* __restrict__ y,
-    int ytype, int n_row_blocks, int n_tok_blocks) {
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(const GemmArgs g, int64_t K,
+                                                          const int8_t* __restrict__ q,
+                                                          const float* __restrict__ d, int64_t M,
+                                                          int n_tok_blocks) {
   using C = GemmCfg<RT, TT, WRW>;
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
 
   // XCD-aware order: block b runs on XCD b % 8; give each XCD a contiguous run
   // of the tile sequence (token-tile major) so its blocks share activations.
+  const int n_row_blocks = g.total_rb;
   const int nb = n_row_blocks * n_tok_blocks;
   int lin = blockIdx.x;
   if (nb % kXcds == 0) lin = (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds;
-  const int tb = lin / n_row_blocks, rb = lin % n_row_blocks;
+  const int tb = lin / n_row_blocks;
+  int rb = lin % n_row_blocks;
+  int pi = 0;                                         // problem of this block (uniform)
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < g.count && rb >= g.rb0[i]) pi = i;
+  rb -= g.rb0[pi];
+  const uint8_t* __restrict__ packed = g.p[pi].packed;
+  const int64_t N = g.p[pi].N;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -244,48 +262,80 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(
   wait_vm<0>();                // no LDS write may still be in flight when the block ends
 
   // D layout: lane holds token (column) lane%16 and features 4*(lane/16) + v.
+  const int ytype = g.p[pi].ytype;
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
     const int64_t tok = m_blk + wt * TT * 16 + tt * 16 + r;
     if (tok >= M) continue;
-    const float c = ytype ? gamma[0] * d[tok] : 0.0f;
+    const float c = ytype ? g.p[pi].gamma[0] * d[tok] : 0.0f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int64_t n = n_blk + wr * RT * 16 + rt * 16 + 4 * h;
-      if (n < N) store_quad(y, ytype, N, tok, n, acc[rt][tt], c);
+      if (n < N) store_quad(g.p[pi].y, ytype, N, tok, n, acc[rt][tt], c);
     }
   }
 }
 
 template <int RT, int TT, int WRW>
-hipError_t launch_cfg(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
-                      const int8_t* q, const float* d, int64_t M, void* y, int ytype,
-                      hipStream_t s) {
+hipError_t launch_cfg(const GemmProblem* const* p, int count, int64_t K, const int8_t* q,
+                      const float* d, int64_t M, hipStream_t s) {
   using C = GemmCfg<RT, TT, WRW>;
-  const int nrb = (int)((N + C::BN - 1) / C::BN);
-  const int ntb = (int)((M + C::BM - 1) / C::BM);
+  GemmArgs a{};
+  int64_t rb = 0;
+  for (int i = 0; i < count; ++i) {
+    a.rb0[i] = (int)rb;
+    a.p[i] = *p[i];
+    rb += (p[i]->N + C::BN - 1) / C::BN;
+  }
+  a.count = count;
+  a.rb0[count] = (int)rb;
+  a.total_rb = (int)rb;
+  const int64_t ntb = (M + C::BM - 1) / C::BM;
+  if (rb * ntb > INT32_MAX) return hipErrorInvalidValue;
   if (C::kLds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&k_gemm_i2s<RT, TT, WRW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW>), dim3((unsigned)(nrb * ntb)),
-                     dim3(kThreads), C::kLds, s, packed, gamma, N, K, q, d, M, y, ytype, nrb, ntb);
+  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW>), dim3((unsigned)(rb * ntb)), dim3(kThreads),
+                     C::kLds, s, a, K, q, d, M, (int)ntb);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const int8_t* q,
+                             const float* d, int64_t M, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (K % 64 != 0 || M <= 16) {
+    for (int i = 0; i < count && e == hipSuccess; ++i)
+      e = K % 64 != 0 ? launch_generic(p[i].packed, p[i].gamma, p[i].N, K, q, d, M, p[i].y,
+                                       p[i].ytype, s)
+                      : launch_gemv(p[i].packed, p[i].gamma, p[i].N, K, q, d, M, p[i].y,
+                                    p[i].ytype, s);
+    return e;
+  }
+  // Problems big enough to fill the chip with 128x256 tiles share one launch
+  // of those (their blocks then fill whole rounds together); the rest share
+  // one launch of 64x128 tiles.
+  const GemmProblem* big[kMaxGroup];
+  const GemmProblem* small[kMaxGroup];
+  int nbig = 0, nsmall = 0;
+  for (int i = 0; i < count; ++i) {
+    if (((p[i].N + 127) / 128) * ((M + 255) / 256) >= 256) big[nbig++] = &p[i];
+    else small[nsmall++] = &p[i];
+  }
+  if (nbig) e = launch_cfg<4, 8, 2>(big, nbig, K, q, d, M, s);
+  if (e == hipSuccess && nsmall) e = launch_cfg<2, 4, 2>(small, nsmall, K, q, d, M, s);
+  return e;
+}
+
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                        const int8_t* q, const float* d, int64_t M, void* y, int ytype,
                        hipStream_t s) {
-  if (K % 64 != 0) return launch_generic(packed, gamma, N, K, q, d, M, y, ytype, s);
-  if (M <= 16) return launch_gemv(packed, gamma, N, K, q, d, M, y, ytype, s);
-  // large tiles when they still give every CU work, smaller ones otherwise
-  const int64_t big = ((N + 127) / 128) * ((M + 255) / 256);
-  if (big >= 256) return launch_cfg<4, 8, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
-  return launch_cfg<2, 4, 2>(packed, gamma, N, K, q, d, M, y, ytype, s);
+  const GemmProblem p{packed, gamma, y, N, ytype};
+  return launch_gemm_group(&p, 1, K, q, d, M, s);
 }
 
 }  // namespace bl

@@ -57,6 +57,18 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, int64_t N, int
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                        const int8_t* q, const float* d, int64_t M, void* y, int ytype,
                        hipStream_t s);
+// Several GEMMs over the same int8 activations q [M][K] (scales d): problem i
+// has its own packed [N_i][K/4], gamma, y [M][N_i] and output type.
+struct GemmProblem {
+  const uint8_t* packed;
+  const float* gamma;
+  void* y;
+  int64_t N;
+  int ytype;
+};
+hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const int8_t* q,
+                             const float* d, int64_t M, hipStream_t s);
+
 // Shapes off the fast paths (K % 64 != 0): one thread per output element.
 hipError_t launch_generic(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                           const int8_t* q, const float* d, int64_t M, void* y, int ytype,

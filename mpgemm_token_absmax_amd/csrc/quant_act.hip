@@ -6,9 +6,10 @@
 //   m = max |x[t][:]|, s = fl32(127/m), q = clamp(rne(fl32(x*s)), -127, 127),
 //   d[t] = fl32(m/127); an all-zero row gives q = 0, d = 0.
 //
-// One workgroup of 256 threads per token. Each thread reads 4 bf16 (8 bytes)
-// per chunk; for K <= 256*4*NC the row stays in registers between the max
-// and the quantize pass, otherwise the second pass re-reads it (an L2 hit).
+// One workgroup of 256 threads per token. Each thread reads 8 bf16 (16 bytes,
+// when K and ldx are multiples of 8) or 4 bf16 per chunk; up to 32768 values
+// the row stays in registers between the max and the quantize pass,
+// otherwise the second pass re-reads it (an L2 hit).
 // The max is taken on the magnitude bits: for finite values the ordering of
 // the bit patterns of |x| is the ordering of the values.
 #include "common.hpp"
@@ -69,6 +70,46 @@ __global__ __launch_bounds__(kQThreads) void k_quant_absmax(
   }
 }
 
+// 16-byte variant (K % 8 == 0, ldx % 8 == 0): 8 bf16 per chunk, the row in
+// registers (K <= 2048*NC). Loads are unconditional (chunk index clamped, the
+// value of a chunk past the row ignored) so they are all in flight at once.
+template <int NC>
+__global__ __launch_bounds__(kQThreads) void k_quant_absmax16(
+    const uint16_t* __restrict__ x, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    float* __restrict__ d) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  const int64_t t = blockIdx.x;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + t * ldx);
+  uint2* qr = reinterpret_cast<uint2*>(q + t * K);
+  const int nchunk = (int)(K / 8);
+  uint4 v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = (int)threadIdx.x + i * kQThreads;
+    v[i] = xr[c < nchunk ? c : nchunk - 1];
+  }
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = (int)threadIdx.x + i * kQThreads;
+    const uint32_t m8 = max(absmax4_bf16(make_uint2(v[i].x, v[i].y)),
+                            absmax4_bf16(make_uint2(v[i].z, v[i].w)));
+    mb = max(mb, c < nchunk ? m8 : 0u);
+  }
+  mb = block_max_u32(mb, red);
+  const float m = __uint_as_float(mb << 16);
+  const float s = mb ? 127.0f / m : 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = (int)threadIdx.x + i * kQThreads;
+    if (c < nchunk)
+      qr[c] = mb ? make_uint2(quant4_bf16(make_uint2(v[i].x, v[i].y), s),
+                              quant4_bf16(make_uint2(v[i].z, v[i].w), s))
+                 : make_uint2(0u, 0u);
+  }
+  if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
+}
+
 __global__ void k_fill_zero_f32(float* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -82,6 +123,14 @@ hipError_t launch_nc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_
   return hipGetLastError();
 }
 
+template <int NC>
+hipError_t launch_nc16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* d,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_quant_absmax16<NC>, dim3((unsigned)M), dim3(kQThreads), 0, s, x, K, ldx,
+                     q, d);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
@@ -89,6 +138,14 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
   if (K == 0) {
     hipLaunchKernelGGL(k_fill_zero_f32, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, d, M);
     return hipGetLastError();
+  }
+  if (K % 8 == 0 && ldx % 8 == 0 && K <= 2048 * 16) {
+    const int64_t per_thread = (K / 8 + kQThreads - 1) / kQThreads;
+    if (per_thread <= 1) return launch_nc16<1>(x, M, K, ldx, q, d, s);
+    if (per_thread <= 2) return launch_nc16<2>(x, M, K, ldx, q, d, s);
+    if (per_thread <= 4) return launch_nc16<4>(x, M, K, ldx, q, d, s);
+    if (per_thread <= 8) return launch_nc16<8>(x, M, K, ldx, q, d, s);
+    return launch_nc16<16>(x, M, K, ldx, q, d, s);
   }
   const int64_t per_thread = (K / 4 + kQThreads - 1) / kQThreads;
   if (per_thread <= 1) return launch_nc<1>(x, M, K, ldx, q, d, s);

@@ -151,3 +151,35 @@ def test_decode_group_validation(lib):
     assert call([prob()], M=0) == L.BL_OK
     assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK      # nothing to compute
     assert lib.bl_decode_group(None, 1, 1, None) == L.BL_ERR_NULL
+
+
+def test_gemm_group_validation(lib):
+    P = L.GemmProblem
+
+    def prob(**kw):
+        base = dict(packed=A16, gamma=B16, N=64, y=E16, ytype=2)
+        base.update(kw)
+        return P(**base)
+
+    def call(probs, K=256, q=C16, d=D16, M=32):
+        arr = (P * max(1, len(probs)))(*probs)
+        return lib.bl_gemm_group(arr, len(probs), K, q, d, M, None)
+
+    assert call([prob()] * 9) == L.BL_ERR_SHAPE            # more than 8 problems
+    assert call([prob()], K=6) == L.BL_ERR_SHAPE
+    assert call([prob()], M=-1) == L.BL_ERR_SHAPE
+    assert call([prob(N=-2)]) == L.BL_ERR_SHAPE
+    assert call([prob(ytype=3)]) == L.BL_ERR_DTYPE
+    assert call([prob(), prob(y=None)]) == L.BL_ERR_NULL    # every problem is checked
+    assert call([prob(packed=None)]) == L.BL_ERR_NULL
+    assert call([prob(gamma=None)]) == L.BL_ERR_NULL
+    assert call([prob()], q=None) == L.BL_ERR_NULL
+    assert call([prob()], d=None) == L.BL_ERR_NULL
+    assert call([prob(packed=A16 + 4)]) == L.BL_ERR_ALIGN
+    assert call([prob(y=E16 + 2)]) == L.BL_ERR_ALIGN
+    assert call([prob()], q=C16 + 8) == L.BL_ERR_ALIGN
+    assert call([prob()], K=132108) == L.BL_ERR_SHAPE      # fp32-exact bound
+    assert call([], M=4) == L.BL_OK
+    assert call([prob()], M=0) == L.BL_OK
+    assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK
+    assert lib.bl_gemm_group(None, 1, 256, C16, D16, 4, None) == L.BL_ERR_NULL

@@ -93,7 +93,7 @@ def run_all_outputs(bl, fn, packed_d, gamma_d, q_d, d_d):
 # ---------------------------------------------------------------------------
 
 QUANT_SHAPES = [(1, 4), (1, 64), (3, 260), (16, 1024), (17, 2560), (5, 6912), (4, 11008),
-                (2, 28672), (3, 36000), (64, 4096), (1, 8)]
+                (2, 28672), (3, 36000), (64, 4096), (1, 8), (1, 32768), (2, 32776), (6, 520)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES, ids=[f"M{m}K{k}" for m, k in QUANT_SHAPES])
@@ -132,6 +132,14 @@ def test_quantize_special_rows_and_stride():
     torch.cuda.synchronize()
     assert np.array_equal(host(q), q_ref)
     assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+    # row stride 12 (not a multiple of 8 elements): the 8-byte load path
+    wide12 = np.zeros((x.shape[0], 12), dtype=np.uint16)
+    wide12[:, :8] = x
+    x12 = dev_bf16(wide12)[:, :8]
+    q12, d12 = bl.quantize_act(x12)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q12), q_ref)
+    assert np.array_equal(host(d12).view(np.uint32), d_ref.view(np.uint32))
     # the golden q values themselves
     assert host(q)[0, :4].tolist() == [-127, 32, 16, 95]
     assert host(q)[1, :6].tolist() == [127, 62, -62, 0, 2, -2]
@@ -277,6 +285,45 @@ def test_gemm_parity(M, N, K):
     bl = _bl()
     _run_mm(bl, "gemm", M, N, K, seed=2000 + M * 31 + N * 7 + K, zero_rows=(M - 2,) if M > 3
             else ())
+
+
+GROUP_CASES = [
+    # (M, K, [N per problem], [out dtype per problem]); the first case has a
+    # problem big enough for the 128x256-tile launch next to small ones
+    (512, 128, [16484, 640, 0, 33], ["bf16", "f32", "bf16", "i32"]),
+    (300, 1024, [100, 257], ["f32", "bf16"]),
+    (2048, 256, [1024, 1024, 8192], ["bf16", "bf16", "i32"]),
+    (40, 260, [7, 64], ["f32", "i32"]),          # K % 64 != 0
+    (9, 512, [50, 3], ["bf16", "f32"]),           # M <= 16
+]
+
+
+@pytest.mark.parametrize("M,K,Ns,outs", GROUP_CASES,
+                         ids=[f"M{c[0]}K{c[1]}N{'-'.join(map(str, c[2]))}" for c in GROUP_CASES])
+def test_gemm_group_parity(M, K, Ns, outs):
+    """Every problem of a group against the oracle, and bit-identical to the
+    same problem run alone through bl_gemm."""
+    bl = _bl()
+    seed = 3000 + M + K
+    say(f"gemm_group M={M} K={K} N={Ns} outs={outs}")
+    q = W.int8_codes(seed, M, K, (M - 1,))
+    d = W.positive_scales(seed + 1, M, (M - 1,))
+    qd, dd = dev(q), dev(d)
+    probs, refs = [], []
+    for i, (N, o) in enumerate(zip(Ns, outs)):
+        t = W.ternary_drawn(seed + 10 + i, N, K, 0.3 + 0.05 * i)
+        g = np.float32(GAMMA * (1 + i))
+        probs.append(dict(packed=bl.pack_i2s(dev(t)), gamma=dev(np.array([g], np.float32)),
+                          out_dtype=o))
+        refs.append((t, g))
+    ys = bl.gemm_group(probs, qd, dd)
+    alone = [bl.gemm(p["packed"], p["gamma"], qd, dd, out_dtype=p["out_dtype"]) for p in probs]
+    torch.cuda.synchronize()
+    for (t, g), o, y, y1 in zip(refs, outs, ys, alone):
+        assert torch.equal(y, y1), "group output differs from the single-problem call"
+        acc = oracle.mpgemm_acc_f64blas(q, t) if M * t.shape[0] * K > 2e8 else \
+            oracle.mpgemm_acc(q, t)
+        check_outputs(acc, g, d, **{f"y_{o}": host(y)})
 
 
 def test_gemv_equals_gemm_and_deterministic():
@@ -471,6 +518,38 @@ def test_config4_sparse_variant():
     cfg = W.CONFIGS[4]
     for proj in cfg.projs:
         _pipeline(bl, cfg, proj, 1, p_zero_override=0.65)
+
+
+def test_config5_grouped_sampled():
+    """100B-class layer at 2048 tokens through bl_gemm_group: {q, k, v} and
+    {gate, up} share one quantized input; sampled entries against the oracle,
+    full outputs equal to the per-projection bl_gemm."""
+    bl = _bl()
+    cfg = W.CONFIGS[5]
+    by = {p.name: p for p in cfg.projs}
+    for names in (("q", "k", "v"), ("gate", "up")):
+        K = by[names[0]].K
+        inps = [W.proj_inputs(cfg, by[n], 2048) for n in names]
+        x = inps[0].x_bf16
+        say(f"config 5 group {names} K={K}")
+        q_ref, d_ref = oracle.quantize_act_absmax(x)
+        q, d = bl.quantize_act(dev_bf16(x))
+        probs = []
+        for inp in inps:
+            probs.append(dict(packed=bl.pack_i2s(dev(inp.w_tern)),
+                              gamma=dev(np.array([inp.gamma], np.float32)), out_dtype="f32"))
+        ys = bl.gemm_group(probs, q, d)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), q_ref)
+        for n, inp, pr, y in zip(names, inps, probs, ys):
+            y1 = bl.gemm(pr["packed"], pr["gamma"], q, d, out_dtype="f32")
+            assert torch.equal(y, y1), n
+            r = W.rng(6000 + by[n].index)
+            rows = np.concatenate([r.integers(0, 2048, 256), [0, 2047]])
+            cols = np.concatenate([r.integers(0, by[n].N, 256), [by[n].N - 1, 0]])
+            acc = oracle.mpgemm_acc_entries(q_ref, inp.w_tern, rows, cols)
+            check_outputs(acc, np.float32(inp.gamma), d_ref, None, host(y), rows=rows, cols=cols)
+            del y1
 
 
 def test_config5_sampled():
