@@ -76,6 +76,55 @@ __device__ __forceinline__ uint32_t quant4_bf16(uint2 v, float s) {
          (quant1_bf16(v.y & 0xFFFFu, s) << 16) | (quant1_bf16(v.y >> 16, s) << 24);
 }
 
+// Max of the 8 bf16 magnitudes of a 16-byte chunk (packed 16-bit max).
+__device__ __forceinline__ uint32_t absmax8_bf16(uint4 v) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
+  const u16x2 b = __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu);
+  const u16x2 c = __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu);
+  const u16x2 d = __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu);
+  const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                            __builtin_elementwise_max(c, d));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// The int8 code of one bf16 value as the low byte of fl32(fl32(x*s) + 1.5*2^23):
+// for |y| < 2^22, adding 1.5*2^23 rounds y to an integer with ties to even and
+// leaves it in the low mantissa bits (two's complement, so the low byte is
+// the int8 code). With s = fl32(127/m) and |x| <= m, |fl32(x*s)| < 127.5, so
+// the clamp to +-127 of the definition never binds: identical to quant1_bf16.
+__device__ __forceinline__ uint32_t qbits_bf16(uint32_t bf16_in_high_half, float s) {
+  return __float_as_uint(__fadd_rn(__fmul_rn(__uint_as_float(bf16_in_high_half), s),
+                                   12582912.0f));
+}
+
+// 8 bf16 (16 bytes) -> 8 int8 codes (8 bytes), same codes as quant4_bf16.
+__device__ __forceinline__ uint2 quant8_bf16(uint4 v, float s) {
+  uint32_t w[4];
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = qbits_bf16(in[i] << 16, s);
+    const uint32_t hi = qbits_bf16(in[i] & 0xFFFF0000u, s);
+    w[i] = __builtin_amdgcn_perm(hi, lo, 0x0C0C0400u);     // bytes: lo.b0, hi.b0, 0, 0
+  }
+  return make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                    __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
+}
+
+// Max over the wave of a value held by every lane (all lanes active): DPP
+// within each row of 16 lanes, then the four row results through SGPRs.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  int x = (int)v;
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));   // row_mirror
+  const int r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const int r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  return (uint32_t)max(max(r0, r1), max(r2, r3));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));

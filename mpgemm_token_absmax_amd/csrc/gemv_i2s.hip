@@ -278,6 +278,147 @@ __global__ __launch_bounds__(kThreads) void k_gemv_i2s(DecodeGroup grp) {
   }
 }
 
+// One-token fused decode (M == 1, bf16 x, K <= 16384): per block 16 output
+// rows, the four waves split K into quarters. Each wave loads only its
+// quarter of x (before its weights: vector loads retire in order), takes the
+// absmax of it (packed 16-bit max, DPP), and the block combines the four
+// maxima with one barrier; each wave then quantizes its own quarter into a
+// wave-private LDS region (the exact add-1.5*2^23 rounding of quant8_bf16),
+// runs its MFMA steps with every lane reading token 0's fragments (lanes of
+// tokens 1..15 feed output columns that are never stored) and the block sums
+// the four partial accumulators with a second barrier.
+// Grid: x = row blocks of the largest problem, y = problem (so a block finds
+// its problem without first loading a table); blocks past a problem's rows
+// exit at once.
+// XR: 16-byte x chunks per lane (covers len*32 chunks), U: steps per load batch.
+template <int XR, int U>
+__global__ __launch_bounds__(kThreads) void k_decode1(DecodeGroup grp, int len_max) {
+  extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][len_max*256]
+  __shared__ v4i red[kWavesPerBlock - 1][kWave];
+  __shared__ uint32_t wmax[kWavesPerBlock];
+
+  const DecodeProblem& P = grp.p[blockIdx.y];
+  const int64_t N = P.N;
+  const int K = (int)P.K;
+  const uint8_t* __restrict__ packed = P.packed;
+  const uint16_t* __restrict__ xg = P.x;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  // all fields in one scalar round trip, before the exit test
+  asm volatile("" ::"s"(packed), "s"(xg), "s"(K));
+  if (n0 >= N) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wk = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & 3;   // K quarter
+  const int h = lane >> 4;
+  const int RB = K / 4;
+  const bool first_block = blockIdx.x == 0;
+
+  const int nsteps = (K + 255) / 256;
+  const int len = (nsteps + 3) / 4;
+  const int ja = min(wk * len, nsteps);
+  const int jb = min(ja + len, nsteps);
+  const int klo = min(ja * 256, K);
+  const int khi = min(jb * 256, K);
+  const int nch = (khi - klo) / 8;                    // 8-value chunks of this quarter
+  int8_t* wact = act + wk * len_max * 256;
+
+  // ---- 1. loads: this quarter of x, then the first weight batch ---------
+  const uint4* xs = reinterpret_cast<const uint4*>(xg) + (nch > 0 ? klo / 8 : 0);
+  const int clast = nch > 0 ? nch - 1 : 0;
+  uint4 xv[XR];
+#pragma unroll
+  for (int u = 0; u < XR; ++u) xv[u] = xs[min(lane + u * kWave, clast)];
+  int64_t row = n0 + (lane & 15);
+  row = row < N ? row : N - 1;
+  const uint8_t* wrow = packed + row * RB;
+  v4i wa[U], wb[U];
+  auto load_w = [&](v4i (&dst)[U], int j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int step = max(min(j + u, jb - 1), 0);
+      int off = step * 64 + 16 * h;
+      off = off < RB ? off : RB - 16;
+      dst[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow + off));
+    }
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(wa, ja);
+  __builtin_amdgcn_sched_barrier(0);
+  const float gam = P.ytype ? P.gamma[0] : 0.0f;      // epilogue operand
+
+  // ---- 2. absmax of the row: quarter maxima, one barrier ----------------
+  uint32_t m = 0u;
+#pragma unroll
+  for (int u = 0; u < XR; ++u) m = max(m, lane + u * kWave < nch ? absmax8_bf16(xv[u]) : 0u);
+  m = wave_max_u32(m);
+  if (lane == 0) wmax[wk] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float mf = __uint_as_float(m << 16);
+  const float sq = m ? 127.0f / mf : 0.0f;
+  const float dv = m ? mf / 127.0f : 0.0f;
+  if (first_block && wk == 0 && lane == 0 && P.d) P.d[0] = dv;
+
+  // ---- 3. int8 codes of this quarter -> the wave's LDS region -----------
+  const bool write_q = first_block && P.q;
+#pragma unroll
+  for (int u = 0; u < XR; ++u) {
+    const int c = lane + u * kWave;
+    if (c < nch) {
+      const uint2 qv = quant8_bf16(xv[u], sq);
+      *reinterpret_cast<uint2*>(wact + 8 * c) = qv;
+      if (write_q) *reinterpret_cast<uint2*>(P.q + klo + 8 * c) = qv;
+    }
+  }
+  // zeros past K in the last partial step (K % 256 != 0)
+  for (int b = (khi - klo) + 16 * lane; b < (jb - ja) * 256; b += 16 * kWave)
+    *reinterpret_cast<v4i*>(wact + b) = v4i{0, 0, 0, 0};
+  // the region is this wave's alone and LDS serves a wave in order
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- 4. MFMA over this quarter's steps --------------------------------
+  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};  // two chains (even / odd s)
+  const int8_t* arow = wact + 64 * h;
+  auto read_b = [&](v4i (&b)[4], int j) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      b[s] = *reinterpret_cast<const v4i*>(arow + (j - ja) * 256 + 16 * s);
+  };
+  auto compute = [&](const v4i (&w)[U], int j) {
+    v4i bn[4];
+    read_b(bn, j);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j + u < jb) {
+        v4i b[4] = {bn[0], bn[1], bn[2], bn[3]};
+        if (u + 1 < U && j + u + 1 < jb) read_b(bn, j + u + 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          v4i& a = (s & 1) ? acc1 : acc0;
+          a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][s]), b[s], a, 0,
+                                                    0, 0);
+        }
+      }
+    }
+  };
+  for (int j = ja; j < jb; j += 2 * U) {
+    if (j + U < jb) load_w(wb, j + U);
+    compute(wa, j);
+    if (j + 2 * U < jb) load_w(wa, j + 2 * U);
+    if (j + U < jb) compute(wb, j + U);
+  }
+  v4i acc = acc0 + acc1;
+
+  // ---- 5. sum of the quarters, dequant, store ---------------------------
+  if (wk > 0) red[wk - 1][lane] = acc;
+  __syncthreads();
+  if (wk > 0) return;
+  acc += red[0][lane] + red[1][lane] + red[2][lane];
+  // D layout: lane holds token lane%16 and rows 4*(lane/16) + v; token 0 only
+  if ((lane & 15) != 0) return;
+  const int64_t n = n0 + 4 * h;
+  if (n < N) store_quad(P.y, P.ytype, N, 0, n, acc, gam * dv);
+}
+
 // Fast decode kernel (every problem's per-wave activation slice fits in LDS).
 // Each wave owns a contiguous range of 256-weight steps and builds the int8
 // activations of exactly that range in a wave-private LDS region.
@@ -645,6 +786,20 @@ hipError_t launch_fast(DecodeGroup& g, int len_max, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int XR, int U>
+hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < g.count; ++i) {
+    const int64_t b = (g.p[i].N + 15) / 16;
+    blocks = b > blocks ? b : blocks;
+  }
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = (size_t)kWavesPerBlock * len_max * 256;
+  hipLaunchKernelGGL((k_decode1<XR, U>), dim3((unsigned)blocks, (unsigned)g.count),
+                     dim3(kThreads), lds, s, g, len_max);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
   // problems with K == 0 only need zero outputs; keep them away from the
   // MFMA kernels (whose loads assume at least one 64-weight group per row)
@@ -668,6 +823,14 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
     const int64_t steps = (g.p[i].K + 255) / 256;
     const int len = (int)((steps + kFastWK - 1) / kFastWK);
     if (len > len_max) len_max = len;
+  }
+  bool all_x = true;
+  for (int i = 0; i < g.count; ++i) all_x = all_x && g.p[i].x != nullptr;
+  if (g.M == 1 && all_x && len_max <= 16) {         // one token, fused quantize
+    if (len_max <= 2) return launch_one_token<1, 4>(g, len_max, s);
+    if (len_max <= 4) return launch_one_token<2, 4>(g, len_max, s);
+    if (len_max <= 8) return launch_one_token<4, 8>(g, len_max, s);
+    return launch_one_token<8, 8>(g, len_max, s);
   }
   if ((int64_t)kWavesPerBlock * g.M * len_max * 256 <= kActLds) {
     int64_t kmax = 0;

@@ -407,6 +407,13 @@ def test_decode_group_parity(M):
                        seed=40 + M)
 
 
+def test_decode_group_one_token_long_k():
+    """One-token groups whose quarters need 4 and 8 x chunks per lane, with a
+    K % 256 != 0 tail and a K of exactly 16384."""
+    bl = _bl()
+    _decode_group_case(bl, 1, [(33, 16384), (17, 4160), (3, 1088), (20, 64)], seed=77)
+
+
 def test_decode_group_chunked_k_and_no_qd():
     """K larger than one LDS chunk (several chunks per block), q/d not requested."""
     bl = _bl()

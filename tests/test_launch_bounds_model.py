@@ -70,6 +70,57 @@ def decode_fast_ranges(N, K, M, WK=4, U=None, ldx=None):
                 yield "q", lo.min(), (lo + 16).max(), M * K
 
 
+def decode1_xr_u(K):
+    """(XR, U) that launch_decode_group picks for a one-token group whose
+    largest K is K (None: the kernel does not take it)."""
+    length = ((K + 255) // 256 + 3) // 4
+    if length <= 2:
+        return 1, 4
+    if length <= 4:
+        return 2, 4
+    if length <= 8:
+        return 4, 8
+    if length <= 16:
+        return 8, 8
+    return None
+
+
+def decode1_ranges(N, K, len_max=None):
+    """Yield (buffer, lo, hi, size) of every global load and LDS access of
+    k_decode1 for one problem (one token), and check the launch covers K."""
+    assert K % 64 == 0 and K >= 64
+    XR, U = decode1_xr_u(K if len_max is None else len_max * 1024)
+    RB = K // 4
+    nsteps = (K + 255) // 256
+    length = (nsteps + 3) // 4
+    len_max = length if len_max is None else len_max
+    assert XR * WAVE * 8 >= length * 256          # the x chunks cover the quarter
+    for b, wk in itertools.product(range((N + 15) // 16), range(4)):
+        n0 = b * 16
+        ja = min(wk * length, nsteps)
+        jb = min(ja + length, nsteps)
+        klo, khi = min(ja * 256, K), min(jb * 256, K)
+        nch = (khi - klo) // 8
+        cbase = klo // 8 if nch > 0 else 0
+        clast = nch - 1 if nch > 0 else 0
+        for u in range(XR):
+            c = cbase + np.minimum(LANES + u * WAVE, clast)
+            yield "x", (16 * c).min(), (16 * c + 16).max(), 2 * K
+        rows = np.minimum(n0 + R_OF, N - 1)
+        starts = list(range(ja, jb, 2 * U)) or [ja]
+        for j in starts:
+            for base in (j, j + U, j + 2 * U):
+                for u in range(U):
+                    step = max(min(base + u, jb - 1), 0)
+                    off = np.minimum(step * 64 + 16 * H_OF, RB - 16)
+                    lo = rows * RB + off
+                    yield "packed", lo.min(), (lo + 16).max(), N * RB
+        region = len_max * 256                     # the wave's LDS region
+        if nch > 0:
+            yield "lds", 0, 8 * nch, region
+        yield "lds", 0, (jb - ja) * 256, region   # tail zeros and fragment reads
+
+
 def gemm_ranges(N, K, M, RT=4, TT=8, WRW=2):
     """Yield byte ranges of every direct-to-LDS load of k_gemm_i2s."""
     BK = 128
@@ -111,6 +162,25 @@ DECODE_SHAPES = [(1, 64, 1), (5, 64, 1), (17, 128, 1), (640, 2560, 1), (2560, 69
 def test_decode_loads_in_bounds(N, K, M):
     for U in (4, 8):
         for buf, lo, hi, size in decode_fast_ranges(N, K, M, U=U):
+            assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+DECODE1_SHAPES = [(1, 64), (5, 64), (100, 320), (640, 2560), (2560, 2560), (6912, 2560),
+                  (2560, 6912), (33, 16384), (17, 4160), (3, 1088), (2049, 256), (5, 6912),
+                  (7, 11008)]
+
+
+@pytest.mark.parametrize("N,K", DECODE1_SHAPES, ids=[f"N{n}K{k}" for n, k in DECODE1_SHAPES])
+def test_decode1_loads_in_bounds(N, K):
+    for buf, lo, hi, size in decode1_ranges(N, K):
+        assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_decode1_group_len_max():
+    """In a group the LDS region is sized by the largest K; smaller problems
+    stay inside it."""
+    for K in (64, 320, 2560):
+        for buf, lo, hi, size in decode1_ranges(40, K, len_max=7):
             assert 0 <= lo and hi <= size, (buf, lo, hi, size)
 
 
