@@ -290,35 +290,44 @@ __global__ __launch_bounds__(kThreads) void k_gemv_i2s(DecodeGroup grp) {
 // Grid: x = row blocks of the largest problem, y = problem (so a block finds
 // its problem without first loading a table); blocks past a problem's rows
 // exit at once.
-// XR: 16-byte x chunks per lane (covers len*32 chunks), U: steps per load batch.
-template <int XR, int U>
-__global__ __launch_bounds__(kThreads) void k_decode1(DecodeGroup grp, int len_max) {
+// WPB: waves per block (each takes 1/WPB of K), XR: 16-byte x chunks per lane
+// (covers len*32 chunks), U: steps per load batch.
+template <int WPB, int XR, int U>
+__global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int len_max) {
   extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][len_max*256]
-  __shared__ v4i red[kWavesPerBlock - 1][kWave];
-  __shared__ uint32_t wmax[kWavesPerBlock];
+  __shared__ v4i red[WPB - 1][kWave];
+  __shared__ uint32_t wmax[WPB];
 
   const DecodeProblem& P = grp.p[blockIdx.y];
   const int64_t N = P.N;
   const int K = (int)P.K;
   const uint8_t* __restrict__ packed = P.packed;
   const uint16_t* __restrict__ xg = P.x;
+  const float* gptr = P.gamma;
+  void* yp = P.y;
+  int8_t* qp = P.q;
+  float* dp = P.d;
+  const int ytype = P.ytype;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  // all fields in one scalar round trip, before the exit test
-  asm volatile("" ::"s"(packed), "s"(xg), "s"(K));
+  // Every field in one scalar round trip, before the exit test: a scalar
+  // load still in flight later would make each LDS wait a full wait (they
+  // share a counter and scalar loads complete out of order).
+  asm volatile("" ::"s"(packed), "s"(xg), "s"(K), "s"(gptr), "s"(yp), "s"(qp), "s"(dp),
+               "s"(ytype), "s"(len_max));
   if (n0 >= N) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wk = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & 3;   // K quarter
+  const int wk = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & (WPB - 1);   // K part
   const int h = lane >> 4;
   const int RB = K / 4;
   const bool first_block = blockIdx.x == 0;
 
   const int nsteps = (K + 255) / 256;
-  const int len = (nsteps + 3) / 4;
+  const int len = (nsteps + WPB - 1) / WPB;
   const int ja = min(wk * len, nsteps);
   const int jb = min(ja + len, nsteps);
   const int klo = min(ja * 256, K);
   const int khi = min(jb * 256, K);
-  const int nch = (khi - klo) / 8;                    // 8-value chunks of this quarter
+  const int nch = (khi - klo) / 8;                    // 8-value chunks of this part
   int8_t* wact = act + wk * len_max * 256;
 
   // ---- 1. loads: this quarter of x, then the first weight batch ---------
@@ -327,6 +336,8 @@ __global__ __launch_bounds__(kThreads) void k_decode1(DecodeGroup grp, int len_m
   uint4 xv[XR];
 #pragma unroll
   for (int u = 0; u < XR; ++u) xv[u] = xs[min(lane + u * kWave, clast)];
+  // gamma by a vector load, issued with x (counted with the vector loads)
+  const float gam = ytype ? __builtin_nontemporal_load(gptr) : 0.0f;
   int64_t row = n0 + (lane & 15);
   row = row < N ? row : N - 1;
   const uint8_t* wrow = packed + row * RB;
@@ -343,7 +354,6 @@ __global__ __launch_bounds__(kThreads) void k_decode1(DecodeGroup grp, int len_m
   __builtin_amdgcn_sched_barrier(0);
   load_w(wa, ja);
   __builtin_amdgcn_sched_barrier(0);
-  const float gam = P.ytype ? P.gamma[0] : 0.0f;      // epilogue operand
 
   // ---- 2. absmax of the row: quarter maxima, one barrier ----------------
   uint32_t m = 0u;
@@ -352,21 +362,22 @@ __global__ __launch_bounds__(kThreads) void k_decode1(DecodeGroup grp, int len_m
   m = wave_max_u32(m);
   if (lane == 0) wmax[wk] = m;
   __syncthreads();
-  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+#pragma unroll
+  for (int w = 0; w < WPB; ++w) m = max(m, wmax[w]);
   const float mf = __uint_as_float(m << 16);
   const float sq = m ? 127.0f / mf : 0.0f;
   const float dv = m ? mf / 127.0f : 0.0f;
-  if (first_block && wk == 0 && lane == 0 && P.d) P.d[0] = dv;
+  if (first_block && wk == 0 && lane == 0 && dp) dp[0] = dv;
 
   // ---- 3. int8 codes of this quarter -> the wave's LDS region -----------
-  const bool write_q = first_block && P.q;
+  const bool write_q = first_block && qp;
 #pragma unroll
   for (int u = 0; u < XR; ++u) {
     const int c = lane + u * kWave;
     if (c < nch) {
       const uint2 qv = quant8_bf16(xv[u], sq);
       *reinterpret_cast<uint2*>(wact + 8 * c) = qv;
-      if (write_q) *reinterpret_cast<uint2*>(P.q + klo + 8 * c) = qv;
+      if (write_q) *reinterpret_cast<uint2*>(qp + klo + 8 * c) = qv;
     }
   }
   // zeros past K in the last partial step (K % 256 != 0)
@@ -412,11 +423,12 @@ __global__ __launch_bounds__(kThreads) void k_decode1(DecodeGroup grp, int len_m
   if (wk > 0) red[wk - 1][lane] = acc;
   __syncthreads();
   if (wk > 0) return;
-  acc += red[0][lane] + red[1][lane] + red[2][lane];
+#pragma unroll
+  for (int w = 0; w < WPB - 1; ++w) acc += red[w][lane];
   // D layout: lane holds token lane%16 and rows 4*(lane/16) + v; token 0 only
   if ((lane & 15) != 0) return;
   const int64_t n = n0 + 4 * h;
-  if (n < N) store_quad(P.y, P.ytype, N, 0, n, acc, gam * dv);
+  if (n < N) store_quad(yp, ytype, N, 0, n, acc, gam * dv);
 }
 
 // Fast decode kernel (every problem's per-wave activation slice fits in LDS).
@@ -786,7 +798,7 @@ hipError_t launch_fast(DecodeGroup& g, int len_max, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int XR, int U>
+template <int WPB, int XR, int U>
 hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
   int64_t blocks = 0;
   for (int i = 0; i < g.count; ++i) {
@@ -794,9 +806,9 @@ hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
     blocks = b > blocks ? b : blocks;
   }
   if (blocks == 0) return hipSuccess;
-  const size_t lds = (size_t)kWavesPerBlock * len_max * 256;
-  hipLaunchKernelGGL((k_decode1<XR, U>), dim3((unsigned)blocks, (unsigned)g.count),
-                     dim3(kThreads), lds, s, g, len_max);
+  const size_t lds = (size_t)WPB * len_max * 256;
+  hipLaunchKernelGGL((k_decode1<WPB, XR, U>), dim3((unsigned)blocks, (unsigned)g.count),
+                     dim3(WPB * kWave), lds, s, g, len_max);
   return hipGetLastError();
 }
 
@@ -827,10 +839,17 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
   bool all_x = true;
   for (int i = 0; i < g.count; ++i) all_x = all_x && g.p[i].x != nullptr;
   if (g.M == 1 && all_x && len_max <= 16) {         // one token, fused quantize
-    if (len_max <= 2) return launch_one_token<1, 4>(g, len_max, s);
-    if (len_max <= 4) return launch_one_token<2, 4>(g, len_max, s);
-    if (len_max <= 8) return launch_one_token<4, 8>(g, len_max, s);
-    return launch_one_token<8, 8>(g, len_max, s);
+    if (len_max <= 2) return launch_one_token<4, 1, 4>(g, len_max, s);
+    if (len_max <= 4) return launch_one_token<4, 2, 4>(g, len_max, s);
+    // longer rows: eight waves per block, so each wave's serial step chain
+    // stays at most 8 steps (up to K = 16384)
+    int len8 = 0;
+    for (int i = 0; i < g.count; ++i) {
+      const int len = (int)(((g.p[i].K + 255) / 256 + 7) / 8);
+      len8 = len > len8 ? len : len8;
+    }
+    if (len8 <= 4) return launch_one_token<8, 2, 4>(g, len8, s);
+    return launch_one_token<8, 4, 8>(g, len8, s);
   }
   if ((int64_t)kWavesPerBlock * g.M * len_max * 256 <= kActLds) {
     int64_t kmax = 0;

@@ -70,32 +70,33 @@ def decode_fast_ranges(N, K, M, WK=4, U=None, ldx=None):
                 yield "q", lo.min(), (lo + 16).max(), M * K
 
 
-def decode1_xr_u(K):
-    """(XR, U) that launch_decode_group picks for a one-token group whose
-    largest K is K (None: the kernel does not take it)."""
-    length = ((K + 255) // 256 + 3) // 4
-    if length <= 2:
-        return 1, 4
-    if length <= 4:
-        return 2, 4
-    if length <= 8:
-        return 4, 8
-    if length <= 16:
-        return 8, 8
-    return None
+def decode1_config(K):
+    """(WPB, XR, U, len) that launch_decode_group picks for a one-token group
+    whose largest K is K (None: the kernel does not take it)."""
+    steps = (K + 255) // 256
+    len4 = (steps + 3) // 4
+    if len4 <= 2:
+        return 4, 1, 4, len4
+    if len4 <= 4:
+        return 4, 2, 4, len4
+    if len4 > 16:
+        return None
+    len8 = (steps + 7) // 8
+    return (8, 2, 4, len8) if len8 <= 4 else (8, 4, 8, len8)
 
 
-def decode1_ranges(N, K, len_max=None):
+def decode1_ranges(N, K, group_kmax=None):
     """Yield (buffer, lo, hi, size) of every global load and LDS access of
-    k_decode1 for one problem (one token), and check the launch covers K."""
+    k_decode1 for one problem (one token) of a group whose largest K is
+    group_kmax, and check the launch covers this K."""
     assert K % 64 == 0 and K >= 64
-    XR, U = decode1_xr_u(K if len_max is None else len_max * 1024)
+    WPB, XR, U, len_max = decode1_config(K if group_kmax is None else group_kmax)
     RB = K // 4
     nsteps = (K + 255) // 256
-    length = (nsteps + 3) // 4
-    len_max = length if len_max is None else len_max
-    assert XR * WAVE * 8 >= length * 256          # the x chunks cover the quarter
-    for b, wk in itertools.product(range((N + 15) // 16), range(4)):
+    length = (nsteps + WPB - 1) // WPB
+    assert length <= len_max
+    assert XR * WAVE * 8 >= length * 256          # the x chunks cover the part
+    for b, wk in itertools.product(range((N + 15) // 16), range(WPB)):
         n0 = b * 16
         ja = min(wk * length, nsteps)
         jb = min(ja + length, nsteps)
@@ -179,8 +180,8 @@ def test_decode1_loads_in_bounds(N, K):
 def test_decode1_group_len_max():
     """In a group the LDS region is sized by the largest K; smaller problems
     stay inside it."""
-    for K in (64, 320, 2560):
-        for buf, lo, hi, size in decode1_ranges(40, K, len_max=7):
+    for K in (64, 320, 2560, 6912):
+        for buf, lo, hi, size in decode1_ranges(40, K, group_kmax=7168):
             assert 0 <= lo and hi <= size, (buf, lo, hi, size)
 
 
