@@ -40,7 +40,7 @@ if ROOT not in sys.path:
 PREFILL_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fast_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode1_traffic.json")
 DECODE_SOURCES = ("mpgemm_token_absmax_amd/csrc/gemv_i2s.hip",
                   "mpgemm_token_absmax_amd/csrc/common.hpp",
                   "mpgemm_token_absmax_amd/csrc/launch.hpp")
@@ -248,7 +248,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "k_gemv_i2s (fused decode group)",
+                     "kernel": "k_decode1 (one-token fused decode group)",
                      "us_per_launch": round(us_launch, 3), "bytes_per_launch": bytes_launch},
     }
     del layers, g_all, g_one, g_unfused
