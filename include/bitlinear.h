@@ -200,10 +200,13 @@ int bl_gemm_group(const bl_gemm_problem *problems, int count, int64_t K, const i
  *   M: tokens, 1 <= M <= 16, shared by all problems.
  *   per problem: packed uint8 [N][K/4], gamma (device, 1 float), x bf16 [M]
  *     rows of K values with row stride ldx (ldx >= K, ldx % 4 == 0), y [M][N]
- *     of type ytype; q (int8 [M][K]) and d (fp32 [M]) are optional outputs
- *     (NULL: not written). K % 64 == 0 is required (BL_ERR_SHAPE otherwise);
- *     N == 0 problems are skipped. Outputs must not alias any input or each
- *     other.
+ *     of type ytype; q (int8 [M][K]) and d (fp32 [M]) receive the quantized
+ *     activations. At M == 1 they are optional (NULL: not written); at M > 1
+ *     they are required (BL_ERR_NULL otherwise): the codes are staged there
+ *     by a quantize pass inside the call, ahead of the GEMV launch.
+ *     K % 64 == 0 and K <= 65536 are required (BL_ERR_SHAPE otherwise);
+ *     N == 0 problems are skipped. Outputs must not alias any
+ *     input or each other.
  */
 typedef struct bl_decode_problem {
   const uint8_t *packed;

@@ -232,9 +232,12 @@ class DecodeGroup:
             elif y.dtype != tdt or tuple(y.shape) != (M, N) or not y.is_contiguous():
                 raise ValueError("y has the wrong dtype, shape or layout")
             q, d, gamma = p.get("q"), p.get("d"), p.get("gamma")
+            if M > 1 and (q is None or d is None):     # several tokens stage their codes
+                q = torch.empty((M, K), dtype=torch.int8, device=x.device) if q is None else q
+                d = torch.empty((M,), dtype=torch.float32, device=x.device) if d is None else d
             arr[i] = DecodeProblem(packed.data_ptr(), _ptr(gamma), N, K, x.data_ptr(),
                                    x.stride(0), _ptr(q), _ptr(d), y.data_ptr(), ytype)
-            self.problems.append(dict(p, y=y))
+            self.problems.append(dict(p, y=y, q=q, d=d))
         self.M = M
         self._arr = arr
         self._device = problems[0]["x"].device

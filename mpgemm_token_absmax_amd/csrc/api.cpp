@@ -11,6 +11,7 @@ namespace {
 
 constexpr int64_t kGemvMaxM = 16;
 constexpr int64_t kFp32ExactK = ((int64_t)1 << 24) / 127;   // 127*K < 2^24
+constexpr int64_t kDecodeMaxK = 65536;                       // fused decode: K per problem
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -146,13 +147,15 @@ int bl_decode_group(const bl_decode_problem* problems, int count, int64_t M, voi
   g.M = (int)M;
   for (int i = 0; i < count; ++i) {
     const bl_decode_problem& p = problems[i];
-    if (p.N < 0 || p.K < 0 || p.K % 64 != 0 || p.ldx < p.K) return BL_ERR_SHAPE;
+    if (p.N < 0 || p.K < 0 || p.K % 64 != 0 || p.ldx < p.K || p.K > kDecodeMaxK)
+      return BL_ERR_SHAPE;
     if (p.ytype < BL_OUT_I32 || p.ytype > BL_OUT_BF16) return BL_ERR_DTYPE;
     if (p.ytype != BL_OUT_I32 && p.K > kFp32ExactK) return BL_ERR_SHAPE;
     if (127 * p.K > INT32_MAX) return BL_ERR_SHAPE;
     if (p.N == 0) continue;
     if (!p.y || (p.K > 0 && (!p.packed || !p.x)) || (p.ytype != BL_OUT_I32 && !p.gamma))
       return BL_ERR_NULL;
+    if (M > 1 && p.K > 0 && (!p.q || !p.d)) return BL_ERR_NULL;   // staging of the codes
     if (p.ldx % 4 != 0 || !aligned(p.y, 16)) return BL_ERR_ALIGN;
     if (p.K > 0 && (!aligned(p.packed, 16) || !aligned(p.x, 16))) return BL_ERR_ALIGN;
     if ((p.q && !aligned(p.q, 16)) || (p.d && !aligned(p.d, 4)) ||

@@ -40,6 +40,8 @@ struct DecodeGroup {
 };
 
 hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s);
+// bf16 x -> q, d of every problem of a group (M tokens each), one launch.
+hipError_t launch_quantize_group(const DecodeGroup& g, hipStream_t s);
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                float* d, hipStream_t s);

@@ -74,13 +74,11 @@ __global__ __launch_bounds__(kQThreads) void k_quant_absmax(
 // registers (K <= 2048*NC). Loads are unconditional (chunk index clamped, the
 // value of a chunk past the row ignored) so they are all in flight at once.
 template <int NC>
-__global__ __launch_bounds__(kQThreads) void k_quant_absmax16(
-    const uint16_t* __restrict__ x, int64_t K, int64_t ldx, int8_t* __restrict__ q,
-    float* __restrict__ d) {
-  __shared__ uint32_t red[kQThreads / kWave];
-  const int64_t t = blockIdx.x;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + t * ldx);
-  uint2* qr = reinterpret_cast<uint2*>(q + t * K);
+__device__ __forceinline__ void quant_row16(const uint16_t* __restrict__ xrow, int64_t K,
+                                            int8_t* __restrict__ qrow, float* __restrict__ dt,
+                                            uint32_t* red) {
+  const uint4* xr = reinterpret_cast<const uint4*>(xrow);
+  uint2* qr = reinterpret_cast<uint2*>(qrow);
   const int nchunk = (int)(K / 8);
   uint4 v[NC];
 #pragma unroll
@@ -107,7 +105,26 @@ __global__ __launch_bounds__(kQThreads) void k_quant_absmax16(
                               quant4_bf16(make_uint2(v[i].z, v[i].w), s))
                  : make_uint2(0u, 0u);
   }
-  if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
+  if (threadIdx.x == 0) *dt = mb ? m / 127.0f : 0.0f;
+}
+
+template <int NC>
+__global__ __launch_bounds__(kQThreads) void k_quant_absmax16(
+    const uint16_t* __restrict__ x, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    float* __restrict__ d) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  const int64_t t = blockIdx.x;
+  quant_row16<NC>(x + t * ldx, K, q + t * K, d + t, red);
+}
+
+// Every problem of a decode group at once: grid x = token, y = problem; each
+// problem's x [M][ldx] goes to its q [M][K] and d [M].
+template <int NC>
+__global__ __launch_bounds__(kQThreads) void k_quant_group(DecodeGroup g) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  const DecodeProblem& P = g.p[blockIdx.y];
+  const int64_t t = blockIdx.x;
+  quant_row16<NC>(P.x + t * P.ldx, P.K, P.q + t * P.K, P.d + t, red);
 }
 
 __global__ void k_fill_zero_f32(float* __restrict__ p, int64_t n) {
@@ -131,7 +148,37 @@ hipError_t launch_nc16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int
   return hipGetLastError();
 }
 
+template <int NC>
+hipError_t launch_group_nc(const DecodeGroup& g, hipStream_t s) {
+  hipLaunchKernelGGL(k_quant_group<NC>, dim3((unsigned)g.M, (unsigned)g.count), dim3(kQThreads), 0,
+                     s, g);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_quantize_group(const DecodeGroup& g, hipStream_t s) {
+  int64_t kmax = 0;
+  bool wide = true;
+  for (int i = 0; i < g.count; ++i) {
+    kmax = g.p[i].K > kmax ? g.p[i].K : kmax;
+    wide = wide && g.p[i].K % 8 == 0 && g.p[i].ldx % 8 == 0;
+  }
+  if (wide && kmax > 0 && kmax <= 2048 * 16) {
+    const int64_t per_thread = (kmax / 8 + kQThreads - 1) / kQThreads;
+    if (per_thread <= 1) return launch_group_nc<1>(g, s);
+    if (per_thread <= 2) return launch_group_nc<2>(g, s);
+    if (per_thread <= 4) return launch_group_nc<4>(g, s);
+    if (per_thread <= 8) return launch_group_nc<8>(g, s);
+    return launch_group_nc<16>(g, s);
+  }
+  for (int i = 0; i < g.count; ++i) {
+    const DecodeProblem& p = g.p[i];
+    const hipError_t e = launch_quantize_act(p.x, g.M, p.K, p.ldx, p.q, p.d, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                float* d, hipStream_t s) {

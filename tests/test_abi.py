@@ -147,6 +147,9 @@ def test_decode_group_validation(lib):
     assert call([prob(d=D16 + 2)]) == L.BL_ERR_ALIGN
     assert call([prob(ldx=258)]) == L.BL_ERR_ALIGN
     assert call([prob(K=132160, ldx=132160)]) == L.BL_ERR_SHAPE   # fp32-exact bound
+    assert call([prob(K=65600, ldx=65600, ytype=0)]) == L.BL_ERR_SHAPE   # K <= 65536
+    assert call([prob()], M=2) == L.BL_ERR_NULL             # several tokens need q and d
+    assert call([prob(q=D16)], M=2) == L.BL_ERR_NULL
     assert call([], M=1) == L.BL_OK
     assert call([prob()], M=0) == L.BL_OK
     assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK      # nothing to compute

@@ -408,10 +408,19 @@ def test_decode_group_parity(M):
 
 
 def test_decode_group_one_token_long_k():
-    """One-token groups whose quarters need 4 and 8 x chunks per lane, with a
-    K % 256 != 0 tail and a K of exactly 16384."""
+    """One-token groups whose parts need 4 and 8 x chunks per lane, with a
+    K % 256 != 0 tail, K of exactly 16384, and the 16-wave block at the
+    largest K the call takes (65536)."""
     bl = _bl()
     _decode_group_case(bl, 1, [(33, 16384), (17, 4160), (3, 1088), (20, 64)], seed=77)
+    _decode_group_case(bl, 1, [(3, 65536), (9, 40960)], seed=78, out_types=["f32", "bf16"])
+
+
+def test_decode_group_tokens_long_k():
+    """Several tokens (quantize launch + GEMV over the codes) at the largest K."""
+    bl = _bl()
+    _decode_group_case(bl, 2, [(3, 65536), (40, 64)], seed=79, out_types=["i32", "bf16"])
+    _decode_group_case(bl, 16, [(17, 28672)], seed=80, out_types=["f32"])
 
 
 def test_decode_group_chunked_k_and_no_qd():

@@ -4,7 +4,7 @@ The kernels' loads are made unconditional (clamped) so the compiler can
 overlap them; this model recomputes, for every block, wave, lane and
 unrolled slot, the byte ranges those loads touch and checks they stay inside
 the buffers, for the shapes the GPU tests and the benchmark use plus edge
-cases. It mirrors the index arithmetic of k_decode_fast (gemv_i2s.hip) and
+cases. It mirrors the index arithmetic of k_decode1 and k_gemvq (gemv_i2s.hip) and
 k_gemm_i2s (gemm_i2s.hip); it runs on the CPU and launches nothing.
 """
 import itertools
@@ -18,28 +18,49 @@ R_OF = LANES & 15
 H_OF = LANES >> 4
 
 
-def decode_fast_ranges(N, K, M, WK=4, U=None, ldx=None):
-    """Yield (buffer, lo, hi) byte ranges of every load of one decode problem."""
-    assert K % 64 == 0
-    if K == 0:                      # routed to the zero-output kernel: no loads
-        return
-    ldx = K if ldx is None else ldx
+def steps_per_wave(K, wpb):
+    return ((K + 255) // 256 + wpb - 1) // wpb
+
+
+def decode1_config(K):
+    """(WPB, XR, U, len) that launch_decode_group picks for a one-token group
+    whose largest K is K."""
+    len4 = steps_per_wave(K, 4)
+    if len4 <= 2:
+        return 4, 1, 4, len4
+    if len4 <= 4:
+        return 4, 2, 4, len4
+    len8 = steps_per_wave(K, 8)
+    if len8 <= 4:
+        return 8, 2, 4, len8
+    if len8 <= 8:
+        return 8, 4, 8, len8
+    len16 = steps_per_wave(K, 16)
+    assert len16 <= 16, "K above 65536 is rejected at the boundary"
+    return (16, 4, 8, len16) if len16 <= 8 else (16, 8, 8, len16)
+
+
+def gemvq_config(K):
+    """(WPB, U) of launch_gemvq for a group whose largest K is K."""
+    if steps_per_wave(K, 4) <= 4:
+        return 4, 4
+    if steps_per_wave(K, 8) <= 4:
+        return 8, 4
+    return 16, 2
+
+
+def gemvq_ranges(N, K, M, group_kmax=None):
+    """Yield (buffer, lo, hi, size) of every global load of k_gemvq."""
+    assert K % 64 == 0 and K >= 64 and 1 <= M <= 16
+    WPB, U = gemvq_config(K if group_kmax is None else group_kmax)
     RB = K // 4
     nsteps = (K + 255) // 256
-    length = (nsteps + WK - 1) // WK
-    if U is None:
-        U = 4 if length <= 4 else 8
-    WR = 4 // WK
-    blocks = (N + 16 * WR - 1) // (16 * WR)
-    XREG, QREG = 8, 2
-    for b, wv in itertools.product(range(blocks), range(4)):
-        wr, wk = wv // WK, wv % WK
-        n0 = (b * WR + wr) * 16
+    length = (nsteps + WPB - 1) // WPB
+    tok = np.minimum(R_OF, M - 1)
+    for b, wk in itertools.product(range((N + 15) // 16), range(WPB)):
         ja = min(wk * length, nsteps)
         jb = min(ja + length, nsteps)
-        klo, khi = min(ja * 256, K), min(jb * 256, K)
-        kw = khi - klo
-        rows = np.minimum(n0 + R_OF, N - 1)
+        rows = np.minimum(b * 16 + R_OF, N - 1)
         starts = list(range(ja, jb, 2 * U)) or [ja]
         for j in starts:
             for base in (j, j + U, j + 2 * U):
@@ -48,41 +69,10 @@ def decode_fast_ranges(N, K, M, WK=4, U=None, ldx=None):
                     off = np.minimum(step * 64 + 16 * H_OF, RB - 16)
                     lo = rows * RB + off
                     yield "packed", lo.min(), (lo + 16).max(), N * RB
-        XF = (8 if length <= 4 else 16) if M == 1 else 0
-        full_row = XF > 0 and K <= XF * 512            # whole bf16 row per wave (fused, M = 1)
-        if full_row:
-            nch8 = K // 8
-            for u in range(XF):
-                c = np.minimum(LANES + u * WAVE, nch8 - 1)
-                lo = 16 * c
-                yield "x", lo.min(), (lo + 16).max(), 2 * K
-        cpt = kw // 4
-        if M == 1 and not full_row and 0 < cpt <= XREG * WAVE:   # x range kept in registers
-            for u in range(XREG):
-                c = np.minimum(LANES + u * WAVE, cpt - 1)
-                lo = 2 * (klo + 4 * c)
-                yield "x", lo.min(), (lo + 8).max(), 2 * ((M - 1) * ldx + K)
-        c16 = kw // 16
-        if M == 1 and 0 < c16 <= QREG * WAVE:          # q chunks kept in registers
-            for u in range(QREG):
-                c = np.minimum(LANES + u * WAVE, c16 - 1)
-                lo = klo + 16 * c
-                yield "q", lo.min(), (lo + 16).max(), M * K
-
-
-def decode1_config(K):
-    """(WPB, XR, U, len) that launch_decode_group picks for a one-token group
-    whose largest K is K (None: the kernel does not take it)."""
-    steps = (K + 255) // 256
-    len4 = (steps + 3) // 4
-    if len4 <= 2:
-        return 4, 1, 4, len4
-    if len4 <= 4:
-        return 4, 2, 4, len4
-    if len4 > 16:
-        return None
-    len8 = (steps + 7) // 8
-    return (8, 2, 4, len8) if len8 <= 4 else (8, 4, 8, len8)
+                    kk = np.minimum(step * 256 + 64 * H_OF, K - 64)
+                    for s in range(4):
+                        lo = tok * K + kk + 16 * s
+                        yield "q", lo.min(), (lo + 16).max(), M * K
 
 
 def decode1_ranges(N, K, group_kmax=None):
@@ -154,21 +144,9 @@ def gemm_ranges(N, K, M, RT=4, TT=8, WRW=2):
                 yield "packed", lo.min(), (lo + 16).max(), N * RB
 
 
-DECODE_SHAPES = [(1, 64, 1), (5, 64, 1), (17, 128, 1), (640, 2560, 1), (2560, 6912, 1),
-                 (100, 320, 4), (33, 64, 16), (2049, 256, 2), (5, 6912, 1), (300, 11008, 1),
-                 (8, 64, 1), (1, 128, 1), (3, 0, 1), (130, 1024, 4), (7, 4096, 1)]
-
-
-@pytest.mark.parametrize("N,K,M", DECODE_SHAPES, ids=[f"N{n}K{k}M{m}" for n, k, m in DECODE_SHAPES])
-def test_decode_loads_in_bounds(N, K, M):
-    for U in (4, 8):
-        for buf, lo, hi, size in decode_fast_ranges(N, K, M, U=U):
-            assert 0 <= lo and hi <= size, (buf, lo, hi, size)
-
-
 DECODE1_SHAPES = [(1, 64), (5, 64), (100, 320), (640, 2560), (2560, 2560), (6912, 2560),
                   (2560, 6912), (33, 16384), (17, 4160), (3, 1088), (2049, 256), (5, 6912),
-                  (7, 11008)]
+                  (7, 11008), (3, 28672), (2, 32832), (2, 65536), (1, 40960)]
 
 
 @pytest.mark.parametrize("N,K", DECODE1_SHAPES, ids=[f"N{n}K{k}" for n, k in DECODE1_SHAPES])
@@ -181,12 +159,26 @@ def test_decode1_group_len_max():
     """In a group the LDS region is sized by the largest K; smaller problems
     stay inside it."""
     for K in (64, 320, 2560, 6912):
-        for buf, lo, hi, size in decode1_ranges(40, K, group_kmax=7168):
+        for kmax in (7168, 28672, 65536):
+            for buf, lo, hi, size in decode1_ranges(40, K, group_kmax=kmax):
+                assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+GEMVQ_SHAPES = [(1, 64, 1), (5, 64, 16), (17, 128, 3), (640, 2560, 1), (2560, 6912, 4),
+                (100, 320, 16), (33, 11008, 16), (2049, 256, 2), (5, 28672, 4),
+                (300, 11008, 1), (7, 4160, 9), (3, 65536, 2)]
+
+
+@pytest.mark.parametrize("N,K,M", GEMVQ_SHAPES, ids=[f"N{n}K{k}M{m}" for n, k, m in GEMVQ_SHAPES])
+def test_gemvq_loads_in_bounds(N, K, M):
+    for buf, lo, hi, size in gemvq_ranges(N, K, M):
+        assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_gemvq_group_kmax():
+    for K in (64, 320, 4096):
+        for buf, lo, hi, size in gemvq_ranges(20, K, 5, group_kmax=28672):
             assert 0 <= lo and hi <= size, (buf, lo, hi, size)
-
-
-def test_decode_zero_k_launches_no_loads():
-    assert list(decode_fast_ranges(5, 0, 3)) == []
 
 
 GEMM_SHAPES = [(1, 64, 17), (130, 256, 17), (64, 2560, 64), (640, 320, 100), (257, 576, 129),
