@@ -65,6 +65,126 @@ def measured_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+def capture_fns(torch, stream, fns):
+    """HIP graph of the given launch callables, captured on `stream`."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in fns:
+            f()
+    return g
+
+
+def replay_us(torch, stream, g, launches, reps=20):
+    """Mean microseconds per launch over `reps` replays of graph g."""
+    with torch.cuda.stream(stream):
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * launches)
+
+
+def measure_floors(torch, dev, stream, capture_fn, R, groups):
+    """Floors of a decode launch on this machine, with the measurement aids of
+    libblprobe.so in the same setting as the decode step (graph replays over R
+    cold buffer copies): an empty kernel, a streaming read of each group's
+    packed bytes by as many 256-thread blocks as its decode launch has, and a
+    1 GiB streaming read (practical HBM peak)."""
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "mpgemm_token_absmax_amd", "libblprobe.so"))
+    probe.blp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    probe.blp_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+
+    def read(buf, nbytes, blocks):
+        def f():
+            rc = probe.blp_stream_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream)
+            if rc:
+                raise RuntimeError(f"blp_stream_read failed ({rc})")
+        return f
+
+    def empty():
+        if probe.blp_empty(160, torch.cuda.current_stream().cuda_stream):
+            raise RuntimeError("blp_empty failed")
+
+    out = {}
+    g = capture_fn(torch, stream, [empty] * 128)
+    out["empty_launch_us"] = round(replay_us(torch, stream, g, 128), 3)
+    stream_us = {}
+    for names, nbytes, blocks in groups:
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+        g = capture_fn(torch, stream, [read(b, nbytes, blocks) for b in bufs])
+        stream_us["+".join(names)] = round(replay_us(torch, stream, g, R), 3)
+        del g, bufs
+    out["stream_read_us"] = stream_us
+    total = sum(nb for _, nb, _ in groups)
+    out["layer_floor_us"] = round(sum(stream_us.values()), 3)
+    out["layer_floor_gbs"] = round(total / (out["layer_floor_us"] * 1e-6) / 1e9, 1)
+    big = 1 << 30
+    bufs = [torch.ones(big, dtype=torch.uint8, device=dev) for _ in range(2)]
+    g = capture_fn(torch, stream, [read(b, big, 2048) for b in bufs])
+    out["practical_peak_gbs"] = round(big / (replay_us(torch, stream, g, 2, reps=5) * 1e-6) / 1e9,
+                                      1)
+    del g, bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_more(torch, bl, W, dev, stream):
+    """The 7B-class layer at 1, 4 and 16 tokens (4 group launches per layer,
+    16 rotating layer copies = 810 MB) and one-token GEMVs of the 100B-class
+    shapes (one launch, rotating copies), in GB/s of packed weights."""
+    out = {}
+    cfg = W.CONFIGS[4]
+    layer_groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    packed = {}
+    for proj in cfg.projs:
+        inp = W.proj_inputs(cfg, proj, 1, with_acts=False)
+        packed[proj.name] = bl.pack_i2s(torch.from_numpy(inp.w_f32).to(dev))
+        del inp
+    R = 16
+    copies = [{n: (pg[0] if r == 0 else pg[0].clone(), pg[1]) for n, pg in packed.items()}
+              for r in range(R)]
+    for M in (1, 4, 16):
+        xs = {}
+        for proj in cfg.projs:
+            bits = W.activations_bf16(W.seed_for(cfg.cid, proj.index, 1), M, proj.K,
+                                      cfg.outlier_frac, cfg.outlier_scale)
+            xs[proj.name] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        launches = [bl.DecodeGroup([dict(packed=copies[r][n][0], gamma=copies[r][n][1], x=xs[n])
+                                    for n in names]) for r in range(R) for names in layer_groups]
+        for f in launches[:len(layer_groups)]:
+            f()
+        g = capture_fns(torch, stream, launches)
+        us = replay_us(torch, stream, g, 1, reps=10) / R
+        out[f"7b_layer_M{M}"] = {"us_per_layer": round(us, 3),
+                                 "gbs": round(cfg.packed_bytes / (us * 1e-6) / 1e9, 1)}
+        del g, launches
+    del copies, packed
+    torch.cuda.empty_cache()
+    for N, K in ((28672, 8192), (8192, 28672)):
+        t = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev)
+        x = torch.randn(1, K, device=dev).to(torch.bfloat16)
+        gam = torch.tensor([0.01], device=dev)
+        R = 8
+        launches = [bl.DecodeGroup([dict(packed=bl.pack_i2s(t), gamma=gam, x=x)]) for _ in range(R)]
+        del t
+        launches[0]()
+        g = capture_fns(torch, stream, launches)
+        us = replay_us(torch, stream, g, R, reps=10)
+        out[f"one_token_gemv_N{N}_K{K}"] = {"us": round(us, 3),
+                                           "gbs": round(N * K / 4 / (us * 1e-6) / 1e9, 1)}
+        del g, launches
+        torch.cuda.empty_cache()
+    return out
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -74,6 +194,8 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=5)
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the 7B-layer and 100B-shape decode measurements")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--traffic", action="store_true",
                    help="counter-collection mode: a 256 MiB plain copy (calibration) and "
@@ -226,6 +348,41 @@ def main():
     log(f"fused decode kernel: {us_launch:.2f} us/launch avg, {gemv_gbs:.1f} GB/s; "
         f"unfused 7x(quantize+gemv): {us_unfused:.2f} us/step")
 
+    # per-replay spread: each replay of g_all is R steps
+    marks = []
+    with torch.cuda.stream(stream):
+        for _ in range(max(8, min(64, args.steps // R))):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            g_all.replay()
+            a1.record(stream)
+            marks.append((a0, a1))
+    torch.cuda.synchronize()
+    per_step = np.array([x0.elapsed_time(x1) * 1e3 / R for x0, x1 in marks])
+    spread = [round(float(np.percentile(per_step, q)), 3) for q in (10, 50, 90)]
+
+    # warm mode: every step reuses layer copy 0 (weights stay in the Infinity Cache)
+    g_warm = capture(step, [0] * R)
+    with torch.cuda.stream(stream):
+        g_warm.replay()
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for _ in range(reps):
+            g_warm.replay()
+        w1.record(stream)
+    torch.cuda.synchronize()
+    us_warm = w0.elapsed_time(w1) * 1e3 / (reps * R)
+
+    floors = measure_floors(torch, dev, stream, capture_fn=capture_fns, R=R,
+                            groups=[(names, sum(inputs[n]["packed"].numel() for n in names),
+                                     sum((inputs[n]["packed"].shape[0] + 15) // 16 for n in names))
+                                    for names in GROUPS])
+    log(f"decode spread p10/p50/p90 {spread} us/step; warm (cache-resident weights) "
+        f"{us_warm:.2f} us/step; floors {floors}")
+    del g_warm
+
     result = {
         "metric": "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM int8 TOPS (% peak)",
         "value": round(gbs, 2),
@@ -244,7 +401,11 @@ def main():
                    "step": "4 fused launches {q,k,v},{o},{gate,up},{down}: per-token absmax "
                            "int8 quantize + I2_S GEMV + bf16 dequant",
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                   "unfused_us_per_step": round(us_unfused, 3)},
+                   "unfused_us_per_step": round(us_unfused, 3),
+                   "us_per_step_p10_p50_p90": spread,
+                   "warm_us_per_step": round(us_warm, 3),
+                   "floors": floors,
+                   "frac_of_layer_floor": round(floors["layer_floor_us"] / (ms_step * 1e3), 4)},
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
@@ -254,6 +415,11 @@ def main():
     del layers, g_all, g_one, g_unfused
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+
+    # ------------------------------------------------ more decode workloads
+    if not args.no_extras:
+        result["decode_more"] = decode_more(torch, bl, W, dev, stream)
+        log(f"more decode: {result['decode_more']}")
 
     # ----------------------------------------------------------------- prefill
     if not args.no_gemm:

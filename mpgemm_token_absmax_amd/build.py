@@ -1,4 +1,5 @@
-"""Build libbitlinear.so (HIP, gfx950) in-tree with hipcc.
+"""Build libbitlinear.so (HIP, gfx950) in-tree with hipcc, and the benchmark's
+measurement aids libblprobe.so (include/bl_probe.h).
 
     python -m mpgemm_token_absmax_amd.build        # or build() from Python
 
@@ -23,6 +24,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 SOURCES = ["api.cpp", "quant_act.hip", "pack_i2s.hip", "gemv_i2s.hip", "gemm_i2s.hip"]
+PROBE_LIB = os.path.join(HERE, "libblprobe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 
@@ -48,19 +51,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libbitlinear.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libbitlinear.so and libblprobe.so; returns
+    the path of libbitlinear.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

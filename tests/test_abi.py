@@ -186,3 +186,25 @@ def test_gemm_group_validation(lib):
     assert call([prob()], M=0) == L.BL_OK
     assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK
     assert lib.bl_gemm_group(None, 1, 256, C16, D16, 4, None) == L.BL_ERR_NULL
+
+
+def test_probe_library_exports_and_validation():
+    """The benchmark's measurement aids: libblprobe.so exports what
+    include/bl_probe.h declares and rejects bad arguments before launching."""
+    path = os.path.join(ROOT, "mpgemm_token_absmax_amd", "libblprobe.so")
+    if not os.path.exists(path):
+        pytest.skip("libblprobe.so not built (run __graft_entry__.build())")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "bl_probe.h")).read(),
+                  flags=re.S)
+    declared = sorted(set(re.findall(r"\b(blp_\w+)\s*\(", text)))
+    assert declared == ["blp_empty", "blp_stream_read"]
+    probe = ctypes.CDLL(path)
+    f = probe.blp_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(A16, 4096, 0, B16, None) == -1            # no blocks
+    assert f(A16, 4100, 4, B16, None) == -1            # bytes not a multiple of 16 * blocks
+    assert f(A16 + 8, 4096, 4, B16, None) == -1        # misaligned source
+    assert f(None, 4096, 4, B16, None) == -1
+    assert f(A16, 4096, 4, None, None) == -1
+    probe.blp_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    assert probe.blp_empty(0, None) == -1
