@@ -82,10 +82,10 @@ __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_
 // exit at once.
 // WPB: waves per block (each takes 1/WPB of K), XR: 16-byte x chunks per lane
 // (covers len*32 chunks), U: steps per load batch.
-template <int WPB, int XR, int U>
+template <int WPB, int RTW, int XR, int U>
 __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int len_max) {
   extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][len_max*256]
-  __shared__ v4i red[WPB - 1][kWave];
+  __shared__ v4i red[WPB - 1][RTW][kWave];
   __shared__ uint32_t wmax[WPB];
 
   const DecodeProblem& P = grp.p[blockIdx.y];
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   int8_t* qp = P.q;
   float* dp = P.d;
   const int ytype = P.ytype;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * RTW);
   // Every field in one scalar round trip, before the exit test: a scalar
   // load still in flight later would make each LDS wait a full wait (they
   // share a counter and scalar loads complete out of order).
@@ -128,17 +128,23 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   for (int u = 0; u < XR; ++u) xv[u] = xs[min(lane + u * kWave, clast)];
   // gamma by a vector load, issued with x (counted with the vector loads)
   const float gam = ytype ? __builtin_nontemporal_load(gptr) : 0.0f;
-  int64_t row = n0 + (lane & 15);
-  row = row < N ? row : N - 1;
-  const uint8_t* wrow = packed + row * RB;
-  v4i wa[U], wb[U];
-  auto load_w = [&](v4i (&dst)[U], int j) {
+  const uint8_t* wrow[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    int64_t row = n0 + rt * 16 + (lane & 15);
+    row = row < N ? row : N - 1;
+    wrow[rt] = packed + row * RB;
+  }
+  v4i wa[U][RTW], wb[U][RTW];
+  auto load_w = [&](v4i (&dst)[U][RTW], int j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int step = max(min(j + u, jb - 1), 0);
       int off = step * 64 + 16 * h;
       off = off < RB ? off : RB - 16;
-      dst[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow + off));
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+        dst[u][rt] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow[rt] + off));
     }
   };
   __builtin_amdgcn_sched_barrier(0);
@@ -177,14 +183,16 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   __builtin_amdgcn_wave_barrier();
 
   // ---- 4. MFMA over this quarter's steps --------------------------------
-  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};  // two chains (even / odd s)
+  v4i acc0[RTW], acc1[RTW];                           // two chains (even / odd s)
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) acc0[rt] = acc1[rt] = v4i{0, 0, 0, 0};
   const int8_t* arow = wact + 64 * h;
   auto read_b = [&](v4i (&b)[4], int j) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       b[s] = *reinterpret_cast<const v4i*>(arow + (j - ja) * 256 + 16 * s);
   };
-  auto compute = [&](const v4i (&w)[U], int j) {
+  auto compute = [&](const v4i (&w)[U][RTW], int j) {
     v4i bn[4];
     read_b(bn, j);
 #pragma unroll
@@ -193,11 +201,13 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
         v4i b[4] = {bn[0], bn[1], bn[2], bn[3]};
         if (u + 1 < U && j + u + 1 < jb) read_b(bn, j + u + 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          v4i& a = (s & 1) ? acc1 : acc0;
-          a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][s]), b[s], a, 0,
-                                                    0, 0);
-        }
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int rt = 0; rt < RTW; ++rt) {
+            v4i& a = (s & 1) ? acc1[rt] : acc0[rt];
+            a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]), b[s], a,
+                                                      0, 0, 0);
+          }
       }
     }
   };
@@ -207,18 +217,28 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
     if (j + 2 * U < jb) load_w(wa, j + 2 * U);
     if (j + U < jb) compute(wb, j + U);
   }
-  v4i acc = acc0 + acc1;
+  v4i acc[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) acc[rt] = acc0[rt] + acc1[rt];
 
-  // ---- 5. sum of the quarters, dequant, store ---------------------------
-  if (wk > 0) red[wk - 1][lane] = acc;
+  // ---- 5. sum of the parts, dequant, store ------------------------------
+  if (wk > 0) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) red[wk - 1][rt][lane] = acc[rt];
+  }
   __syncthreads();
   if (wk > 0) return;
 #pragma unroll
-  for (int w = 0; w < WPB - 1; ++w) acc += red[w][lane];
+  for (int w = 0; w < WPB - 1; ++w)
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) acc[rt] += red[w][rt][lane];
   // D layout: lane holds token lane%16 and rows 4*(lane/16) + v; token 0 only
   if ((lane & 15) != 0) return;
-  const int64_t n = n0 + 4 * h;
-  if (n < N) store_quad(yp, ytype, N, 0, n, acc, gam * dv);
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    const int64_t n = n0 + rt * 16 + 4 * h;
+    if (n < N) store_quad(yp, ytype, N, 0, n, acc[rt], gam * dv);
+  }
 }
 
 // Decode contraction over int8 activations q [M][K] (scales d), M <= 16.
@@ -336,16 +356,16 @@ __global__ void k_generic(const uint8_t* __restrict__ packed, const float* __res
   }
 }
 
-template <int WPB, int XR, int U>
+template <int WPB, int RTW, int XR, int U>
 hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
   int64_t blocks = 0;
   for (int i = 0; i < g.count; ++i) {
-    const int64_t b = (g.p[i].N + 15) / 16;
+    const int64_t b = (g.p[i].N + 16 * RTW - 1) / (16 * RTW);
     blocks = b > blocks ? b : blocks;
   }
   if (blocks == 0) return hipSuccess;
   const size_t lds = (size_t)WPB * len_max * 256;
-  hipLaunchKernelGGL((k_decode1<WPB, XR, U>), dim3((unsigned)blocks, (unsigned)g.count),
+  hipLaunchKernelGGL((k_decode1<WPB, RTW, XR, U>), dim3((unsigned)blocks, (unsigned)g.count),
                      dim3(WPB * kWave), lds, s, g, len_max);
   return hipGetLastError();
 }
@@ -374,10 +394,16 @@ hipError_t launch_q(DecodeGroup& g, hipStream_t s) {
 }
 
 // int8 activations in (p.qin, p.din): enough waves per block that each walks
-// at most about 4 steps of K.
+// at most about 4 steps of K, in one load batch of exactly that many steps.
 hipError_t launch_gemvq(DecodeGroup& g, hipStream_t s) {
-  if (steps_per_wave(g, 4) <= 4) return launch_q<4, 4>(g, s);
-  if (steps_per_wave(g, 8) <= 4) return launch_q<8, 4>(g, s);
+  const int len4 = steps_per_wave(g, 4);
+  if (len4 <= 1) return launch_q<4, 1>(g, s);
+  if (len4 == 2) return launch_q<4, 2>(g, s);
+  if (len4 == 3) return launch_q<4, 3>(g, s);
+  if (len4 == 4) return launch_q<4, 4>(g, s);
+  const int len8 = steps_per_wave(g, 8);
+  if (len8 == 3) return launch_q<8, 3>(g, s);
+  if (len8 == 4) return launch_q<8, 4>(g, s);
   return launch_q<16, 2>(g, s);
 }
 
@@ -427,14 +453,19 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
   for (int i = 0; i < g.count; ++i) fused = fused && g.p[i].x != nullptr;
   if (fused && g.M == 1) {                          // one token: quantize in the kernel
     const int len4 = steps_per_wave(g, 4);
-    if (len4 <= 2) return launch_one_token<4, 1, 4>(g, len4, s);
-    if (len4 <= 4) return launch_one_token<4, 2, 4>(g, len4, s);
+    // one load batch of exactly the steps of the longest wave when it is
+    // short (a clamped extra load still costs a request), else batches of 4
+    if (len4 <= 1) return launch_one_token<4, 1, 1, 1>(g, len4, s);
+    if (len4 == 2) return launch_one_token<4, 1, 1, 2>(g, len4, s);
+    if (len4 == 3) return launch_one_token<4, 1, 2, 3>(g, len4, s);
+    if (len4 == 4) return launch_one_token<4, 1, 2, 4>(g, len4, s);
     const int len8 = steps_per_wave(g, 8);
-    if (len8 <= 4) return launch_one_token<8, 2, 4>(g, len8, s);
-    if (len8 <= 8) return launch_one_token<8, 4, 8>(g, len8, s);
+    if (len8 == 3) return launch_one_token<8, 1, 2, 3>(g, len8, s);
+    if (len8 == 4) return launch_one_token<8, 1, 2, 4>(g, len8, s);
+    if (len8 <= 8) return launch_one_token<8, 1, 4, 4>(g, len8, s);
     const int len16 = steps_per_wave(g, 16);       // <= 16 for K <= 65536
-    if (len16 <= 8) return launch_one_token<16, 4, 8>(g, len16, s);
-    return launch_one_token<16, 8, 8>(g, len16, s);
+    if (len16 <= 8) return launch_one_token<16, 1, 4, 4>(g, len16, s);
+    return launch_one_token<16, 1, 8, 4>(g, len16, s);
   }
   if (fused) {
     // several tokens: one launch quantizes every problem's x into its q and

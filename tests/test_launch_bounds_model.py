@@ -26,26 +26,24 @@ def decode1_config(K):
     """(WPB, XR, U, len) that launch_decode_group picks for a one-token group
     whose largest K is K."""
     len4 = steps_per_wave(K, 4)
-    if len4 <= 2:
-        return 4, 1, 4, len4
     if len4 <= 4:
-        return 4, 2, 4, len4
+        return 4, (1 if len4 <= 2 else 2), max(len4, 1), len4
     len8 = steps_per_wave(K, 8)
     if len8 <= 4:
-        return 8, 2, 4, len8
+        return 8, 2, len8, len8
     if len8 <= 8:
-        return 8, 4, 8, len8
+        return 8, 4, 4, len8
     len16 = steps_per_wave(K, 16)
     assert len16 <= 16, "K above 65536 is rejected at the boundary"
-    return (16, 4, 8, len16) if len16 <= 8 else (16, 8, 8, len16)
+    return (16, 4, 4, len16) if len16 <= 8 else (16, 8, 4, len16)
 
 
 def gemvq_config(K):
     """(WPB, U) of launch_gemvq for a group whose largest K is K."""
     if steps_per_wave(K, 4) <= 4:
-        return 4, 4
+        return 4, max(steps_per_wave(K, 4), 1)
     if steps_per_wave(K, 8) <= 4:
-        return 8, 4
+        return 8, steps_per_wave(K, 8)
     return 16, 2
 
 
