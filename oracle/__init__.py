@@ -20,7 +20,7 @@ Sources (web pages on the method; cited by title and section):
     matmul's multiply-adds become additions and subtractions.
 
 Modules:
-  quant    per-token absmax int8 activation quantization
+  quant    absmax int8 activation quantization, per token or per tensor
   ternary  absmean weight scale (exact sum) and the +-0.5*gamma threshold
   i2s      2-bit I2_S pack / unpack (code table and bit layout)
   dot      exact integer contraction (int64), plus an fp64-BLAS exact variant
@@ -32,7 +32,7 @@ hand-worked examples (tests/golden/), closed forms, brute force and
 invariants. Parity unpinned: byte compatibility with bitnet.cpp's own i2_s
 GGUF layout, and end-to-end "lossless vs Float16" (needs trained weights).
 """
-from .quant import widen_bf16, quantize_act_absmax
+from .quant import widen_bf16, quantize_act_absmax, quantize_act_absmax_tensor
 from .ternary import absmean_gamma, ternarize, ternarize_absmean
 from .i2s import pack_i2s, unpack_i2s, CODE_ZERO, CODE_POS, CODE_NEG
 from .dot import mpgemm_acc, mpgemm_acc_entries, mpgemm_acc_f64blas

@@ -14,6 +14,10 @@ to even; zero row -> zeros with scale 0):
   s_t  = fl32(127 / m_t)
   q    = clamp(round_half_even(fl32(x * s_t)), -127, 127)
   d_t  = fl32(m_t / 127)                (the dequantization multiplier)
+
+quantize_act_absmax_tensor is the pages' literal setting for several tokens:
+one scale over the whole activation tensor (same formulas with m = max over
+every token and k; every token's d is the same value).
 """
 from __future__ import annotations
 
@@ -62,4 +66,40 @@ def quantize_act_absmax(x_bits: np.ndarray):
     r = _round_half_even(v)
     q[nz] = np.clip(r, -QMAX, QMAX).astype(np.int8)
     d[nz] = m[nz] / np.float32(QMAX)                      # fp32 IEEE quotient
+    return q, d
+
+
+def _tensor_absmax(x: np.ndarray) -> np.float32:
+    return np.float32(np.max(np.abs(x)))
+
+
+def quantize_act_absmax_tensor(x_bits: np.ndarray):
+    """One scale for the whole activation tensor ([BN] Part A 2.3 and 4.1:
+    int8 activations with one per-tensor scale).
+
+      m = max_{t,k} |x[t][k]|,  s = fl32(127 / m),
+      q = clamp(round_half_even(fl32(x * s)), -127, 127),  d[t] = fl32(m / 127) for every t.
+
+    x_bits: uint16 bf16 patterns [M][K] -> (q int8 [M][K], d fp32 [M]).
+    Same domain as quantize_act_absmax.
+    """
+    x = widen_bf16(x_bits)
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D [M][K]")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite activation")
+    M, K = x.shape
+    q = np.zeros((M, K), dtype=np.int8)
+    d = np.zeros(M, dtype=np.float32)
+    if M == 0 or K == 0:
+        return q, d
+    m = _tensor_absmax(x)
+    if m == 0:
+        return q, d
+    s = np.float32(QMAX) / m                              # fp32 IEEE quotient
+    if not np.isfinite(s):
+        raise ValueError("absmax too small: 127/m overflows fp32")
+    v = (x * s).astype(np.float32)                        # fp32 product
+    q[:] = np.clip(_round_half_even(v), -QMAX, QMAX).astype(np.int8)
+    d[:] = m / np.float32(QMAX)                           # fp32 IEEE quotient
     return q, d

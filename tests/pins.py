@@ -124,6 +124,43 @@ def pin_quant_rejects():
         raise AssertionError("inf accepted")
 
 
+def pin_quant_tensor_golden():
+    g = golden("e8_quant_tensor.json")
+    q, d = oracle.quantize_act_absmax_tensor(bf16_bits(g["x"]))
+    assert q.tolist() == g["q"], q.tolist()
+    assert d.view(np.uint32).tolist() == g["d_bits"], d
+    qt, _ = oracle.quantize_act_absmax(bf16_bits(g["x"]))
+    assert qt[0].tolist() == g["q_per_token_row0"]       # the modes differ on token 0
+
+
+def pin_quant_tensor_reductions(seed=22):
+    """Per-tensor equals per-token for one token and for any token holding
+    the tensor's absmax; every token shares d; bounds and symmetries."""
+    r = _rng(seed)
+    for scale in (1.0, 3e-2, 5e3):
+        xb = _rand_bf16(r, (7, 45), scale)
+        x = oracle.widen_bf16(xb).astype(np.float64)
+        q, d = oracle.quantize_act_absmax_tensor(xb)
+        qt, dt = oracle.quantize_act_absmax(xb)
+        m = np.max(np.abs(x))
+        for t in range(x.shape[0]):
+            q1, d1 = oracle.quantize_act_absmax_tensor(xb[t:t + 1])
+            assert np.array_equal(q1, qt[t:t + 1]) and np.array_equal(d1, dt[t:t + 1])
+            if np.max(np.abs(x[t])) == m:
+                assert np.array_equal(q[t], qt[t]) and d[t] == dt[t]
+        assert np.all(d == d[0]) and abs(float(d[0]) * 127.0 - m) <= m * 2.0**-23
+        err = np.abs(q - x * 127.0 / m)
+        assert np.all(err <= 0.5 + 1e-4), err.max()
+        assert np.max(np.abs(q.astype(np.int64))) == 127
+        qn, dn = oracle.quantize_act_absmax_tensor(xb ^ np.uint16(0x8000))
+        assert np.array_equal(qn, -q) and np.array_equal(dn, d)
+        # monotone over the whole tensor (one scale)
+        o = np.argsort(x.ravel(), kind="stable")
+        assert np.all(np.diff(q.ravel()[o].astype(np.int64)) >= 0)
+    z, dz = oracle.quantize_act_absmax_tensor(np.zeros((3, 8), dtype=np.uint16))
+    assert not z.any() and not dz.any()
+
+
 # ----------------------------------------------------------------------------
 # absmean gamma and ternarize
 # ----------------------------------------------------------------------------
@@ -417,6 +454,7 @@ def pin_bf16_bruteforce(seed=21):
 
 ALL_PINS = [
     pin_quant_golden, pin_quant_special, pin_quant_invariants, pin_quant_rejects,
+    pin_quant_tensor_golden, pin_quant_tensor_reductions,
     pin_ternary_golden, pin_gamma_exact, pin_ternary_roundclip, pin_ternary_invariants,
     pin_ternary_statistics,
     pin_pack_golden, pin_pack_exhaustive, pin_pack_layout,

@@ -15,6 +15,9 @@ MUTATIONS = {
     "quant_round_truncate": (oracle.quant, "_round_half_even", np.trunc),
     "quant_scale_128": (oracle.quant, "QMAX", 128),
     "quant_signed_max": (oracle.quant, "_row_absmax", lambda x: np.max(x, axis=1)),
+    "quant_tensor_first_row_max": (oracle.quant, "_tensor_absmax",
+                                   lambda x: np.float32(np.max(np.abs(x[0])))),
+    "quant_tensor_signed_max": (oracle.quant, "_tensor_absmax", lambda x: np.float32(np.max(x))),
     "ternary_ge_threshold": (oracle.ternary, "_above", lambda w, t: w >= t),
     "ternary_threshold_0.7": (oracle.ternary, "THRESHOLD_FRACTION", 0.7),
     "ternary_fp32_sum": (oracle.ternary, "_exact_abs_sum",
