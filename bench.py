@@ -473,6 +473,38 @@ def main():
         torch.cuda.synchronize()
         ms_gemm = b0.elapsed_time(b1) / args.gemm_steps
         gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
+        # one activation scale per layer input (per tensor) instead of per token
+        ws_t = torch.empty((max(16, int(bl.lib().bl_quantize_act_tensor_workspace(M5))),),
+                           dtype=torch.uint8, device=dev)
+
+        def quantize_all(per_tensor):
+            for e in G:
+                if per_tensor:
+                    bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t)
+                else:
+                    bl.quantize_act(e["x"], e["q"], e["d"])
+
+        def layer_pt():
+            for e in G:
+                bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t)
+                e["group"]()
+
+        def timed(fn, n):
+            fn()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(n):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / n
+
+        ms_layer_pt = timed(layer_pt, args.gemm_steps)
+        tops_pt = ops / (ms_layer_pt * 1e-3) / 1e12
+        us_q_tok = timed(lambda: quantize_all(False), 10) * 1e3
+        us_q_ten = timed(lambda: quantize_all(True), 10) * 1e3
         per_group = {}
         for e in G:
             c0 = torch.cuda.Event(enable_timing=True)
@@ -485,14 +517,19 @@ def main():
             ms = c0.elapsed_time(c1) / 3
             per_group["+".join(e["names"])] = round(e["ops"] / (ms * 1e-3) / 1e12, 1)
         log(f"prefill: {ms_layer:.3f} ms/layer ({tops:.1f} TOPS incl. quantize), "
-            f"GEMM only {gemm_tops:.1f} TOPS; per group {per_group}")
+            f"GEMM only {gemm_tops:.1f} TOPS; per group {per_group}; per-tensor scale "
+            f"{tops_pt:.1f} TOPS; quantize per layer {us_q_tok:.1f} us per token, "
+            f"{us_q_ten:.1f} us per tensor")
         result["gemm"] = {"workload": cfg5.name, "tokens": M5, "ops_per_layer": ops,
                           "ms_per_layer": round(ms_layer, 4), "tops": round(tops, 1),
                           "gemm_only_tops": round(gemm_tops, 1), "peak_tops": INT8_PEAK_TOPS,
                           "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
                           "step": "per input: bl_quantize_act, then one bl_gemm_group for "
                                   "{q,k,v}, {o}, {gate,up}, {down}",
-                          "tops_per_group": per_group}
+                          "tops_per_group": per_group,
+                          "tops_per_tensor_scale": round(tops_pt, 1),
+                          "quantize_us_per_layer": {"per_token": round(us_q_tok, 1),
+                                                    "per_tensor": round(us_q_ten, 1)}}
         del G
         torch.cuda.empty_cache()
 

@@ -107,6 +107,28 @@ int bl_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                     int8_t *q, float *d, void *stream);
 
 /*
+ * bl_quantize_act_tensor_workspace -- bytes of workspace bl_quantize_act_tensor
+ * needs for M tokens (4*M rounded up to 16; 0 for M <= 0).
+ */
+size_t bl_quantize_act_tensor_workspace(int64_t M);
+
+/*
+ * bl_quantize_act_tensor -- absmax int8 quantization with ONE scale for the
+ * whole activation tensor (all M tokens).
+ * Defines: [BN] Part A 2.3 / 4.1 (int8 activations with one per-tensor
+ * scale), the literal setting of the pages for several tokens.
+ *   m = max over every t, k of |x[t][k]|; if m == 0: q = 0 and d[:] = 0; else
+ *   s = fl32(127 / m), q[t][k] = clamp(rne(fl32(x[t][k] * s)), -127, 127), and
+ *   every d[t] = fl32(m / 127) (so bl_gemv / bl_gemm apply it unchanged).
+ * Arguments as bl_quantize_act, plus a workspace of ws_bytes bytes (>=
+ * bl_quantize_act_tensor_workspace(M), 16-byte aligned; not needed when
+ * K == 0): it receives the row maxima between the two launches the call
+ * enqueues (row maxima, then quantize with the tensor's maximum).
+ */
+int bl_quantize_act_tensor(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                           int8_t *q, float *d, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * bl_pack_i2s_workspace -- bytes of workspace bl_pack_i2s needs for an
  * N x K fp32 matrix (BL_W_F32). BL_W_TERNARY_I8 needs none.
  */

@@ -7,6 +7,7 @@ computation runs in the library's HIP kernels. PyTorch provides device memory
 and streams only.
 
     q, d        = quantize_act(x_bf16)              # per-token absmax int8
+    q, d        = quantize_act_tensor(x_bf16)       # one absmax scale for all tokens
     packed, g   = pack_i2s(w_fp32)                  # absmean ternary -> 2-bit I2_S
     packed      = pack_i2s(w_ternary_int8)          # pack only (caller keeps gamma)
     y           = gemv(packed, g, q, d)             # M <= 16 tokens
@@ -23,7 +24,7 @@ import torch
 from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I8, MAX_GROUP,
                    BitLinearError, DecodeProblem, GemmProblem, check, lib, status_string)
 
-__all__ = ["quantize_act", "pack_i2s", "pack_i2s_workspace", "gemv", "gemm",
+__all__ = ["quantize_act", "quantize_act_tensor", "pack_i2s", "pack_i2s_workspace", "gemv", "gemm",
            "gemm_workspace", "gemm_group", "GemmGroup", "decode_group", "DecodeGroup",
            "BitLinearError", "status_string",
            "lib", "OUT_TYPES"]
@@ -61,6 +62,27 @@ def quantize_act(x: torch.Tensor, q: torch.Tensor | None = None, d: torch.Tensor
         d = torch.empty((M,), dtype=torch.float32, device=x.device)
     check("bl_quantize_act", lib().bl_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d),
                                                    _stream(x.device)))
+    return q, d
+
+
+def quantize_act_tensor(x: torch.Tensor, q: torch.Tensor | None = None,
+                        d: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """x: bf16 [M][K] -> (q int8 [M][K], d fp32 [M]) with ONE scale for the
+    whole tensor (every d[t] equal)."""
+    _need(x, "x", torch.bfloat16, 2)
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((M,), dtype=torch.float32, device=x.device)
+    nws = int(lib().bl_quantize_act_tensor_workspace(M))
+    if workspace is None:
+        workspace = torch.empty((max(nws, 16),), dtype=torch.uint8, device=x.device)
+    check("bl_quantize_act_tensor",
+          lib().bl_quantize_act_tensor(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d),
+                                       _ptr(workspace), workspace.numel(), _stream(x.device)))
     return q, d
 
 

@@ -27,7 +27,8 @@ BL_OUT_I32 = 0
 BL_OUT_F32 = 1
 BL_OUT_BF16 = 2
 
-EXPORTS = ("bl_abi_version", "bl_status_string", "bl_quantize_act", "bl_pack_i2s_workspace",
+EXPORTS = ("bl_abi_version", "bl_status_string", "bl_quantize_act",
+           "bl_quantize_act_tensor_workspace", "bl_quantize_act_tensor", "bl_pack_i2s_workspace",
            "bl_pack_i2s", "bl_gemv", "bl_gemm_workspace", "bl_gemm", "bl_gemm_group",
            "bl_decode_group")
 
@@ -70,6 +71,10 @@ def _declare(lib):
     lib.bl_quantize_act.restype = INT
     lib.bl_quantize_act.argtypes = [P, I64, I64, I64, P, P, P]
     lib.bl_pack_i2s_workspace.restype = SZ
+    lib.bl_quantize_act_tensor_workspace.restype = SZ
+    lib.bl_quantize_act_tensor_workspace.argtypes = [I64]
+    lib.bl_quantize_act_tensor.restype = INT
+    lib.bl_quantize_act_tensor.argtypes = [P, I64, I64, I64, P, P, P, SZ, P]
     lib.bl_pack_i2s_workspace.argtypes = [I64, I64]
     lib.bl_pack_i2s.restype = INT
     lib.bl_pack_i2s.argtypes = [P, INT, I64, I64, P, P, P, SZ, P]

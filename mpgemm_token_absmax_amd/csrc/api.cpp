@@ -66,6 +66,26 @@ int bl_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t
   return hip_status(bl::launch_quantize_act(x, M, K, ldx, q, d, as_stream(stream)));
 }
 
+size_t bl_quantize_act_tensor_workspace(int64_t M) {
+  if (M <= 0) return 0;
+  return (size_t)((4 * M + 15) / 16 * 16);
+}
+
+int bl_quantize_act_tensor(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                           float* d, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || K < 0 || K % 4 != 0 || ldx < K) return BL_ERR_SHAPE;
+  if (M == 0) return BL_OK;
+  if (!d || (K > 0 && (!x || !q))) return BL_ERR_NULL;
+  if (K > 0 && ldx % 4 != 0) return BL_ERR_ALIGN;
+  if (!aligned(d, 4)) return BL_ERR_ALIGN;
+  if (K > 0 && (!aligned(x, 16) || !aligned(q, 16))) return BL_ERR_ALIGN;
+  if (M > INT32_MAX) return BL_ERR_SHAPE;
+  if (K > 0 && (!ws || ws_bytes < bl_quantize_act_tensor_workspace(M))) return BL_ERR_WORKSPACE;
+  if (K > 0 && !aligned(ws, 16)) return BL_ERR_ALIGN;
+  return hip_status(bl::launch_quantize_act_tensor(x, M, K, ldx, q, d,
+                                                   static_cast<uint32_t*>(ws), as_stream(stream)));
+}
+
 size_t bl_pack_i2s_workspace(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0) return 0;
   return bl::pack_workspace_bytes(N, K);

@@ -148,7 +148,7 @@ __device__ __forceinline__ void issue_step(int8_t* smem, int ks, int wv, int lan
 }
 
 template <int RT, int TT, int WRW>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_i2s(const GemmArgs g, int64_t K,
+__global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(const GemmArgs g, int64_t K,
                                                           const int8_t* __restrict__ q,
                                                           const float* __restrict__ d, int64_t M,
                                                           int n_tok_blocks) {

@@ -45,6 +45,9 @@ hipError_t launch_quantize_group(const DecodeGroup& g, hipStream_t s);
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                float* d, hipStream_t s);
+// One scale for the whole tensor; maxb: M words of workspace (row maxima).
+hipError_t launch_quantize_act_tensor(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      int8_t* q, float* d, uint32_t* maxb, hipStream_t s);
 
 size_t pack_workspace_bytes(int64_t N, int64_t K);
 hipError_t launch_pack_f32(const float* w, int64_t N, int64_t K, uint8_t* packed, float* gamma,

@@ -73,10 +73,12 @@ __global__ __launch_bounds__(kQThreads) void k_quant_absmax(
 // 16-byte variant (K % 8 == 0, ldx % 8 == 0): 8 bf16 per chunk, the row in
 // registers (K <= 2048*NC). Loads are unconditional (chunk index clamped, the
 // value of a chunk past the row ignored) so they are all in flight at once.
+// given_max: nullptr -> the row's own absmax (per token); else the absmax
+// bits to use (per tensor, the same for every row).
 template <int NC>
 __device__ __forceinline__ void quant_row16(const uint16_t* __restrict__ xrow, int64_t K,
                                             int8_t* __restrict__ qrow, float* __restrict__ dt,
-                                            uint32_t* red) {
+                                            uint32_t* red, const uint32_t* given_max = nullptr) {
   const uint4* xr = reinterpret_cast<const uint4*>(xrow);
   uint2* qr = reinterpret_cast<uint2*>(qrow);
   const int nchunk = (int)(K / 8);
@@ -87,14 +89,18 @@ __device__ __forceinline__ void quant_row16(const uint16_t* __restrict__ xrow, i
     v[i] = xr[c < nchunk ? c : nchunk - 1];
   }
   uint32_t mb = 0;
+  if (given_max) {
+    mb = *given_max;
+  } else {
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = (int)threadIdx.x + i * kQThreads;
-    const uint32_t m8 = max(absmax4_bf16(make_uint2(v[i].x, v[i].y)),
-                            absmax4_bf16(make_uint2(v[i].z, v[i].w)));
-    mb = max(mb, c < nchunk ? m8 : 0u);
+    for (int i = 0; i < NC; ++i) {
+      const int c = (int)threadIdx.x + i * kQThreads;
+      const uint32_t m8 = max(absmax4_bf16(make_uint2(v[i].x, v[i].y)),
+                              absmax4_bf16(make_uint2(v[i].z, v[i].w)));
+      mb = max(mb, c < nchunk ? m8 : 0u);
+    }
+    mb = block_max_u32(mb, red);
   }
-  mb = block_max_u32(mb, red);
   const float m = __uint_as_float(mb << 16);
   const float s = mb ? 127.0f / m : 0.0f;
 #pragma unroll
@@ -125,6 +131,55 @@ __global__ __launch_bounds__(kQThreads) void k_quant_group(DecodeGroup g) {
   const DecodeProblem& P = g.p[blockIdx.y];
   const int64_t t = blockIdx.x;
   quant_row16<NC>(P.x + t * P.ldx, P.K, P.q + t * P.K, P.d + t, red);
+}
+
+// ---- one scale for the whole tensor: row maxima first, then quantize -----
+
+// Absmax bits of each row (any K % 4 == 0): maxb[t] = max_k |x[t][k]| bits.
+__global__ __launch_bounds__(kQThreads) void k_row_absmax(const uint16_t* __restrict__ x,
+                                                          int64_t K, int64_t ldx,
+                                                          uint32_t* __restrict__ maxb) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  const int64_t t = blockIdx.x;
+  const uint2* xr = reinterpret_cast<const uint2*>(x + t * ldx);
+  uint32_t mb = 0;
+  for (int64_t c = threadIdx.x; c < K / 4; c += kQThreads) mb = max(mb, absmax4_bf16(xr[c]));
+  mb = block_max_u32(mb, red);
+  if (threadIdx.x == 0) maxb[t] = mb;
+}
+
+// The tensor's absmax bits from the M row maxima (every block reads them all).
+__device__ __forceinline__ uint32_t tensor_absmax(const uint32_t* __restrict__ maxb, int64_t M,
+                                                  uint32_t* red) {
+  uint32_t mb = 0;
+  for (int64_t i = threadIdx.x; i < M; i += kQThreads) mb = max(mb, maxb[i]);
+  return block_max_u32(mb, red);
+}
+
+template <int NC>
+__global__ __launch_bounds__(kQThreads) void k_quant_tensor16(
+    const uint16_t* __restrict__ x, int64_t K, int64_t ldx, const uint32_t* __restrict__ maxb,
+    int64_t M, int8_t* __restrict__ q, float* __restrict__ d) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  __shared__ uint32_t red2[kQThreads / kWave];
+  const uint32_t mb = tensor_absmax(maxb, M, red);
+  const int64_t t = blockIdx.x;
+  quant_row16<NC>(x + t * ldx, K, q + t * K, d + t, red2, &mb);
+}
+
+// Any K % 4 == 0 and row stride: 4 values per chunk, the row read once.
+__global__ __launch_bounds__(kQThreads) void k_quant_tensor_any(
+    const uint16_t* __restrict__ x, int64_t K, int64_t ldx, const uint32_t* __restrict__ maxb,
+    int64_t M, int8_t* __restrict__ q, float* __restrict__ d) {
+  __shared__ uint32_t red[kQThreads / kWave];
+  const uint32_t mb = tensor_absmax(maxb, M, red);
+  const int64_t t = blockIdx.x;
+  const uint2* xr = reinterpret_cast<const uint2*>(x + t * ldx);
+  uint32_t* qr = reinterpret_cast<uint32_t*>(q + t * K);
+  const float m = __uint_as_float(mb << 16);
+  const float s = mb ? 127.0f / m : 0.0f;
+  for (int64_t c = threadIdx.x; c < K / 4; c += kQThreads) qr[c] = mb ? quant4_bf16(xr[c], s) : 0u;
+  if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
 }
 
 __global__ void k_fill_zero_f32(float* __restrict__ p, int64_t n) {
@@ -178,6 +233,30 @@ hipError_t launch_quantize_group(const DecodeGroup& g, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_quantize_act_tensor(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      int8_t* q, float* d, uint32_t* maxb, hipStream_t s) {
+  if (K == 0) {
+    hipLaunchKernelGGL(k_fill_zero_f32, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, d, M);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)M), dim3(kQThreads), 0, s, x, K, ldx, maxb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (K % 8 == 0 && ldx % 8 == 0 && K <= 2048 * 16) {
+    const int64_t per_thread = (K / 8 + kQThreads - 1) / kQThreads;
+    const dim3 g((unsigned)M), b(kQThreads);
+    if (per_thread <= 1) hipLaunchKernelGGL(k_quant_tensor16<1>, g, b, 0, s, x, K, ldx, maxb, M, q, d);
+    else if (per_thread <= 2) hipLaunchKernelGGL(k_quant_tensor16<2>, g, b, 0, s, x, K, ldx, maxb, M, q, d);
+    else if (per_thread <= 4) hipLaunchKernelGGL(k_quant_tensor16<4>, g, b, 0, s, x, K, ldx, maxb, M, q, d);
+    else if (per_thread <= 8) hipLaunchKernelGGL(k_quant_tensor16<8>, g, b, 0, s, x, K, ldx, maxb, M, q, d);
+    else hipLaunchKernelGGL(k_quant_tensor16<16>, g, b, 0, s, x, K, ldx, maxb, M, q, d);
+  } else {
+    hipLaunchKernelGGL(k_quant_tensor_any, dim3((unsigned)M), dim3(kQThreads), 0, s, x, K, ldx, maxb,
+                       M, q, d);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,

@@ -208,3 +208,20 @@ def test_probe_library_exports_and_validation():
     assert f(A16, 4096, 4, None, None) == -1
     probe.blp_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
     assert probe.blp_empty(0, None) == -1
+
+
+def test_quantize_tensor_validation(lib):
+    f = lib.bl_quantize_act_tensor
+    ws = lib.bl_quantize_act_tensor_workspace(2)
+    assert ws == 16 and lib.bl_quantize_act_tensor_workspace(0) == 0
+    assert lib.bl_quantize_act_tensor_workspace(5) == 32
+    assert f(A16, 2, 6, 6, B16, C16, D16, ws, None) == L.BL_ERR_SHAPE       # K % 4
+    assert f(A16, 2, 8, 4, B16, C16, D16, ws, None) == L.BL_ERR_SHAPE       # ldx < K
+    assert f(None, 2, 8, 8, B16, C16, D16, ws, None) == L.BL_ERR_NULL
+    assert f(A16, 2, 8, 8, B16, None, D16, ws, None) == L.BL_ERR_NULL
+    assert f(A16, 2, 8, 8, B16, C16, None, ws, None) == L.BL_ERR_WORKSPACE
+    assert f(A16, 2, 8, 8, B16, C16, D16, ws - 1, None) == L.BL_ERR_WORKSPACE
+    assert f(A16, 2, 8, 8, B16, C16, D16 + 4, ws, None) == L.BL_ERR_ALIGN
+    assert f(A16 + 8, 2, 8, 8, B16, C16, D16, ws, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 8, 10, B16, C16, D16, ws, None) == L.BL_ERR_ALIGN     # ldx % 4
+    assert f(None, 0, 8, 8, None, None, None, 0, None) == L.BL_OK            # M == 0

@@ -145,6 +145,74 @@ def test_quantize_special_rows_and_stride():
     assert host(q)[1, :6].tolist() == [127, 62, -62, 0, 2, -2]
 
 
+QUANT_TENSOR_SHAPES = [(1, 64), (3, 260), (17, 2560), (5, 6912), (2, 28672), (3, 36000),
+                       (64, 4096), (2048, 8192), (300, 8), (1, 4)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_TENSOR_SHAPES, ids=[f"M{m}K{k}" for m, k in QUANT_TENSOR_SHAPES])
+def test_quantize_tensor_parity(M, K):
+    """One scale over all tokens: bit-exact q and d against the oracle (both
+    the 16-byte path and the any-K path)."""
+    bl = _bl()
+    say(f"quantize per tensor M={M} K={K}")
+    x = W.activations_bf16(700 + M * 7 + K, M, K, outlier_frac=0.01, outlier_scale=20.0)
+    if M > 2:
+        x[M // 2] = 0                                  # a zero token keeps the shared scale
+    q_ref, d_ref = oracle.quantize_act_absmax_tensor(x)
+    q, d = bl.quantize_act_tensor(dev_bf16(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+
+
+def test_quantize_tensor_special():
+    bl = _bl()
+    say("quantize per tensor: golden e8, zero tensor, strided rows")
+    import pins
+    g = pins.golden("e8_quant_tensor.json")
+    xg = pins.bf16_bits(g["x"])
+    q, d = bl.quantize_act_tensor(dev_bf16(xg))
+    torch.cuda.synchronize()
+    assert host(q).tolist() == g["q"]
+    assert host(d).view(np.uint32).tolist() == g["d_bits"]
+    z, dz = bl.quantize_act_tensor(dev_bf16(np.zeros((4, 16), np.uint16)))
+    torch.cuda.synchronize()
+    assert not host(z).any() and not host(dz).any()
+    x = W.activations_bf16(71, 6, 24, 0.0, 1.0)
+    for ldx in (32, 28):                               # 16-byte path, then the any-K path
+        wide = np.zeros((6, ldx), np.uint16)
+        wide[:, :24] = x
+        qs, ds = bl.quantize_act_tensor(dev_bf16(wide)[:, :24])
+        q_ref, d_ref = oracle.quantize_act_absmax_tensor(x)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(qs), q_ref)
+        assert np.array_equal(host(ds).view(np.uint32), d_ref.view(np.uint32))
+
+
+def test_config3_prefill_per_tensor_scale():
+    """2B-layer prefill (512 tokens) with one activation scale per layer input:
+    per-tensor quantize then bl_gemm_group, every output against the oracle."""
+    bl = _bl()
+    cfg = W.CONFIGS[3]
+    by = {p.name: p for p in cfg.projs}
+    for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        inps = [W.proj_inputs(cfg, by[n], 512) for n in names]
+        x = inps[0].x_bf16
+        say(f"config 3 per-tensor group {names}")
+        q_ref, d_ref = oracle.quantize_act_absmax_tensor(x)
+        q, d = bl.quantize_act_tensor(dev_bf16(x))
+        probs = [dict(packed=bl.pack_i2s(dev(inp.w_tern)),
+                      gamma=dev(np.array([inp.gamma], np.float32)), out_dtype="bf16")
+                 for inp in inps]
+        ys = bl.gemm_group(probs, q, d)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), q_ref)
+        assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+        for inp, y in zip(inps, ys):
+            acc = oracle.mpgemm_acc_f64blas(q_ref, inp.w_tern)
+            check_outputs(acc, np.float32(inp.gamma), d_ref, y_bf16=host(y))
+
+
 def test_quantize_empty():
     bl = _bl()
     say("quantize empty")
