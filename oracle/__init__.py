@@ -18,9 +18,12 @@ Sources (web pages on the method; cited by title and section):
     add or subtract the activation per nonzero weight).
   * bitnet.cpp how-to blog (mhpq.cn) §1.2: with weights in {-1,0,+1} the
     matmul's multiply-adds become additions and subtractions.
+  * BinaryAI Engine forum post, "关键技术机制解析" §2: the residual add and
+    the RMS normalization fused into one pass.
 
 Modules:
   quant    absmax int8 activation quantization, per token or per tensor
+  norm     residual add + RMSNorm fused with the per-token quantizer
   ternary  absmean weight scale (exact sum) and the +-0.5*gamma threshold
   i2s      2-bit I2_S pack / unpack (code table and bit layout)
   dot      exact integer contraction (int64), plus an fp64-BLAS exact variant
@@ -33,6 +36,7 @@ invariants. Parity unpinned: byte compatibility with bitnet.cpp's own i2_s
 GGUF layout, and end-to-end "lossless vs Float16" (needs trained weights).
 """
 from .quant import widen_bf16, quantize_act_absmax, quantize_act_absmax_tensor
+from .norm import rmsnorm_quant, round_fraction_to_f32
 from .ternary import absmean_gamma, ternarize, ternarize_absmean
 from .i2s import pack_i2s, unpack_i2s, CODE_ZERO, CODE_POS, CODE_NEG
 from .dot import mpgemm_acc, mpgemm_acc_entries, mpgemm_acc_f64blas

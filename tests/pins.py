@@ -162,6 +162,99 @@ def pin_quant_tensor_reductions(seed=22):
 
 
 # ----------------------------------------------------------------------------
+# residual + RMSNorm + quantize
+# ----------------------------------------------------------------------------
+
+def pin_norm_golden():
+    for c in golden("e9_rmsnorm_quant.json")["cases"]:
+        r = None if c["r"] is None else bf16_bits([c["r"]])
+        h, q, d = oracle.rmsnorm_quant(bf16_bits([c["x"]]), r, bf16_bits(c["g"]), c["eps"])
+        assert h[0].tolist() == c["h_bits"], (c["derivation"], h)
+        assert q[0].tolist() == c["q"], (c["derivation"], q)
+        assert int(d.view(np.uint32)[0]) == c["d_bits"], (c["derivation"], d)
+
+
+def _ms_by_mantissas(hb):
+    """sum h^2 / K from integer significands and exponents (exact rational)."""
+    from fractions import Fraction
+    total = Fraction(0)
+    for b in np.asarray(hb, dtype=np.uint16).tolist():
+        e, m = (b >> 7) & 0xFF, b & 0x7F
+        sig, ex = (m, -133) if e == 0 else (m | 0x80, e - 134)
+        total += Fraction(sig * sig) * (Fraction(2) ** (2 * ex))
+    return total / len(hb)
+
+
+def pin_norm_exact_ms(seed=23):
+    """The oracle's mean square is the exact rational (checked from integer
+    significands), and its fp32 rounding is the nearest fp32 value."""
+    r = _rng(seed)
+    xb = _rand_bf16(r, (5, 37), 3.0)
+    rb = _rand_bf16(r, (5, 37), 0.5)
+    g = _rand_bf16(r, (37,), 1.0)
+    h, q, d, ms = oracle.rmsnorm_quant(xb, rb, g, 1e-5, return_ms=True)
+    for t in range(5):
+        exact = _ms_by_mantissas(h[t])
+        assert ms[t] == exact
+        f = oracle.round_fraction_to_f32(exact)
+        lo, hi = np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(np.inf))
+        from fractions import Fraction
+        assert abs(Fraction(float(f)) - exact) <= abs(Fraction(float(lo)) - exact)
+        assert abs(Fraction(float(f)) - exact) <= abs(Fraction(float(hi)) - exact)
+
+
+def pin_norm_invariants(seed=24):
+    r = _rng(seed)
+    K = 48
+    xb = _rand_bf16(r, (6, K), 1.0)
+    g = _rand_bf16(r, (K,), 1.0)
+    h, q, d = oracle.rmsnorm_quant(xb, None, g, 0.0)
+    assert np.array_equal(h, xb)
+    # power-of-two scaling of x (eps = 0): identical codes and scales
+    for e in (-4, 3):
+        xs = (oracle.widen_bf16(xb) * np.float32(2.0**e)).astype(np.float32)
+        hs, qs, ds = oracle.rmsnorm_quant((xs.view(np.uint32) >> 16).astype(np.uint16), None, g, 0.0)
+        assert np.array_equal(qs, q) and np.array_equal(ds, d)
+    # sign symmetry
+    hn, qn, dn = oracle.rmsnorm_quant(xb ^ np.uint16(0x8000), None, g, 0.0)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d)
+    # a permutation of the features (with g) permutes the codes
+    p = r.permutation(K)
+    hp, qp, dp = oracle.rmsnorm_quant(xb[:, p], None, g[p], 0.0)
+    assert np.array_equal(qp, q[:, p]) and np.array_equal(dp, d)
+    # a zero residual leaves h = x
+    h0, q0, d0 = oracle.rmsnorm_quant(xb, np.zeros_like(xb), g, 0.0)
+    assert np.array_equal(h0, xb) and np.array_equal(q0, q)
+    # rows whose mean square is a power of 4, g = 1, eps = 0: rinv is a power
+    # of two, so the codes are the plain per-token quantizer's codes
+    ones = bf16_bits(np.ones(4))
+    rows = bf16_bits([[2.0, -2.0, 2.0, 2.0], [0.5, 0.25, -0.5, 0.5], [4.0, 0.0, 0.0, 0.0]])
+    for t in range(3):
+        hx, qx, dx = oracle.rmsnorm_quant(rows[t:t + 1], None, ones, 0.0)
+        qa, _ = oracle.quantize_act_absmax(rows[t:t + 1])
+        msr = _ms_by_mantissas(rows[t])
+        if msr.numerator in (1, 4, 16) and msr.denominator in (1, 4, 16, 64):
+            assert np.array_equal(qx, qa), (t, qx, qa)
+
+
+def pin_norm_error_bound(seed=25):
+    """y within the stated fp32 roundings of the exact x/rms*g, codes within
+    0.5 of y*127/max|y|."""
+    from fractions import Fraction
+    r = _rng(seed)
+    xb = _rand_bf16(r, (4, 64), 2.0)
+    g = _rand_bf16(r, (64,), 1.0)
+    h, q, d, ms = oracle.rmsnorm_quant(xb, None, g, 1e-6, return_ms=True)
+    hx = oracle.widen_bf16(h).astype(np.float64)
+    gx = oracle.widen_bf16(g).astype(np.float64)
+    for t in range(4):
+        y = hx[t] / np.sqrt(float(ms[t]) + 1e-6) * gx
+        m = np.max(np.abs(y))
+        err = np.abs(q[t] - y * 127.0 / m)
+        assert np.all(err <= 0.5 + 127 * 2.0**-20), err.max()
+
+
+# ----------------------------------------------------------------------------
 # absmean gamma and ternarize
 # ----------------------------------------------------------------------------
 
@@ -455,6 +548,7 @@ def pin_bf16_bruteforce(seed=21):
 ALL_PINS = [
     pin_quant_golden, pin_quant_special, pin_quant_invariants, pin_quant_rejects,
     pin_quant_tensor_golden, pin_quant_tensor_reductions,
+    pin_norm_golden, pin_norm_exact_ms, pin_norm_invariants, pin_norm_error_bound,
     pin_ternary_golden, pin_gamma_exact, pin_ternary_roundclip, pin_ternary_invariants,
     pin_ternary_statistics,
     pin_pack_golden, pin_pack_exhaustive, pin_pack_layout,

@@ -6,6 +6,7 @@ import pytest
 import oracle.dequant
 import oracle.dot
 import oracle.i2s
+import oracle.norm
 import oracle.quant
 import oracle.ternary
 import pins
@@ -18,6 +19,12 @@ MUTATIONS = {
     "quant_tensor_first_row_max": (oracle.quant, "_tensor_absmax",
                                    lambda x: np.float32(np.max(np.abs(x[0])))),
     "quant_tensor_signed_max": (oracle.quant, "_tensor_absmax", lambda x: np.float32(np.max(x))),
+    "norm_sum_not_mean": (oracle.norm, "_mean_square", lambda h: oracle.norm._exact_sum_squares(h)),
+    "norm_residual_half_up": (oracle.norm, "_bf16_rne_from_f32",
+                              lambda v: ((np.asarray(v, np.float32).view(np.uint32).astype(np.uint64)
+                                          + 0x8000) >> 16).astype(np.uint16)),
+    "norm_mean_over_k_minus_1": (oracle.norm, "_mean_square",
+                                 lambda h: oracle.norm._exact_sum_squares(h) / (h.shape[0] - 1)),
     "ternary_ge_threshold": (oracle.ternary, "_above", lambda w, t: w >= t),
     "ternary_threshold_0.7": (oracle.ternary, "THRESHOLD_FRACTION", 0.7),
     "ternary_fp32_sum": (oracle.ternary, "_exact_abs_sum",
