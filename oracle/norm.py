@@ -14,6 +14,11 @@ with a per-feature weight, fp32 arithmetic with the roundings named here):
   rinv_t   = fl32(1 / fl32(sqrt(fl32(ms_t + eps))))
   y[t][k]  = fl32(fl32(h[t][k] * rinv_t) * g[k])  (g: bf16 norm weight)
   q, d     = per-token absmax int8 of y (as quantize_act_absmax, on fp32 y)
+
+Degenerate rows (the pages are silent; the limit is taken): when
+fl32(ms + eps) is zero (an all-zero row with eps = 0, or a mean square that
+underflows fp32) the row normalizes to zero, so q = 0 and d = 0. eps must be
+finite and >= 0; a y that overflows fp32 is rejected.
 """
 from __future__ import annotations
 
@@ -85,6 +90,8 @@ def rmsnorm_quant(x_bits, r_bits, g_bits, eps: float, return_ms: bool = False):
     g = widen_bf16(g_bits)
     if not (np.all(np.isfinite(h)) and np.all(np.isfinite(g)) and np.isfinite(eps)):
         raise ValueError("non-finite input")
+    if eps < 0:
+        raise ValueError("eps must be >= 0")
     eps32 = np.float32(eps)
     q = np.zeros((M, K), dtype=np.int8)
     d = np.zeros(M, dtype=np.float32)
@@ -94,10 +101,12 @@ def rmsnorm_quant(x_bits, r_bits, g_bits, eps: float, return_ms: bool = False):
         mss.append(msf)
         ms = round_fraction_to_f32(msf)
         v = np.float32(ms + eps32)
-        if not v > 0:
-            raise ValueError("ms + eps must be positive")
+        if v == 0:
+            continue                                            # the row normalizes to zero
         rinv = np.float32(np.float32(1) / np.sqrt(v))           # fp32 sqrt, fp32 divide
         y = ((h[t] * rinv).astype(np.float32) * g).astype(np.float32)
+        if not np.all(np.isfinite(y)):
+            raise ValueError("normalized value overflows fp32")
         m = np.float32(np.max(np.abs(y))) if K else np.float32(0)
         if m == 0:
             continue

@@ -174,6 +174,26 @@ def pin_norm_golden():
         assert int(d.view(np.uint32)[0]) == c["d_bits"], (c["derivation"], d)
 
 
+def pin_norm_zero_rows():
+    """A zero row gives q = 0, d = 0 with or without eps; so does a row whose
+    residual cancels x exactly; negative eps is rejected."""
+    g = bf16_bits([1.0, 2.0, 0.5, 1.0])
+    x = bf16_bits([[0.0, 0.0, 0.0, 0.0], [1.5, -2.0, 0.25, 3.0], [1.0, 1.0, 1.0, 1.0]])
+    r = bf16_bits([[0.0, 0.0, 0.0, 0.0], [-1.5, 2.0, -0.25, -3.0], [0.0, 0.0, 0.0, 0.0]])
+    for eps in (0.0, 1e-6):
+        h, q, d = oracle.rmsnorm_quant(x, r, g, eps)
+        assert not q[:2].any() and not d[:2].any()
+        assert (h[1] & 0x7FFF == 0).all()
+        if eps == 0.0:
+            assert q[2].tolist() == [64, 127, 32, 64]    # y = [1, 2, 0.5, 1], ties to even
+    try:
+        oracle.rmsnorm_quant(x, r, g, -1e-6)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("negative eps accepted")
+
+
 def _ms_by_mantissas(hb):
     """sum h^2 / K from integer significands and exponents (exact rational)."""
     from fractions import Fraction
@@ -548,7 +568,7 @@ def pin_bf16_bruteforce(seed=21):
 ALL_PINS = [
     pin_quant_golden, pin_quant_special, pin_quant_invariants, pin_quant_rejects,
     pin_quant_tensor_golden, pin_quant_tensor_reductions,
-    pin_norm_golden, pin_norm_exact_ms, pin_norm_invariants, pin_norm_error_bound,
+    pin_norm_golden, pin_norm_zero_rows, pin_norm_exact_ms, pin_norm_invariants, pin_norm_error_bound,
     pin_ternary_golden, pin_gamma_exact, pin_ternary_roundclip, pin_ternary_invariants,
     pin_ternary_statistics,
     pin_pack_golden, pin_pack_exhaustive, pin_pack_layout,
