@@ -185,6 +185,52 @@ def decode_more(torch, bl, W, dev, stream):
     return out
 
 
+def norm_bench(torch, bl, W, dev, stream):
+    """Fused residual add + RMSNorm + per-token quantize (bl_rmsnorm_quant)
+    on the prefill and decode shapes, against the same step done unfused
+    (torch bf16 add, torch rms_norm, bl_quantize_act). Each figure is a graph
+    replay over R copies of the buffers (about 600 MB in all, so the data come
+    from HBM). Algorithmic bytes per token: x, r and h (2K each) plus q (K)
+    plus d (4); g once (2K)."""
+    out = {}
+    for name, cid, M in (("100b-prefill-2048", 5, 2048), ("2b-prefill-512", 3, 512),
+                         ("100b-decode-1", 5, 1), ("2b-decode-1", 3, 1)):
+        cfg = W.CONFIGS[cid]
+        K = cfg.projs[0].K
+        xb, rb, gb = W.norm_inputs(4242 + cid, M, K, cfg.outlier_frac, cfg.outlier_scale)
+        t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        g = t(gb)
+        nbytes = M * (7 * K + 4) + 2 * K
+        R = max(1, min(64, -(-600_000_000 // nbytes)))
+        bufs = [dict(x=t(xb), r=t(rb), h=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                     q=torch.empty((M, K), dtype=torch.int8, device=dev),
+                     d=torch.empty((M,), dtype=torch.float32, device=dev)) for _ in range(R)]
+
+        def fused(b):
+            return lambda: bl.rmsnorm_quant(b["x"], g, 1e-5, residual=b["r"], h_out=b["h"],
+                                            q=b["q"], d=b["d"])
+
+        def unfused(b):
+            def f():
+                hh = b["x"] + b["r"]
+                y = torch.nn.functional.rms_norm(hh, (K,), weight=g, eps=1e-5)
+                bl.quantize_act(y, b["q"], b["d"])
+            return f
+
+        gr = capture_fns(torch, stream, [fused(b) for b in bufs])
+        us = replay_us(torch, stream, gr, R)
+        del gr
+        gr = capture_fns(torch, stream, [unfused(b) for b in bufs])
+        us_unf = replay_us(torch, stream, gr, R)
+        del gr, bufs
+        torch.cuda.empty_cache()
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"M": M, "K": K, "us": round(us, 3), "gbs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes,
+                     "unfused_us": round(us_unf, 3), "copies": R}
+    return out
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -268,6 +314,16 @@ def main():
         for r in range(R):                    # each launch reads weights no earlier launch read
             step(r)
         torch.cuda.synchronize()
+        if not args.no_extras:                # 4 fused norm launches, 100B prefill shape
+            cfg5 = W.CONFIGS[5]
+            K5 = cfg5.projs[0].K
+            xb, rb, gb = W.norm_inputs(4247, 2048, K5, cfg5.outlier_frac, cfg5.outlier_scale)
+            t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            gn = t(gb)
+            for _ in range(4):
+                xn, rn = t(xb), t(rb)
+                bl.rmsnorm_quant(xn, gn, 1e-5, residual=rn, h_out=rn)
+            torch.cuda.synchronize()
         log(f"traffic mode: 1 calibration kernel over {src.numel()} B, {R * len(GROUPS)} decode launches "
             f"({step_bytes // len(GROUPS)} packed bytes per launch on average)")
         return
@@ -532,6 +588,11 @@ def main():
                                                     "per_tensor": round(us_q_ten, 1)}}
         del G
         torch.cuda.empty_cache()
+
+    # ------------------------------------- residual add + RMSNorm + quantize
+    if not args.no_extras:
+        result["rmsnorm_quant"] = norm_bench(torch, bl, W, dev, stream)
+        log(f"rmsnorm_quant: {result['rmsnorm_quant']}")
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:

@@ -18,6 +18,9 @@
  *   [HB]  bitnet.cpp how-to blog: 1.1 (decode streams every weight once per
  *         token, so it is memory-bandwidth bound), 1.2 (ternary weights turn
  *         multiply-adds into adds and subtracts).
+ *   [BE]  "BinaryAI Engine：从零构建的CPU推理引擎如何超越llama.cpp":
+ *         "关键技术机制解析" §2 (residual add and RMSNorm fused, halving the
+ *         memory passes of a layer).
  *
  * Conventions (all calls):
  *   - Every array argument is a DEVICE pointer owned by the caller. The
@@ -68,7 +71,8 @@ enum {
   BL_ERR_ALIGN = -3,     /* a pointer or stride breaks the alignment rules    */
   BL_ERR_DTYPE = -4,     /* unknown weight or output type enum                */
   BL_ERR_WORKSPACE = -5, /* workspace missing or smaller than required        */
-  BL_ERR_HIP = -6        /* the HIP runtime refused a launch                  */
+  BL_ERR_HIP = -6,       /* the HIP runtime refused a launch                  */
+  BL_ERR_ALIAS = -7      /* an output overlaps an input it may not share      */
 };
 
 /* Weight input type of bl_pack_i2s. */
@@ -127,6 +131,35 @@ size_t bl_quantize_act_tensor_workspace(int64_t M);
  */
 int bl_quantize_act_tensor(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                            int8_t *q, float *d, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * bl_rmsnorm_quant -- residual add + RMSNorm fused with the per-token absmax
+ * int8 quantizer, one pass over the activations.
+ * Defines: [BE] "关键技术机制解析" §2 (residual add and RMS normalization
+ * fused in one pass) feeding [BN] Part A 2.3 / 4.1 (per-token absmax int8).
+ * The pages give no normalization formula; plain RMSNorm with a per-feature
+ * weight is taken. Per token t:
+ *   h[t][k] = bf16_rne(fl32(x[t][k] + r[t][k]))    (h = x when r is NULL)
+ *   ms_t    = fl32(sum_k h[t][k]^2 / K)
+ *   rinv_t  = fl32(1 / fl32(sqrt(fl32(ms_t + eps))))
+ *   y[t][k] = fl32(fl32(h[t][k] * rinv_t) * g[k])
+ *   then q, d of y exactly as bl_quantize_act (m = max|y|, s = fl32(127/m),
+ *   q = rne(fl32(y*s)), d = fl32(m/127)); q = 0 and d[t] = 0 when m = 0 or
+ *   fl32(ms_t + eps) = 0.
+ * The sum of squares runs in fp64 (each square exact): ms_t is the correctly
+ * rounded value unless the exact mean square lies within ~2^-40 (relative) of
+ * a midpoint between two fp32 numbers, where either neighbour may result.
+ * x, r: bf16 [M][K] row stride ldx (r may be NULL); g: bf16 [K];
+ * h_out: bf16 [M][K] row stride ldx, or NULL (not written); it may be r or x
+ * itself (in-place update of the residual stream) but must not otherwise
+ * overlap them; q: int8 [M][K] (row stride K); d: fp32 [M]. eps: finite,
+ * >= 0. Inputs must be finite, and neither ms_t nor y may overflow fp32
+ * (|h| below about 1.8e19; codes are unspecified otherwise). K % 4 == 0, ldx >= K, ldx % 4 == 0; x, r, g, h_out
+ * and q 16-byte aligned. K == 0: d[:] = 0. One launch.
+ */
+int bl_rmsnorm_quant(const uint16_t *x, const uint16_t *r, const uint16_t *g, float eps,
+                     int64_t M, int64_t K, int64_t ldx, uint16_t *h_out, int8_t *q,
+                     float *d, void *stream);
 
 /*
  * bl_pack_i2s_workspace -- bytes of workspace bl_pack_i2s needs for an

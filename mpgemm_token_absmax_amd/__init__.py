@@ -8,6 +8,7 @@ and streams only.
 
     q, d        = quantize_act(x_bf16)              # per-token absmax int8
     q, d        = quantize_act_tensor(x_bf16)       # one absmax scale for all tokens
+    h, q, d     = rmsnorm_quant(x, g, eps, residual=r)  # fused add + RMSNorm + quantize
     packed, g   = pack_i2s(w_fp32)                  # absmean ternary -> 2-bit I2_S
     packed      = pack_i2s(w_ternary_int8)          # pack only (caller keeps gamma)
     y           = gemv(packed, g, q, d)             # M <= 16 tokens
@@ -24,7 +25,7 @@ import torch
 from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I8, MAX_GROUP,
                    BitLinearError, DecodeProblem, GemmProblem, check, lib, status_string)
 
-__all__ = ["quantize_act", "quantize_act_tensor", "pack_i2s", "pack_i2s_workspace", "gemv", "gemm",
+__all__ = ["quantize_act", "quantize_act_tensor", "rmsnorm_quant", "pack_i2s", "pack_i2s_workspace", "gemv", "gemm",
            "gemm_workspace", "gemm_group", "GemmGroup", "decode_group", "DecodeGroup",
            "BitLinearError", "status_string",
            "lib", "OUT_TYPES"]
@@ -84,6 +85,41 @@ def quantize_act_tensor(x: torch.Tensor, q: torch.Tensor | None = None,
           lib().bl_quantize_act_tensor(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d),
                                        _ptr(workspace), workspace.numel(), _stream(x.device)))
     return q, d
+
+
+def rmsnorm_quant(x: torch.Tensor, g: torch.Tensor, eps: float, residual: torch.Tensor | None = None,
+                  h_out: torch.Tensor | None = None, q: torch.Tensor | None = None,
+                  d: torch.Tensor | None = None, write_h: bool = True):
+    """Residual add + RMSNorm + per-token absmax int8 in one kernel.
+
+    x, residual: bf16 [M][K] with the same row stride; g: bf16 [K]. Returns
+    (h, q, d): h = bf16(x + residual) (x itself without a residual; None when
+    write_h is False and no h_out is given), q int8 [M][K], d fp32 [M].
+    h_out may be residual itself (in-place update of the residual stream).
+    """
+    _need(x, "x", torch.bfloat16, 2)
+    _need(g, "g", torch.bfloat16, 1)
+    if x.stride(1) != 1 or g.stride(0) != 1:
+        raise ValueError("x rows and g must be contiguous")
+    M, K = x.shape
+    if g.shape[0] != K:
+        raise ValueError("g must have K entries")
+    for t, name in ((residual, "residual"), (h_out, "h_out")):
+        if t is not None:
+            _need(t, name, torch.bfloat16, 2)
+            if tuple(t.shape) != (M, K) or t.stride() != x.stride():
+                raise ValueError(f"{name} must match x's shape and strides")
+    if h_out is None and write_h and residual is not None:     # x's row stride
+        h_out = torch.empty_strided((M, K), x.stride(), dtype=torch.bfloat16, device=x.device)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((M,), dtype=torch.float32, device=x.device)
+    check("bl_rmsnorm_quant",
+          lib().bl_rmsnorm_quant(_ptr(x), _ptr(residual), _ptr(g), float(eps), M, K, x.stride(0),
+                                 _ptr(h_out), _ptr(q), _ptr(d), _stream(x.device)))
+    h = h_out if h_out is not None else (x if residual is None and write_h else None)
+    return h, q, d
 
 
 def pack_i2s_workspace(N: int, K: int) -> int:

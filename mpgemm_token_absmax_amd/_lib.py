@@ -19,6 +19,7 @@ BL_ERR_ALIGN = -3
 BL_ERR_DTYPE = -4
 BL_ERR_WORKSPACE = -5
 BL_ERR_HIP = -6
+BL_ERR_ALIAS = -7
 
 BL_W_F32 = 0
 BL_W_TERNARY_I8 = 1
@@ -28,7 +29,8 @@ BL_OUT_F32 = 1
 BL_OUT_BF16 = 2
 
 EXPORTS = ("bl_abi_version", "bl_status_string", "bl_quantize_act",
-           "bl_quantize_act_tensor_workspace", "bl_quantize_act_tensor", "bl_pack_i2s_workspace",
+           "bl_quantize_act_tensor_workspace", "bl_quantize_act_tensor", "bl_rmsnorm_quant",
+           "bl_pack_i2s_workspace",
            "bl_pack_i2s", "bl_gemv", "bl_gemm_workspace", "bl_gemm", "bl_gemm_group",
            "bl_decode_group")
 
@@ -76,6 +78,8 @@ def _declare(lib):
     lib.bl_quantize_act_tensor.restype = INT
     lib.bl_quantize_act_tensor.argtypes = [P, I64, I64, I64, P, P, P, SZ, P]
     lib.bl_pack_i2s_workspace.argtypes = [I64, I64]
+    lib.bl_rmsnorm_quant.restype = INT
+    lib.bl_rmsnorm_quant.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P, P, P]
     lib.bl_pack_i2s.restype = INT
     lib.bl_pack_i2s.argtypes = [P, INT, I64, I64, P, P, P, SZ, P]
     lib.bl_gemv.restype = INT

@@ -50,6 +50,7 @@ const char* bl_status_string(int status) {
     case BL_ERR_DTYPE: return "unknown weight or output type";
     case BL_ERR_WORKSPACE: return "workspace missing or too small";
     case BL_ERR_HIP: return "HIP runtime error while launching";
+    case BL_ERR_ALIAS: return "an output overlaps an input it may not share";
     default: return "unknown status";
   }
 }
@@ -84,6 +85,37 @@ int bl_quantize_act_tensor(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
   if (K > 0 && !aligned(ws, 16)) return BL_ERR_ALIGN;
   return hip_status(bl::launch_quantize_act_tensor(x, M, K, ldx, q, d,
                                                    static_cast<uint32_t*>(ws), as_stream(stream)));
+}
+
+namespace {
+
+// Byte range [p, p + rows*ld + K) * 2 of a bf16 [rows][K] array of row stride ld.
+bool overlap_bf16(const uint16_t* a, const uint16_t* b, int64_t M, int64_t K, int64_t ld) {
+  const uintptr_t n = (uintptr_t)(((M - 1) * ld + K) * 2);
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + n && pb < pa + n;
+}
+
+}  // namespace
+
+int bl_rmsnorm_quant(const uint16_t* x, const uint16_t* r, const uint16_t* g, float eps,
+                     int64_t M, int64_t K, int64_t ldx, uint16_t* h_out, int8_t* q, float* d,
+                     void* stream) {
+  if (M < 0 || K < 0 || K % 4 != 0 || ldx < K) return BL_ERR_SHAPE;
+  if (!(eps >= 0.0f) || eps > 3.4028235e38f) return BL_ERR_SHAPE;     // NaN, inf, < 0
+  if (M == 0) return BL_OK;
+  if (!d || (K > 0 && (!x || !g || !q))) return BL_ERR_NULL;
+  if (M > INT32_MAX) return BL_ERR_SHAPE;
+  if (!aligned(d, 4)) return BL_ERR_ALIGN;
+  if (K > 0) {
+    if (ldx % 4 != 0) return BL_ERR_ALIGN;
+    if (!aligned(x, 16) || !aligned(g, 16) || !aligned(q, 16)) return BL_ERR_ALIGN;
+    if ((r && !aligned(r, 16)) || (h_out && !aligned(h_out, 16))) return BL_ERR_ALIGN;
+    if (h_out && h_out != x && overlap_bf16(h_out, x, M, K, ldx)) return BL_ERR_ALIAS;
+    if (h_out && r && h_out != r && overlap_bf16(h_out, r, M, K, ldx)) return BL_ERR_ALIAS;
+  }
+  return hip_status(bl::launch_rmsnorm_quant(x, r, g, eps, M, K, ldx, h_out, q, d,
+                                             as_stream(stream)));
 }
 
 size_t bl_pack_i2s_workspace(int64_t N, int64_t K) {

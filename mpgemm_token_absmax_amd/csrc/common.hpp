@@ -125,6 +125,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)max(max(r0, r1), max(r2, r3));
 }
 
+// Max over a block of kThreads threads (every thread gets it); red: one word
+// per wave in LDS.
+template <int kThreads>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
+  __syncthreads();
+  uint32_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) m = max(m, red[w]);
+  return m;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));

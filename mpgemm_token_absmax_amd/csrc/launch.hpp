@@ -49,6 +49,13 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
 hipError_t launch_quantize_act_tensor(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                       int8_t* q, float* d, uint32_t* maxb, hipStream_t s);
 
+// Residual add + RMSNorm + per-token absmax int8 (r and h_out may be NULL;
+// h_out may be x or r itself). x, r, h_out share the row stride ldx.
+constexpr int64_t kRmsNormFastMaxK = 32768;
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* r, const uint16_t* g,
+                                float eps, int64_t M, int64_t K, int64_t ldx, uint16_t* h_out,
+                                int8_t* q, float* d, hipStream_t s);
+
 size_t pack_workspace_bytes(int64_t N, int64_t K);
 hipError_t launch_pack_f32(const float* w, int64_t N, int64_t K, uint8_t* packed, float* gamma,
                            void* ws, hipStream_t s);

@@ -1,0 +1,308 @@
+// Residual add + RMSNorm fused with the per-token absmax int8 quantizer (gfx950).
+//
+// Source: BinaryAI Engine forum post, "关键技术机制解析" §2 (the residual add and
+// the RMS normalization run as one pass over the activations) feeding the
+// per-token absmax quantizer of the Bitnet.cpp reading notes, Part A 2.3 / 4.1.
+// Per token t (row of x, r):
+//   h  = bf16_rne(fl32(x + r))            (h = x without r; written to h_out)
+//   ms = fl32(sum_k h^2 / K)
+//   rinv = fl32(1 / fl32(sqrt(fl32(ms + eps))))
+//   y  = fl32(fl32(h * rinv) * g)         (g: bf16 norm weight, one per feature)
+//   m = max |y|, s = fl32(127 / m), q = rne(fl32(y * s)), d = fl32(m / 127);
+//   q = 0 and d = 0 when m = 0 or fl32(ms + eps) = 0.
+// Rounding: every h^2 is exact in fp64 and the sum runs in fp64, so ms is the
+// correctly rounded fp32 mean square except when the exact value lies within
+// about (K/256 + 8) * 2^-53 (relative) of a midpoint between two fp32 values.
+// sqrt and 1/x run in fp64 and are rounded once to fp32, which gives the
+// correctly rounded fp32 result (fp64 carries more than 2*24 + 2 bits).
+//
+// One workgroup per token. Fast path (K % 8 == 0, ldx % 8 == 0, K <= 32768):
+// each thread holds NC 16-byte chunks of the row in registers, so x, r and g
+// are read once and h, q written once: 2K + 2K (+ 2K h) + K bytes per token.
+// Other shapes: the generic kernel makes three passes over the row, the later
+// two hitting L2.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bl {
+namespace {
+
+// Sum over a block of kThreads threads. The butterfly gives every lane of a
+// wave the same value (fp addition is commutative), and every thread adds the
+// wave partials in the same order, so the result is uniform.
+template <int kThreads>
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
+  __syncthreads();
+  double s = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) s += red[w];
+  return s;
+}
+
+// Two packed bf16 sums: bf16_rne(fl32(x + r)) per half.
+__device__ __forceinline__ uint32_t add2_bf16(uint32_t x, uint32_t r) {
+  const float lo = __fadd_rn(__uint_as_float(x << 16), __uint_as_float(r << 16));
+  const float hi = __fadd_rn(__uint_as_float(x & 0xFFFF0000u), __uint_as_float(r & 0xFFFF0000u));
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ double sumsq2_bf16(uint32_t w, double acc) {
+  const double lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+  acc += lo * lo;    // exact product; one fp64 rounding per add
+  acc += hi * hi;
+  return acc;
+}
+
+// The mean square of a row from its fp64 sum of squares, and the factor
+// rinv = fl32(1/fl32(sqrt(fl32(ms + eps)))) (0 when ms + eps is 0).
+__device__ __forceinline__ float norm_factor(double sumsq, int64_t K, float eps) {
+  const float ms = (float)(sumsq / (double)K);
+  const float v = __fadd_rn(ms, eps);
+  if (!(v > 0.0f)) return 0.0f;
+  const float root = (float)__dsqrt_rn((double)v);
+  return (float)__ddiv_rn(1.0, (double)root);
+}
+
+__device__ __forceinline__ float norm1(uint32_t h_high, float rinv, uint32_t g_high) {
+  return __fmul_rn(__fmul_rn(__uint_as_float(h_high), rinv), __uint_as_float(g_high));
+}
+
+// int8 code of fp32 y: low byte of fl32(fl32(y*s) + 1.5*2^23); |y| <= m and
+// s = fl32(127/m) keep |fl32(y*s)| < 127.5, so it is rne(y*s) in [-127, 127].
+__device__ __forceinline__ uint32_t qbits_f32(float y, float s) {
+  return __float_as_uint(__fadd_rn(__fmul_rn(y, s), 12582912.0f));
+}
+
+// Four fp32 values -> four int8 codes packed little-endian.
+__device__ __forceinline__ uint32_t quant4_f32(const float* y, float s) {
+  const uint32_t a = __builtin_amdgcn_perm(qbits_f32(y[1], s), qbits_f32(y[0], s), 0x0C0C0400u);
+  const uint32_t b = __builtin_amdgcn_perm(qbits_f32(y[3], s), qbits_f32(y[2], s), 0x0C0C0400u);
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+
+// 16 bytes at a uniform base plus a 32-bit byte offset (one SGPR base and a
+// single VGPR offset per load, instead of a 64-bit address per load).
+__device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off);
+}
+
+// y of the 8 values of a 16-byte chunk (h and g as packed bf16 pairs).
+__device__ __forceinline__ void norm8(uint4 h, uint4 g, float rinv, float* y) {
+  const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    y[2 * j] = norm1(hw[j] << 16, rinv, gw[j] << 16);
+    y[2 * j + 1] = norm1(hw[j] & 0xFFFF0000u, rinv, gw[j] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint32_t absbits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// Fast path. x, r and h_out are not __restrict__: h_out may be r or x itself
+// (every chunk is loaded before the same thread stores it). Registers: the x
+// and r chunks, then h and g; y is recomputed from them for the codes rather
+// than kept, so the kernel stays at 8 waves per SIMD.
+template <int NT, int NC, bool kRes>
+__global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
+    const uint16_t* x, const uint16_t* r, const uint16_t* __restrict__ g, float eps, int64_t K,
+    int64_t ldx, uint16_t* h_out, int8_t* __restrict__ q, float* __restrict__ d) {
+  __shared__ double red_s[NT / kWave];
+  __shared__ uint32_t red_m[NT / kWave];
+  const int64_t t = blockIdx.x;
+  const int nchunk = (int)(K / 8);
+  const uint16_t* xrow = x + t * ldx;
+  const uint16_t* rrow = r + t * ldx;
+  uint32_t off[NC];                         // byte offset of each chunk (clamped)
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const uint32_t c = threadIdx.x + (uint32_t)(i * NT);
+    off[i] = 16u * (c < (uint32_t)nchunk ? c : (uint32_t)nchunk - 1u);
+  }
+  uint4 hv[NC], gv[NC];
+  // Every x and r load issued before any use (a chunk past the row is
+  // ignored below).
+#pragma unroll
+  for (int i = 0; i < NC; ++i) hv[i] = ld16(xrow, off[i]);
+  uint4 rv[kRes ? NC : 1];
+  if constexpr (kRes) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) rv[i] = ld16(rrow, off[i]);
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = (int)threadIdx.x + i * NT;
+    if constexpr (kRes) {
+      hv[i].x = add2_bf16(hv[i].x, rv[i].x);
+      hv[i].y = add2_bf16(hv[i].y, rv[i].y);
+      hv[i].z = add2_bf16(hv[i].z, rv[i].z);
+      hv[i].w = add2_bf16(hv[i].w, rv[i].w);
+    }
+    if (c < nchunk) {
+      ss = sumsq2_bf16(hv[i].x, ss);
+      ss = sumsq2_bf16(hv[i].y, ss);
+      ss = sumsq2_bf16(hv[i].z, ss);
+      ss = sumsq2_bf16(hv[i].w, ss);
+      if (h_out) reinterpret_cast<uint4*>(h_out + t * ldx)[c] = hv[i];
+    }
+  }
+  // g (the same for every token, an L2 hit) is in flight during the sum.
+#pragma unroll
+  for (int i = 0; i < NC; ++i) gv[i] = ld16(g, off[i]);
+  const float rinv = norm_factor(block_sum_f64<NT>(ss, red_s), K, eps);
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    float y[8];
+    norm8(hv[i], gv[i], rinv, y);
+    uint32_t m8 = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m8 = max(m8, absbits(y[j]));
+    const int c = (int)threadIdx.x + i * NT;
+    mb = max(mb, c < nchunk ? m8 : 0u);
+  }
+  mb = block_max_u32<NT>(mb, red_m);
+  const float m = __uint_as_float(mb);
+  const float s = mb ? 127.0f / m : 0.0f;
+  uint2* qr = reinterpret_cast<uint2*>(q + t * K);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = (int)threadIdx.x + i * NT;
+    if (c < nchunk) {
+      float y[8];
+      norm8(hv[i], gv[i], rinv, y);
+      qr[c] = mb ? make_uint2(quant4_f32(&y[0], s), quant4_f32(&y[4], s)) : make_uint2(0u, 0u);
+    }
+  }
+  if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
+}
+
+// Generic path (K % 4 == 0, ldx % 4 == 0): three passes of 4 values per chunk.
+// Passes 2 and 3 read h back from h_out when it is given (h_out may be x or r),
+// else recompute it from x and r.
+constexpr int kGenThreads = 256;
+
+__device__ __forceinline__ uint2 load_h4(const uint2* xr, const uint2* rr, int64_t c) {
+  uint2 v = xr[c];
+  if (rr) {
+    const uint2 w = rr[c];
+    v = make_uint2(add2_bf16(v.x, w.x), add2_bf16(v.y, w.y));
+  }
+  return v;
+}
+
+__device__ __forceinline__ void norm4(uint2 h, uint2 gw, float rinv, float* y) {
+  y[0] = norm1(h.x << 16, rinv, gw.x << 16);
+  y[1] = norm1(h.x & 0xFFFF0000u, rinv, gw.x & 0xFFFF0000u);
+  y[2] = norm1(h.y << 16, rinv, gw.y << 16);
+  y[3] = norm1(h.y & 0xFFFF0000u, rinv, gw.y & 0xFFFF0000u);
+}
+
+__global__ __launch_bounds__(kGenThreads) void k_rmsnorm_quant_any(
+    const uint16_t* x, const uint16_t* r, const uint16_t* __restrict__ g, float eps, int64_t K,
+    int64_t ldx, uint16_t* h_out, int8_t* __restrict__ q, float* __restrict__ d) {
+  __shared__ double red_s[kGenThreads / kWave];
+  __shared__ uint32_t red_m[kGenThreads / kWave];
+  const int64_t t = blockIdx.x;
+  const int64_t nchunk = K / 4;
+  const uint2* xr = reinterpret_cast<const uint2*>(x + t * ldx);
+  const uint2* rr = r ? reinterpret_cast<const uint2*>(r + t * ldx) : nullptr;
+  uint2* hr = h_out ? reinterpret_cast<uint2*>(h_out + t * ldx) : nullptr;
+  const uint2* gr = reinterpret_cast<const uint2*>(g);
+  double ss = 0.0;
+  for (int64_t c = threadIdx.x; c < nchunk; c += kGenThreads) {
+    const uint2 h = load_h4(xr, rr, c);
+    ss = sumsq2_bf16(h.y, sumsq2_bf16(h.x, ss));
+    if (hr) hr[c] = h;
+  }
+  const float rinv = norm_factor(block_sum_f64<kGenThreads>(ss, red_s), K, eps);
+  uint32_t mb = 0;
+  for (int64_t c = threadIdx.x; c < nchunk; c += kGenThreads) {
+    float y[4];
+    norm4(hr ? hr[c] : load_h4(xr, rr, c), gr[c], rinv, y);
+    mb = max(max(mb, max(absbits(y[0]), absbits(y[1]))), max(absbits(y[2]), absbits(y[3])));
+  }
+  mb = block_max_u32<kGenThreads>(mb, red_m);
+  const float m = __uint_as_float(mb);
+  const float s = mb ? 127.0f / m : 0.0f;
+  uint32_t* qr = reinterpret_cast<uint32_t*>(q + t * K);
+  for (int64_t c = threadIdx.x; c < nchunk; c += kGenThreads) {
+    float y[4];
+    norm4(hr ? hr[c] : load_h4(xr, rr, c), gr[c], rinv, y);
+    qr[c] = mb ? quant4_f32(y, s) : 0u;
+  }
+  if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
+}
+
+__global__ void k_zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+template <int NT, int NC>
+hipError_t launch16(const uint16_t* x, const uint16_t* r, const uint16_t* g, float eps, int64_t M,
+                    int64_t K, int64_t ldx, uint16_t* h_out, int8_t* q, float* d, hipStream_t s) {
+  if (r)
+    hipLaunchKernelGGL((k_rmsnorm_quant16<NT, NC, true>), dim3((unsigned)M), dim3(NT), 0, s, x, r,
+                       g, eps, K, ldx, h_out, q, d);
+  else
+    hipLaunchKernelGGL((k_rmsnorm_quant16<NT, NC, false>), dim3((unsigned)M), dim3(NT), 0, s, x,
+                       r, g, eps, K, ldx, h_out, q, d);
+  return hipGetLastError();
+}
+
+// Fast-path shape: NT threads, NC 16-byte chunks per thread (0 if generic).
+int rmsnorm_quant_config(int64_t K, int64_t ldx, int* threads, int* chunks) {
+  if (K <= 0 || K % 8 != 0 || ldx % 8 != 0 || K > kRmsNormFastMaxK) {
+    *threads = kGenThreads;
+    *chunks = 0;
+    return 0;
+  }
+  const int64_t nchunk = K / 8;
+  if (nchunk <= 4 * 256) {
+    *threads = 256;
+    *chunks = (int)((nchunk + 255) / 256);
+  } else {
+    *threads = 1024;
+    *chunks = (int)((nchunk + 1023) / 1024);
+  }
+  return 1;
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* r, const uint16_t* g,
+                                float eps, int64_t M, int64_t K, int64_t ldx, uint16_t* h_out,
+                                int8_t* q, float* d, hipStream_t s) {
+  if (K == 0) {
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, d, M);
+    return hipGetLastError();
+  }
+  int nt = 0, nc = 0;
+  if (rmsnorm_quant_config(K, ldx, &nt, &nc)) {
+    if (nt == 256) {
+      switch (nc) {
+        case 1: return launch16<256, 1>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+        case 2: return launch16<256, 2>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+        case 3: return launch16<256, 3>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+        default: return launch16<256, 4>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+      }
+    }
+    switch (nc) {
+      case 1: return launch16<1024, 1>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+      case 2: return launch16<1024, 2>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+      case 3: return launch16<1024, 3>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+      default: return launch16<1024, 4>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+    }
+  }
+  hipLaunchKernelGGL(k_rmsnorm_quant_any, dim3((unsigned)M), dim3(kGenThreads), 0, s, x, r, g, eps,
+                     K, ldx, h_out, q, d);
+  return hipGetLastError();
+}
+
+}  // namespace bl

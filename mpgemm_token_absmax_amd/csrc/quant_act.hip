@@ -20,18 +20,6 @@ namespace {
 
 constexpr int kQThreads = 256;
 
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
-  const int wid = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
-  __syncthreads();
-  uint32_t m = red[0];
-#pragma unroll
-  for (int w = 1; w < kQThreads / kWave; ++w) m = max(m, red[w]);
-  return m;
-}
-
 // NC > 0: row cached in registers (K <= 1024*NC). NC == 0: two passes over x.
 template <int NC>
 __global__ __launch_bounds__(kQThreads) void k_quant_absmax(
@@ -51,7 +39,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_absmax(
       v[i] = c < nchunk ? xr[c] : make_uint2(0u, 0u);
       mb = max(mb, absmax4_bf16(v[i]));
     }
-    mb = block_max_u32(mb, red);
+    mb = block_max_u32<kQThreads>(mb, red);
     const float m = __uint_as_float(mb << 16);
     const float s = mb ? 127.0f / m : 0.0f;
 #pragma unroll
@@ -62,7 +50,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_absmax(
     if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
   } else {
     for (int64_t c = threadIdx.x; c < nchunk; c += kQThreads) mb = max(mb, absmax4_bf16(xr[c]));
-    mb = block_max_u32(mb, red);
+    mb = block_max_u32<kQThreads>(mb, red);
     const float m = __uint_as_float(mb << 16);
     const float s = mb ? 127.0f / m : 0.0f;
     for (int64_t c = threadIdx.x; c < nchunk; c += kQThreads) qr[c] = mb ? quant4_bf16(xr[c], s) : 0u;
@@ -99,7 +87,7 @@ __device__ __forceinline__ void quant_row16(const uint16_t* __restrict__ xrow, i
                               absmax4_bf16(make_uint2(v[i].z, v[i].w)));
       mb = max(mb, c < nchunk ? m8 : 0u);
     }
-    mb = block_max_u32(mb, red);
+    mb = block_max_u32<kQThreads>(mb, red);
   }
   const float m = __uint_as_float(mb << 16);
   const float s = mb ? 127.0f / m : 0.0f;
@@ -144,7 +132,7 @@ __global__ __launch_bounds__(kQThreads) void k_row_absmax(const uint16_t* __rest
   const uint2* xr = reinterpret_cast<const uint2*>(x + t * ldx);
   uint32_t mb = 0;
   for (int64_t c = threadIdx.x; c < K / 4; c += kQThreads) mb = max(mb, absmax4_bf16(xr[c]));
-  mb = block_max_u32(mb, red);
+  mb = block_max_u32<kQThreads>(mb, red);
   if (threadIdx.x == 0) maxb[t] = mb;
 }
 
@@ -153,7 +141,7 @@ __device__ __forceinline__ uint32_t tensor_absmax(const uint32_t* __restrict__ m
                                                   uint32_t* red) {
   uint32_t mb = 0;
   for (int64_t i = threadIdx.x; i < M; i += kQThreads) mb = max(mb, maxb[i]);
-  return block_max_u32(mb, red);
+  return block_max_u32<kQThreads>(mb, red);
 }
 
 template <int NC>

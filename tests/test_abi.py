@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert lib.bl_abi_version() == 1
     for s in (L.BL_OK, L.BL_ERR_NULL, L.BL_ERR_SHAPE, L.BL_ERR_ALIGN, L.BL_ERR_DTYPE,
-              L.BL_ERR_WORKSPACE, L.BL_ERR_HIP):
+              L.BL_ERR_WORKSPACE, L.BL_ERR_HIP, L.BL_ERR_ALIAS):
         assert lib.bl_status_string(s)
     assert lib.bl_status_string(12345) == b"unknown status"
 
@@ -225,3 +225,40 @@ def test_quantize_tensor_validation(lib):
     assert f(A16 + 8, 2, 8, 8, B16, C16, D16, ws, None) == L.BL_ERR_ALIGN
     assert f(A16, 2, 8, 10, B16, C16, D16, ws, None) == L.BL_ERR_ALIGN     # ldx % 4
     assert f(None, 0, 8, 8, None, None, None, 0, None) == L.BL_OK            # M == 0
+
+
+def test_rmsnorm_quant_validation(lib):
+    f = lib.bl_rmsnorm_quant
+    F16 = 0x60000
+    # (x, r, g, eps, M, K, ldx, h_out, q, d)
+    ok = (A16, B16, C16, 1e-5, 2, 8, 8, E16, F16, D16)
+
+    def call(**kw):
+        names = ("x", "r", "g", "eps", "M", "K", "ldx", "h", "q", "d")
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return f(*(a[n] for n in names), None)
+
+    assert call(K=6, ldx=6) == L.BL_ERR_SHAPE                 # K % 4
+    assert call(ldx=4) == L.BL_ERR_SHAPE                      # ldx < K
+    assert call(M=-1) == L.BL_ERR_SHAPE
+    assert call(eps=-1e-6) == L.BL_ERR_SHAPE
+    assert call(eps=float("nan")) == L.BL_ERR_SHAPE
+    assert call(eps=float("inf")) == L.BL_ERR_SHAPE
+    assert call(x=None) == L.BL_ERR_NULL
+    assert call(g=None) == L.BL_ERR_NULL
+    assert call(q=None) == L.BL_ERR_NULL
+    assert call(d=None) == L.BL_ERR_NULL
+    assert call(x=A16 + 8) == L.BL_ERR_ALIGN
+    assert call(r=B16 + 8) == L.BL_ERR_ALIGN
+    assert call(g=C16 + 8) == L.BL_ERR_ALIGN
+    assert call(h=E16 + 8) == L.BL_ERR_ALIGN
+    assert call(q=F16 + 4) == L.BL_ERR_ALIGN
+    assert call(d=D16 + 2) == L.BL_ERR_ALIGN
+    assert call(ldx=10) == L.BL_ERR_ALIGN                     # ldx % 4
+    # h_out may be x or r exactly, but must not partly overlap either
+    assert call(h=A16 + 16) == L.BL_ERR_ALIAS
+    assert call(h=B16 + 16) == L.BL_ERR_ALIAS
+    assert call(h=B16 - 16) == L.BL_ERR_ALIAS
+    assert call(M=0, x=None, g=None, q=None, d=None) == L.BL_OK
+    assert lib.bl_status_string(L.BL_ERR_ALIAS)

@@ -224,6 +224,164 @@ def test_quantize_empty():
 
 
 # ---------------------------------------------------------------------------
+# residual add + RMSNorm + quantize
+# ---------------------------------------------------------------------------
+
+MS_AMBIGUOUS_REL = 2.0 ** -40    # the kernel's fp64 sum of squares is this close
+
+
+def _near_f32_midpoint(ms):
+    """True where the exact mean square lies within MS_AMBIGUOUS_REL of a
+    midpoint between two fp32 values (either rounding of it is correct for
+    the kernel's fp64 sum; everything downstream then follows that choice)."""
+    from fractions import Fraction
+    out = []
+    for v in ms:
+        if v == 0:
+            out.append(False)
+            continue
+        f = oracle.round_fraction_to_f32(v)
+        lo, hi = np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(np.inf))
+        mids = ((Fraction(float(lo)) + Fraction(float(f))) / 2,
+                (Fraction(float(f)) + Fraction(float(hi))) / 2)
+        out.append(min(abs(v - m) for m in mids) <= v * Fraction(MS_AMBIGUOUS_REL))
+    return np.array(out, dtype=bool)
+
+
+def check_norm(x, r, g, eps, h, q, d, rows=None):
+    """GPU h, q, d (full [M] arrays) against the oracle on `rows` (all by
+    default): h bit-exact; q and d bit-exact except on tokens whose mean
+    square sits on an fp32 rounding midpoint, where q is within 1 and d
+    within 2^-22 relative. Returns the number of such tokens."""
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    h_ref, q_ref, d_ref, ms = oracle.rmsnorm_quant(x[rows], None if r is None else r[rows], g,
+                                                   eps, return_ms=True)
+    if h is not None:
+        assert np.array_equal(h[rows], h_ref), "h differs"
+    amb = _near_f32_midpoint(ms)
+    ok = ~amb
+    assert np.array_equal(q[rows][ok], q_ref[ok]), "codes differ"
+    assert np.array_equal(d[rows][ok].view(np.uint32), d_ref[ok].view(np.uint32)), "scales differ"
+    if amb.any():
+        dq = np.abs(q[rows][amb].astype(np.int32) - q_ref[amb].astype(np.int32))
+        assert dq.max() <= 1
+        rel = np.abs(d[rows][amb].astype(np.float64) - d_ref[amb]) / np.maximum(d_ref[amb], 1e-38)
+        assert rel.max() <= 2.0 ** -22
+    return int(amb.sum())
+
+
+# (M, K, ldx, residual, h mode, eps): h mode "new" (a fresh h_out), "none"
+# (no h_out), "in_r" (h_out is r), "in_x" (h_out is x). K % 8 == 0 with
+# ldx % 8 == 0 and K <= 32768 takes the register-row kernel (256 threads up to
+# K = 8192, 1024 above); the rest the generic three-pass kernel.
+NORM_CASES = [
+    (1, 2560, 2560, True, "new", 1e-5), (5, 2560, 2560, True, "in_r", 1e-5),
+    (3, 4096, 4096, False, "none", 1e-6), (2, 6912, 6912, True, "new", 1e-5),
+    (2, 8192, 8192, True, "in_x", 1e-5), (3, 11008, 11008, True, "new", 1e-6),
+    (2, 28672, 28672, False, "none", 1e-5), (1, 32768, 32768, True, "new", 0.0),
+    (7, 40, 40, True, "new", 1e-5), (3, 8, 8, False, "none", 1e-5),
+    (2, 2560, 2568, True, "new", 1e-5), (64, 1024, 1024, True, "new", 1e-5),
+    (4, 36, 36, True, "new", 1e-5), (3, 2564, 2568, True, "in_r", 1e-5),
+    (2, 2560, 2564, False, "none", 1e-5), (2, 32776, 32776, True, "new", 1e-5),
+    (1, 4, 4, False, "none", 1e-5), (2, 40000, 40004, True, "in_r", 1e-6),
+]
+
+
+def _norm_run(bl, x, r, g, eps, ldx, mode):
+    M, K = x.shape
+    def padded(a):
+        wide = np.zeros((M, ldx), np.uint16)
+        wide[:, :K] = a
+        return dev_bf16(wide)[:, :K]
+    xd = padded(x)
+    rd = None if r is None else padded(r)
+    gd = dev_bf16(g)
+    h_out = {"new": None, "none": None, "in_r": rd, "in_x": xd}[mode]
+    h, q, d = bl.rmsnorm_quant(xd, gd, eps, residual=rd, h_out=h_out, write_h=mode != "none")
+    torch.cuda.synchronize()
+    return (None if h is None else host(h)), host(q), host(d)
+
+
+@pytest.mark.parametrize("M,K,ldx,res,mode,eps", NORM_CASES,
+                         ids=[f"M{c[0]}K{c[1]}ld{c[2]}{'r' if c[3] else ''}-{c[4]}" for c in NORM_CASES])
+def test_rmsnorm_quant_parity(M, K, ldx, res, mode, eps):
+    bl = _bl()
+    say(f"rmsnorm_quant M={M} K={K} ldx={ldx} residual={res} h={mode} eps={eps}")
+    x, r, g = W.norm_inputs(900 + 3 * M + K, M, K, outlier_frac=0.01, outlier_scale=20.0)
+    if not res:
+        r = None
+    h, q, d = _norm_run(bl, x, r, g, eps, ldx, mode)
+    n_amb = check_norm(x, r, g, eps, h if mode != "none" else None, q, d)
+    assert n_amb <= 1
+
+
+def test_rmsnorm_quant_golden_and_special():
+    bl = _bl()
+    say("rmsnorm_quant golden e9 + special rows")
+    import pins
+    for c in pins.golden("e9_rmsnorm_quant.json")["cases"]:
+        x = pins.bf16_bits([c["x"]])
+        r = None if c["r"] is None else pins.bf16_bits([c["r"]])
+        h, q, d = _norm_run(bl, x, r, pins.bf16_bits(c["g"]), c["eps"], 4,
+                            "new" if r is not None else "none")
+        assert q[0].tolist() == c["q"], c["derivation"]
+        assert int(d.view(np.uint32)[0]) == c["d_bits"], c["derivation"]
+        if r is not None:
+            assert h[0].tolist() == c["h_bits"], c["derivation"]
+    # zero rows (eps 0 and > 0), a residual that cancels x, a single spike,
+    # tiny and large magnitudes; both kernels (K = 64 and K = 68)
+    for K in (64, 68):
+        x, r, g = W.norm_inputs(31 + K, 8, K)
+        x[0] = 0
+        r[0] = 0
+        r[1] = x[1] ^ np.uint16(0x8000)                      # x + r = 0 exactly
+        x[2] = 0
+        r[2] = 0
+        x[2, 5] = W.f32_to_bf16_bits(np.array([7.0], np.float32))[0]
+        x[3] = W.f32_to_bf16_bits(np.full(K, 2.0 ** -60, np.float32))
+        r[3] = 0
+        x[4] = W.f32_to_bf16_bits(np.full(K, 1.0e18, np.float32))
+        r[4] = 0
+        for eps in (0.0, 1e-6):
+            h, q, d = _norm_run(bl, x, r, g, eps, K, "new")
+            check_norm(x, r, g, eps, h, q, d)
+            assert not q[:2].any() and not d[:2].any()
+
+
+def test_rmsnorm_quant_empty():
+    bl = _bl()
+    say("rmsnorm_quant empty")
+    g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    h, q, d = bl.rmsnorm_quant(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), g, 1e-5)
+    assert q.shape == (0, 64) and d.shape == (0,)
+    g0 = torch.ones(0, dtype=torch.bfloat16, device="cuda")
+    h, q, d = bl.rmsnorm_quant(torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda"), g0, 1e-5)
+    torch.cuda.synchronize()
+    assert host(d).tolist() == [0.0, 0.0, 0.0]
+
+
+@pytest.mark.parametrize("cid,M,n_rows", [(3, 512, 48), (5, 2048, 24)])
+def test_rmsnorm_quant_prefill_sampled(cid, M, n_rows):
+    """Full prefill shapes (2B layer: 512 x 2560; 100B layer: 2048 x 8192)
+    with the configs' outlier channels and the residual stream updated in
+    place, as in a decoder layer: sampled tokens against the oracle, and the
+    whole h against the residual add done once on the CPU."""
+    bl = _bl()
+    cfg = W.CONFIGS[cid]
+    K = cfg.projs[0].K
+    say(f"rmsnorm_quant config {cid}: M={M} K={K}")
+    x, r, g = W.norm_inputs(5000 + cid, M, K, cfg.outlier_frac, cfg.outlier_scale)
+    h, q, d = _norm_run(bl, x, r, g, 1e-5, K, "in_r")
+    rows = np.sort(W.rng(77 + cid).permutation(M)[:n_rows])
+    rows[0], rows[-1] = 0, M - 1
+    assert check_norm(x, r, g, 1e-5, None, q, d, rows=rows) <= 1
+    xs = oracle.widen_bf16(x)
+    rs = oracle.widen_bf16(r)
+    h_all = oracle.norm._bf16_rne_from_f32((xs + rs).astype(np.float32))
+    assert np.array_equal(h, h_all)
+
+
+# ---------------------------------------------------------------------------
 # pack_i2s
 # ---------------------------------------------------------------------------
 

@@ -282,3 +282,59 @@ def test_gemm_lds_fragments(tile):
                 want = [(wr * RT * 16 + rt * 16 + R_OF[l], 8 * H_OF[l] + b) for b in range(8)]
                 assert got == want
             assert banks_conflict_free(addr, 8)
+
+
+# ---- residual add + RMSNorm + quantize ------------------------------------
+
+def rmsnorm_config(K, ldx):
+    """(threads, chunks per thread) of the register-row kernel, or (256, 0)
+    for the generic three-pass kernel (mirrors rmsnorm_quant_config)."""
+    if K <= 0 or K % 8 or ldx % 8 or K > 32768:
+        return 256, 0
+    n = K // 8
+    if n <= 4 * 256:
+        return 256, -(-n // 256)
+    return 1024, -(-n // 1024)
+
+
+def rmsnorm_ranges(M, K, ldx):
+    """Byte ranges touched per array: (lo, hi) over every thread and token."""
+    nt, nc = rmsnorm_config(K, ldx)
+    tid = np.arange(nt)
+    row_lo, row_hi, qhi, ghi = [], [], [], []
+    if nc:
+        n = K // 8
+        for i in range(nc):
+            c = tid + i * nt
+            load = np.minimum(c, n - 1)                       # clamped unconditional loads
+            row_lo.append(16 * load.min())
+            row_hi.append(16 * load.max() + 16)
+            ghi.append(16 * load.max() + 16)
+            st = c[c < n]
+            if st.size:
+                row_hi.append(16 * st.max() + 16)             # h_out store
+                qhi.append(8 * st.max() + 8)
+    else:
+        c = np.arange(K // 4)
+        row_lo.append(0)
+        row_hi.append(8 * c.max() + 8)
+        ghi.append(8 * c.max() + 8)
+        qhi.append(4 * c.max() + 4)
+    last = (M - 1) * ldx * 2
+    return dict(x=(min(row_lo), last + max(row_hi)), g=(0, max(ghi)), q=(0, (M - 1) * K + max(qhi)),
+                chunks=nc, threads=nt)
+
+
+@pytest.mark.parametrize("K,ldx", [(8, 8), (40, 40), (2560, 2560), (2560, 2568), (4096, 4096),
+                                   (6912, 6912), (8192, 8192), (8200, 8200), (11008, 11008),
+                                   (28672, 28672), (32768, 32768), (36, 36), (2560, 2564),
+                                   (32776, 32776), (40000, 40004), (4, 4)])
+def test_rmsnorm_loads_in_bounds(K, ldx):
+    M = 3
+    r = rmsnorm_ranges(M, K, ldx)
+    assert r["x"][0] >= 0 and r["x"][1] <= ((M - 1) * ldx + K) * 2      # x, r and h_out
+    assert r["g"][1] <= 2 * K
+    assert r["q"][1] <= M * K
+    assert r["chunks"] <= 4 and r["threads"] in (256, 1024)
+    if r["chunks"]:
+        assert r["threads"] * r["chunks"] >= K // 8                     # every chunk covered

@@ -134,6 +134,18 @@ def activations_bf16(seed: int, M: int, K: int, outlier_frac: float = 0.0,
     return f32_to_bf16_bits(x)
 
 
+def norm_inputs(seed: int, M: int, K: int, outlier_frac: float = 0.0,
+                outlier_scale: float = 1.0, residual_sigma: float = 4.0):
+    """bf16 bits for the fused residual add + RMSNorm + quantize step:
+    x [M][K] (a sublayer's output: N(0, 1) with the outlier columns scaled),
+    r [M][K] (the residual stream: N(0, residual_sigma^2)) and the norm weight
+    g [K] (1 + 0.1 * N(0, 1)). The pages give no norm weights; these stand in."""
+    x = activations_bf16(seed, M, K, outlier_frac, outlier_scale)
+    r = rng(seed + 104729).standard_normal((M, K), dtype=np.float32) * np.float32(residual_sigma)
+    g = np.float32(1.0) + np.float32(0.1) * rng(seed + 1299709).standard_normal(K, dtype=np.float32)
+    return x, f32_to_bf16_bits(r), f32_to_bf16_bits(g)
+
+
 @dataclass
 class ProjInputs:
     proj: Proj
