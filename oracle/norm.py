@@ -18,7 +18,7 @@ with a per-feature weight, fp32 arithmetic with the roundings named here):
 Degenerate rows (the pages are silent; the limit is taken): when
 fl32(ms + eps) is zero (an all-zero row with eps = 0, or a mean square that
 underflows fp32) the row normalizes to zero, so q = 0 and d = 0. eps must be
-finite and >= 0; a y that overflows fp32 is rejected.
+finite and >= 0; a mean square or a y that overflows fp32 is rejected.
 """
 from __future__ import annotations
 
@@ -27,6 +27,9 @@ from fractions import Fraction
 import numpy as np
 
 from .quant import QMAX, widen_bf16
+
+
+_F32_MAX = Fraction(float(np.finfo(np.float32).max))
 
 
 def _bf16_rne_from_f32(v: np.ndarray) -> np.ndarray:
@@ -98,6 +101,8 @@ def rmsnorm_quant(x_bits, r_bits, g_bits, eps: float, return_ms: bool = False):
     mss = []
     for t in range(M):
         msf = _mean_square(h[t]) if K else Fraction(0)
+        if msf > _F32_MAX:
+            raise ValueError("mean square overflows fp32")
         mss.append(msf)
         ms = round_fraction_to_f32(msf)
         v = np.float32(ms + eps32)
