@@ -223,11 +223,19 @@ def norm_bench(torch, bl, W, dev, stream):
         gr = capture_fns(torch, stream, [unfused(b) for b in bufs])
         us_unf = replay_us(torch, stream, gr, R)
         del gr, bufs
+        # floor: a plain device copy moving the same bytes (half read, half written)
+        half = nbytes // 2
+        cbufs = [(torch.empty(half, dtype=torch.uint8, device=dev),
+                  torch.ones(half, dtype=torch.uint8, device=dev)) for _ in range(R)]
+        gr = capture_fns(torch, stream, [(lambda a=a, b=b: a.copy_(b)) for a, b in cbufs])
+        us_copy = replay_us(torch, stream, gr, R)
+        del gr, cbufs
         torch.cuda.empty_cache()
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"M": M, "K": K, "us": round(us, 3), "gbs": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes,
-                     "unfused_us": round(us_unf, 3), "copies": R}
+                     "unfused_us": round(us_unf, 3), "copy_floor_us": round(us_copy, 3),
+                     "copies": R}
     return out
 
 
