@@ -33,6 +33,11 @@
 namespace bl {
 namespace {
 
+// Problems with at least this many output rows take the whole-line decode
+// kernel (k_decode1w); smaller ones k_decode1, whose shorter steps spread a
+// small launch over more waves.
+constexpr int64_t kWideN = 8192;
+
 __device__ __forceinline__ void store_out(void* y, int ytype, int64_t idx, int acc, float c) {
   if (ytype == 0) {
     static_cast<int*>(y)[idx] = acc;
@@ -241,6 +246,177 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   }
 }
 
+// One-token fused decode for wide problems (N >= kWideN): the same quantize
+// and contraction as k_decode1, with the weight loads shaped for whole cache
+// lines. Each load instruction covers 8 rows x 128 contiguous bytes (lane
+// (r8 = lane%8, c = lane/8) reads row r8, bytes 16c..16c+15 of the row's
+// 128-byte segment), where k_decode1's covers 16 rows x 64 bytes (half
+// lines, the other half fetched by the next step). A step is 512 weights of
+// the block's 16 rows: two loads (rows 0-7 and 8-15).
+// MFMA mapping: lane l of a load holds row r8 + 8i and the 64-weight chunk c of
+// the segment. As the A operand of v_mfma_i32_16x16x64_i8 the lane sits at
+// row m = l%16 = r8 + 8(c&1) and k-group h = l/16 = c/2, so MFMA rows m < 8
+// carry the even chunks and rows m >= 8 the odd chunks of the same 8 real
+// rows. The B operand gives column n the activations of chunk 2h + (n&1):
+// column 0 pairs with the even chunks, column 1 with the odd ones, and row r
+// of half i is D[r][0] + D[8 + r][1] (lanes 0/16 and 33/49 of the result).
+// The WPB waves split K into runs of 512-weight steps; SINGLE: every step of
+// a wave's run is in one load batch (U >= run length), so no second buffer
+// is held.
+template <int WPB, int XR, int U, bool SINGLE>
+__global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int len_max) {
+  extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][len_max*512]
+  __shared__ v4i red[WPB - 1][2][kWave];
+  __shared__ uint32_t wmax[WPB];
+
+  const DecodeProblem& P = grp.p[blockIdx.y];
+  const int64_t N = P.N;
+  const int K = (int)P.K;
+  const uint8_t* __restrict__ packed = P.packed;
+  const uint16_t* __restrict__ xg = P.x;
+  const float* gptr = P.gamma;
+  void* yp = P.y;
+  int8_t* qp = P.q;
+  float* dp = P.d;
+  const int ytype = P.ytype;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  asm volatile("" ::"s"(packed), "s"(xg), "s"(K), "s"(gptr), "s"(yp), "s"(qp), "s"(dp),
+               "s"(ytype), "s"(len_max));
+  if (n0 >= N) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wk = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & (WPB - 1);
+  const int h = lane >> 4, c = lane >> 3, r8 = lane & 7;
+  const int RB = K / 4;
+  const bool first_block = blockIdx.x == 0;
+
+  const int nsteps = (K + 511) / 512;
+  const int len = (nsteps + WPB - 1) / WPB;
+  const int ja = min(wk * len, nsteps);
+  const int jb = min(ja + len, nsteps);
+  const int klo = min(ja * 512, K);
+  const int khi = min(jb * 512, K);
+  const int nch = (khi - klo) / 8;
+  int8_t* wact = act + wk * len_max * 512;
+
+  // ---- 1. loads: this wave's part of x, then the first weight batch -----
+  const uint4* xs = reinterpret_cast<const uint4*>(xg) + (nch > 0 ? klo / 8 : 0);
+  const int clast = nch > 0 ? nch - 1 : 0;
+  uint4 xv[XR];
+#pragma unroll
+  for (int u = 0; u < XR; ++u) xv[u] = xs[min(lane + u * kWave, clast)];
+  const float gam = ytype ? __builtin_nontemporal_load(gptr) : 0.0f;
+  int64_t ra = n0 + r8, rb = n0 + 8 + r8;
+  ra = ra < N ? ra : N - 1;
+  rb = rb < N ? rb : N - 1;
+  const uint8_t* wrow0 = packed + ra * RB;
+  const uint8_t* wrow1 = packed + rb * RB;
+  v4i wa[U][2], wb[SINGLE ? 1 : U][2];
+  auto load_w = [&](auto& dst, int j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int step = max(min(j + u, jb - 1), 0);
+      int off = step * 128 + 16 * c;
+      off = off < RB ? off : RB - 16;        // lanes past K (masked below)
+      dst[u][0] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow0 + off));
+      dst[u][1] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow1 + off));
+    }
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(wa, ja);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. absmax of the row: part maxima, one barrier -------------------
+  uint32_t m = 0u;
+#pragma unroll
+  for (int u = 0; u < XR; ++u) m = max(m, lane + u * kWave < nch ? absmax8_bf16(xv[u]) : 0u);
+  m = wave_max_u32(m);
+  if (lane == 0) wmax[wk] = m;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < WPB; ++w) m = max(m, wmax[w]);
+  const float mf = __uint_as_float(m << 16);
+  const float sq = m ? 127.0f / mf : 0.0f;
+  const float dv = m ? mf / 127.0f : 0.0f;
+  if (first_block && wk == 0 && lane == 0 && dp) dp[0] = dv;
+
+  // ---- 3. int8 codes of this part -> the wave's LDS region --------------
+  const bool write_q = first_block && qp;
+#pragma unroll
+  for (int u = 0; u < XR; ++u) {
+    const int cc = lane + u * kWave;
+    if (cc < nch) {
+      const uint2 qv = quant8_bf16(xv[u], sq);
+      *reinterpret_cast<uint2*>(wact + 8 * cc) = qv;
+      if (write_q) *reinterpret_cast<uint2*>(qp + klo + 8 * cc) = qv;
+    }
+  }
+  // (activation bytes past K in a partial last step are never paired with a
+  // weight: those weights are masked to 0)
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- 4. MFMA over this part's steps ----------------------------------
+  v4i acc[2][2];                                       // [half][chain]
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = v4i{0, 0, 0, 0};
+  const int8_t* arow = wact + 64 * (2 * h + (lane & 1));
+  auto compute = [&](const auto& w, int j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j + u < jb) {
+        const uint32_t kmask = (j + u) * 512 + 64 * c < K ? 0xFFFFFFFFu : 0u;
+        v4i b[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          b[s] = *reinterpret_cast<const v4i*>(arow + (j + u - ja) * 512 + 16 * s);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[i][s & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                decode_word((uint32_t)w[u][i][s] & kmask), b[s], acc[i][s & 1], 0, 0, 0);
+      }
+    }
+  };
+  if constexpr (SINGLE) {
+    compute(wa, ja);
+  } else {
+    for (int j = ja; j < jb; j += 2 * U) {
+      if (j + U < jb) load_w(wb, j + U);
+      compute(wa, j);
+      if (j + 2 * U < jb) load_w(wa, j + 2 * U);
+      if (j + U < jb) compute(wb, j + U);
+    }
+  }
+  v4i a2[2] = {acc[0][0] + acc[0][1], acc[1][0] + acc[1][1]};
+
+  // ---- 5. sum of the parts, even + odd chunks, dequant, store -----------
+  if (wk > 0) {
+    red[wk - 1][0][lane] = a2[0];
+    red[wk - 1][1][lane] = a2[1];
+  }
+  __syncthreads();
+  if (wk > 0) return;
+#pragma unroll
+  for (int w = 0; w < WPB - 1; ++w) {
+    a2[0] += red[w][0][lane];
+    a2[1] += red[w][1][lane];
+  }
+  v4i o[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    o[i].x = a2[i].x + __shfl(a2[i].x, lane + 33, kWave);
+    o[i].y = a2[i].y + __shfl(a2[i].y, lane + 33, kWave);
+    o[i].z = a2[i].z + __shfl(a2[i].z, lane + 33, kWave);
+    o[i].w = a2[i].w + __shfl(a2[i].w, lane + 33, kWave);
+  }
+  if ((lane & 15) != 0 || lane >= 32) return;          // lanes 0 and 16
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t n = n0 + 8 * i + 4 * h;
+    if (n < N) store_quad(yp, ytype, N, 0, n, o[i], gam * dv);
+  }
+}
+
 // Decode contraction over int8 activations q [M][K] (scales d), M <= 16.
 // The activation fragments are read straight from global memory in the MFMA
 // B layout (lane r, h: token r's 64 bytes at k = 256*step + 64h): every block
@@ -370,6 +546,30 @@ hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int WPB, int XR, int U, bool SINGLE>
+hipError_t launch_one_token_w(DecodeGroup& g, int len_max, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int i = 0; i < g.count; ++i) {
+    const int64_t b = (g.p[i].N + 15) / 16;
+    blocks = b > blocks ? b : blocks;
+  }
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = (size_t)WPB * len_max * 512;
+  hipLaunchKernelGGL((k_decode1w<WPB, XR, U, SINGLE>), dim3((unsigned)blocks, (unsigned)g.count),
+                     dim3(WPB * kWave), lds, s, g, len_max);
+  return hipGetLastError();
+}
+
+// Longest per-wave run of 512-weight steps in the group when WPB waves split K.
+int wide_steps_per_wave(const DecodeGroup& g, int wpb) {
+  int len = 0;
+  for (int i = 0; i < g.count; ++i) {
+    const int l = (int)(((g.p[i].K + 511) / 512 + wpb - 1) / wpb);
+    len = l > len ? l : len;
+  }
+  return len;
+}
+
 // Longest per-wave run of 256-weight steps in the group when WPB waves split K.
 int steps_per_wave(const DecodeGroup& g, int wpb) {
   int len = 0;
@@ -452,6 +652,20 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
   bool fused = true;
   for (int i = 0; i < g.count; ++i) fused = fused && g.p[i].x != nullptr;
   if (fused && g.M == 1) {                          // one token: quantize in the kernel
+    int64_t nmax = 0;
+    for (int i = 0; i < g.count; ++i) nmax = g.p[i].N > nmax ? g.p[i].N : nmax;
+    if (nmax >= kWideN) {                           // whole-line weight loads
+      const int w4 = wide_steps_per_wave(g, 4);
+      if (w4 <= 1) return launch_one_token_w<4, 1, 1, true>(g, w4, s);
+      if (w4 == 2) return launch_one_token_w<4, 2, 2, true>(g, w4, s);
+      if (w4 == 3) return launch_one_token_w<4, 3, 3, true>(g, w4, s);
+      if (w4 == 4) return launch_one_token_w<4, 4, 4, true>(g, w4, s);
+      const int w8 = wide_steps_per_wave(g, 8);
+      if (w8 <= 4) return launch_one_token_w<8, 4, 4, true>(g, w8, s);
+      if (w8 <= 8) return launch_one_token_w<8, 8, 4, false>(g, w8, s);
+      const int w16 = wide_steps_per_wave(g, 16);  // <= 8 for K <= 65536
+      return launch_one_token_w<16, 8, 4, false>(g, w16, s);
+    }
     const int len4 = steps_per_wave(g, 4);
     // one load batch of exactly the steps of the longest wave when it is
     // short (a clamped extra load still costs a request), else batches of 4

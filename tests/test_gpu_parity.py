@@ -642,6 +642,41 @@ def test_decode_group_one_token_long_k():
     _decode_group_case(bl, 1, [(3, 65536), (9, 40960)], seed=78, out_types=["f32", "bf16"])
 
 
+def test_decode_group_wide():
+    """One-token groups with a problem of >= 8192 rows take the whole-line
+    kernel: one batch per wave at K = 512, 2560, 4160 (K % 512 != 0) and 8192
+    (waves without steps at the small K), small problems riding in the same
+    launch, a ragged last row block, and two batches per wave at K = 28672."""
+    bl = _bl()
+    _decode_group_case(bl, 1, [(8192, 8192)], seed=90)
+    _decode_group_case(bl, 1, [(8200, 4160), (1000, 4160)], seed=91)
+    _decode_group_case(bl, 1, [(8192, 2560), (640, 2560), (640, 2560)], seed=92,
+                       out_types=["bf16", "i32", "f32"])
+    _decode_group_case(bl, 1, [(9000, 512), (16, 64)], seed=93)
+    _decode_group_case(bl, 1, [(8193, 28672)], seed=94, out_types=["i32"])
+
+
+def test_decode_group_wide_longest_k():
+    """The 16-wave whole-line block at the largest K the call takes (65536):
+    byte-identical to quantize + bl_gemv, sampled rows against the oracle."""
+    bl = _bl()
+    N, K = 8208, 65536
+    say(f"decode_group wide N={N} K={K}")
+    x = W.activations_bf16(95, 1, K, outlier_frac=0.01, outlier_scale=20.0)
+    t = W.ternary_drawn(96, N, K, 0.4)
+    packed = bl.pack_i2s(dev(t))
+    gamma = dev(np.array([GAMMA], np.float32))
+    (y,) = bl.decode_group([dict(packed=packed, gamma=gamma, x=dev_bf16(x))], out_dtype="f32")
+    q, d = bl.quantize_act(dev_bf16(x))
+    y2 = bl.gemv(packed, gamma, q, d, out_dtype="f32")
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+    q_ref, d_ref = oracle.quantize_act_absmax(x)
+    rows = np.unique(np.concatenate([W.rng(97).integers(0, N, 40), [0, 15, 16, N - 17, N - 1]]))
+    acc = oracle.mpgemm_acc(q_ref, t[rows])
+    check_outputs(acc, GAMMA, d_ref, y_f32=host(y)[:, rows])
+
+
 def test_decode_group_tokens_long_k():
     """Several tokens (quantize launch + GEMV over the codes) at the largest K."""
     bl = _bl()

@@ -338,3 +338,100 @@ def test_rmsnorm_loads_in_bounds(K, ldx):
     assert r["chunks"] <= 4 and r["threads"] in (256, 1024)
     if r["chunks"]:
         assert r["threads"] * r["chunks"] >= K // 8                     # every chunk covered
+
+
+# ---- one-token decode of wide problems (whole-line weight loads) -----------
+
+def wide_steps_per_wave(K, wpb):
+    return ((K + 511) // 512 + wpb - 1) // wpb
+
+
+def decode1w_config(K):
+    """(WPB, XR, U, SINGLE, len) that launch_decode_group picks for a
+    one-token group of wide problems whose largest K is K."""
+    w4 = wide_steps_per_wave(K, 4)
+    if w4 <= 4:
+        w = max(w4, 1)
+        return 4, w, w, True, w4
+    w8 = wide_steps_per_wave(K, 8)
+    if w8 <= 4:
+        return 8, 4, 4, True, w8
+    if w8 <= 8:
+        return 8, 8, 4, False, w8
+    w16 = wide_steps_per_wave(K, 16)
+    assert w16 <= 8, "K above 65536 is rejected at the boundary"
+    return 16, 8, 4, False, w16
+
+
+C_OF = LANES >> 3
+R8_OF = LANES & 7
+
+
+def decode1w_ranges(N, K, group_kmax=None):
+    """Yield (buffer, lo, hi, size) of every global load and LDS access of
+    k_decode1w for one problem of a group whose largest K is group_kmax."""
+    assert K % 64 == 0 and K >= 64
+    WPB, XR, U, single, len_max = decode1w_config(K if group_kmax is None else group_kmax)
+    RB = K // 4
+    nsteps = (K + 511) // 512
+    length = (nsteps + WPB - 1) // WPB
+    assert length <= len_max
+    assert XR * WAVE * 8 >= length * 512              # the x chunks cover the part
+    if single:
+        assert U >= length                            # one batch holds the whole run
+    for b, wk in itertools.product(range((N + 15) // 16), range(WPB)):
+        n0 = b * 16
+        ja = min(wk * length, nsteps)
+        jb = min(ja + length, nsteps)
+        klo, khi = min(ja * 512, K), min(jb * 512, K)
+        nch = (khi - klo) // 8
+        cbase = klo // 8 if nch > 0 else 0
+        clast = nch - 1 if nch > 0 else 0
+        for u in range(XR):
+            c = cbase + np.minimum(LANES + u * WAVE, clast)
+            yield "x", (16 * c).min(), (16 * c + 16).max(), 2 * K
+        rows = [np.minimum(n0 + R8_OF, N - 1), np.minimum(n0 + 8 + R8_OF, N - 1)]
+        bases = [ja] if single else sorted({bb for j in (range(ja, jb, 2 * U) or [ja])
+                                            for bb in (j, j + U, j + 2 * U)})
+        for base in bases:
+            for u in range(U):
+                step = max(min(base + u, jb - 1), 0)
+                off = np.minimum(step * 128 + 16 * C_OF, RB - 16)
+                for r in rows:
+                    lo = r * RB + off
+                    yield "packed", lo.min(), (lo + 16).max(), N * RB
+        region = len_max * 512
+        if nch > 0:
+            yield "lds", 0, 8 * nch, region
+        if jb > ja:                                   # fragment reads of the last step
+            hi = 64 * (2 * (H_OF.max()) + 1) + (jb - 1 - ja) * 512 + 48 + 16
+            yield "lds", 0, hi, region
+
+
+DECODE1W_SHAPES = [(8192, 64), (8200, 4160), (8192, 8192), (28672, 8192), (8192, 28672),
+                   (8193, 11008), (9000, 512), (8192, 65536), (8192, 32768), (8208, 16448)]
+
+
+@pytest.mark.parametrize("N,K", DECODE1W_SHAPES, ids=[f"N{n}K{k}" for n, k in DECODE1W_SHAPES])
+def test_decode1w_loads_in_bounds(N, K):
+    for buf, lo, hi, size in decode1w_ranges(N, K):
+        assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_decode1w_group_len_max():
+    for K in (64, 512, 4160, 8192):
+        for kmax in (8192, 28672, 65536):
+            for buf, lo, hi, size in decode1w_ranges(40, K, group_kmax=kmax):
+                assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_decode1w_mfma_pairing():
+    """The chunk a lane loads and the activation chunk its MFMA column pairs
+    with agree for the columns that are kept (0 for rows m < 8, 1 for m >= 8)."""
+    for lane in range(WAVE):
+        r8, c = lane & 7, lane >> 3
+        m, h = lane & 15, lane >> 4                   # A operand position
+        assert m == r8 + 8 * (c & 1) and h == c // 2
+        col = 0 if m < 8 else 1                       # column kept for this row
+        b_chunk = 2 * h + (col & 1)                   # activation chunk of that column
+        assert b_chunk == c
