@@ -26,6 +26,7 @@ Modules:
   norm     residual add + RMSNorm fused with the per-token quantizer
   ternary  absmean weight scale (exact sum) and the +-0.5*gamma threshold
   i2s      2-bit I2_S pack / unpack (code table and bit layout)
+  t3       base-3 pack / unpack, five weights per byte (1.6 bits per weight)
   dot      exact integer contraction (int64), plus an fp64-BLAS exact variant
   lut      element-wise lookup-table sums (TL1/TL2 style), a cross-check only
   dequant  y = acc * gamma * d in fp64; the fp32 epilogue; bf16 rounding
@@ -39,6 +40,7 @@ from .quant import widen_bf16, quantize_act_absmax, quantize_act_absmax_tensor
 from .norm import rmsnorm_quant, round_fraction_to_f32
 from .ternary import absmean_gamma, ternarize, ternarize_absmean
 from .i2s import pack_i2s, unpack_i2s, CODE_ZERO, CODE_POS, CODE_NEG
+from .t3 import pack_t3, unpack_t3
 from .dot import mpgemm_acc, mpgemm_acc_entries, mpgemm_acc_f64blas
 from .lut import lut_dot
 from .dequant import dequant_f64, dequant_f32, round_f64_to_bf16_bits, bf16_bits_to_f64
@@ -47,6 +49,7 @@ __all__ = [
     "widen_bf16", "quantize_act_absmax",
     "absmean_gamma", "ternarize", "ternarize_absmean",
     "pack_i2s", "unpack_i2s", "CODE_ZERO", "CODE_POS", "CODE_NEG",
+    "pack_t3", "unpack_t3",
     "mpgemm_acc", "mpgemm_acc_entries", "mpgemm_acc_f64blas",
     "lut_dot",
     "dequant_f64", "dequant_f32", "round_f64_to_bf16_bits", "bf16_bits_to_f64",

@@ -565,9 +565,104 @@ def pin_bf16_bruteforce(seed=21):
         assert b == _bf16_nearest_rational(x), (x, hex(b))
 
 
+# ----------------------------------------------------------------------------
+# base-3 packing, five weights per byte
+# ----------------------------------------------------------------------------
+
+def pin_t3_golden():
+    for c in golden("e10_t3_bytes.json")["cases"]:
+        t = np.array(c["tern"], dtype=np.int8)
+        b = oracle.pack_t3(t)
+        assert b.tolist() == c["bytes"], c["derivation"]
+        assert np.array_equal(oracle.unpack_t3(np.array(c["bytes"], np.uint8), c["K"]), t)
+
+
+def pin_t3_exhaustive():
+    """Every 5-tuple of ternary weights <-> one of 243 distinct bytes; the other
+    13 byte values are rejected; the digits can be taken off the byte by
+    repeated multiplication by 3 (y = 3x, digit = y >> 8, x = y mod 256)."""
+    tuples = np.array(list(itertools.product((-1, 0, 1), repeat=5)), dtype=np.int8)
+    w = np.zeros((243, 80), dtype=np.int8)
+    for i in range(5):
+        w[:, 16 * i] = tuples[:, i]                   # byte 0, planes 0..4
+    b = oracle.pack_t3(w)
+    assert len(set(b[:, 0].tolist())) == 243
+    assert np.all(b[:, 1:] == b[0, 1:].min()) and b[0, 1] == 128    # zeros elsewhere
+    valid = set(b[:, 0].tolist())
+    for q in range(256):
+        row = np.full((1, 64), 128, dtype=np.uint8)
+        row[0, 0] = q
+        if q in valid:
+            got = oracle.unpack_t3(row, 80)
+            assert tuple(got[0, 16 * np.arange(5)].tolist()) == tuple(
+                tuples[b[:, 0].tolist().index(q)].tolist())
+        else:
+            try:
+                oracle.unpack_t3(row, 80)
+            except ValueError:
+                continue
+            raise AssertionError(f"byte {q} accepted")
+    for t, q in zip(tuples.tolist(), b[:, 0].tolist()):
+        x, digits = q, []
+        for _ in range(5):
+            y = 3 * x
+            digits.append(y >> 8)
+            x = y & 255
+        assert [d - 1 for d in digits] == t, (t, q, digits)
+
+
+def pin_t3_layout():
+    """One nonzero weight at a time: exactly one byte changes, at 16u + (k%80)%16,
+    by w * 3^(4-plane) in the base-3 value."""
+    K = 400                                           # two row quanta, the second partial
+    base = oracle.pack_t3(np.zeros((1, K), np.int8))
+    assert base.shape == (1, 128) and np.all(base == 128)
+    for k in (0, 15, 16, 63, 64, 79, 80, 159, 319, 320, 399):
+        for w in (1, -1):
+            t = np.zeros((1, K), np.int8)
+            t[0, k] = w
+            b = oracle.pack_t3(t)
+            diff = np.nonzero(b[0] != base[0])[0].tolist()
+            pos = 16 * (k // 80) + (k % 80) % 16
+            assert diff == [pos], (k, diff)
+            plane = (k % 80) // 16
+            v = (243 * int(b[0, pos])) // 256
+            assert v - 121 == w * 3 ** (4 - plane), (k, w, v)
+
+
+def pin_t3_roundtrip_dot(seed=31):
+    """unpack(pack(w)) = w; the contraction over the unpacked base-3 weights is
+    the I2_S one; bytes per row = 64 * ceil(K / 320) (1.6 bits per weight when
+    320 divides K); non-zero padding is rejected."""
+    r = _rng(seed)
+    for N, K in ((3, 16), (5, 320), (4, 336), (2, 2560), (3, 4160)):
+        w = (r.integers(0, 3, (N, K)) - 1).astype(np.int8)
+        b = oracle.pack_t3(w)
+        assert b.shape == (N, 64 * -(-K // 320))
+        assert np.array_equal(oracle.unpack_t3(b, K), w)
+        q = r.integers(-127, 128, (2, K)).astype(np.int8)
+        acc_t3 = oracle.mpgemm_acc(q, oracle.unpack_t3(b, K))
+        acc_i2 = oracle.mpgemm_acc(q, oracle.unpack_i2s(oracle.pack_i2s(w), K))
+        assert np.array_equal(acc_t3, acc_i2)
+        assert np.array_equal(acc_t3, q.astype(np.int64) @ w.astype(np.int64).T)
+    assert oracle.pack_t3(np.zeros((1, 3200), np.int8)).size * 8 / 3200 == 1.6
+    bad = oracle.pack_t3(np.zeros((1, 16), np.int8))
+    bad[0, 0] = 213                                    # plane 0 of byte 0 is real
+    assert oracle.unpack_t3(bad, 16)[0, 0] == 1
+    bad[0, 0] = 128 + 0                                # restore, then hit padding
+    bad[0, 20] = 213                                   # byte 20: weight 84 > K
+    try:
+        oracle.unpack_t3(bad, 16)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("non-zero padding accepted")
+
+
 ALL_PINS = [
     pin_quant_golden, pin_quant_special, pin_quant_invariants, pin_quant_rejects,
     pin_quant_tensor_golden, pin_quant_tensor_reductions,
+    pin_t3_golden, pin_t3_exhaustive, pin_t3_layout, pin_t3_roundtrip_dot,
     pin_norm_golden, pin_norm_zero_rows, pin_norm_exact_ms, pin_norm_invariants, pin_norm_error_bound,
     pin_ternary_golden, pin_gamma_exact, pin_ternary_roundclip, pin_ternary_invariants,
     pin_ternary_statistics,

@@ -7,6 +7,7 @@ import oracle.dequant
 import oracle.dot
 import oracle.i2s
 import oracle.norm
+import oracle.t3
 import oracle.quant
 import oracle.ternary
 import pins
@@ -25,6 +26,10 @@ MUTATIONS = {
                                           + 0x8000) >> 16).astype(np.uint16)),
     "norm_mean_over_k_minus_1": (oracle.norm, "_mean_square",
                                  lambda h: oracle.norm._exact_sum_squares(h) / (h.shape[0] - 1)),
+    "t3_digits_reversed": (oracle.t3, "POW3", oracle.t3.POW3[::-1].copy()),
+    "t3_encode_floor": (oracle.t3, "_encode", lambda v: (256 * v) // 243),
+    "t3_bytes_sequential": (oracle.t3, "_planes",
+                            lambda w: w.reshape(w.shape[0], -1, 16, 5).transpose(0, 1, 3, 2)),
     "ternary_ge_threshold": (oracle.ternary, "_above", lambda w, t: w >= t),
     "ternary_threshold_0.7": (oracle.ternary, "THRESHOLD_FRACTION", 0.7),
     "ternary_fp32_sum": (oracle.ternary, "_exact_abs_sum",
