@@ -201,6 +201,45 @@ int bl_gemv(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
             const int8_t *q, const float *d, int64_t M, void *y, int ytype,
             void *stream);
 
+/*
+ * Base-3 weights, five per byte (1.6 bits per weight).
+ * Defines: [BN] Part A 2.3 (the format table's element-wise multiply-add
+ * formats below 2 bits per weight, TQ1_0 at 1.69 and TL2 at 1.67 bits per
+ * weight: three values per weight, so five weights fit one byte, 3^5 = 243).
+ * The byte layout is the library's:
+ *   - a row of K weights is padded with zero weights to a multiple of 320
+ *     and takes bl_pack_t3_row_bytes(K) = 64*ceil(K/320) bytes;
+ *   - unit u of a row (weights 80u .. 80u+79) is the 16 bytes at row offset
+ *     16u; byte j of a unit (0..15) holds weights 80u + j + 16i, i = 0..4;
+ *   - those five weights give digits d_i = w + 1 and v = sum d_i 3^(4-i)
+ *     (d_0 most significant); the byte stores ceil(256 v / 243).
+ * The contraction over these weights is the I2_S one, exactly.
+ */
+size_t bl_pack_t3_row_bytes(int64_t K);
+
+/*
+ * bl_pack_t3 -- ternarize (optionally) and pack weights into the base-3
+ * format. Arguments, wtype rules, gamma and workspace exactly as bl_pack_i2s
+ * (BL_W_F32 computes gamma and the same ternary values; the workspace size is
+ * bl_pack_i2s_workspace(N, K)); packed: uint8 [N][bl_pack_t3_row_bytes(K)].
+ * K % 16 == 0.
+ */
+int bl_pack_t3(const void *w, int wtype, int64_t N, int64_t K, uint8_t *packed,
+               float *gamma, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * bl_gemv_t3 -- bl_gemv over base-3 packed weights.
+ * Defines: as bl_gemv ([BN] Part A 2.3 / 4.1): acc[t][n] = sum_k q[t][k] *
+ * w[n][k] exactly, then the same dequant and output types, so the outputs
+ * equal bl_gemv's on the I2_S packing of the same weights.
+ * packed: uint8 [N][bl_pack_t3_row_bytes(K)] from bl_pack_t3 (padding must
+ * be the zero weights bl_pack_t3 writes); q: int8 [M][K]; d: fp32 [M];
+ * 0 <= M <= 16; K % 16 == 0 (BL_ERR_SHAPE otherwise); K == 0 gives zeros.
+ */
+int bl_gemv_t3(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
+               const int8_t *q, const float *d, int64_t M, void *y, int ytype,
+               void *stream);
+
 /* bl_gemm_workspace -- bytes of workspace bl_gemm needs (currently 0). */
 size_t bl_gemm_workspace(int64_t M, int64_t N, int64_t K);
 

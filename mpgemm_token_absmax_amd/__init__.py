@@ -13,6 +13,8 @@ and streams only.
     packed      = pack_i2s(w_ternary_int8)          # pack only (caller keeps gamma)
     y           = gemv(packed, g, q, d)             # M <= 16 tokens
     y           = gemm(packed, g, q, d)             # any M (int8 MFMA)
+    p3, g       = pack_t3(w_fp32)                   # base-3, 5 weights per byte (1.6 bpw)
+    y           = gemv_t3(p3, g, q, d)              # M <= 16 over the base-3 packing
     ys          = gemm_group([dict(packed=.., gamma=..), ...], q, d)
                                                     # GEMMs sharing one q, fewest launches
     ys          = decode_group([dict(packed=.., gamma=.., x=..), ...])
@@ -25,7 +27,8 @@ import torch
 from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I8, MAX_GROUP,
                    BitLinearError, DecodeProblem, GemmProblem, check, lib, status_string)
 
-__all__ = ["quantize_act", "quantize_act_tensor", "rmsnorm_quant", "pack_i2s", "pack_i2s_workspace", "gemv", "gemm",
+__all__ = ["quantize_act", "quantize_act_tensor", "rmsnorm_quant", "pack_i2s", "pack_i2s_workspace",
+           "pack_t3", "gemv_t3", "gemv", "gemm",
            "gemm_workspace", "gemm_group", "GemmGroup", "decode_group", "DecodeGroup",
            "BitLinearError", "status_string",
            "lib", "OUT_TYPES"]
@@ -155,6 +158,59 @@ def pack_i2s(w: torch.Tensor, packed: torch.Tensor | None = None,
                                                None, None, 0, s))
         return packed
     raise TypeError("w must be float32 or int8")
+
+
+def pack_t3(w: torch.Tensor, packed: torch.Tensor | None = None,
+            gamma: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """As pack_i2s, into the base-3 format (five weights per byte): packed is
+    uint8 [N][64*ceil(K/320)]. K % 16 == 0."""
+    if not isinstance(w, torch.Tensor) or not w.is_cuda or w.dim() != 2:
+        raise TypeError("w must be a 2-D CUDA tensor")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    N, K = w.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    if packed is None:
+        packed = torch.empty((N, int(lib().bl_pack_t3_row_bytes(K))), dtype=torch.uint8,
+                             device=w.device)
+    s = _stream(w.device)
+    if w.dtype == torch.float32:
+        if gamma is None:
+            gamma = torch.empty((1,), dtype=torch.float32, device=w.device)
+        nws = pack_i2s_workspace(N, K)
+        if workspace is None:
+            workspace = torch.empty((max(nws, 16),), dtype=torch.uint8, device=w.device)
+        check("bl_pack_t3", lib().bl_pack_t3(_ptr(w), BL_W_F32, N, K, _ptr(packed), _ptr(gamma),
+                                             _ptr(workspace), workspace.numel(), s))
+        return packed, gamma
+    if w.dtype == torch.int8:
+        check("bl_pack_t3", lib().bl_pack_t3(_ptr(w), BL_W_TERNARY_I8, N, K, _ptr(packed),
+                                             None, None, 0, s))
+        return packed
+    raise TypeError("w must be float32 or int8")
+
+
+def gemv_t3(packed: torch.Tensor, gamma: torch.Tensor, q: torch.Tensor, d: torch.Tensor,
+            out_dtype: str = "bf16", out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M][N] for M <= 16 tokens over base-3 packed weights."""
+    _need(packed, "packed", torch.uint8, 2)
+    _need(q, "q", torch.int8, 2)
+    N, RB = packed.shape
+    M, K = q.shape
+    if RB != int(lib().bl_pack_t3_row_bytes(K)):
+        raise ValueError(f"packed [{N}][{RB}] does not match q [{M}][{K}]")
+    ytype, tdt = OUT_TYPES[out_dtype]
+    if ytype != BL_OUT_I32:
+        _need(gamma, "gamma", torch.float32, 1)
+        _need(d, "d", torch.float32, 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=tdt, device=q.device)
+    elif out.dtype != tdt or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out has the wrong dtype, shape or layout")
+    check("bl_gemv_t3", lib().bl_gemv_t3(_ptr(packed), _ptr(gamma), N, K, _ptr(q), _ptr(d), M,
+                                         _ptr(out), ytype, _stream(q.device)))
+    return out
 
 
 def _matmul_args(packed, gamma, q, d, out, out_dtype):

@@ -30,8 +30,8 @@ BL_OUT_BF16 = 2
 
 EXPORTS = ("bl_abi_version", "bl_status_string", "bl_quantize_act",
            "bl_quantize_act_tensor_workspace", "bl_quantize_act_tensor", "bl_rmsnorm_quant",
-           "bl_pack_i2s_workspace",
-           "bl_pack_i2s", "bl_gemv", "bl_gemm_workspace", "bl_gemm", "bl_gemm_group",
+           "bl_pack_i2s_workspace", "bl_pack_i2s", "bl_pack_t3_row_bytes", "bl_pack_t3",
+           "bl_gemv", "bl_gemv_t3", "bl_gemm_workspace", "bl_gemm", "bl_gemm_group",
            "bl_decode_group")
 
 MAX_GROUP = 8
@@ -82,6 +82,12 @@ def _declare(lib):
     lib.bl_rmsnorm_quant.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P, P, P]
     lib.bl_pack_i2s.restype = INT
     lib.bl_pack_i2s.argtypes = [P, INT, I64, I64, P, P, P, SZ, P]
+    lib.bl_pack_t3_row_bytes.restype = SZ
+    lib.bl_pack_t3_row_bytes.argtypes = [I64]
+    lib.bl_pack_t3.restype = INT
+    lib.bl_pack_t3.argtypes = [P, INT, I64, I64, P, P, P, SZ, P]
+    lib.bl_gemv_t3.restype = INT
+    lib.bl_gemv_t3.argtypes = [P, P, I64, I64, P, P, I64, P, INT, P]
     lib.bl_gemv.restype = INT
     lib.bl_gemv.argtypes = [P, P, I64, I64, P, P, I64, P, INT, P]
     lib.bl_gemm_workspace.restype = SZ

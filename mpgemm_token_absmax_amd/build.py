@@ -23,7 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
-SOURCES = ["api.cpp", "quant_act.hip", "norm_quant.hip", "pack_i2s.hip", "gemv_i2s.hip", "gemm_i2s.hip"]
+SOURCES = ["api.cpp", "quant_act.hip", "norm_quant.hip", "t3.hip", "pack_i2s.hip", "gemv_i2s.hip", "gemm_i2s.hip"]
 PROBE_LIB = os.path.join(HERE, "libblprobe.so")
 PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"

@@ -145,6 +145,44 @@ int bl_pack_i2s(const void* w, int wtype, int64_t N, int64_t K, uint8_t* packed,
                                             as_stream(stream)));
 }
 
+size_t bl_pack_t3_row_bytes(int64_t K) {
+  if (K <= 0) return 0;
+  return (size_t)(64 * ((K + 319) / 320));
+}
+
+int bl_pack_t3(const void* w, int wtype, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+               void* ws, size_t ws_bytes, void* stream) {
+  if (N < 0 || K < 0 || K % 16 != 0) return BL_ERR_SHAPE;
+  if (wtype != BL_W_F32 && wtype != BL_W_TERNARY_I8) return BL_ERR_DTYPE;
+  if (wtype == BL_W_F32) {
+    if (N == 0 || K == 0) return BL_ERR_SHAPE;     // gamma of an empty matrix is undefined
+    if (N > ((int64_t)1 << 38) / K) return BL_ERR_SHAPE;
+    if (!w || !packed || !gamma) return BL_ERR_NULL;
+    if (!ws) return BL_ERR_WORKSPACE;
+    if (ws_bytes < bl::pack_workspace_bytes(N, K)) return BL_ERR_WORKSPACE;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(ws, 16))
+      return BL_ERR_ALIGN;
+    hipError_t e = bl::launch_absmean_gamma(static_cast<const float*>(w), N, K, gamma, ws,
+                                            as_stream(stream));
+    if (e == hipSuccess) e = bl::launch_pack_t3(w, true, N, K, packed, gamma, as_stream(stream));
+    return hip_status(e);
+  }
+  if (N == 0 || K == 0) return BL_OK;
+  if (!w || !packed) return BL_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(packed, 16)) return BL_ERR_ALIGN;
+  return hip_status(bl::launch_pack_t3(w, false, N, K, packed, nullptr, as_stream(stream)));
+}
+
+int bl_gemv_t3(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, const int8_t* q,
+               const float* d, int64_t M, void* y, int ytype, void* stream) {
+  if (M > kGemvMaxM || K % 16 != 0) return BL_ERR_SHAPE;
+  const int st = check_matmul(packed, gamma, N, K, q, d, M, y, ytype);
+  if (st != BL_OK || M == 0 || N == 0) return st;
+  if (N * 64 * ((K + 319) / 320) > ((int64_t)1 << 40)) return BL_ERR_SHAPE;
+  return hip_status(bl::launch_gemv_t3(packed, gamma, N, K, q, d, M, y, ytype,
+                                       as_stream(stream)));
+}
+
 int bl_gemv(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, const int8_t* q,
             const float* d, int64_t M, void* y, int ytype, void* stream) {
   if (M > kGemvMaxM) return BL_ERR_SHAPE;

@@ -56,6 +56,17 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* r, const uint
                                 float eps, int64_t M, int64_t K, int64_t ldx, uint16_t* h_out,
                                 int8_t* q, float* d, hipStream_t s);
 
+// Base-3 weights, five per byte: rows of 64*ceil(K/320) bytes.
+hipError_t launch_pack_t3(const void* w, bool f32, int64_t N, int64_t K, uint8_t* packed,
+                          const float* gamma, hipStream_t s);
+hipError_t launch_gemv_t3(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
+                          const int8_t* q, const float* d, int64_t M, void* y, int ytype,
+                          hipStream_t s);
+// Exponent bins and gamma of an fp32 matrix (the first two launches of the
+// fp32 I2_S packing): gamma[0] = fl32(exact sum |w| / (N*K)).
+hipError_t launch_absmean_gamma(const float* w, int64_t N, int64_t K, float* gamma, void* ws,
+                                hipStream_t s);
+
 size_t pack_workspace_bytes(int64_t N, int64_t K);
 hipError_t launch_pack_f32(const float* w, int64_t N, int64_t K, uint8_t* packed, float* gamma,
                            void* ws, hipStream_t s);

@@ -196,14 +196,22 @@ size_t pack_workspace_bytes(int64_t N, int64_t K) {
   return (size_t)bin_blocks(N * K) * kBins * sizeof(unsigned long long);
 }
 
-hipError_t launch_pack_f32(const float* w, int64_t N, int64_t K, uint8_t* packed, float* gamma,
-                           void* ws, hipStream_t s) {
+hipError_t launch_absmean_gamma(const float* w, int64_t N, int64_t K, float* gamma, void* ws,
+                                hipStream_t s) {
   const int64_t n = N * K;
   const int64_t nblk = bin_blocks(n);
   auto* bins = static_cast<unsigned long long*>(ws);
   hipLaunchKernelGGL(k_absmean_bins, dim3((unsigned)nblk), dim3(kBinThreads), 0, s,
                      reinterpret_cast<const float4*>(w), n / 4, bins);
   hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(kBins), 0, s, bins, (int)nblk, n, gamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_f32(const float* w, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                           void* ws, hipStream_t s) {
+  const int64_t n = N * K;
+  const hipError_t e = launch_absmean_gamma(w, N, K, gamma, ws, s);
+  if (e != hipSuccess) return e;
   if (K % 16 == 0) {
     const int64_t nw = n / 16;
     hipLaunchKernelGGL(k_pack_f32_words, dim3(grid_for(nw, 256)), dim3(256), 0, s,

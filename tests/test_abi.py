@@ -262,3 +262,29 @@ def test_rmsnorm_quant_validation(lib):
     assert call(h=B16 - 16) == L.BL_ERR_ALIAS
     assert call(M=0, x=None, g=None, q=None, d=None) == L.BL_OK
     assert lib.bl_status_string(L.BL_ERR_ALIAS)
+
+
+def test_t3_validation(lib):
+    assert lib.bl_pack_t3_row_bytes(0) == 0
+    assert lib.bl_pack_t3_row_bytes(16) == 64 and lib.bl_pack_t3_row_bytes(320) == 64
+    assert lib.bl_pack_t3_row_bytes(336) == 128 and lib.bl_pack_t3_row_bytes(2560) == 512
+    p = lib.bl_pack_t3
+    assert p(A16, L.BL_W_TERNARY_I8, 2, 20, B16, None, None, 0, None) == L.BL_ERR_SHAPE  # K % 16
+    assert p(A16, 7, 2, 32, B16, None, None, 0, None) == L.BL_ERR_DTYPE
+    assert p(None, L.BL_W_TERNARY_I8, 2, 32, B16, None, None, 0, None) == L.BL_ERR_NULL
+    assert p(A16 + 4, L.BL_W_TERNARY_I8, 2, 32, B16, None, None, 0, None) == L.BL_ERR_ALIGN
+    assert p(A16, L.BL_W_F32, 2, 32, B16, C16, None, 0, None) == L.BL_ERR_WORKSPACE
+    assert p(A16, L.BL_W_F32, 0, 32, B16, C16, D16, 1 << 20, None) == L.BL_ERR_SHAPE
+    assert p(A16, L.BL_W_F32, 2, 32, B16, None, D16, 1 << 20, None) == L.BL_ERR_NULL
+    assert p(None, L.BL_W_TERNARY_I8, 0, 32, None, None, None, 0, None) == L.BL_OK
+    g = lib.bl_gemv_t3
+    # (packed, gamma, N, K, q, d, M, y, ytype)
+    assert g(A16, B16, 8, 20, C16, D16, 1, E16, L.BL_OUT_BF16, None) == L.BL_ERR_SHAPE   # K % 16
+    assert g(A16, B16, 8, 32, C16, D16, 17, E16, L.BL_OUT_BF16, None) == L.BL_ERR_SHAPE  # M > 16
+    assert g(A16, B16, 8, 32, C16, D16, 1, None, L.BL_OUT_BF16, None) == L.BL_ERR_NULL
+    assert g(None, B16, 8, 32, C16, D16, 1, E16, L.BL_OUT_BF16, None) == L.BL_ERR_NULL
+    assert g(A16, None, 8, 32, C16, D16, 1, E16, L.BL_OUT_F32, None) == L.BL_ERR_NULL
+    assert g(A16, B16, 8, 32, C16, D16, 1, E16, 9, None) == L.BL_ERR_DTYPE
+    assert g(A16 + 8, B16, 8, 32, C16, D16, 1, E16, L.BL_OUT_BF16, None) == L.BL_ERR_ALIGN
+    assert g(A16, B16, 8, 1 << 18, C16, D16, 1, E16, L.BL_OUT_F32, None) == L.BL_ERR_SHAPE
+    assert g(None, None, 8, 32, None, None, 0, None, L.BL_OUT_BF16, None) == L.BL_OK     # M == 0

@@ -677,6 +677,77 @@ def test_decode_group_wide_longest_k():
     check_outputs(acc, GAMMA, d_ref, y_f32=host(y)[:, rows])
 
 
+# ---------------------------------------------------------------------------
+# base-3 weights, five per byte
+# ---------------------------------------------------------------------------
+
+T3_PACK_SHAPES = [(1, 16), (3, 320), (5, 336), (17, 2560), (7, 4160), (640, 2560), (9, 28672)]
+
+
+@pytest.mark.parametrize("N,K", T3_PACK_SHAPES, ids=[f"N{n}K{k}" for n, k in T3_PACK_SHAPES])
+def test_pack_t3_parity(N, K):
+    """Packed bytes bit-exact against the oracle, from int8 ternary weights and
+    from fp32 weights (same gamma and ternary values as the I2_S packing)."""
+    bl = _bl()
+    say(f"pack_t3 N={N} K={K}")
+    t = W.ternary_drawn(300 + N + K, N, K, 0.4)
+    got = bl.pack_t3(dev(t))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), oracle.pack_t3(t))
+    w = W.weights_f32_normal(400 + N + K, N, K)
+    p3, g3 = bl.pack_t3(dev(w))
+    p2, g2 = bl.pack_i2s(dev(w))
+    torch.cuda.synchronize()
+    t_ref = oracle.ternarize_absmean(w)[0]
+    assert host(g3).view(np.uint32)[0] == host(g2).view(np.uint32)[0]
+    assert np.array_equal(host(p3), oracle.pack_t3(t_ref))
+
+
+T3_GEMV_CASES = [(1, 1, 16), (1, 5, 320), (1, 17, 336), (2, 33, 2560), (4, 100, 4160),
+                 (16, 64, 1296), (1, 640, 6912), (3, 300, 8192), (1, 129, 28672), (16, 40, 65536)]
+
+
+@pytest.mark.parametrize("M,N,K", T3_GEMV_CASES, ids=[f"M{m}N{n}K{k}" for m, n, k in T3_GEMV_CASES])
+def test_gemv_t3_parity(M, N, K):
+    """Every output type against the oracle, and byte-identical to bl_gemv on
+    the I2_S packing of the same weights."""
+    bl = _bl()
+    say(f"gemv_t3 M={M} N={N} K={K}")
+    x = W.activations_bf16(500 + M + N, M, K, outlier_frac=0.01, outlier_scale=20.0)
+    if M > 2:
+        x[1] = 0
+    t = W.ternary_drawn(600 + N + K, N, K, 0.4)
+    q, d = bl.quantize_act(dev_bf16(x))
+    p3 = bl.pack_t3(dev(t))
+    p2 = bl.pack_i2s(dev(t))
+    gamma = dev(np.array([GAMMA], np.float32))
+    q_ref, d_ref = oracle.quantize_act_absmax(x)
+    acc = oracle.mpgemm_acc(q_ref, t)
+    for ot in ("i32", "f32", "bf16"):
+        y3 = bl.gemv_t3(p3, gamma, q, d, out_dtype=ot)
+        y2 = bl.gemv(p2, gamma, q, d, out_dtype=ot)
+        torch.cuda.synchronize()
+        kw = {"i32": "y_i32", "f32": "y_f32", "bf16": "y_bf16"}[ot]
+        if ot != "f32" or 127 * K < 2 ** 24:
+            check_outputs(acc, GAMMA, d_ref, **{kw: host(y3)})
+        assert np.array_equal(host(y3).view(np.uint8), host(y2).view(np.uint8))
+
+
+def test_gemv_t3_empty_and_zero_k():
+    bl = _bl()
+    say("gemv_t3 empty / K = 0")
+    gamma = dev(np.array([GAMMA], np.float32))
+    q = torch.zeros((2, 0), dtype=torch.int8, device="cuda")
+    d = torch.ones(2, dtype=torch.float32, device="cuda")
+    p3 = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    y = bl.gemv_t3(p3, gamma, q, d, out_dtype="f32")
+    torch.cuda.synchronize()
+    assert host(y).shape == (2, 5) and not host(y).any()
+    y0 = bl.gemv_t3(torch.zeros((0, 64), dtype=torch.uint8, device="cuda"), gamma,
+                    torch.zeros((1, 16), dtype=torch.int8, device="cuda"), d[:1])
+    assert y0.shape == (1, 0)
+
+
 def test_decode_group_tokens_long_k():
     """Several tokens (quantize launch + GEMV over the codes) at the largest K."""
     bl = _bl()

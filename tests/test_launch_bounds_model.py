@@ -435,3 +435,45 @@ def test_decode1w_mfma_pairing():
         col = 0 if m < 8 else 1                       # column kept for this row
         b_chunk = 2 * h + (col & 1)                   # activation chunk of that column
         assert b_chunk == c
+
+
+# ---- base-3 GEMV ------------------------------------------------------------
+
+def t3_config(K):
+    """(WPB, U) of launch_gemv_t3."""
+    steps = lambda wpb: ((K + 319) // 320 + wpb - 1) // wpb
+    if steps(4) <= 2:
+        return 4, max(steps(4), 1)
+    if steps(8) <= 2:
+        return 8, 2
+    return 16, 2
+
+
+def t3_ranges(N, K, M):
+    WPB, U = t3_config(K)
+    nsteps = (K + 319) // 320
+    RBt = 64 * nsteps
+    length = (nsteps + WPB - 1) // WPB
+    for b, wk in itertools.product(range((N + 15) // 16), range(WPB)):
+        ja = min(wk * length, nsteps)
+        jb = min(ja + length, nsteps)
+        rows = np.minimum(b * 16 + R_OF, N - 1)
+        toks = np.minimum(R_OF, M - 1)
+        starts = list(range(ja, jb, 2 * U)) or [ja]
+        for j in starts:
+            for base in (j, j + U, j + 2 * U):
+                for u in range(U):
+                    step = max(min(base + u, jb - 1), 0)
+                    lo = rows * RBt + step * 64 + 16 * H_OF
+                    yield "packed", lo.min(), (lo + 16).max(), N * RBt
+                    for i in range(5):
+                        kk = np.minimum(step * 320 + 80 * H_OF + 16 * i, K - 16)
+                        lo = toks * K + kk
+                        yield "q", lo.min(), (lo + 16).max(), M * K
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 16, 1), (17, 336, 3), (100, 2560, 16), (40, 4160, 2),
+                                   (33, 6912, 1), (20, 28672, 4), (3, 65536, 16), (8, 1296, 1)])
+def test_t3_loads_in_bounds(N, K, M):
+    for buf, lo, hi, size in t3_ranges(N, K, M):
+        assert 0 <= lo and hi <= size, (buf, lo, hi, size)
