@@ -185,6 +185,37 @@ def decode_more(torch, bl, W, dev, stream):
     return out
 
 
+def t3_bench(torch, bl, W, dev, stream):
+    """Base-3 weights (five per byte, 1.6 bits per weight) against I2_S (2 bits
+    per weight) through the GEMV kernels of the same structure (int8 codes in,
+    one token): bl_gemv_t3 and bl_gemv, graph replays over copies of the
+    packed weights (>= 700 MB). Reported per format: microseconds per call,
+    GB/s of packed bytes and billions of weights per second."""
+    out = {}
+    for N, K in ((2560, 2560), (6912, 2560), (2560, 6912), (28672, 8192), (8192, 28672)):
+        t = torch.from_numpy(W.ternary_drawn(7 + N + K, N, K, 1.0 / 3.0)).to(dev)
+        p2, p3 = bl.pack_i2s(t), bl.pack_t3(t)
+        del t
+        x = torch.from_numpy(W.activations_bf16(9 + K, 1, K, 0.005, 50.0).view(np.int16)).to(dev)
+        q, d = bl.quantize_act(x.view(torch.bfloat16))
+        gam = torch.tensor([W.GAMMA_DRAWN], dtype=torch.float32, device=dev)
+        R = max(2, -(-700_000_000 // p3.numel()))
+        y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+        rec = {}
+        for name, p, fn in (("i2s", p2, bl.gemv), ("t3", p3, bl.gemv_t3)):
+            copies = [p] + [p.clone() for _ in range(R - 1)]
+            g = capture_fns(torch, stream, [(lambda c=c: fn(c, gam, q, d, out=y)) for c in copies])
+            us = replay_us(torch, stream, g, R, reps=10)
+            rec[name] = {"us": round(us, 3), "packed_bytes": p.numel(),
+                         "gbs": round(p.numel() / (us * 1e-6) / 1e9, 1),
+                         "gweights_s": round(N * K / (us * 1e-6) / 1e9, 1)}
+            del g, copies
+        out[f"N{N}_K{K}"] = rec
+        del p2, p3
+        torch.cuda.empty_cache()
+    return out
+
+
 def norm_bench(torch, bl, W, dev, stream):
     """Fused residual add + RMSNorm + per-token quantize (bl_rmsnorm_quant)
     on the prefill and decode shapes, against the same step done unfused
@@ -601,6 +632,8 @@ def main():
     if not args.no_extras:
         result["rmsnorm_quant"] = norm_bench(torch, bl, W, dev, stream)
         log(f"rmsnorm_quant: {result['rmsnorm_quant']}")
+        result["t3_gemv"] = t3_bench(torch, bl, W, dev, stream)
+        log(f"t3_gemv: {result['t3_gemv']}")
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
