@@ -185,6 +185,57 @@ def decode_more(torch, bl, W, dev, stream):
     return out
 
 
+def norm_layer_bench(torch, bl, W, dev, stream):
+    """The BitNet-2B-like decode layer (batch 1) with its two RMSNorms before
+    {q,k,v} and {gate,up} (residual add included): fused, 4 launches (two
+    bl_decode_norm_group, two bl_decode_group), against unfused, 9 launches
+    (bl_rmsnorm_quant, then one bl_gemv per projection of the normed input).
+    32 rotating layer copies, graph replays; us per layer and packed GB/s."""
+    cfg = W.CONFIGS[2]
+    by = {p.name: p for p in cfg.projs}
+    K = 2560
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    x1, r1, g1 = W.norm_inputs(2001, 1, K, cfg.outlier_frac, cfg.outlier_scale)
+    x2, r2, g2 = W.norm_inputs(2002, 1, K, cfg.outlier_frac, cfg.outlier_scale)
+    xo = W.activations_bf16(2003, 1, K, cfg.outlier_frac, cfg.outlier_scale)
+    xd = W.activations_bf16(2004, 1, 6912, cfg.outlier_frac, cfg.outlier_scale)
+    X1, R1, G1, X2, R2, G2, XO, XD = (t(a) for a in (x1, r1, g1, x2, r2, g2, xo, xd))
+    H1, H2 = torch.empty_like(X1), torch.empty_like(X2)
+    gam = torch.tensor([W.GAMMA_DRAWN], dtype=torch.float32, device=dev)
+    base = {n: bl.pack_i2s(torch.from_numpy(W.proj_inputs(cfg, by[n], 1, with_acts=False).w_tern).to(dev))
+            for n in by}
+    R = 32
+    copies = [{n: (p if r == 0 else p.clone()) for n, p in base.items()} for r in range(R)]
+    fused, unfused = [], []
+    q1 = torch.empty((1, K), dtype=torch.int8, device=dev)
+    d1 = torch.empty((1,), dtype=torch.float32, device=dev)
+    q2, d2 = torch.empty_like(q1), torch.empty_like(d1)
+    for c in copies:
+        prob = lambda n: dict(packed=c[n], gamma=gam)
+        fused += [bl.NormDecodeGroup([prob("q"), prob("k"), prob("v")], X1, G1, 1e-5, residual=R1, h_out=H1),
+                  bl.DecodeGroup([dict(prob("o"), x=XO)]),
+                  bl.NormDecodeGroup([prob("gate"), prob("up")], X2, G2, 1e-5, residual=R2, h_out=H2),
+                  bl.DecodeGroup([dict(prob("down"), x=XD)])]
+        ys = {n: torch.empty((1, by[n].N), dtype=torch.bfloat16, device=dev) for n in by}
+        unfused += [(lambda: bl.rmsnorm_quant(X1, G1, 1e-5, residual=R1, h_out=H1, q=q1, d=d1))]
+        unfused += [(lambda c=c, n=n, ys=ys: bl.gemv(c[n], gam, q1, d1, out=ys[n])) for n in ("q", "k", "v")]
+        unfused += [bl.DecodeGroup([dict(prob("o"), x=XO)])]
+        unfused += [(lambda: bl.rmsnorm_quant(X2, G2, 1e-5, residual=R2, h_out=H2, q=q2, d=d2))]
+        unfused += [(lambda c=c, n=n, ys=ys: bl.gemv(c[n], gam, q2, d2, out=ys[n])) for n in ("gate", "up")]
+        unfused += [bl.DecodeGroup([dict(prob("down"), x=XD)])]
+    out = {"layer": cfg.name, "packed_bytes": cfg.packed_bytes}
+    for name, fns in (("fused_4_launches", fused), ("unfused_9_launches", unfused)):
+        for f in fns[:9]:
+            f()
+        g = capture_fns(torch, stream, fns)
+        us = replay_us(torch, stream, g, 1, reps=10) / R
+        out[name] = {"us_per_layer": round(us, 3), "gbs": round(cfg.packed_bytes / (us * 1e-6) / 1e9, 1)}
+        del g
+    del copies, fused, unfused
+    torch.cuda.empty_cache()
+    return out
+
+
 def t3_bench(torch, bl, W, dev, stream):
     """Base-3 weights (five per byte, 1.6 bits per weight) against I2_S (2 bits
     per weight) through the GEMV kernels of the same structure (int8 codes in,
@@ -632,6 +683,8 @@ def main():
     if not args.no_extras:
         result["rmsnorm_quant"] = norm_bench(torch, bl, W, dev, stream)
         log(f"rmsnorm_quant: {result['rmsnorm_quant']}")
+        result["decode_layer_with_norms"] = norm_layer_bench(torch, bl, W, dev, stream)
+        log(f"decode layer with norms: {result['decode_layer_with_norms']}")
         result["t3_gemv"] = t3_bench(torch, bl, W, dev, stream)
         log(f"t3_gemv: {result['t3_gemv']}")
 

@@ -317,6 +317,27 @@ typedef struct bl_decode_problem {
 
 int bl_decode_group(const bl_decode_problem *problems, int count, int64_t M, void *stream);
 
+/*
+ * bl_decode_norm_group -- one token through the residual add, RMSNorm and the
+ * per-token quantizer, then up to 8 projections of the normalized token, in
+ * one launch.
+ * Defines: bl_rmsnorm_quant ([BE] "关键技术机制解析" §2 with [BN] Part A 2.3 /
+ * 4.1) composed with bl_gemv, fused as in [FF] "融合内核设计". Every problem
+ * reads the same x (bf16 [1][K], its x field) and has the same K; r (bf16
+ * [K] or NULL) is the residual, g (bf16 [K]) the norm weight, eps finite and
+ * >= 0. Each problem's y is bl_gemv's output for the codes and scale of
+ * y_norm = RMSNorm(h) * g, h = bf16(x + r); q and d, when given, receive those
+ * codes and scale; h_out (bf16 [K] or NULL) receives h. h_out must not
+ * overlap x or r (other blocks still read them while it is written).
+ * M is 1. K % 64 == 0 and K <= 32768; N, ytype, gamma and alignment as in
+ * bl_decode_group; g, r and h_out 16-byte aligned. The sum of squares runs in
+ * fp64 per K part, so as for bl_rmsnorm_quant a mean square within ~2^-40 of
+ * an fp32 rounding midpoint may round either way.
+ */
+int bl_decode_norm_group(const bl_decode_problem *problems, int count, const uint16_t *r,
+                         const uint16_t *g, float eps, uint16_t *h_out, void *stream);
+
+
 #ifdef __cplusplus
 }
 #endif

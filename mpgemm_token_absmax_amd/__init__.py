@@ -19,6 +19,8 @@ and streams only.
                                                     # GEMMs sharing one q, fewest launches
     ys          = decode_group([dict(packed=.., gamma=.., x=..), ...])
                                                     # fused quantize + GEMV, one launch
+    ys          = NormDecodeGroup([dict(packed=.., gamma=..), ...], x, g, eps, residual=r)()
+                                                    # + residual add and RMSNorm, one launch
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I
 __all__ = ["quantize_act", "quantize_act_tensor", "rmsnorm_quant", "pack_i2s", "pack_i2s_workspace",
            "pack_t3", "gemv_t3", "gemv", "gemm",
            "gemm_workspace", "gemm_group", "GemmGroup", "decode_group", "DecodeGroup",
+           "NormDecodeGroup",
            "BitLinearError", "status_string",
            "lib", "OUT_TYPES"]
 
@@ -363,6 +366,40 @@ class DecodeGroup:
     def __call__(self):
         check("bl_decode_group", lib().bl_decode_group(self._arr, len(self.problems), self.M,
                                                        _stream(self._device)))
+        return self.outputs
+
+
+class NormDecodeGroup(DecodeGroup):
+    """A prepared bl_decode_norm_group call: one token's residual add, RMSNorm
+    and quantize, then every problem's GEMV, in one launch.
+
+    x: bf16 [1][K], the input every problem reads; g: bf16 [K] norm weight;
+    residual: bf16 [1][K] or None; h_out: bf16 [1][K] or None (receives
+    bf16(x + residual); must not overlap x or residual). problems: dicts with
+    packed, gamma and optional y, q, d, out_dtype."""
+
+    def __init__(self, problems, x, g, eps: float, residual=None, h_out=None,
+                 out_dtype: str = "bf16"):
+        _need(x, "x", torch.bfloat16, 2)
+        if x.shape[0] != 1 or not x.is_contiguous():
+            raise ValueError("x must be one contiguous token [1][K]")
+        super().__init__([dict(p, x=x) for p in problems], out_dtype)
+        K = x.shape[1]
+        _need(g, "g", torch.bfloat16, 1)
+        if g.shape[0] != K or not g.is_contiguous():
+            raise ValueError("g must be contiguous [K]")
+        for t, name in ((residual, "residual"), (h_out, "h_out")):
+            if t is not None:
+                _need(t, name, torch.bfloat16, 2)
+                if tuple(t.shape) != (1, K) or not t.is_contiguous():
+                    raise ValueError(f"{name} must be contiguous [1][K]")
+        self.x, self.g, self.eps, self.residual, self.h_out = x, g, float(eps), residual, h_out
+
+    def __call__(self):
+        check("bl_decode_norm_group",
+              lib().bl_decode_norm_group(self._arr, len(self.problems), _ptr(self.residual),
+                                         _ptr(self.g), self.eps, _ptr(self.h_out),
+                                         _stream(self._device)))
         return self.outputs
 
 

@@ -229,6 +229,54 @@ int bl_gemm_group(const bl_gemm_problem* problems, int count, int64_t K, const i
   return hip_status(bl::launch_gemm_group(g, n, K, q, d, M, as_stream(stream)));
 }
 
+int bl_decode_norm_group(const bl_decode_problem* problems, int count, const uint16_t* r,
+                         const uint16_t* g, float eps, uint16_t* h_out, void* stream) {
+  if (count < 0 || count > bl::kMaxGroup) return BL_ERR_SHAPE;
+  if (!(eps >= 0.0f) || eps > 3.4028235e38f) return BL_ERR_SHAPE;
+  if (count == 0) return BL_OK;
+  if (!problems) return BL_ERR_NULL;
+  const uint16_t* x = problems[0].x;
+  const int64_t K = problems[0].K;
+  if (K <= 0 || K % 64 != 0 || K > 32768) return BL_ERR_SHAPE;
+  if (!x || !g) return BL_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(g, 16) || (r && !aligned(r, 16)) ||
+      (h_out && !aligned(h_out, 16)))
+    return BL_ERR_ALIGN;
+  if (h_out && (overlap_bf16(h_out, x, 1, K, K) || (r && overlap_bf16(h_out, r, 1, K, K))))
+    return BL_ERR_ALIAS;
+  bl::DecodeGroup gr{};
+  gr.M = 1;
+  for (int i = 0; i < count; ++i) {
+    const bl_decode_problem& p = problems[i];
+    if (p.x != x || p.K != K) return BL_ERR_SHAPE;   // one normalized input per group
+    if (p.N < 0) return BL_ERR_SHAPE;
+    if (p.ytype < BL_OUT_I32 || p.ytype > BL_OUT_BF16) return BL_ERR_DTYPE;
+    if (p.N == 0) continue;
+    if (!p.y || !p.packed || (p.ytype != BL_OUT_I32 && !p.gamma)) return BL_ERR_NULL;
+    if (!aligned(p.y, 16) || !aligned(p.packed, 16)) return BL_ERR_ALIGN;
+    if ((p.q && !aligned(p.q, 16)) || (p.d && !aligned(p.d, 4)) ||
+        (p.gamma && !aligned(p.gamma, 4)))
+      return BL_ERR_ALIGN;
+    bl::DecodeProblem& d = gr.p[gr.count++];
+    d.packed = p.packed;
+    d.gamma = p.gamma;
+    d.N = p.N;
+    d.K = K;
+    d.x = x;
+    d.ldx = K;
+    d.q = p.q;
+    d.d = p.d;
+    d.y = p.y;
+    d.ytype = p.ytype;
+  }
+  if (gr.count == 0) return BL_OK;
+  gr.nr = r;
+  gr.ng = g;
+  gr.nh = h_out;
+  gr.eps = eps;
+  return hip_status(bl::launch_decode_norm_group(gr, as_stream(stream)));
+}
+
 int bl_decode_group(const bl_decode_problem* problems, int count, int64_t M, void* stream) {
   if (count < 0 || count > bl::kMaxGroup || M < 0 || M > kGemvMaxM) return BL_ERR_SHAPE;
   if (count == 0 || M == 0) return BL_OK;

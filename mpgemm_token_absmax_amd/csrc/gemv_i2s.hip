@@ -87,11 +87,17 @@ __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_
 // exit at once.
 // WPB: waves per block (each takes 1/WPB of K), XR: 16-byte x chunks per lane
 // (covers len*32 chunks), U: steps per load batch.
-template <int WPB, int RTW, int XR, int U>
+// NORM: the residual add and RMSNorm of the token come first (the group's
+// nr, ng, eps, nh): each wave adds its part of r to its part of x, the block
+// sums the parts' fp64 sums of squares (one barrier), each wave normalizes
+// its part and the block takes the absmax of y (a second barrier); the codes
+// are those of y. The first block writes h (and q, d when asked).
+template <int WPB, int RTW, int XR, int U, bool NORM = false>
 __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int len_max) {
   extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][len_max*256]
   __shared__ v4i red[WPB - 1][RTW][kWave];
   __shared__ uint32_t wmax[WPB];
+  __shared__ double wss[NORM ? WPB : 1];
 
   const DecodeProblem& P = grp.p[blockIdx.y];
   const int64_t N = P.N;
@@ -109,6 +115,11 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   // share a counter and scalar loads complete out of order).
   asm volatile("" ::"s"(packed), "s"(xg), "s"(K), "s"(gptr), "s"(yp), "s"(qp), "s"(dp),
                "s"(ytype), "s"(len_max));
+  const uint16_t* nr = NORM ? grp.nr : nullptr;
+  const uint16_t* ng = NORM ? grp.ng : nullptr;
+  uint16_t* nh = NORM ? grp.nh : nullptr;
+  const float eps = NORM ? grp.eps : 0.0f;
+  if constexpr (NORM) asm volatile("" ::"s"(nr), "s"(ng), "s"(nh), "s"(eps));
   if (n0 >= N) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wk = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & (WPB - 1);   // K part
@@ -131,6 +142,18 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   uint4 xv[XR];
 #pragma unroll
   for (int u = 0; u < XR; ++u) xv[u] = xs[min(lane + u * kWave, clast)];
+  uint4 rv[NORM ? XR : 1], gv[NORM ? XR : 1];
+  if constexpr (NORM) {
+    const int cb = nch > 0 ? klo / 8 : 0;
+    if (nr) {
+#pragma unroll
+      for (int u = 0; u < XR; ++u)
+        rv[u] = reinterpret_cast<const uint4*>(nr)[cb + min(lane + u * kWave, clast)];
+    }
+#pragma unroll
+    for (int u = 0; u < XR; ++u)
+      gv[u] = reinterpret_cast<const uint4*>(ng)[cb + min(lane + u * kWave, clast)];
+  }
   // gamma by a vector load, issued with x (counted with the vector loads)
   const float gam = ytype ? __builtin_nontemporal_load(gptr) : 0.0f;
   const uint8_t* wrow[RTW];
@@ -157,17 +180,68 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. absmax of the row: quarter maxima, one barrier ----------------
-  uint32_t m = 0u;
+  float sq, dv;
+  float rinv = 0.0f;
+  if constexpr (NORM) {
+    // h = bf16(x + r), the fp64 sum of squares of the row (parts in wave order)
+    if (nr) {
 #pragma unroll
-  for (int u = 0; u < XR; ++u) m = max(m, lane + u * kWave < nch ? absmax8_bf16(xv[u]) : 0u);
-  m = wave_max_u32(m);
-  if (lane == 0) wmax[wk] = m;
-  __syncthreads();
+      for (int u = 0; u < XR; ++u) {
+        xv[u].x = add2_bf16(xv[u].x, rv[u].x);
+        xv[u].y = add2_bf16(xv[u].y, rv[u].y);
+        xv[u].z = add2_bf16(xv[u].z, rv[u].z);
+        xv[u].w = add2_bf16(xv[u].w, rv[u].w);
+      }
+    }
+    double ss = 0.0;
 #pragma unroll
-  for (int w = 0; w < WPB; ++w) m = max(m, wmax[w]);
-  const float mf = __uint_as_float(m << 16);
-  const float sq = m ? 127.0f / mf : 0.0f;
-  const float dv = m ? mf / 127.0f : 0.0f;
+    for (int u = 0; u < XR; ++u) {
+      if (lane + u * kWave < nch) {
+        ss = sumsq2_bf16(xv[u].x, ss);
+        ss = sumsq2_bf16(xv[u].y, ss);
+        ss = sumsq2_bf16(xv[u].z, ss);
+        ss = sumsq2_bf16(xv[u].w, ss);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    if (lane == 0) wss[wk] = ss;
+    __syncthreads();
+    double tot = wss[0];
+#pragma unroll
+    for (int w = 1; w < WPB; ++w) tot += wss[w];
+    rinv = norm_factor(tot, K, eps);
+    uint32_t mb = 0u;
+#pragma unroll
+    for (int u = 0; u < XR; ++u) {
+      float y[8];
+      norm8(xv[u], gv[u], rinv, y);
+      uint32_t m8 = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m8 = max(m8, absbits(y[i]));
+      mb = max(mb, lane + u * kWave < nch ? m8 : 0u);
+    }
+    mb = wave_max_u32(mb);
+    if (lane == 0) wmax[wk] = mb;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) mb = max(mb, wmax[w]);
+    const float mf = __uint_as_float(mb);
+    sq = mb ? 127.0f / mf : 0.0f;
+    dv = mb ? mf / 127.0f : 0.0f;
+  } else {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int u = 0; u < XR; ++u) m = max(m, lane + u * kWave < nch ? absmax8_bf16(xv[u]) : 0u);
+    m = wave_max_u32(m);
+    if (lane == 0) wmax[wk] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) m = max(m, wmax[w]);
+    const float mf = __uint_as_float(m << 16);
+    sq = m ? 127.0f / mf : 0.0f;
+    dv = m ? mf / 127.0f : 0.0f;
+  }
   if (first_block && wk == 0 && lane == 0 && dp) dp[0] = dv;
 
   // ---- 3. int8 codes of this quarter -> the wave's LDS region -----------
@@ -176,7 +250,15 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   for (int u = 0; u < XR; ++u) {
     const int c = lane + u * kWave;
     if (c < nch) {
-      const uint2 qv = quant8_bf16(xv[u], sq);
+      uint2 qv;
+      if constexpr (NORM) {
+        float y[8];
+        norm8(xv[u], gv[u], rinv, y);
+        qv = make_uint2(quant4_f32(&y[0], sq), quant4_f32(&y[4], sq));
+        if (first_block && nh) reinterpret_cast<uint4*>(nh + klo)[c] = xv[u];
+      } else {
+        qv = quant8_bf16(xv[u], sq);
+      }
       *reinterpret_cast<uint2*>(wact + 8 * c) = qv;
       if (write_q) *reinterpret_cast<uint2*>(qp + klo + 8 * c) = qv;
     }
@@ -532,7 +614,7 @@ __global__ void k_generic(const uint8_t* __restrict__ packed, const float* __res
   }
 }
 
-template <int WPB, int RTW, int XR, int U>
+template <int WPB, int RTW, int XR, int U, bool NORM = false>
 hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
   int64_t blocks = 0;
   for (int i = 0; i < g.count; ++i) {
@@ -541,7 +623,7 @@ hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
   }
   if (blocks == 0) return hipSuccess;
   const size_t lds = (size_t)WPB * len_max * 256;
-  hipLaunchKernelGGL((k_decode1<WPB, RTW, XR, U>), dim3((unsigned)blocks, (unsigned)g.count),
+  hipLaunchKernelGGL((k_decode1<WPB, RTW, XR, U, NORM>), dim3((unsigned)blocks, (unsigned)g.count),
                      dim3(WPB * kWave), lds, s, g, len_max);
   return hipGetLastError();
 }
@@ -694,6 +776,22 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
     }
   }
   return launch_gemvq(g, s);
+}
+
+hipError_t launch_decode_norm_group(DecodeGroup& g, hipStream_t s) {
+  // the same configurations as the one-token decode (every problem has K)
+  const int len4 = steps_per_wave(g, 4);
+  if (len4 <= 1) return launch_one_token<4, 1, 1, 1, true>(g, len4, s);
+  if (len4 == 2) return launch_one_token<4, 1, 1, 2, true>(g, len4, s);
+  if (len4 == 3) return launch_one_token<4, 1, 2, 3, true>(g, len4, s);
+  if (len4 == 4) return launch_one_token<4, 1, 2, 4, true>(g, len4, s);
+  const int len8 = steps_per_wave(g, 8);
+  if (len8 == 3) return launch_one_token<8, 1, 2, 3, true>(g, len8, s);
+  if (len8 == 4) return launch_one_token<8, 1, 2, 4, true>(g, len8, s);
+  if (len8 <= 8) return launch_one_token<8, 1, 4, 4, true>(g, len8, s);
+  const int len16 = steps_per_wave(g, 16);
+  if (len16 <= 8) return launch_one_token<16, 1, 4, 4, true>(g, len16, s);
+  return hipErrorInvalidValue;                      // K > 32768: rejected at the boundary
 }
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,

@@ -37,9 +37,19 @@ struct DecodeGroup {
   int M;
   int block0[kMaxGroup];      // first block of each problem (set by the launcher)
   DecodeProblem p[kMaxGroup];
+  // One-token groups with the residual add and RMSNorm folded in (every
+  // problem reads the same x and K): residual (or NULL), norm weight [K], h
+  // out (or NULL), eps.
+  const uint16_t* nr;
+  const uint16_t* ng;
+  uint16_t* nh;
+  float eps;
 };
 
 hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s);
+// M == 1, every problem with the same x and K (K % 64 == 0): h = x (+ r),
+// RMSNorm with g and eps, per-token quantize, then each problem's GEMV.
+hipError_t launch_decode_norm_group(DecodeGroup& g, hipStream_t s);
 // bf16 x -> q, d of every problem of a group (M tokens each), one launch.
 hipError_t launch_quantize_group(const DecodeGroup& g, hipStream_t s);
 

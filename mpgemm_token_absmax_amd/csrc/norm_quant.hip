@@ -43,65 +43,12 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   return s;
 }
 
-// Two packed bf16 sums: bf16_rne(fl32(x + r)) per half.
-__device__ __forceinline__ uint32_t add2_bf16(uint32_t x, uint32_t r) {
-  const float lo = __fadd_rn(__uint_as_float(x << 16), __uint_as_float(r << 16));
-  const float hi = __fadd_rn(__uint_as_float(x & 0xFFFF0000u), __uint_as_float(r & 0xFFFF0000u));
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
-}
-
-__device__ __forceinline__ double sumsq2_bf16(uint32_t w, double acc) {
-  const double lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
-  acc += lo * lo;    // exact product; one fp64 rounding per add
-  acc += hi * hi;
-  return acc;
-}
-
-// The mean square of a row from its fp64 sum of squares, and the factor
-// rinv = fl32(1/fl32(sqrt(fl32(ms + eps)))) (0 when ms + eps is 0).
-__device__ __forceinline__ float norm_factor(double sumsq, int64_t K, float eps) {
-  const float ms = (float)(sumsq / (double)K);
-  const float v = __fadd_rn(ms, eps);
-  if (!(v > 0.0f)) return 0.0f;
-  const float root = (float)__dsqrt_rn((double)v);
-  return (float)__ddiv_rn(1.0, (double)root);
-}
-
-__device__ __forceinline__ float norm1(uint32_t h_high, float rinv, uint32_t g_high) {
-  return __fmul_rn(__fmul_rn(__uint_as_float(h_high), rinv), __uint_as_float(g_high));
-}
-
-// int8 code of fp32 y: low byte of fl32(fl32(y*s) + 1.5*2^23); |y| <= m and
-// s = fl32(127/m) keep |fl32(y*s)| < 127.5, so it is rne(y*s) in [-127, 127].
-__device__ __forceinline__ uint32_t qbits_f32(float y, float s) {
-  return __float_as_uint(__fadd_rn(__fmul_rn(y, s), 12582912.0f));
-}
-
-// Four fp32 values -> four int8 codes packed little-endian.
-__device__ __forceinline__ uint32_t quant4_f32(const float* y, float s) {
-  const uint32_t a = __builtin_amdgcn_perm(qbits_f32(y[1], s), qbits_f32(y[0], s), 0x0C0C0400u);
-  const uint32_t b = __builtin_amdgcn_perm(qbits_f32(y[3], s), qbits_f32(y[2], s), 0x0C0C0400u);
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-
 // 16 bytes at a uniform base plus a 32-bit byte offset (one SGPR base and a
 // single VGPR offset per load, instead of a 64-bit address per load).
 __device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off);
 }
 
-// y of the 8 values of a 16-byte chunk (h and g as packed bf16 pairs).
-__device__ __forceinline__ void norm8(uint4 h, uint4 g, float rinv, float* y) {
-  const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
-  const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    y[2 * j] = norm1(hw[j] << 16, rinv, gw[j] << 16);
-    y[2 * j + 1] = norm1(hw[j] & 0xFFFF0000u, rinv, gw[j] & 0xFFFF0000u);
-  }
-}
-
-__device__ __forceinline__ uint32_t absbits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
 // Fast path. x, r and h_out are not __restrict__: h_out may be r or x itself
 // (every chunk is loaded before the same thread stores it). Registers: the x

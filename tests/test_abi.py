@@ -288,3 +288,29 @@ def test_t3_validation(lib):
     assert g(A16 + 8, B16, 8, 32, C16, D16, 1, E16, L.BL_OUT_BF16, None) == L.BL_ERR_ALIGN
     assert g(A16, B16, 8, 1 << 18, C16, D16, 1, E16, L.BL_OUT_F32, None) == L.BL_ERR_SHAPE
     assert g(None, None, 8, 32, None, None, 0, None, L.BL_OUT_BF16, None) == L.BL_OK     # M == 0
+
+
+def test_decode_norm_group_validation(lib):
+    f = lib.bl_decode_norm_group
+    P = L.DecodeProblem
+
+    def probs(*specs):
+        arr = (P * len(specs))()
+        for i, (N, K, x) in enumerate(specs):
+            arr[i] = P(A16 + 0x1000 * i, B16, N, K, x, K, None, None, 0x80000 + 0x1000 * i,
+                       L.BL_OUT_BF16)
+        return arr
+
+    X, G, R, H = 0x90000, 0xA0000, 0xB0000, 0xC0000
+    ok = probs((64, 256, X), (32, 256, X))
+    assert f(ok, 9, R, G, 1e-5, H, None) == L.BL_ERR_SHAPE
+    assert f(ok, 2, R, G, -1.0, H, None) == L.BL_ERR_SHAPE
+    assert f(ok, 2, R, None, 1e-5, H, None) == L.BL_ERR_NULL
+    assert f(probs((64, 256, X), (32, 512, X)), 2, R, G, 1e-5, H, None) == L.BL_ERR_SHAPE  # K differs
+    assert f(probs((64, 256, X), (32, 256, X + 0x400)), 2, R, G, 1e-5, H, None) == L.BL_ERR_SHAPE
+    assert f(probs((64, 96, X)), 1, R, G, 1e-5, H, None) == L.BL_ERR_SHAPE      # K % 64
+    assert f(probs((64, 32832, X)), 1, R, G, 1e-5, H, None) == L.BL_ERR_SHAPE   # K > 32768
+    assert f(probs((64, 256, X)), 1, R + 8, G, 1e-5, H, None) == L.BL_ERR_ALIGN
+    assert f(probs((64, 256, X)), 1, R, G, 1e-5, X + 16, None) == L.BL_ERR_ALIAS
+    assert f(probs((64, 256, X)), 1, R, G, 1e-5, R, None) == L.BL_ERR_ALIAS   # no in-place here
+    assert f(None, 0, None, None, 0.0, None, None) == L.BL_OK

@@ -748,6 +748,86 @@ def test_gemv_t3_empty_and_zero_k():
     assert y0.shape == (1, 0)
 
 
+NORM_GROUP_CASES = [
+    ("qkv_2b", [(2560, 2560), (640, 2560), (640, 2560)], True, 1e-5),
+    ("gate_up_2b", [(6912, 2560), (6912, 2560)], True, 1e-6),
+    ("down_2b_subnorm", [(2560, 6912)], False, 1e-5),
+    ("7b", [(4096, 4096), (11008, 4096)], True, 1e-5),
+    ("100b_q", [(8192, 8192), (1024, 8192)], True, 1e-5),
+    ("k32768_16waves", [(64, 32768), (17, 32768)], True, 0.0),
+    ("tiny", [(33, 64), (5, 64)], False, 1e-5),
+    ("k_tail", [(40, 4160)], True, 1e-5),
+]
+
+
+@pytest.mark.parametrize("name,shapes,res,eps", NORM_GROUP_CASES, ids=[c[0] for c in NORM_GROUP_CASES])
+def test_decode_norm_group_parity(name, shapes, res, eps):
+    """Residual add + RMSNorm + quantize + GEMV in one launch: h, q, d and
+    every output against the oracle, and byte-identical to bl_rmsnorm_quant
+    followed by bl_gemv (tokens whose mean square sits on an fp32 rounding
+    midpoint excepted, as for the fused norm)."""
+    bl = _bl()
+    K = shapes[0][1]
+    say(f"decode_norm_group {name}: shapes={shapes} residual={res} eps={eps}")
+    x, r, g = W.norm_inputs(1100 + K, 1, K, outlier_frac=0.01, outlier_scale=20.0)
+    if not res:
+        r = None
+    xd, gd = dev_bf16(x), dev_bf16(g)
+    rd = None if r is None else dev_bf16(r)
+    hd = torch.empty_like(xd) if res else None
+    probs, ts = [], []
+    for i, (N, _) in enumerate(shapes):
+        t = W.ternary_drawn(1200 + N + i, N, K, 0.4)
+        ts.append(t)
+        probs.append(dict(packed=bl.pack_i2s(dev(t)), gamma=dev(np.array([GAMMA], np.float32)),
+                          q=torch.empty((1, K), dtype=torch.int8, device="cuda"),
+                          d=torch.empty((1,), dtype=torch.float32, device="cuda"),
+                          out_dtype=("bf16", "f32", "i32")[i % 3]))
+    grp = bl.NormDecodeGroup(probs, xd, gd, eps, residual=rd, h_out=hd)
+    ys = grp()
+    h_ref, q_ref, d_ref, ms = oracle.rmsnorm_quant(x, r, g, eps, return_ms=True)
+    # the unfused path: fused norm kernel, then the GEMV over its codes
+    h2, q2, d2 = bl.rmsnorm_quant(xd, gd, eps, residual=rd)
+    torch.cuda.synchronize()
+    if res:
+        assert np.array_equal(host(hd), h_ref)
+    amb = bool(_near_f32_midpoint(ms)[0])
+    say(f"  near-midpoint mean square: {amb}")
+    for p, y, t in zip(grp.problems, ys, ts):
+        ot = p["out_dtype"]
+        if not amb:
+            assert np.array_equal(host(p["q"]), q_ref)
+            assert host(p["d"]).view(np.uint32)[0] == d_ref.view(np.uint32)[0]
+            acc = oracle.mpgemm_acc(q_ref, t)
+            kw = {"i32": "y_i32", "f32": "y_f32", "bf16": "y_bf16"}[ot]
+            check_outputs(acc, GAMMA, d_ref, **{kw: host(y)})
+            y2 = bl.gemv(p["packed"], p["gamma"], q2, d2, out_dtype=ot)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(y2).view(np.uint8), host(y).view(np.uint8))
+
+
+def test_decode_norm_group_graph_replay():
+    """Graph replays of the fused norm decode give the eager result every time."""
+    bl = _bl()
+    K = 2560
+    say("decode_norm_group graph replay")
+    x, r, g = W.norm_inputs(1300, 1, K)
+    t = W.ternary_drawn(1301, 640, K, 0.4)
+    grp = bl.NormDecodeGroup([dict(packed=bl.pack_i2s(dev(t)),
+                                   gamma=dev(np.array([GAMMA], np.float32)))],
+                             dev_bf16(x), dev_bf16(g), 1e-5, residual=dev_bf16(r))
+    ref = host(grp()[0]).copy()
+    s = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        grp()
+    for _ in range(3):
+        grp.outputs[0].zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(grp.outputs[0]), ref)
+
+
 def test_decode_group_tokens_long_k():
     """Several tokens (quantize launch + GEMV over the codes) at the largest K."""
     bl = _bl()
