@@ -521,6 +521,9 @@ GROUP_CASES = [
     (2048, 256, [1024, 1024, 8192], ["bf16", "bf16", "i32"]),
     (40, 260, [7, 64], ["f32", "i32"]),          # K % 64 != 0
     (9, 512, [50, 3], ["bf16", "f32"]),           # M <= 16
+    # two big problems of >= 32768 rows together: the 256x128-tile launch,
+    # each problem alone the 128x256 one
+    (300, 256, [16400, 16400], ["bf16", "i32"]),
 ]
 
 
