@@ -296,8 +296,10 @@ int bl_gemm_group(const bl_gemm_problem *problems, int count, int64_t K, const i
  *     rows of K values with row stride ldx (ldx >= K, ldx % 4 == 0), y [M][N]
  *     of type ytype; q (int8 [M][K]) and d (fp32 [M]) receive the quantized
  *     activations. At M == 1 they are optional (NULL: not written); at M > 1
- *     they are required (BL_ERR_NULL otherwise): the codes are staged there
- *     by a quantize pass inside the call, ahead of the GEMV launch.
+ *     they are required (BL_ERR_NULL otherwise). Up to 4 tokens (every
+ *     ldx % 8 == 0, K <= 32768) the GEMV launch quantizes and writes them
+ *     itself; otherwise the codes are staged there by a quantize pass inside
+ *     the call, ahead of the GEMV launch.
  *     K % 64 == 0 and K <= 65536 are required (BL_ERR_SHAPE otherwise);
  *     N == 0 problems are skipped. Outputs must not alias any
  *     input or each other.

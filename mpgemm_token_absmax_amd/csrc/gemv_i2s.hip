@@ -1,9 +1,9 @@
 // Decode-time ternary GEMV (1 <= M <= 16 tokens) on gfx950: the fused
 // one-token decode group (bf16 activations in: per-token absmax quantization,
 // GEMV and dequant in one launch for up to kMaxGroup independent projections),
-// the GEMV over int8 activations (bl_gemv, and decode groups of M > 1 tokens
-// after one grouped quantize launch), and the generic kernel for shapes off
-// the fast paths.
+// the same with the quantization in the kernel for 2..4 tokens, the GEMV over
+// int8 activations (bl_gemv, and larger decode groups after one grouped
+// quantize launch), and the generic kernel for shapes off the fast paths.
 //
 // Sources: "Bitnet.cpp: Efficient Edge Inference for Ternary LLMs" reading
 // notes, Part A 2.3 / 4.1 (I2_S: element-wise multiply-add over 2-bit ternary
@@ -37,6 +37,9 @@ namespace {
 // kernel (k_decode1w); smaller ones k_decode1, whose shorter steps spread a
 // small launch over more waves.
 constexpr int64_t kWideN = 8192;
+
+// One-token-style fused decode (quantize in the kernel) up to this many tokens.
+constexpr int kFusedTokens = 4;
 
 __device__ __forceinline__ void store_out(void* y, int ytype, int64_t idx, int acc, float c) {
   if (ytype == 0) {
@@ -326,6 +329,163 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
     const int64_t n = n0 + rt * 16 + 4 * h;
     if (n < N) store_quad(yp, ytype, N, 0, n, acc[rt], gam * dv);
   }
+}
+
+// Fused decode for 2..MT tokens: k_decode1 with every token's activations
+// quantized in the kernel (each wave its K part of each token; the block
+// combines the per-token part maxima with one barrier). The tokens' int8 rows
+// sit in the wave's LDS region at a stride of len_max*256 + 16 bytes, so the
+// 16 lanes of a fragment read spread over the banks; lane (n, h) reads token
+// n's fragments (token MT-1 for n >= MT: those output columns are dropped).
+// Tokens M..MT-1 repeat token M-1 (read, quantized, never stored).
+template <int WPB, int XR, int U, int MT>
+__global__ __launch_bounds__(WPB * kWave) void k_decodeT(DecodeGroup grp, int len_max) {
+  extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][MT][tstride]
+  __shared__ v4i red[WPB - 1][kWave];
+  __shared__ uint32_t wmax[MT][WPB];
+
+  const DecodeProblem& P = grp.p[blockIdx.y];
+  const int64_t N = P.N;
+  const int K = (int)P.K;
+  const uint8_t* __restrict__ packed = P.packed;
+  const uint16_t* __restrict__ xg = P.x;
+  const int64_t ldx = P.ldx;
+  const float* gptr = P.gamma;
+  void* yp = P.y;
+  int8_t* qp = P.q;
+  float* dp = P.d;
+  const int ytype = P.ytype;
+  const int M = grp.M;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  asm volatile("" ::"s"(packed), "s"(xg), "s"(K), "s"(ldx), "s"(gptr), "s"(yp), "s"(qp),
+               "s"(dp), "s"(ytype), "s"(M), "s"(len_max));
+  if (n0 >= N) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wk = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & (WPB - 1);
+  const int h = lane >> 4;
+  const int RB = K / 4;
+  const bool first_block = blockIdx.x == 0;
+  const int nsteps = (K + 255) / 256;
+  const int len = (nsteps + WPB - 1) / WPB;
+  const int ja = min(wk * len, nsteps);
+  const int jb = min(ja + len, nsteps);
+  const int klo = min(ja * 256, K);
+  const int khi = min(jb * 256, K);
+  const int nch = (khi - klo) / 8;
+  const int tstride = len_max * 256 + 16;
+  int8_t* wact = act + wk * MT * tstride;
+
+  // ---- 1. loads: this part of every token's x, then the first weight batch
+  const int cb = nch > 0 ? klo / 8 : 0;
+  const int clast = nch > 0 ? nch - 1 : 0;
+  uint4 xv[MT][XR];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const uint4* xs = reinterpret_cast<const uint4*>(xg + (int64_t)min(t, M - 1) * ldx) + cb;
+#pragma unroll
+    for (int u = 0; u < XR; ++u) xv[t][u] = xs[min(lane + u * kWave, clast)];
+  }
+  const float gam = ytype ? __builtin_nontemporal_load(gptr) : 0.0f;
+  int64_t row = n0 + (lane & 15);
+  row = row < N ? row : N - 1;
+  const uint8_t* wrow = packed + row * RB;
+  v4i wa[U], wb[U];
+  auto load_w = [&](v4i (&dst)[U], int j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int step = max(min(j + u, jb - 1), 0);
+      int off = step * 64 + 16 * h;
+      off = off < RB ? off : RB - 16;
+      dst[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow + off));
+    }
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(wa, ja);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. per-token absmax: part maxima, one barrier ---------------------
+  float sq[MT], dv[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int u = 0; u < XR; ++u) m = max(m, lane + u * kWave < nch ? absmax8_bf16(xv[t][u]) : 0u);
+    m = wave_max_u32(m);
+    if (lane == 0) wmax[t][wk] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) m = max(m, wmax[t][w]);
+    const float mf = __uint_as_float(m << 16);
+    sq[t] = m ? 127.0f / mf : 0.0f;
+    dv[t] = m ? mf / 127.0f : 0.0f;
+  }
+  if (first_block && wk == 0 && lane < M && dp) {
+    float dl = dv[0];
+#pragma unroll
+    for (int t = 1; t < MT; ++t) dl = lane == t ? dv[t] : dl;
+    dp[lane] = dl;
+  }
+
+  // ---- 3. int8 codes of this part of every token -> LDS ------------------
+  const bool write_q = first_block && qp;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+#pragma unroll
+    for (int u = 0; u < XR; ++u) {
+      const int c = lane + u * kWave;
+      if (c < nch) {
+        const uint2 qv = quant8_bf16(xv[t][u], sq[t]);
+        *reinterpret_cast<uint2*>(wact + t * tstride + 8 * c) = qv;
+        if (write_q && t < M) *reinterpret_cast<uint2*>(qp + (int64_t)t * K + klo + 8 * c) = qv;
+      }
+    }
+    for (int b = (khi - klo) + 16 * lane; b < (jb - ja) * 256; b += 16 * kWave)
+      *reinterpret_cast<v4i*>(wact + t * tstride + b) = v4i{0, 0, 0, 0};
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- 4. MFMA over this part's steps ------------------------------------
+  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
+  const int tok = min(lane & 15, MT - 1);
+  const int8_t* arow = wact + tok * tstride + 64 * h;
+  auto compute = [&](const v4i (&w)[U], int j) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j + u < jb) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const v4i b = *reinterpret_cast<const v4i*>(arow + (j + u - ja) * 256 + 16 * s);
+          v4i& a = (s & 1) ? acc1 : acc0;
+          a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][s]), b, a, 0, 0, 0);
+        }
+      }
+    }
+  };
+  for (int j = ja; j < jb; j += 2 * U) {
+    if (j + U < jb) load_w(wb, j + U);
+    compute(wa, j);
+    if (j + 2 * U < jb) load_w(wa, j + 2 * U);
+    if (j + U < jb) compute(wb, j + U);
+  }
+  v4i acc = acc0 + acc1;
+
+  // ---- 5. sum of the parts, dequant, store -------------------------------
+  if (wk > 0) red[wk - 1][lane] = acc;
+  __syncthreads();
+  if (wk > 0) return;
+#pragma unroll
+  for (int w = 0; w < WPB - 1; ++w) acc += red[w][lane];
+  const int n = lane & 15;                              // token of this lane's column
+  if (n >= M) return;
+  float dn = dv[0];
+#pragma unroll
+  for (int t = 1; t < MT; ++t) dn = n == t ? dv[t] : dn;
+  const int64_t r0 = n0 + 4 * h;
+  if (r0 < N) store_quad(yp, ytype, N, n, r0, acc, gam * dn);
 }
 
 // One-token fused decode for wide problems (N >= kWideN): the same quantize
@@ -642,6 +802,27 @@ hipError_t launch_one_token_w(DecodeGroup& g, int len_max, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int WPB, int XR, int U>
+hipError_t launch_tokens(DecodeGroup& g, int len_max, hipStream_t s) {
+  constexpr int MT = kFusedTokens;
+  int64_t blocks = 0;
+  for (int i = 0; i < g.count; ++i) {
+    const int64_t b = (g.p[i].N + 15) / 16;
+    blocks = b > blocks ? b : blocks;
+  }
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = (size_t)WPB * MT * (len_max * 256 + 16);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_decodeT<WPB, XR, U, MT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_decodeT<WPB, XR, U, MT>), dim3((unsigned)blocks, (unsigned)g.count),
+                     dim3(WPB * kWave), lds, s, g, len_max);
+  return hipGetLastError();
+}
+
 // Longest per-wave run of 512-weight steps in the group when WPB waves split K.
 int wide_steps_per_wave(const DecodeGroup& g, int wpb) {
   int len = 0;
@@ -762,6 +943,19 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
     const int len16 = steps_per_wave(g, 16);       // <= 16 for K <= 65536
     if (len16 <= 8) return launch_one_token<16, 1, 4, 4>(g, len16, s);
     return launch_one_token<16, 1, 8, 4>(g, len16, s);
+  }
+  bool tokens_ok = fused && g.M <= kFusedTokens;
+  for (int i = 0; i < g.count && tokens_ok; ++i)
+    tokens_ok = g.p[i].ldx % 8 == 0 && g.p[i].K <= 32768;
+  if (tokens_ok) {                                  // 2..4 tokens: quantize in the kernel
+    const int len4 = steps_per_wave(g, 4);
+    if (len4 <= 2) return launch_tokens<4, 1, 2>(g, len4, s);
+    if (len4 <= 4) return launch_tokens<4, 2, 4>(g, len4, s);
+    const int len8 = steps_per_wave(g, 8);
+    if (len8 <= 4) return launch_tokens<8, 2, 4>(g, len8, s);
+    if (len8 <= 8) return launch_tokens<8, 4, 4>(g, len8, s);
+    const int len16 = steps_per_wave(g, 16);       // <= 8 for K <= 32768
+    return launch_tokens<16, 4, 4>(g, len16, s);
   }
   if (fused) {
     // several tokens: one launch quantizes every problem's x into its q and

@@ -629,7 +629,7 @@ def _decode_group_case(bl, M, shapes, seed, with_qd=True, out_types=None):
     return grp
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16])
 def test_decode_group_parity(M):
     bl = _bl()
     _decode_group_case(bl, M, [(100, 320), (640, 2560), (33, 64), (2049, 256), (5, 6912)],
@@ -836,6 +836,38 @@ def test_decode_group_tokens_long_k():
     bl = _bl()
     _decode_group_case(bl, 2, [(3, 65536), (40, 64)], seed=79, out_types=["i32", "bf16"])
     _decode_group_case(bl, 16, [(17, 28672)], seed=80, out_types=["f32"])
+
+
+@pytest.mark.parametrize("pad", [8, 4])
+def test_decode_group_tokens_strided_x(pad):
+    """2..4 tokens with x rows further apart than K: a row stride that keeps
+    every row 16-byte aligned (pad 8) quantizes in the GEMV launch, pad 4 takes
+    the quantize launch + code GEMV; both against the oracle and the unfused
+    calls."""
+    bl = _bl()
+    for M, shapes, seed in ((3, [(100, 320), (640, 2560), (33, 6912)], 110),
+                            (4, [(2560, 2560), (7, 27648)], 111)):
+        say(f"decode_group strided x M={M} pad={pad} shapes={shapes}")
+        probs, refs = [], []
+        for i, (N, K) in enumerate(shapes):
+            x = W.activations_bf16(seed + 10 * i, M, K, outlier_frac=0.01, outlier_scale=20.0)
+            wide = np.zeros((M, K + pad), dtype=x.dtype)
+            wide[:, :K] = x
+            wide[:, K:] = x[:, :pad]                        # junk past K must be ignored
+            xd = dev_bf16(wide)[:, :K]
+            t = W.ternary_drawn(seed + 10 * i + 1, N, K, 0.4)
+            probs.append(dict(packed=bl.pack_i2s(dev(t)), gamma=dev(np.array([GAMMA], np.float32)),
+                              x=xd, out_dtype="f32",
+                              q=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                              d=torch.empty((M,), dtype=torch.float32, device="cuda")))
+            refs.append((x, t))
+        ys = bl.DecodeGroup(probs)()
+        torch.cuda.synchronize()
+        for p, y, (x, t) in zip(probs, ys, refs):
+            q_ref, d_ref = oracle.quantize_act_absmax(x)
+            assert np.array_equal(host(p["q"]), q_ref)
+            assert np.array_equal(host(p["d"]).view(np.uint32), d_ref.view(np.uint32))
+            check_outputs(oracle.mpgemm_acc(q_ref, t), GAMMA, d_ref, y_f32=host(y))
 
 
 def test_decode_group_chunked_k_and_no_qd():

@@ -477,3 +477,96 @@ def t3_ranges(N, K, M):
 def test_t3_loads_in_bounds(N, K, M):
     for buf, lo, hi, size in t3_ranges(N, K, M):
         assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def decodet_config(K):
+    """(WPB, XR, U, len) that launch_decode_group picks for a 2..4-token group
+    (every ldx % 8 == 0, K <= 32768) whose largest K is K."""
+    assert K <= 32768
+    len4 = steps_per_wave(K, 4)
+    if len4 <= 2:
+        return 4, 1, 2, len4
+    if len4 <= 4:
+        return 4, 2, 4, len4
+    len8 = steps_per_wave(K, 8)
+    if len8 <= 4:
+        return 8, 2, 4, len8
+    if len8 <= 8:
+        return 8, 4, 4, len8
+    len16 = steps_per_wave(K, 16)
+    assert len16 <= 8
+    return 16, 4, 4, len16
+
+
+MT = 4
+
+
+def decodet_ranges(N, K, M, ldx, group_kmax=None):
+    """Yield (buffer, lo, hi, size) of every global load and LDS access of
+    k_decodeT (MT = 4 token slots) for one problem of an M-token group."""
+    assert K % 64 == 0 and K >= 64 and 2 <= M <= MT and ldx >= K and ldx % 8 == 0
+    WPB, XR, U, len_max = decodet_config(K if group_kmax is None else group_kmax)
+    RB = K // 4
+    nsteps = (K + 255) // 256
+    length = (nsteps + WPB - 1) // WPB
+    assert length <= len_max
+    assert XR * WAVE * 8 >= length * 256
+    tstride = len_max * 256 + 16
+    assert tstride % 16 == 0
+    lds_total = WPB * MT * tstride
+    assert lds_total + (WPB - 1) * WAVE * 16 + MT * WPB * 4 <= 160 * 1024
+    xsize = 2 * ((M - 1) * ldx + K)
+    for b, wk in itertools.product(range((N + 15) // 16), range(WPB)):
+        n0 = b * 16
+        ja = min(wk * length, nsteps)
+        jb = min(ja + length, nsteps)
+        klo, khi = min(ja * 256, K), min(jb * 256, K)
+        nch = (khi - klo) // 8
+        cbase = klo // 8 if nch > 0 else 0
+        clast = nch - 1 if nch > 0 else 0
+        for t in range(MT):
+            for u in range(XR):
+                c = cbase + np.minimum(LANES + u * WAVE, clast)
+                base = 2 * min(t, M - 1) * ldx
+                assert base % 16 == 0
+                yield "x", base + (16 * c).min(), base + (16 * c + 16).max(), xsize
+        rows = np.minimum(n0 + R_OF, N - 1)
+        starts = list(range(ja, jb, 2 * U)) or [ja]
+        for j in starts:
+            for base in (j, j + U, j + 2 * U):
+                for u in range(U):
+                    step = max(min(base + u, jb - 1), 0)
+                    off = np.minimum(step * 64 + 16 * H_OF, RB - 16)
+                    lo = rows * RB + off
+                    yield "packed", lo.min(), (lo + 16).max(), N * RB
+        wbase = wk * MT * tstride
+        for t in range(MT):
+            tb = wbase + t * tstride
+            if nch > 0:
+                yield "lds", tb, tb + 8 * nch, lds_total
+            yield "lds", tb, tb + (jb - ja) * 256, lds_total
+            # a token's region never reaches the next one
+            assert (jb - ja) * 256 <= tstride - 16
+        if b == 0 and nch > 0:
+            for t in range(M):
+                yield "q", t * K + klo, t * K + klo + 8 * nch, M * K
+
+
+DECODET_SHAPES = [(1, 64, 2, 64), (5, 64, 4, 72), (100, 320, 3, 320), (2560, 2560, 4, 2560),
+                  (6912, 2560, 2, 2568), (2560, 6912, 4, 6912), (33, 16384, 3, 16384),
+                  (17, 4160, 4, 4168), (3, 1088, 2, 1088), (5, 11008, 4, 11008),
+                  (3, 28672, 4, 28672), (2, 32768, 3, 32768), (4, 27648, 2, 27648)]
+
+
+@pytest.mark.parametrize("N,K,M,ldx", DECODET_SHAPES,
+                         ids=[f"N{n}K{k}M{m}ld{l}" for n, k, m, l in DECODET_SHAPES])
+def test_decodet_loads_in_bounds(N, K, M, ldx):
+    for buf, lo, hi, size in decodet_ranges(N, K, M, ldx):
+        assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_decodet_group_len_max():
+    for K in (64, 320, 2560, 6912):
+        for kmax in (7168, 28672, 32768):
+            for buf, lo, hi, size in decodet_ranges(20, K, 4, K, group_kmax=kmax):
+                assert 0 <= lo and hi <= size, (buf, lo, hi, size)
