@@ -582,20 +582,25 @@ def main():
             x = to_dev(inps[0].x_bf16.view(np.int16)).view(torch.bfloat16)
             q = torch.empty((M5, K), dtype=torch.int8, device=dev)
             d = torch.empty((M5,), dtype=torch.float32, device=dev)
+            qs = torch.empty((M5,), dtype=torch.int32, device=dev)
             probs = [dict(packed=bl.pack_i2s(to_dev(inp.w_tern)),
                           gamma=to_dev(np.array([inp.gamma], np.float32)),
                           y=torch.empty((M5, by[n].N), dtype=torch.bfloat16, device=dev))
                      for n, inp in zip(names, inps)]
-            G.append(dict(names=names, x=x, q=q, d=d, group=bl.GemmGroup(probs, q, d),
+            # the quantizer also writes the token sums; the GEMMs take them
+            # (offset weights). `plain` is the same group without them.
+            G.append(dict(names=names, x=x, q=q, d=d, qs=qs,
+                          group=bl.GemmGroup(probs, q, d, qsum=qs),
+                          plain=bl.GemmGroup(probs, q, d),
                           ops=sum(2 * M5 * by[n].N * by[n].K for n in names)))
             del inps
         torch.cuda.synchronize()
 
-        def layer(gemm_only=False):
+        def layer(gemm_only=False, plain=False):
             for e in G:
                 if not gemm_only:
-                    bl.quantize_act(e["x"], e["q"], e["d"])
-                e["group"]()
+                    bl.quantize_act(e["x"], e["q"], e["d"], qsum=e["qs"])
+                e["plain" if plain else "group"]()
 
         layer()
         layer()
@@ -619,6 +624,12 @@ def main():
         torch.cuda.synchronize()
         ms_gemm = b0.elapsed_time(b1) / args.gemm_steps
         gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
+        b0.record()
+        for _ in range(args.gemm_steps):
+            layer(gemm_only=True, plain=True)
+        b1.record()
+        torch.cuda.synchronize()
+        gemm_tops_plain = ops / (b0.elapsed_time(b1) / args.gemm_steps * 1e-3) / 1e12
         # one activation scale per layer input (per tensor) instead of per token
         ws_t = torch.empty((max(16, int(bl.lib().bl_quantize_act_tensor_workspace(M5))),),
                            dtype=torch.uint8, device=dev)
@@ -626,13 +637,13 @@ def main():
         def quantize_all(per_tensor):
             for e in G:
                 if per_tensor:
-                    bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t)
+                    bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t, qsum=e["qs"])
                 else:
-                    bl.quantize_act(e["x"], e["q"], e["d"])
+                    bl.quantize_act(e["x"], e["q"], e["d"], qsum=e["qs"])
 
         def layer_pt():
             for e in G:
-                bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t)
+                bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t, qsum=e["qs"])
                 e["group"]()
 
         def timed(fn, n):
@@ -663,15 +674,18 @@ def main():
             ms = c0.elapsed_time(c1) / 3
             per_group["+".join(e["names"])] = round(e["ops"] / (ms * 1e-3) / 1e12, 1)
         log(f"prefill: {ms_layer:.3f} ms/layer ({tops:.1f} TOPS incl. quantize), "
-            f"GEMM only {gemm_tops:.1f} TOPS; per group {per_group}; per-tensor scale "
+            f"GEMM only {gemm_tops:.1f} TOPS ({gemm_tops_plain:.1f} without token sums); "
+            f"per group {per_group}; per-tensor scale "
             f"{tops_pt:.1f} TOPS; quantize per layer {us_q_tok:.1f} us per token, "
             f"{us_q_ten:.1f} us per tensor")
         result["gemm"] = {"workload": cfg5.name, "tokens": M5, "ops_per_layer": ops,
                           "ms_per_layer": round(ms_layer, 4), "tops": round(tops, 1),
                           "gemm_only_tops": round(gemm_tops, 1), "peak_tops": INT8_PEAK_TOPS,
                           "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                          "step": "per input: bl_quantize_act, then one bl_gemm_group for "
-                                  "{q,k,v}, {o}, {gate,up}, {down}",
+                          "gemm_only_tops_without_token_sums": round(gemm_tops_plain, 1),
+                          "step": "per input: bl_quantize_act (codes, scales and token sums), "
+                                  "then one bl_gemm_group for {q,k,v}, {o}, {gate,up}, {down} "
+                                  "(offset weights)",
                           "tops_per_group": per_group,
                           "tops_per_tensor_scale": round(tops_pt, 1),
                           "quantize_us_per_layer": {"per_token": round(us_q_tok, 1),

@@ -47,7 +47,7 @@
  *   4, 8 or 12 weights (b = 1, 2 or 3 bytes). Within a group of b bytes,
  *   weight o (0 <= o < 4b) is stored in byte (o mod b) at bits
  *   2*(o div b) .. 2*(o div b)+1. Code 00 = 0, 01 = +1, 10 = -1; 11 is never
- *   written (it decodes as 0). For a full group, shifting its little-endian
+ *   written (results over bytes that hold it are unspecified). For a full group, shifting its little-endian
  *   32-bit word right by 2i and masking 0x03030303 yields the codes of
  *   weights 4i .. 4i+3 in byte order.
  */
@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define BL_ABI_VERSION 1
+#define BL_ABI_VERSION 2
 
 /* Status codes returned by every call. */
 enum {
@@ -104,11 +104,15 @@ const char *bl_status_string(int status);
  * x:   bf16 bit patterns, [M] rows of K values, row stride ldx elements
  *      (ldx >= K, ldx % 4 == 0).
  * q:   int8 [M][K], row stride K.     d: fp32 [M].
+ * qsum: NULL, or int32 [M] (4-byte aligned) that receives the exact token
+ *   sums qsum[t] = sum_k q[t][k] (needs 127*K <= INT32_MAX). Passed on to
+ *   bl_gemm / bl_gemm_group they let the GEMM run on offset weights; the
+ *   quantizer computes them from the codes it already holds.
  * Inputs must be finite; rows whose absmax is below 2^-120 (where 127/m
- * overflows fp32) give unspecified q. K == 0 writes d[:] = 0.
+ * overflows fp32) give unspecified q. K == 0 writes d[:] = 0 (and qsum[:] = 0).
  */
 int bl_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
-                    int8_t *q, float *d, void *stream);
+                    int8_t *q, float *d, int32_t *qsum, void *stream);
 
 /*
  * bl_quantize_act_tensor_workspace -- bytes of workspace bl_quantize_act_tensor
@@ -124,13 +128,14 @@ size_t bl_quantize_act_tensor_workspace(int64_t M);
  *   m = max over every t, k of |x[t][k]|; if m == 0: q = 0 and d[:] = 0; else
  *   s = fl32(127 / m), q[t][k] = clamp(rne(fl32(x[t][k] * s)), -127, 127), and
  *   every d[t] = fl32(m / 127) (so bl_gemv / bl_gemm apply it unchanged).
- * Arguments as bl_quantize_act, plus a workspace of ws_bytes bytes (>=
+ * Arguments as bl_quantize_act (qsum included), plus a workspace of ws_bytes bytes (>=
  * bl_quantize_act_tensor_workspace(M), 16-byte aligned; not needed when
  * K == 0): it receives the row maxima between the two launches the call
  * enqueues (row maxima, then quantize with the tensor's maximum).
  */
 int bl_quantize_act_tensor(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
-                           int8_t *q, float *d, void *ws, size_t ws_bytes, void *stream);
+                           int8_t *q, float *d, int32_t *qsum, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /*
  * bl_rmsnorm_quant -- residual add + RMSNorm fused with the per-token absmax
@@ -152,14 +157,15 @@ int bl_quantize_act_tensor(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  * x, r: bf16 [M][K] row stride ldx (r may be NULL); g: bf16 [K];
  * h_out: bf16 [M][K] row stride ldx, or NULL (not written); it may be r or x
  * itself (in-place update of the residual stream) but must not otherwise
- * overlap them; q: int8 [M][K] (row stride K); d: fp32 [M]. eps: finite,
+ * overlap them; q: int8 [M][K] (row stride K); d: fp32 [M]; qsum: NULL or the
+ * token sums of q, as in bl_quantize_act. eps: finite,
  * >= 0. Inputs must be finite, and neither ms_t nor y may overflow fp32
  * (|h| below about 1.8e19; codes are unspecified otherwise). K % 4 == 0, ldx >= K, ldx % 4 == 0; x, r, g, h_out
- * and q 16-byte aligned. K == 0: d[:] = 0. One launch.
+ * and q 16-byte aligned. K == 0: d[:] = 0 (and qsum[:] = 0). One launch.
  */
 int bl_rmsnorm_quant(const uint16_t *x, const uint16_t *r, const uint16_t *g, float eps,
                      int64_t M, int64_t K, int64_t ldx, uint16_t *h_out, int8_t *q,
-                     float *d, void *stream);
+                     float *d, int32_t *qsum, void *stream);
 
 /*
  * bl_pack_i2s_workspace -- bytes of workspace bl_pack_i2s needs for an
@@ -248,11 +254,18 @@ size_t bl_gemm_workspace(int64_t M, int64_t N, int64_t K);
  * Defines: as bl_gemv ([BN] Part A 2.3 / 4.1); the pages leave prefill
  * unoptimized ([BN] 4.4), so this is the dense contraction on matrix cores.
  * Same arguments and results as bl_gemv, plus a workspace of ws_bytes
- * (>= bl_gemm_workspace(M, N, K); may be NULL when that is 0).
+ * (>= bl_gemm_workspace(M, N, K); may be NULL when that is 0) and qsum:
+ *   qsum: NULL, or int32 [M] (4-byte aligned) holding the token sums
+ *     qsum[t] = sum_k q[t][k] of exactly this q (as bl_quantize_act or
+ *     bl_rmsnorm_quant write them; they are not checked). With them the
+ *     matrix cores get the weights plus one, in {0, 1, 2}, and the kernel
+ *     subtracts qsum[t] from each accumulator: the same exact acc, computed
+ *     with operands that switch fewer bits, which keeps the power-limited
+ *     clock higher. Results are bit-identical with and without qsum.
  */
 int bl_gemm(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
-            const int8_t *q, const float *d, int64_t M, void *y, int ytype,
-            void *ws, size_t ws_bytes, void *stream);
+            const int8_t *q, const float *d, const int32_t *qsum, int64_t M, void *y,
+            int ytype, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * bl_gemm_problem / bl_gemm_group -- several BitLinear GEMMs over the SAME
@@ -263,7 +276,8 @@ int bl_gemm(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
  *     the call only; every pointer inside is a device pointer.
  *   per problem: packed uint8 [N][K/4], gamma (device, 1 float), y [M][N] of
  *     type ytype (see the output enum), row stride N; N == 0 is skipped.
- *   shared: K (K % 4 == 0), q int8 [M][K], d fp32 [M], M >= 0 tokens.
+ *   shared: K (K % 4 == 0), q int8 [M][K], d fp32 [M], qsum (NULL or the
+ *     token sums of q, as in bl_gemm), M >= 0 tokens.
  * Each y is bit-identical to what bl_gemm gives for that problem alone.
  * Validation is bl_gemm's, problem by problem; nothing is launched when any
  * problem fails it. Outputs must not alias any input or each other.
@@ -277,7 +291,7 @@ typedef struct bl_gemm_problem {
 } bl_gemm_problem;
 
 int bl_gemm_group(const bl_gemm_problem *problems, int count, int64_t K, const int8_t *q,
-                  const float *d, int64_t M, void *stream);
+                  const float *d, const int32_t *qsum, int64_t M, void *stream);
 
 /*
  * bl_decode_problem / bl_decode_group -- fused decode BitLinear for a group

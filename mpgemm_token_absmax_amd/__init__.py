@@ -57,8 +57,21 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int):
         raise ValueError(f"{name} must be {ndim}-D")
 
 
-def quantize_act(x: torch.Tensor, q: torch.Tensor | None = None, d: torch.Tensor | None = None):
-    """x: bf16 [M][K] (row stride x.stride(0)) -> (q int8 [M][K], d fp32 [M])."""
+def _sums(qsum, with_sums, M, device):
+    """The token-sum output buffer: the given one, a new int32 [M], or None."""
+    if qsum is not None:
+        _need(qsum, "qsum", torch.int32, 1)
+        if qsum.shape[0] != M or not qsum.is_contiguous():
+            raise ValueError("qsum must be a contiguous int32 [M]")
+        return qsum
+    return torch.empty((M,), dtype=torch.int32, device=device) if with_sums else None
+
+
+def quantize_act(x: torch.Tensor, q: torch.Tensor | None = None, d: torch.Tensor | None = None,
+                 qsum: torch.Tensor | None = None, with_sums: bool = False):
+    """x: bf16 [M][K] (row stride x.stride(0)) -> (q int8 [M][K], d fp32 [M]),
+    plus qsum int32 [M] (the token sums of q, for gemm / gemm_group) when
+    with_sums is set or a qsum buffer is given."""
     _need(x, "x", torch.bfloat16, 2)
     if x.stride(1) != 1:
         raise ValueError("x rows must be contiguous")
@@ -67,15 +80,17 @@ def quantize_act(x: torch.Tensor, q: torch.Tensor | None = None, d: torch.Tensor
         q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if d is None:
         d = torch.empty((M,), dtype=torch.float32, device=x.device)
+    qs = _sums(qsum, with_sums, M, x.device)
     check("bl_quantize_act", lib().bl_quantize_act(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d),
-                                                   _stream(x.device)))
-    return q, d
+                                                   _ptr(qs), _stream(x.device)))
+    return (q, d) if qs is None else (q, d, qs)
 
 
 def quantize_act_tensor(x: torch.Tensor, q: torch.Tensor | None = None,
-                        d: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                        d: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        qsum: torch.Tensor | None = None, with_sums: bool = False):
     """x: bf16 [M][K] -> (q int8 [M][K], d fp32 [M]) with ONE scale for the
-    whole tensor (every d[t] equal)."""
+    whole tensor (every d[t] equal); qsum as in quantize_act."""
     _need(x, "x", torch.bfloat16, 2)
     if x.stride(1) != 1:
         raise ValueError("x rows must be contiguous")
@@ -87,20 +102,23 @@ def quantize_act_tensor(x: torch.Tensor, q: torch.Tensor | None = None,
     nws = int(lib().bl_quantize_act_tensor_workspace(M))
     if workspace is None:
         workspace = torch.empty((max(nws, 16),), dtype=torch.uint8, device=x.device)
+    qs = _sums(qsum, with_sums, M, x.device)
     check("bl_quantize_act_tensor",
-          lib().bl_quantize_act_tensor(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d),
+          lib().bl_quantize_act_tensor(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d), _ptr(qs),
                                        _ptr(workspace), workspace.numel(), _stream(x.device)))
-    return q, d
+    return (q, d) if qs is None else (q, d, qs)
 
 
 def rmsnorm_quant(x: torch.Tensor, g: torch.Tensor, eps: float, residual: torch.Tensor | None = None,
                   h_out: torch.Tensor | None = None, q: torch.Tensor | None = None,
-                  d: torch.Tensor | None = None, write_h: bool = True):
+                  d: torch.Tensor | None = None, write_h: bool = True,
+                  qsum: torch.Tensor | None = None, with_sums: bool = False):
     """Residual add + RMSNorm + per-token absmax int8 in one kernel.
 
     x, residual: bf16 [M][K] with the same row stride; g: bf16 [K]. Returns
     (h, q, d): h = bf16(x + residual) (x itself without a residual; None when
-    write_h is False and no h_out is given), q int8 [M][K], d fp32 [M].
+    write_h is False and no h_out is given), q int8 [M][K], d fp32 [M]; and
+    qsum int32 [M] as a fourth item when with_sums is set or qsum is given.
     h_out may be residual itself (in-place update of the residual stream).
     """
     _need(x, "x", torch.bfloat16, 2)
@@ -121,11 +139,12 @@ def rmsnorm_quant(x: torch.Tensor, g: torch.Tensor, eps: float, residual: torch.
         q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if d is None:
         d = torch.empty((M,), dtype=torch.float32, device=x.device)
+    qs = _sums(qsum, with_sums, M, x.device)
     check("bl_rmsnorm_quant",
           lib().bl_rmsnorm_quant(_ptr(x), _ptr(residual), _ptr(g), float(eps), M, K, x.stride(0),
-                                 _ptr(h_out), _ptr(q), _ptr(d), _stream(x.device)))
+                                 _ptr(h_out), _ptr(q), _ptr(d), _ptr(qs), _stream(x.device)))
     h = h_out if h_out is not None else (x if residual is None and write_h else None)
-    return h, q, d
+    return (h, q, d) if qs is None else (h, q, d, qs)
 
 
 def pack_i2s_workspace(N: int, K: int) -> int:
@@ -247,15 +266,26 @@ def gemm_workspace(M: int, N: int, K: int) -> int:
     return int(lib().bl_gemm_workspace(M, N, K))
 
 
+def _qsum_in(qsum, M):
+    if qsum is not None:
+        _need(qsum, "qsum", torch.int32, 1)
+        if qsum.shape[0] != M or not qsum.is_contiguous():
+            raise ValueError("qsum must be a contiguous int32 [M]")
+    return qsum
+
+
 def gemm(packed: torch.Tensor, gamma: torch.Tensor, q: torch.Tensor, d: torch.Tensor,
          out_dtype: str = "bf16", out: torch.Tensor | None = None,
-         workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y[M][N] for any M (prefill path, int8 MFMA)."""
+         workspace: torch.Tensor | None = None, qsum: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M][N] for any M (prefill path, int8 MFMA). qsum: the token sums of q
+    (from quantize_act(..., with_sums=True)); with them the kernel runs on
+    offset weights, same results."""
     N, K, M, ytype, out = _matmul_args(packed, gamma, q, d, out, out_dtype)
+    qsum = _qsum_in(qsum, M)
     nws = gemm_workspace(M, N, K)
     if nws and workspace is None:
         workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
-    check("bl_gemm", lib().bl_gemm(_ptr(packed), _ptr(gamma), N, K, _ptr(q), _ptr(d), M,
+    check("bl_gemm", lib().bl_gemm(_ptr(packed), _ptr(gamma), N, K, _ptr(q), _ptr(d), _ptr(qsum), M,
                                    _ptr(out), ytype, _ptr(workspace),
                                    0 if workspace is None else workspace.numel(),
                                    _stream(q.device)))
@@ -270,12 +300,14 @@ class GemmGroup:
     problems: list of dicts with keys packed (uint8 [N][K/4]), gamma (fp32 [1])
     and optional y (output [M][N]) and out_dtype."""
 
-    def __init__(self, problems, q: torch.Tensor, d: torch.Tensor, out_dtype: str = "bf16"):
+    def __init__(self, problems, q: torch.Tensor, d: torch.Tensor, out_dtype: str = "bf16",
+                 qsum: torch.Tensor | None = None):
         if not 1 <= len(problems) <= MAX_GROUP:
             raise ValueError(f"1..{MAX_GROUP} problems per group")
         _need(q, "q", torch.int8, 2)
         _need(d, "d", torch.float32, 1)
         M, K = q.shape
+        self.qsum = _qsum_in(qsum, M)
         arr = (GemmProblem * len(problems))()
         self.problems = []
         for i, p in enumerate(problems):
@@ -304,15 +336,17 @@ class GemmGroup:
 
     def __call__(self):
         check("bl_gemm_group", lib().bl_gemm_group(self._arr, len(self.problems), self.K,
-                                                   self.q.data_ptr(), self.d.data_ptr(), self.M,
+                                                   self.q.data_ptr(), self.d.data_ptr(),
+                                                   _ptr(self.qsum), self.M,
                                                    _stream(self.q.device)))
         return self.outputs
 
 
-def gemm_group(problems, q: torch.Tensor, d: torch.Tensor, out_dtype: str = "bf16"):
-    """GEMMs of several projections over the same quantized input q, d.
-    Returns the list of outputs y."""
-    return GemmGroup(problems, q, d, out_dtype)()
+def gemm_group(problems, q: torch.Tensor, d: torch.Tensor, out_dtype: str = "bf16",
+               qsum: torch.Tensor | None = None):
+    """GEMMs of several projections over the same quantized input q, d
+    (qsum: optional token sums of q, as in gemm). Returns the list of outputs y."""
+    return GemmGroup(problems, q, d, out_dtype, qsum)()
 
 
 class DecodeGroup:

@@ -71,15 +71,15 @@ def _declare(lib):
     lib.bl_status_string.restype = ctypes.c_char_p
     lib.bl_status_string.argtypes = [INT]
     lib.bl_quantize_act.restype = INT
-    lib.bl_quantize_act.argtypes = [P, I64, I64, I64, P, P, P]
+    lib.bl_quantize_act.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.bl_pack_i2s_workspace.restype = SZ
     lib.bl_quantize_act_tensor_workspace.restype = SZ
     lib.bl_quantize_act_tensor_workspace.argtypes = [I64]
     lib.bl_quantize_act_tensor.restype = INT
-    lib.bl_quantize_act_tensor.argtypes = [P, I64, I64, I64, P, P, P, SZ, P]
+    lib.bl_quantize_act_tensor.argtypes = [P, I64, I64, I64, P, P, P, P, SZ, P]
     lib.bl_pack_i2s_workspace.argtypes = [I64, I64]
     lib.bl_rmsnorm_quant.restype = INT
-    lib.bl_rmsnorm_quant.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P, P, P]
+    lib.bl_rmsnorm_quant.argtypes = [P, P, P, ctypes.c_float, I64, I64, I64, P, P, P, P, P]
     lib.bl_pack_i2s.restype = INT
     lib.bl_pack_i2s.argtypes = [P, INT, I64, I64, P, P, P, SZ, P]
     lib.bl_pack_t3_row_bytes.restype = SZ
@@ -93,9 +93,9 @@ def _declare(lib):
     lib.bl_gemm_workspace.restype = SZ
     lib.bl_gemm_workspace.argtypes = [I64, I64, I64]
     lib.bl_gemm.restype = INT
-    lib.bl_gemm.argtypes = [P, P, I64, I64, P, P, I64, P, INT, P, SZ, P]
+    lib.bl_gemm.argtypes = [P, P, I64, I64, P, P, P, I64, P, INT, P, SZ, P]
     lib.bl_gemm_group.restype = INT
-    lib.bl_gemm_group.argtypes = [ctypes.POINTER(GemmProblem), INT, I64, P, P, I64, P]
+    lib.bl_gemm_group.argtypes = [ctypes.POINTER(GemmProblem), INT, I64, P, P, P, I64, P]
     lib.bl_decode_group.restype = INT
     lib.bl_decode_group.argtypes = [ctypes.POINTER(DecodeProblem), INT, I64, P]
     lib.bl_decode_norm_group.restype = INT

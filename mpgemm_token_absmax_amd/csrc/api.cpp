@@ -56,15 +56,15 @@ const char* bl_status_string(int status) {
 }
 
 int bl_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* d,
-                    void* stream) {
+                    int32_t* qsum, void* stream) {
   if (M < 0 || K < 0 || K % 4 != 0 || ldx < K) return BL_ERR_SHAPE;
   if (M == 0) return BL_OK;
   if (!d || (K > 0 && (!x || !q))) return BL_ERR_NULL;
   if (K > 0 && ldx % 4 != 0) return BL_ERR_ALIGN;
-  if (!aligned(d, 4)) return BL_ERR_ALIGN;
+  if (!aligned(d, 4) || !aligned(qsum, 4)) return BL_ERR_ALIGN;
   if (K > 0 && (!aligned(x, 16) || !aligned(q, 16))) return BL_ERR_ALIGN;
-  if (M > INT32_MAX) return BL_ERR_SHAPE;
-  return hip_status(bl::launch_quantize_act(x, M, K, ldx, q, d, as_stream(stream)));
+  if (M > INT32_MAX || (qsum && 127 * K > INT32_MAX)) return BL_ERR_SHAPE;
+  return hip_status(bl::launch_quantize_act(x, M, K, ldx, q, d, qsum, as_stream(stream)));
 }
 
 size_t bl_quantize_act_tensor_workspace(int64_t M) {
@@ -73,17 +73,17 @@ size_t bl_quantize_act_tensor_workspace(int64_t M) {
 }
 
 int bl_quantize_act_tensor(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
-                           float* d, void* ws, size_t ws_bytes, void* stream) {
+                           float* d, int32_t* qsum, void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || K < 0 || K % 4 != 0 || ldx < K) return BL_ERR_SHAPE;
   if (M == 0) return BL_OK;
   if (!d || (K > 0 && (!x || !q))) return BL_ERR_NULL;
   if (K > 0 && ldx % 4 != 0) return BL_ERR_ALIGN;
-  if (!aligned(d, 4)) return BL_ERR_ALIGN;
+  if (!aligned(d, 4) || !aligned(qsum, 4)) return BL_ERR_ALIGN;
   if (K > 0 && (!aligned(x, 16) || !aligned(q, 16))) return BL_ERR_ALIGN;
-  if (M > INT32_MAX) return BL_ERR_SHAPE;
+  if (M > INT32_MAX || (qsum && 127 * K > INT32_MAX)) return BL_ERR_SHAPE;
   if (K > 0 && (!ws || ws_bytes < bl_quantize_act_tensor_workspace(M))) return BL_ERR_WORKSPACE;
   if (K > 0 && !aligned(ws, 16)) return BL_ERR_ALIGN;
-  return hip_status(bl::launch_quantize_act_tensor(x, M, K, ldx, q, d,
+  return hip_status(bl::launch_quantize_act_tensor(x, M, K, ldx, q, d, qsum,
                                                    static_cast<uint32_t*>(ws), as_stream(stream)));
 }
 
@@ -100,13 +100,13 @@ bool overlap_bf16(const uint16_t* a, const uint16_t* b, int64_t M, int64_t K, in
 
 int bl_rmsnorm_quant(const uint16_t* x, const uint16_t* r, const uint16_t* g, float eps,
                      int64_t M, int64_t K, int64_t ldx, uint16_t* h_out, int8_t* q, float* d,
-                     void* stream) {
+                     int32_t* qsum, void* stream) {
   if (M < 0 || K < 0 || K % 4 != 0 || ldx < K) return BL_ERR_SHAPE;
   if (!(eps >= 0.0f) || eps > 3.4028235e38f) return BL_ERR_SHAPE;     // NaN, inf, < 0
   if (M == 0) return BL_OK;
   if (!d || (K > 0 && (!x || !g || !q))) return BL_ERR_NULL;
-  if (M > INT32_MAX) return BL_ERR_SHAPE;
-  if (!aligned(d, 4)) return BL_ERR_ALIGN;
+  if (M > INT32_MAX || (qsum && 127 * K > INT32_MAX)) return BL_ERR_SHAPE;
+  if (!aligned(d, 4) || !aligned(qsum, 4)) return BL_ERR_ALIGN;
   if (K > 0) {
     if (ldx % 4 != 0) return BL_ERR_ALIGN;
     if (!aligned(x, 16) || !aligned(g, 16) || !aligned(q, 16)) return BL_ERR_ALIGN;
@@ -114,7 +114,7 @@ int bl_rmsnorm_quant(const uint16_t* x, const uint16_t* r, const uint16_t* g, fl
     if (h_out && h_out != x && overlap_bf16(h_out, x, M, K, ldx)) return BL_ERR_ALIAS;
     if (h_out && r && h_out != r && overlap_bf16(h_out, r, M, K, ldx)) return BL_ERR_ALIAS;
   }
-  return hip_status(bl::launch_rmsnorm_quant(x, r, g, eps, M, K, ldx, h_out, q, d,
+  return hip_status(bl::launch_rmsnorm_quant(x, r, g, eps, M, K, ldx, h_out, q, d, qsum,
                                              as_stream(stream)));
 }
 
@@ -199,21 +199,24 @@ size_t bl_gemm_workspace(int64_t M, int64_t N, int64_t K) {
 }
 
 int bl_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, const int8_t* q,
-            const float* d, int64_t M, void* y, int ytype, void* ws, size_t ws_bytes,
-            void* stream) {
+            const float* d, const int32_t* qsum, int64_t M, void* y, int ytype, void* ws,
+            size_t ws_bytes, void* stream) {
   const int st = check_matmul(packed, gamma, N, K, q, d, M, y, ytype);
   if (st != BL_OK || M == 0 || N == 0) return st;
+  if (!aligned(qsum, 4)) return BL_ERR_ALIGN;
   if (ws_bytes < bl_gemm_workspace(M, N, K)) return BL_ERR_WORKSPACE;
   (void)ws;
   if (N > (int64_t)UINT32_MAX * 64 || M > (int64_t)65535 * 128) return BL_ERR_SHAPE;
-  return hip_status(bl::launch_gemm(packed, gamma, N, K, q, d, M, y, ytype, as_stream(stream)));
+  return hip_status(bl::launch_gemm(packed, gamma, N, K, q, d, qsum, M, y, ytype,
+                                    as_stream(stream)));
 }
 
 int bl_gemm_group(const bl_gemm_problem* problems, int count, int64_t K, const int8_t* q,
-                  const float* d, int64_t M, void* stream) {
+                  const float* d, const int32_t* qsum, int64_t M, void* stream) {
   if (count < 0 || count > bl::kMaxGroup || M < 0 || K < 0 || K % 4 != 0) return BL_ERR_SHAPE;
   if (count == 0 || M == 0) return BL_OK;
   if (!problems) return BL_ERR_NULL;
+  if (!aligned(qsum, 4)) return BL_ERR_ALIGN;
   if (M > (int64_t)65535 * 256) return BL_ERR_SHAPE;
   bl::GemmProblem g[bl::kMaxGroup];
   int n = 0;
@@ -226,7 +229,7 @@ int bl_gemm_group(const bl_gemm_problem* problems, int count, int64_t K, const i
     g[n++] = bl::GemmProblem{p.packed, p.gamma, p.y, p.N, p.ytype};
   }
   if (n == 0) return BL_OK;
-  return hip_status(bl::launch_gemm_group(g, n, K, q, d, M, as_stream(stream)));
+  return hip_status(bl::launch_gemm_group(g, n, K, q, d, qsum, M, as_stream(stream)));
 }
 
 int bl_decode_norm_group(const bl_decode_problem* problems, int count, const uint16_t* r,

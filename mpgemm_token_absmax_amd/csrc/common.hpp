@@ -199,6 +199,26 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   return m;
 }
 
+// Sum over a block of per-thread int32 values (exact), one int32 slot per
+// wave in LDS.
+template <int kThreads>
+__device__ __forceinline__ int block_sum_i32(int v, int* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
+  __syncthreads();
+  int t = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) t += red[w];
+  return t;
+}
+
+// acc + the sum of the four int8 codes packed in w (exact).
+__device__ __forceinline__ int code_sum4(uint32_t w, int acc) {
+  return __builtin_amdgcn_sdot4((int)w, 0x01010101, acc, false);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));

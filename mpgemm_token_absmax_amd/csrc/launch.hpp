@@ -53,18 +53,20 @@ hipError_t launch_decode_norm_group(DecodeGroup& g, hipStream_t s);
 // bf16 x -> q, d of every problem of a group (M tokens each), one launch.
 hipError_t launch_quantize_group(const DecodeGroup& g, hipStream_t s);
 
+// qs (may be NULL): qs[t] = sum_k q[t][k], exact.
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
-                               float* d, hipStream_t s);
+                               float* d, int* qs, hipStream_t s);
 // One scale for the whole tensor; maxb: M words of workspace (row maxima).
 hipError_t launch_quantize_act_tensor(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                      int8_t* q, float* d, uint32_t* maxb, hipStream_t s);
+                                      int8_t* q, float* d, int* qs, uint32_t* maxb,
+                                      hipStream_t s);
 
 // Residual add + RMSNorm + per-token absmax int8 (r and h_out may be NULL;
 // h_out may be x or r itself). x, r, h_out share the row stride ldx.
 constexpr int64_t kRmsNormFastMaxK = 32768;
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* r, const uint16_t* g,
                                 float eps, int64_t M, int64_t K, int64_t ldx, uint16_t* h_out,
-                                int8_t* q, float* d, hipStream_t s);
+                                int8_t* q, float* d, int* qs, hipStream_t s);
 
 // Base-3 weights, five per byte: rows of 64*ceil(K/320) bytes.
 hipError_t launch_pack_t3(const void* w, bool f32, int64_t N, int64_t K, uint8_t* packed,
@@ -87,9 +89,11 @@ hipError_t launch_pack_ternary(const int8_t* w, int64_t N, int64_t K, uint8_t* p
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                        const int8_t* q, const float* d, int64_t M, void* y, int ytype,
                        hipStream_t s);
+// qs (may be NULL): the token sums of q; with them the GEMM runs on offset
+// weights (w + 1) and subtracts qs[t] in the epilogue.
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
-                       const int8_t* q, const float* d, int64_t M, void* y, int ytype,
-                       hipStream_t s);
+                       const int8_t* q, const float* d, const int* qs, int64_t M, void* y,
+                       int ytype, hipStream_t s);
 // Several GEMMs over the same int8 activations q [M][K] (scales d): problem i
 // has its own packed [N_i][K/4], gamma, y [M][N_i] and output type.
 struct GemmProblem {
@@ -100,7 +104,7 @@ struct GemmProblem {
   int ytype;
 };
 hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const int8_t* q,
-                             const float* d, int64_t M, hipStream_t s);
+                             const float* d, const int* qs, int64_t M, hipStream_t s);
 
 // Shapes off the fast paths (K % 64 != 0): one thread per output element.
 hipError_t launch_generic(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,

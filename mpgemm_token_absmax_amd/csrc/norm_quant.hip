@@ -57,9 +57,11 @@ __device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
 template <int NT, int NC, bool kRes>
 __global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
     const uint16_t* x, const uint16_t* r, const uint16_t* __restrict__ g, float eps, int64_t K,
-    int64_t ldx, uint16_t* h_out, int8_t* __restrict__ q, float* __restrict__ d) {
+    int64_t ldx, uint16_t* h_out, int8_t* __restrict__ q, float* __restrict__ d,
+    int* __restrict__ qs) {
   __shared__ double red_s[NT / kWave];
   __shared__ uint32_t red_m[NT / kWave];
+  __shared__ int red_q[NT / kWave];
   const int64_t t = blockIdx.x;
   const int nchunk = (int)(K / 8);
   const uint16_t* xrow = x + t * ldx;
@@ -117,16 +119,24 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
   const float m = __uint_as_float(mb);
   const float s = mb ? 127.0f / m : 0.0f;
   uint2* qr = reinterpret_cast<uint2*>(q + t * K);
+  int sum = 0;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     const int c = (int)threadIdx.x + i * NT;
     if (c < nchunk) {
       float y[8];
       norm8(hv[i], gv[i], rinv, y);
-      qr[c] = mb ? make_uint2(quant4_f32(&y[0], s), quant4_f32(&y[4], s)) : make_uint2(0u, 0u);
+      const uint2 w = mb ? make_uint2(quant4_f32(&y[0], s), quant4_f32(&y[4], s))
+                         : make_uint2(0u, 0u);
+      qr[c] = w;
+      sum = code_sum4(w.y, code_sum4(w.x, sum));
     }
   }
   if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
+  if (qs) {
+    sum = block_sum_i32<NT>(sum, red_q);
+    if (threadIdx.x == 0) qs[t] = sum;
+  }
 }
 
 // Generic path (K % 4 == 0, ldx % 4 == 0): three passes of 4 values per chunk.
@@ -152,9 +162,11 @@ __device__ __forceinline__ void norm4(uint2 h, uint2 gw, float rinv, float* y) {
 
 __global__ __launch_bounds__(kGenThreads) void k_rmsnorm_quant_any(
     const uint16_t* x, const uint16_t* r, const uint16_t* __restrict__ g, float eps, int64_t K,
-    int64_t ldx, uint16_t* h_out, int8_t* __restrict__ q, float* __restrict__ d) {
+    int64_t ldx, uint16_t* h_out, int8_t* __restrict__ q, float* __restrict__ d,
+    int* __restrict__ qs) {
   __shared__ double red_s[kGenThreads / kWave];
   __shared__ uint32_t red_m[kGenThreads / kWave];
+  __shared__ int red_q[kGenThreads / kWave];
   const int64_t t = blockIdx.x;
   const int64_t nchunk = K / 4;
   const uint2* xr = reinterpret_cast<const uint2*>(x + t * ldx);
@@ -178,28 +190,40 @@ __global__ __launch_bounds__(kGenThreads) void k_rmsnorm_quant_any(
   const float m = __uint_as_float(mb);
   const float s = mb ? 127.0f / m : 0.0f;
   uint32_t* qr = reinterpret_cast<uint32_t*>(q + t * K);
+  int sum = 0;
   for (int64_t c = threadIdx.x; c < nchunk; c += kGenThreads) {
     float y[4];
     norm4(hr ? hr[c] : load_h4(xr, rr, c), gr[c], rinv, y);
-    qr[c] = mb ? quant4_f32(y, s) : 0u;
+    const uint32_t w = mb ? quant4_f32(y, s) : 0u;
+    qr[c] = w;
+    sum = code_sum4(w, sum);
   }
   if (threadIdx.x == 0) d[t] = mb ? m / 127.0f : 0.0f;
+  if (qs) {
+    sum = block_sum_i32<kGenThreads>(sum, red_q);
+    if (threadIdx.x == 0) qs[t] = sum;
+  }
 }
 
-__global__ void k_zero_f32(float* __restrict__ p, int64_t n) {
+// d[:] = 0 and, when given, qs[:] = 0 (the K == 0 case).
+__global__ void k_zero_dq(float* __restrict__ d, int* __restrict__ qs, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
+  if (i < n) {
+    d[i] = 0.0f;
+    if (qs) qs[i] = 0;
+  }
 }
 
 template <int NT, int NC>
 hipError_t launch16(const uint16_t* x, const uint16_t* r, const uint16_t* g, float eps, int64_t M,
-                    int64_t K, int64_t ldx, uint16_t* h_out, int8_t* q, float* d, hipStream_t s) {
+                    int64_t K, int64_t ldx, uint16_t* h_out, int8_t* q, float* d, int* qs,
+                    hipStream_t s) {
   if (r)
     hipLaunchKernelGGL((k_rmsnorm_quant16<NT, NC, true>), dim3((unsigned)M), dim3(NT), 0, s, x, r,
-                       g, eps, K, ldx, h_out, q, d);
+                       g, eps, K, ldx, h_out, q, d, qs);
   else
     hipLaunchKernelGGL((k_rmsnorm_quant16<NT, NC, false>), dim3((unsigned)M), dim3(NT), 0, s, x,
-                       r, g, eps, K, ldx, h_out, q, d);
+                       r, g, eps, K, ldx, h_out, q, d, qs);
   return hipGetLastError();
 }
 
@@ -225,30 +249,30 @@ int rmsnorm_quant_config(int64_t K, int64_t ldx, int* threads, int* chunks) {
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* r, const uint16_t* g,
                                 float eps, int64_t M, int64_t K, int64_t ldx, uint16_t* h_out,
-                                int8_t* q, float* d, hipStream_t s) {
+                                int8_t* q, float* d, int* qs, hipStream_t s) {
   if (K == 0) {
-    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, d, M);
+    hipLaunchKernelGGL(k_zero_dq, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, d, qs, M);
     return hipGetLastError();
   }
   int nt = 0, nc = 0;
   if (rmsnorm_quant_config(K, ldx, &nt, &nc)) {
     if (nt == 256) {
       switch (nc) {
-        case 1: return launch16<256, 1>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
-        case 2: return launch16<256, 2>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
-        case 3: return launch16<256, 3>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
-        default: return launch16<256, 4>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+        case 1: return launch16<256, 1>(x, r, g, eps, M, K, ldx, h_out, q, d, qs, s);
+        case 2: return launch16<256, 2>(x, r, g, eps, M, K, ldx, h_out, q, d, qs, s);
+        case 3: return launch16<256, 3>(x, r, g, eps, M, K, ldx, h_out, q, d, qs, s);
+        default: return launch16<256, 4>(x, r, g, eps, M, K, ldx, h_out, q, d, qs, s);
       }
     }
     switch (nc) {
-      case 1: return launch16<1024, 1>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
-      case 2: return launch16<1024, 2>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
-      case 3: return launch16<1024, 3>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
-      default: return launch16<1024, 4>(x, r, g, eps, M, K, ldx, h_out, q, d, s);
+      case 1: return launch16<1024, 1>(x, r, g, eps, M, K, ldx, h_out, q, d, qs, s);
+      case 2: return launch16<1024, 2>(x, r, g, eps, M, K, ldx, h_out, q, d, qs, s);
+      case 3: return launch16<1024, 3>(x, r, g, eps, M, K, ldx, h_out, q, d, qs, s);
+      default: return launch16<1024, 4>(x, r, g, eps, M, K, ldx, h_out, q, d, qs, s);
     }
   }
   hipLaunchKernelGGL(k_rmsnorm_quant_any, dim3((unsigned)M), dim3(kGenThreads), 0, s, x, r, g, eps,
-                     K, ldx, h_out, q, d);
+                     K, ldx, h_out, q, d, qs);
   return hipGetLastError();
 }
 

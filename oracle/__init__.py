@@ -22,7 +22,8 @@ Sources (web pages on the method; cited by title and section):
     the RMS normalization fused into one pass.
 
 Modules:
-  quant    absmax int8 activation quantization, per token or per tensor
+  quant    absmax int8 activation quantization, per token or per tensor;
+           token sums of the codes (the library's side output)
   norm     residual add + RMSNorm fused with the per-token quantizer
   ternary  absmean weight scale (exact sum) and the +-0.5*gamma threshold
   i2s      2-bit I2_S pack / unpack (code table and bit layout)
@@ -36,7 +37,7 @@ hand-worked examples (tests/golden/), closed forms, brute force and
 invariants. Parity unpinned: byte compatibility with bitnet.cpp's own i2_s
 GGUF layout, and end-to-end "lossless vs Float16" (needs trained weights).
 """
-from .quant import widen_bf16, quantize_act_absmax, quantize_act_absmax_tensor
+from .quant import widen_bf16, quantize_act_absmax, quantize_act_absmax_tensor, token_sums
 from .norm import rmsnorm_quant, round_fraction_to_f32
 from .ternary import absmean_gamma, ternarize, ternarize_absmean
 from .i2s import pack_i2s, unpack_i2s, CODE_ZERO, CODE_POS, CODE_NEG
@@ -46,7 +47,7 @@ from .lut import lut_dot
 from .dequant import dequant_f64, dequant_f32, round_f64_to_bf16_bits, bf16_bits_to_f64
 
 __all__ = [
-    "widen_bf16", "quantize_act_absmax",
+    "widen_bf16", "quantize_act_absmax", "quantize_act_absmax_tensor", "token_sums",
     "absmean_gamma", "ternarize", "ternarize_absmean",
     "pack_i2s", "unpack_i2s", "CODE_ZERO", "CODE_POS", "CODE_NEG",
     "pack_t3", "unpack_t3",

@@ -18,6 +18,10 @@ to even; zero row -> zeros with scale 0):
 quantize_act_absmax_tensor is the pages' literal setting for several tokens:
 one scale over the whole activation tensor (same formulas with m = max over
 every token and k; every token's d is the same value).
+
+token_sums is not a quantity of the pages: it is the library's optional side
+output of its quantizers, S_t = sum_k q[t][k], with which a contraction can
+run on weights offset by one (sum_k (w+1) q = sum_k w q + S_t, exactly).
 """
 from __future__ import annotations
 
@@ -103,3 +107,15 @@ def quantize_act_absmax_tensor(x_bits: np.ndarray):
     q[:] = np.clip(_round_half_even(v), -QMAX, QMAX).astype(np.int8)
     d[:] = m / np.float32(QMAX)                           # fp32 IEEE quotient
     return q, d
+
+
+def _row_total(q64: np.ndarray) -> np.ndarray:
+    return q64.sum(axis=1)
+
+
+def token_sums(q: np.ndarray) -> np.ndarray:
+    """int8 codes [M][K] -> int64 [M]: S_t = sum_k q[t][k] (exact)."""
+    q = np.asarray(q)
+    if q.ndim != 2 or q.dtype != np.int8:
+        raise ValueError("codes must be int8 [M][K]")
+    return _row_total(q.astype(np.int64))

@@ -659,8 +659,32 @@ def pin_t3_roundtrip_dot(seed=31):
         raise AssertionError("non-zero padding accepted")
 
 
+def pin_token_sums():
+    """Token sums of the codes: a hand-worked example, the closed form of a
+    constant row, the contraction with an all-ones weight row (the pinned
+    integer dot), and the offset-weight identity the GEMM relies on:
+    sum_k (w+1) q = sum_k w q + S."""
+    q = np.array([[1, -2, 3, -4], [127, -127, 0, 5], [0, 0, 0, 0]], dtype=np.int8)
+    assert oracle.token_sums(q).tolist() == [-2, 5, 0]
+    for c in (-127, -1, 0, 3, 127):
+        assert oracle.token_sums(np.full((2, 4096), c, np.int8)).tolist() == [4096 * c] * 2
+    r = _rng(32)
+    q = r.integers(-127, 128, (7, 192)).astype(np.int8)
+    w = r.integers(-1, 2, (5, 192)).astype(np.int8)
+    s = oracle.token_sums(q)
+    assert np.array_equal(oracle.mpgemm_acc(q, np.ones((1, 192), np.int8))[:, 0], s)
+    acc1 = oracle.mpgemm_acc(q, (w + 1).astype(np.int8))
+    assert np.array_equal(acc1 - s[:, None], oracle.mpgemm_acc(q, w))
+    try:
+        oracle.token_sums(q.astype(np.int16))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("non-int8 codes accepted")
+
+
 ALL_PINS = [
-    pin_quant_golden, pin_quant_special, pin_quant_invariants, pin_quant_rejects,
+    pin_quant_golden, pin_token_sums, pin_quant_special, pin_quant_invariants, pin_quant_rejects,
     pin_quant_tensor_golden, pin_quant_tensor_reductions,
     pin_t3_golden, pin_t3_exhaustive, pin_t3_layout, pin_t3_roundtrip_dot,
     pin_norm_golden, pin_norm_zero_rows, pin_norm_exact_ms, pin_norm_invariants, pin_norm_error_bound,

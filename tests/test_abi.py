@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bl_abi_version() == 1
+    assert lib.bl_abi_version() == 2
     for s in (L.BL_OK, L.BL_ERR_NULL, L.BL_ERR_SHAPE, L.BL_ERR_ALIGN, L.BL_ERR_DTYPE,
               L.BL_ERR_WORKSPACE, L.BL_ERR_HIP, L.BL_ERR_ALIAS):
         assert lib.bl_status_string(s)
@@ -49,17 +49,21 @@ def test_version_and_status_strings(lib):
 
 def test_quantize_validation(lib):
     f = lib.bl_quantize_act
-    assert f(A16, 2, 6, 6, B16, C16, None) == L.BL_ERR_SHAPE        # K % 4
-    assert f(A16, -1, 8, 8, B16, C16, None) == L.BL_ERR_SHAPE
-    assert f(A16, 2, 8, 4, B16, C16, None) == L.BL_ERR_SHAPE        # ldx < K
-    assert f(None, 2, 8, 8, B16, C16, None) == L.BL_ERR_NULL
-    assert f(A16, 2, 8, 8, None, C16, None) == L.BL_ERR_NULL
-    assert f(A16, 2, 8, 8, B16, None, None) == L.BL_ERR_NULL
-    assert f(A16 + 8, 2, 8, 8, B16, C16, None) == L.BL_ERR_ALIGN
-    assert f(A16, 2, 8, 8, B16 + 4, C16, None) == L.BL_ERR_ALIGN
-    assert f(A16, 2, 8, 8, B16, C16 + 2, None) == L.BL_ERR_ALIGN
-    assert f(A16, 2, 8, 10, B16, C16, None) == L.BL_ERR_ALIGN       # ldx % 4
-    assert f(None, 0, 8, 8, None, None, None) == L.BL_OK            # M == 0: nothing to do
+    assert f(A16, 2, 6, 6, B16, C16, None, None) == L.BL_ERR_SHAPE        # K % 4
+    assert f(A16, -1, 8, 8, B16, C16, None, None) == L.BL_ERR_SHAPE
+    assert f(A16, 2, 8, 4, B16, C16, None, None) == L.BL_ERR_SHAPE        # ldx < K
+    assert f(None, 2, 8, 8, B16, C16, None, None) == L.BL_ERR_NULL
+    assert f(A16, 2, 8, 8, None, C16, None, None) == L.BL_ERR_NULL
+    assert f(A16, 2, 8, 8, B16, None, None, None) == L.BL_ERR_NULL
+    assert f(A16 + 8, 2, 8, 8, B16, C16, None, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 8, 8, B16 + 4, C16, None, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 8, 8, B16, C16 + 2, None, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 8, 10, B16, C16, None, None) == L.BL_ERR_ALIGN       # ldx % 4
+    assert f(None, 0, 8, 8, None, None, None, None) == L.BL_OK            # M == 0: nothing to do
+    # qsum (token sums) is optional; when given it must be 4-byte aligned and
+    # 127*K must fit int32
+    assert f(A16, 2, 8, 8, B16, C16, D16 + 2, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 1 << 25, 1 << 25, B16, C16, D16, None) == L.BL_ERR_SHAPE
 
 
 def test_pack_validation(lib):
@@ -86,10 +90,10 @@ def test_pack_validation(lib):
 def test_matmul_validation(lib, name):
     fn = getattr(lib, name)
 
-    def call(packed=A16, gamma=B16, N=64, K=64, q=C16, d=D16, M=2, y=E16, yt=1):
+    def call(packed=A16, gamma=B16, N=64, K=64, q=C16, d=D16, M=2, y=E16, yt=1, qsum=None):
         if name == "bl_gemv":
             return fn(packed, gamma, N, K, q, d, M, y, yt, None)
-        return fn(packed, gamma, N, K, q, d, M, y, yt, None, 0, None)
+        return fn(packed, gamma, N, K, q, d, qsum, M, y, yt, None, 0, None)
 
     assert call(K=6) == L.BL_ERR_SHAPE
     assert call(N=-1) == L.BL_ERR_SHAPE
@@ -111,6 +115,7 @@ def test_matmul_validation(lib, name):
         assert call(M=17) == L.BL_ERR_SHAPE           # gemv covers M <= 16 only
     else:
         assert lib.bl_gemm_workspace(2048, 8192, 8192) == 0
+        assert call(qsum=E16 + 0x1002) == L.BL_ERR_ALIGN   # token sums: 4-byte aligned
 
 
 def test_status_to_exception(lib):
@@ -164,9 +169,9 @@ def test_gemm_group_validation(lib):
         base.update(kw)
         return P(**base)
 
-    def call(probs, K=256, q=C16, d=D16, M=32):
+    def call(probs, K=256, q=C16, d=D16, M=32, qsum=None):
         arr = (P * max(1, len(probs)))(*probs)
-        return lib.bl_gemm_group(arr, len(probs), K, q, d, M, None)
+        return lib.bl_gemm_group(arr, len(probs), K, q, d, qsum, M, None)
 
     assert call([prob()] * 9) == L.BL_ERR_SHAPE            # more than 8 problems
     assert call([prob()], K=6) == L.BL_ERR_SHAPE
@@ -182,10 +187,11 @@ def test_gemm_group_validation(lib):
     assert call([prob(y=E16 + 2)]) == L.BL_ERR_ALIGN
     assert call([prob()], q=C16 + 8) == L.BL_ERR_ALIGN
     assert call([prob()], K=132108) == L.BL_ERR_SHAPE      # fp32-exact bound
+    assert call([prob()], qsum=E16 + 0x1001) == L.BL_ERR_ALIGN
     assert call([], M=4) == L.BL_OK
     assert call([prob()], M=0) == L.BL_OK
     assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK
-    assert lib.bl_gemm_group(None, 1, 256, C16, D16, 4, None) == L.BL_ERR_NULL
+    assert lib.bl_gemm_group(None, 1, 256, C16, D16, None, 4, None) == L.BL_ERR_NULL
 
 
 def test_probe_library_exports_and_validation():
@@ -215,26 +221,28 @@ def test_quantize_tensor_validation(lib):
     ws = lib.bl_quantize_act_tensor_workspace(2)
     assert ws == 16 and lib.bl_quantize_act_tensor_workspace(0) == 0
     assert lib.bl_quantize_act_tensor_workspace(5) == 32
-    assert f(A16, 2, 6, 6, B16, C16, D16, ws, None) == L.BL_ERR_SHAPE       # K % 4
-    assert f(A16, 2, 8, 4, B16, C16, D16, ws, None) == L.BL_ERR_SHAPE       # ldx < K
-    assert f(None, 2, 8, 8, B16, C16, D16, ws, None) == L.BL_ERR_NULL
-    assert f(A16, 2, 8, 8, B16, None, D16, ws, None) == L.BL_ERR_NULL
-    assert f(A16, 2, 8, 8, B16, C16, None, ws, None) == L.BL_ERR_WORKSPACE
-    assert f(A16, 2, 8, 8, B16, C16, D16, ws - 1, None) == L.BL_ERR_WORKSPACE
-    assert f(A16, 2, 8, 8, B16, C16, D16 + 4, ws, None) == L.BL_ERR_ALIGN
-    assert f(A16 + 8, 2, 8, 8, B16, C16, D16, ws, None) == L.BL_ERR_ALIGN
-    assert f(A16, 2, 8, 10, B16, C16, D16, ws, None) == L.BL_ERR_ALIGN     # ldx % 4
-    assert f(None, 0, 8, 8, None, None, None, 0, None) == L.BL_OK            # M == 0
+    # (x, M, K, ldx, q, d, qsum, ws, ws_bytes, stream)
+    assert f(A16, 2, 6, 6, B16, C16, None, D16, ws, None) == L.BL_ERR_SHAPE       # K % 4
+    assert f(A16, 2, 8, 4, B16, C16, None, D16, ws, None) == L.BL_ERR_SHAPE       # ldx < K
+    assert f(None, 2, 8, 8, B16, C16, None, D16, ws, None) == L.BL_ERR_NULL
+    assert f(A16, 2, 8, 8, B16, None, None, D16, ws, None) == L.BL_ERR_NULL
+    assert f(A16, 2, 8, 8, B16, C16, None, None, ws, None) == L.BL_ERR_WORKSPACE
+    assert f(A16, 2, 8, 8, B16, C16, None, D16, ws - 1, None) == L.BL_ERR_WORKSPACE
+    assert f(A16, 2, 8, 8, B16, C16, None, D16 + 4, ws, None) == L.BL_ERR_ALIGN
+    assert f(A16 + 8, 2, 8, 8, B16, C16, None, D16, ws, None) == L.BL_ERR_ALIGN
+    assert f(A16, 2, 8, 10, B16, C16, None, D16, ws, None) == L.BL_ERR_ALIGN     # ldx % 4
+    assert f(None, 0, 8, 8, None, None, None, None, 0, None) == L.BL_OK            # M == 0
+    assert f(A16, 2, 8, 8, B16, C16, E16 + 2, D16, ws, None) == L.BL_ERR_ALIGN    # qsum
 
 
 def test_rmsnorm_quant_validation(lib):
     f = lib.bl_rmsnorm_quant
     F16 = 0x60000
-    # (x, r, g, eps, M, K, ldx, h_out, q, d)
-    ok = (A16, B16, C16, 1e-5, 2, 8, 8, E16, F16, D16)
+    # (x, r, g, eps, M, K, ldx, h_out, q, d, qsum)
+    ok = (A16, B16, C16, 1e-5, 2, 8, 8, E16, F16, D16, None)
 
     def call(**kw):
-        names = ("x", "r", "g", "eps", "M", "K", "ldx", "h", "q", "d")
+        names = ("x", "r", "g", "eps", "M", "K", "ldx", "h", "q", "d", "qsum")
         a = dict(zip(names, ok))
         a.update(kw)
         return f(*(a[n] for n in names), None)
@@ -256,6 +264,7 @@ def test_rmsnorm_quant_validation(lib):
     assert call(q=F16 + 4) == L.BL_ERR_ALIGN
     assert call(d=D16 + 2) == L.BL_ERR_ALIGN
     assert call(ldx=10) == L.BL_ERR_ALIGN                     # ldx % 4
+    assert call(qsum=D16 + 2) == L.BL_ERR_ALIGN
     # h_out may be x or r exactly, but must not partly overlap either
     assert call(h=A16 + 16) == L.BL_ERR_ALIAS
     assert call(h=B16 + 16) == L.BL_ERR_ALIAS

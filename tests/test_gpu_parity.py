@@ -103,9 +103,13 @@ def test_quantize_parity(M, K):
     x = W.activations_bf16(100 + M * 7 + K, M, K, outlier_frac=0.01, outlier_scale=20.0)
     q_ref, d_ref = oracle.quantize_act_absmax(x)
     q, d = bl.quantize_act(dev_bf16(x))
+    q2, d2, qs = bl.quantize_act(dev_bf16(x), with_sums=True)
     torch.cuda.synchronize()
     assert np.array_equal(host(q), q_ref)
     assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+    # the token sums ride along without changing q or d
+    assert torch.equal(q2, q) and torch.equal(d2, d)
+    assert np.array_equal(host(qs), oracle.token_sums(q_ref))
 
 
 def test_quantize_special_rows_and_stride():
@@ -136,10 +140,13 @@ def test_quantize_special_rows_and_stride():
     wide12 = np.zeros((x.shape[0], 12), dtype=np.uint16)
     wide12[:, :8] = x
     x12 = dev_bf16(wide12)[:, :8]
-    q12, d12 = bl.quantize_act(x12)
+    q12, d12, s12 = bl.quantize_act(x12, with_sums=True)
+    _, _, s24 = bl.quantize_act(xd, with_sums=True)
     torch.cuda.synchronize()
     assert np.array_equal(host(q12), q_ref)
     assert np.array_equal(host(d12).view(np.uint32), d_ref.view(np.uint32))
+    assert np.array_equal(host(s12), oracle.token_sums(q_ref))
+    assert np.array_equal(host(s24), oracle.token_sums(q_ref))
     # the golden q values themselves
     assert host(q)[0, :4].tolist() == [-127, 32, 16, 95]
     assert host(q)[1, :6].tolist() == [127, 62, -62, 0, 2, -2]
@@ -159,10 +166,11 @@ def test_quantize_tensor_parity(M, K):
     if M > 2:
         x[M // 2] = 0                                  # a zero token keeps the shared scale
     q_ref, d_ref = oracle.quantize_act_absmax_tensor(x)
-    q, d = bl.quantize_act_tensor(dev_bf16(x))
+    q, d, qs = bl.quantize_act_tensor(dev_bf16(x), with_sums=True)
     torch.cuda.synchronize()
     assert np.array_equal(host(q), q_ref)
     assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+    assert np.array_equal(host(qs), oracle.token_sums(q_ref))
 
 
 def test_quantize_tensor_special():
@@ -219,8 +227,11 @@ def test_quantize_empty():
     q, d = bl.quantize_act(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"))
     assert q.shape == (0, 64) and d.shape == (0,)
     q, d = bl.quantize_act(torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda"))
+    qs = torch.full((3,), 7, dtype=torch.int32, device="cuda")
+    bl.quantize_act(torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda"), qsum=qs)
     torch.cuda.synchronize()
     assert host(d).tolist() == [0.0, 0.0, 0.0]
+    assert host(qs).tolist() == [0, 0, 0]
 
 
 # ---------------------------------------------------------------------------
@@ -297,8 +308,11 @@ def _norm_run(bl, x, r, g, eps, ldx, mode):
     rd = None if r is None else padded(r)
     gd = dev_bf16(g)
     h_out = {"new": None, "none": None, "in_r": rd, "in_x": xd}[mode]
-    h, q, d = bl.rmsnorm_quant(xd, gd, eps, residual=rd, h_out=h_out, write_h=mode != "none")
+    h, q, d, qs = bl.rmsnorm_quant(xd, gd, eps, residual=rd, h_out=h_out, write_h=mode != "none",
+                                   with_sums=True)
     torch.cuda.synchronize()
+    # the token sums are those of the codes written
+    assert np.array_equal(host(qs), oracle.token_sums(host(q)))
     return (None if h is None else host(h)), host(q), host(d)
 
 
@@ -486,6 +500,12 @@ def _run_mm(bl, fn_name, M, N, K, seed, zero_rows=()):
     outs = run_all_outputs(bl, fn, packed, gd, dev(q), dev(d))
     torch.cuda.synchronize()
     check_outputs(acc, GAMMA, d, outs["i32"], outs["f32"], outs["bf16"])
+    if fn_name == "gemm":
+        # with the token sums the kernel runs on offset weights: same bits
+        qs = dev(oracle.token_sums(q).astype(np.int32))
+        for name in ("i32", "f32", "bf16"):
+            y = host(bl.gemm(packed, gd, dev(q), dev(d), out_dtype=name, qsum=qs))
+            assert np.array_equal(y.view(np.uint8), outs[name].view(np.uint8)), name
     return outs
 
 
@@ -547,9 +567,12 @@ def test_gemm_group_parity(M, K, Ns, outs):
         refs.append((t, g))
     ys = bl.gemm_group(probs, qd, dd)
     alone = [bl.gemm(p["packed"], p["gamma"], qd, dd, out_dtype=p["out_dtype"]) for p in probs]
+    qs = dev(oracle.token_sums(q).astype(np.int32))
+    ys_off = [y.clone() for y in bl.gemm_group(probs, qd, dd, qsum=qs)]
     torch.cuda.synchronize()
-    for (t, g), o, y, y1 in zip(refs, outs, ys, alone):
+    for (t, g), o, y, y1, y2 in zip(refs, outs, ys, alone, ys_off):
         assert torch.equal(y, y1), "group output differs from the single-problem call"
+        assert torch.equal(y, y2), "offset-weight (token sums) output differs"
         acc = oracle.mpgemm_acc_f64blas(q, t) if M * t.shape[0] * K > 2e8 else \
             oracle.mpgemm_acc(q, t)
         check_outputs(acc, g, d, **{f"y_{o}": host(y)})
@@ -996,14 +1019,16 @@ def test_config5_grouped_sampled():
         x = inps[0].x_bf16
         say(f"config 5 group {names} K={K}")
         q_ref, d_ref = oracle.quantize_act_absmax(x)
-        q, d = bl.quantize_act(dev_bf16(x))
+        # the benchmark's form: token sums from the quantizer, offset weights
+        q, d, qs = bl.quantize_act(dev_bf16(x), with_sums=True)
         probs = []
         for inp in inps:
             probs.append(dict(packed=bl.pack_i2s(dev(inp.w_tern)),
                               gamma=dev(np.array([inp.gamma], np.float32)), out_dtype="f32"))
-        ys = bl.gemm_group(probs, q, d)
+        ys = bl.gemm_group(probs, q, d, qsum=qs)
         torch.cuda.synchronize()
         assert np.array_equal(host(q), q_ref)
+        assert np.array_equal(host(qs), oracle.token_sums(q_ref))
         for n, inp, pr, y in zip(names, inps, probs, ys):
             y1 = bl.gemm(pr["packed"], pr["gamma"], q, d, out_dtype="f32")
             assert torch.equal(y, y1), n

@@ -20,6 +20,8 @@ MUTATIONS = {
     "quant_tensor_first_row_max": (oracle.quant, "_tensor_absmax",
                                    lambda x: np.float32(np.max(np.abs(x[0])))),
     "quant_tensor_signed_max": (oracle.quant, "_tensor_absmax", lambda x: np.float32(np.max(x))),
+    "token_sums_of_magnitudes": (oracle.quant, "_row_total", lambda q: np.abs(q).sum(axis=1)),
+    "token_sums_drop_last_k": (oracle.quant, "_row_total", lambda q: q[:, :-1].sum(axis=1)),
     "norm_sum_not_mean": (oracle.norm, "_mean_square", lambda h: oracle.norm._exact_sum_squares(h)),
     "norm_residual_half_up": (oracle.norm, "_bf16_rne_from_f32",
                               lambda v: ((np.asarray(v, np.float32).view(np.uint32).astype(np.uint64)
