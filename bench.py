@@ -615,21 +615,23 @@ def main():
         ms_layer = a0.elapsed_time(a1) / args.gemm_steps
         ops = cfg5.ops(M5)
         tops = ops / (ms_layer * 1e-3) / 1e12
+        # GEMMs only, with and without the token sums, interleaved (the clock
+        # drifts with the power state, so back-to-back blocks would favour
+        # whichever runs second): medians over 3 rounds of gemm_steps layers
         b0 = torch.cuda.Event(enable_timing=True)
         b1 = torch.cuda.Event(enable_timing=True)
-        b0.record()
-        for _ in range(args.gemm_steps):
-            layer(gemm_only=True)
-        b1.record()
-        torch.cuda.synchronize()
-        ms_gemm = b0.elapsed_time(b1) / args.gemm_steps
+        ms_by = {False: [], True: []}
+        for rnd in range(3):
+            for plain in ((False, True) if rnd % 2 == 0 else (True, False)):
+                b0.record()
+                for _ in range(args.gemm_steps):
+                    layer(gemm_only=True, plain=plain)
+                b1.record()
+                torch.cuda.synchronize()
+                ms_by[plain].append(b0.elapsed_time(b1) / args.gemm_steps)
+        ms_gemm = float(np.median(ms_by[False]))
         gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
-        b0.record()
-        for _ in range(args.gemm_steps):
-            layer(gemm_only=True, plain=True)
-        b1.record()
-        torch.cuda.synchronize()
-        gemm_tops_plain = ops / (b0.elapsed_time(b1) / args.gemm_steps * 1e-3) / 1e12
+        gemm_tops_plain = ops / (float(np.median(ms_by[True])) * 1e-3) / 1e12
         # one activation scale per layer input (per tensor) instead of per token
         ws_t = torch.empty((max(16, int(bl.lib().bl_quantize_act_tensor_workspace(M5))),),
                            dtype=torch.uint8, device=dev)
