@@ -41,6 +41,9 @@ constexpr int64_t kWideN = 8192;
 // One-token-style fused decode (quantize in the kernel) up to this many tokens.
 constexpr int kFusedTokens = 4;
 
+// Two row tiles per wave in k_gemvq from this many 32-row blocks per launch.
+constexpr int64_t kGemvqTwoTileBlocks = 256;
+
 __device__ __forceinline__ void store_out(void* y, int ytype, int64_t idx, int acc, float c) {
   if (ytype == 0) {
     static_cast<int*>(y)[idx] = acc;
@@ -666,9 +669,9 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int l
 // the weight loads of the same step. No LDS staging and no barrier before the
 // MFMAs. A partial last step (K % 256 != 0) zeroes the packed words of the
 // lanes past K (code 00 is weight 0), whose loads were clamped into the row.
-template <int WPB, int U>
+template <int WPB, int U, int RT>
 __global__ __launch_bounds__(WPB * kWave) void k_gemvq(DecodeGroup grp) {
-  __shared__ v4i red[WPB - 1][kWave];
+  __shared__ v4i red[WPB - 1][RT][kWave];
 
   const DecodeProblem& P = grp.p[blockIdx.y];
   const int64_t N = P.N;
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_gemvq(DecodeGroup grp) {
   void* yp = P.y;
   const int ytype = P.ytype;
   const int M = grp.M;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * RT);
   // every field in one scalar round trip (a scalar load still in flight later
   // would turn each LDS wait into a full wait)
   asm volatile("" ::"s"(packed), "s"(qin), "s"(din), "s"(gptr), "s"(yp), "s"(K), "s"(ytype),
@@ -696,18 +699,24 @@ __global__ __launch_bounds__(WPB * kWave) void k_gemvq(DecodeGroup grp) {
   const int jb = min(ja + len, nsteps);
   const int tok = r < M ? r : M - 1;
   const int8_t* qrow = qin + (int64_t)tok * K;
-  int64_t row = n0 + r;
-  row = row < N ? row : N - 1;
-  const uint8_t* wrow = packed + row * RB;
+  const uint8_t* wrow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int64_t row = n0 + 16 * rt + r;
+    row = row < N ? row : N - 1;
+    wrow[rt] = packed + row * RB;
+  }
 
-  v4i wa[U], wb[U], qa[U][4], qb[U][4];
-  auto load = [&](v4i (&w)[U], v4i (&qf)[U][4], int j) {
+  v4i wa[U][RT], wb[U][RT], qa[U][4], qb[U][4];
+  auto load = [&](v4i (&w)[U][RT], v4i (&qf)[U][4], int j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int step = max(min(j + u, jb - 1), 0);
       int off = step * 64 + 16 * h;
       off = off < RB ? off : RB - 16;
-      w[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow + off));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        w[u][rt] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wrow[rt] + off));
       int kk = step * 256 + 64 * h;
       kk = kk < K ? kk : K - 64;
 #pragma unroll
@@ -719,18 +728,22 @@ __global__ __launch_bounds__(WPB * kWave) void k_gemvq(DecodeGroup grp) {
   const float dtok = ytype ? din[tok] : 0.0f;
   const float gam = ytype ? __builtin_nontemporal_load(gptr) : 0.0f;
 
-  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};   // two chains (even / odd s)
-  auto compute = [&](const v4i (&w)[U], const v4i (&qf)[U][4], int j) {
+  v4i acc0[RT], acc1[RT];                               // two chains (even / odd s)
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc0[rt] = acc1[rt] = v4i{0, 0, 0, 0};
+  auto compute = [&](const v4i (&w)[U][RT], const v4i (&qf)[U][4], int j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j + u < jb) {
         const uint32_t kmask = (j + u) * 256 + 64 * h < K ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          v4i& a = (s & 1) ? acc1 : acc0;
-          a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][s] & kmask),
-                                                    qf[u][s], a, 0, 0, 0);
-        }
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            v4i& a = (s & 1) ? acc1[rt] : acc0[rt];
+            a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s] & kmask),
+                                                      qf[u][s], a, 0, 0, 0);
+          }
       }
     }
   };
@@ -740,17 +753,26 @@ __global__ __launch_bounds__(WPB * kWave) void k_gemvq(DecodeGroup grp) {
     if (j + 2 * U < jb) load(wa, qa, j + 2 * U);
     if (j + U < jb) compute(wb, qb, j + U);
   }
-  v4i acc = acc0 + acc1;
-
-  if (wk > 0) red[wk - 1][lane] = acc;
+  v4i acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = acc0[rt] + acc1[rt];
+  if (wk > 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) red[wk - 1][rt][lane] = acc[rt];
+  }
   __syncthreads();
   if (wk > 0) return;
 #pragma unroll
-  for (int w = 0; w < WPB - 1; ++w) acc += red[w][lane];
+  for (int w = 0; w < WPB - 1; ++w)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] += red[w][rt][lane];
   // D layout: lane holds token lane%16 and rows 4*(lane/16) + v
   if (r >= M) return;
-  const int64_t n = n0 + 4 * h;
-  if (n < N) store_quad(yp, ytype, N, r, n, acc, gam * dtok);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t n = n0 + 16 * rt + 4 * h;
+    if (n < N) store_quad(yp, ytype, N, r, n, acc[rt], gam * dtok);
+  }
 }
 
 // One thread per output: any K % 4 == 0 (group rule applied byte-wise).
@@ -843,31 +865,38 @@ int steps_per_wave(const DecodeGroup& g, int wpb) {
   return len;
 }
 
-template <int WPB, int U>
+template <int WPB, int U, int RT = 1>
 hipError_t launch_q(DecodeGroup& g, hipStream_t s) {
   int64_t blocks = 0;
   for (int i = 0; i < g.count; ++i) {
-    const int64_t b = (g.p[i].N + 15) / 16;
+    const int64_t b = (g.p[i].N + 16 * RT - 1) / (16 * RT);
     blocks = b > blocks ? b : blocks;
   }
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemvq<WPB, U>), dim3((unsigned)blocks, (unsigned)g.count),
+  hipLaunchKernelGGL((k_gemvq<WPB, U, RT>), dim3((unsigned)blocks, (unsigned)g.count),
                      dim3(WPB * kWave), 0, s, g);
   return hipGetLastError();
 }
 
 // int8 activations in (p.qin, p.din): enough waves per block that each walks
 // at most about 4 steps of K, in one load batch of exactly that many steps.
+// Every block reads all M tokens' fragments of its K range (L2 hits), M/4
+// times the weight bytes it streams at M = 16; when the launch has at least
+// one 32-row block per CU, each wave takes two row tiles that share those
+// fragments (half the L2 traffic per weight byte), in half-size load batches.
 hipError_t launch_gemvq(DecodeGroup& g, hipStream_t s) {
+  int64_t blocks32 = 0;
+  for (int i = 0; i < g.count; ++i) blocks32 += (g.p[i].N + 31) / 32;
+  const bool two = blocks32 >= kGemvqTwoTileBlocks;
   const int len4 = steps_per_wave(g, 4);
-  if (len4 <= 1) return launch_q<4, 1>(g, s);
-  if (len4 == 2) return launch_q<4, 2>(g, s);
-  if (len4 == 3) return launch_q<4, 3>(g, s);
-  if (len4 == 4) return launch_q<4, 4>(g, s);
+  if (len4 <= 1) return two ? launch_q<4, 1, 2>(g, s) : launch_q<4, 1>(g, s);
+  if (len4 == 2) return two ? launch_q<4, 1, 2>(g, s) : launch_q<4, 2>(g, s);
+  if (len4 == 3) return two ? launch_q<4, 2, 2>(g, s) : launch_q<4, 3>(g, s);
+  if (len4 == 4) return two ? launch_q<4, 2, 2>(g, s) : launch_q<4, 4>(g, s);
   const int len8 = steps_per_wave(g, 8);
-  if (len8 == 3) return launch_q<8, 3>(g, s);
-  if (len8 == 4) return launch_q<8, 4>(g, s);
-  return launch_q<16, 2>(g, s);
+  if (len8 == 3) return two ? launch_q<8, 2, 2>(g, s) : launch_q<8, 3>(g, s);
+  if (len8 == 4) return two ? launch_q<8, 2, 2>(g, s) : launch_q<8, 4>(g, s);
+  return launch_q<16, 2>(g, s);           // 16 waves: no registers for a second tile
 }
 
 }  // namespace

@@ -861,6 +861,16 @@ def test_decode_group_tokens_long_k():
     _decode_group_case(bl, 16, [(17, 28672)], seed=80, out_types=["f32"])
 
 
+def test_decode_group_two_row_tiles():
+    """5..16 tokens in launches with at least 256 blocks of 32 rows: each wave
+    of the code GEMV takes two row tiles (ragged last tiles, a small problem
+    inside a large group)."""
+    bl = _bl()
+    _decode_group_case(bl, 16, [(8200, 1024), (600, 2048)], seed=120, out_types=["bf16", "i32"])
+    _decode_group_case(bl, 5, [(8193, 4096)], seed=121, out_types=["f32"])
+    _decode_group_case(bl, 12, [(4100, 3072), (4100, 3072), (31, 3072)], seed=122)
+
+
 @pytest.mark.parametrize("pad", [8, 4])
 def test_decode_group_tokens_strided_x(pad):
     """2..4 tokens with x rows further apart than K: a row stride that keeps

@@ -38,35 +38,43 @@ def decode1_config(K):
     return (16, 4, 4, len16) if len16 <= 8 else (16, 8, 4, len16)
 
 
-def gemvq_config(K):
-    """(WPB, U) of launch_gemvq for a group whose largest K is K."""
-    if steps_per_wave(K, 4) <= 4:
-        return 4, max(steps_per_wave(K, 4), 1)
-    if steps_per_wave(K, 8) <= 4:
-        return 8, steps_per_wave(K, 8)
-    return 16, 2
+def gemvq_config(K, blocks32=0):
+    """(WPB, U, RT) of launch_gemvq for a group whose largest K is K and whose
+    problems hold blocks32 blocks of 32 rows in all."""
+    two = blocks32 >= 256
+    len4 = steps_per_wave(K, 4)
+    if len4 <= 4:
+        if two:
+            return 4, (1 if len4 <= 2 else 2), 2
+        return 4, max(len4, 1), 1
+    len8 = steps_per_wave(K, 8)
+    if len8 <= 4:
+        return (8, 2, 2) if two else (8, len8, 1)
+    return 16, 2, 1
 
 
-def gemvq_ranges(N, K, M, group_kmax=None):
+def gemvq_ranges(N, K, M, group_kmax=None, blocks32=None):
     """Yield (buffer, lo, hi, size) of every global load of k_gemvq."""
     assert K % 64 == 0 and K >= 64 and 1 <= M <= 16
-    WPB, U = gemvq_config(K if group_kmax is None else group_kmax)
+    WPB, U, RT = gemvq_config(K if group_kmax is None else group_kmax,
+                              (N + 31) // 32 if blocks32 is None else blocks32)
     RB = K // 4
     nsteps = (K + 255) // 256
     length = (nsteps + WPB - 1) // WPB
     tok = np.minimum(R_OF, M - 1)
-    for b, wk in itertools.product(range((N + 15) // 16), range(WPB)):
+    for b, wk in itertools.product(range((N + 16 * RT - 1) // (16 * RT)), range(WPB)):
         ja = min(wk * length, nsteps)
         jb = min(ja + length, nsteps)
-        rows = np.minimum(b * 16 + R_OF, N - 1)
         starts = list(range(ja, jb, 2 * U)) or [ja]
         for j in starts:
             for base in (j, j + U, j + 2 * U):
                 for u in range(U):
                     step = max(min(base + u, jb - 1), 0)
                     off = np.minimum(step * 64 + 16 * H_OF, RB - 16)
-                    lo = rows * RB + off
-                    yield "packed", lo.min(), (lo + 16).max(), N * RB
+                    for rt in range(RT):
+                        rows = np.minimum(b * 16 * RT + 16 * rt + R_OF, N - 1)
+                        lo = rows * RB + off
+                        yield "packed", lo.min(), (lo + 16).max(), N * RB
                     kk = np.minimum(step * 256 + 64 * H_OF, K - 64)
                     for s in range(4):
                         lo = tok * K + kk + 16 * s
@@ -177,6 +185,19 @@ def test_gemvq_group_kmax():
     for K in (64, 320, 4096):
         for buf, lo, hi, size in gemvq_ranges(20, K, 5, group_kmax=28672):
             assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+@pytest.mark.parametrize("N,K,M,blocks32", [(11008, 4096, 16, 688), (8193, 4096, 16, 257),
+                                            (17, 4096, 8, 300), (4096, 2560, 16, 384),
+                                            (33, 1024, 4, 256), (5000, 6912, 16, 300),
+                                            (31, 64, 16, 256)])
+def test_gemvq_two_row_tiles(N, K, M, blocks32):
+    """Launches with at least 256 blocks of 32 rows give each wave two row
+    tiles (also for a small problem inside a large group: its last block's
+    second tile is clamped onto its last row)."""
+    assert gemvq_config(K, blocks32)[2] == (2 if steps_per_wave(K, 8) <= 4 else 1)
+    for buf, lo, hi, size in gemvq_ranges(N, K, M, blocks32=blocks32):
+        assert 0 <= lo and hi <= size, (buf, lo, hi, size)
 
 
 GEMM_SHAPES = [(1, 64, 17), (130, 256, 17), (64, 2560, 64), (640, 320, 100), (257, 576, 129),
