@@ -333,6 +333,8 @@ def parse():
     p.add_argument("--no-extras", action="store_true",
                    help="skip the 7B-layer and 100B-shape decode measurements")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--mfma-counters", action="store_true",
+                   help="counter-collection mode: only the prefill GEMM layers (eager), no JSON line")
     p.add_argument("--traffic", action="store_true",
                    help="counter-collection mode: a 256 MiB plain copy (calibration) and "
                         "eager decode launches over distinct weight copies; no JSON line")
@@ -341,6 +343,38 @@ def parse():
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def build_prefill(torch, bl, W, dev):
+    """The 100B-class layer at 2048 tokens: one bf16 input per group of
+    projections that read it; each group's GEMMs run through one
+    bl_gemm_group call on its quantized codes. The quantizer also writes the
+    token sums and `group` takes them (offset weights); `plain` is the same
+    group without them."""
+    cfg5 = W.CONFIGS[5]
+    M5 = 2048
+    log(f"setup prefill: {cfg5.name}")
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    by = {proj.name: proj for proj in cfg5.projs}
+    G = []
+    for names in PREFILL_GROUPS:
+        inps = [W.proj_inputs(cfg5, by[n], M5) for n in names]
+        K = by[names[0]].K
+        x = to_dev(inps[0].x_bf16.view(np.int16)).view(torch.bfloat16)
+        q = torch.empty((M5, K), dtype=torch.int8, device=dev)
+        d = torch.empty((M5,), dtype=torch.float32, device=dev)
+        qs = torch.empty((M5,), dtype=torch.int32, device=dev)
+        probs = [dict(packed=bl.pack_i2s(to_dev(inp.w_tern)),
+                      gamma=to_dev(np.array([inp.gamma], np.float32)),
+                      y=torch.empty((M5, by[n].N), dtype=torch.bfloat16, device=dev))
+                 for n, inp in zip(names, inps)]
+        G.append(dict(names=names, x=x, q=q, d=d, qs=qs,
+                      group=bl.GemmGroup(probs, q, d, qsum=qs),
+                      plain=bl.GemmGroup(probs, q, d),
+                      ops=sum(2 * M5 * by[n].N * by[n].K for n in names)))
+        del inps
+    torch.cuda.synchronize()
+    return cfg5, M5, G
 
 
 def main():
@@ -358,6 +392,19 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.mfma_counters:
+        # counter-collection mode for the prefill GEMMs: quantize (with token
+        # sums) and bl_gemm_group per input, --gemm-steps layers, eager
+        _, _, G = build_prefill(torch, bl, W, dev)
+        for _ in range(args.gemm_steps):
+            for e in G:
+                bl.quantize_act(e["x"], e["q"], e["d"], qsum=e["qs"])
+                e["group"]()
+        torch.cuda.synchronize()
+        log(f"mfma-counters mode: {args.gemm_steps} prefill layers ({len(G)} groups each)")
+        return
+
 
     # ----------------------------------------------------------------- decode
     cfg = W.CONFIGS[2]
@@ -569,32 +616,7 @@ def main():
 
     # ----------------------------------------------------------------- prefill
     if not args.no_gemm:
-        cfg5 = W.CONFIGS[5]
-        M5 = 2048
-        log(f"setup prefill: {cfg5.name}")
-        # one bf16 input per group of projections that read it; the group's
-        # GEMMs run through one bl_gemm_group call on its quantized codes
-        by = {proj.name: proj for proj in cfg5.projs}
-        G = []
-        for names in PREFILL_GROUPS:
-            inps = [W.proj_inputs(cfg5, by[n], M5) for n in names]
-            K = by[names[0]].K
-            x = to_dev(inps[0].x_bf16.view(np.int16)).view(torch.bfloat16)
-            q = torch.empty((M5, K), dtype=torch.int8, device=dev)
-            d = torch.empty((M5,), dtype=torch.float32, device=dev)
-            qs = torch.empty((M5,), dtype=torch.int32, device=dev)
-            probs = [dict(packed=bl.pack_i2s(to_dev(inp.w_tern)),
-                          gamma=to_dev(np.array([inp.gamma], np.float32)),
-                          y=torch.empty((M5, by[n].N), dtype=torch.bfloat16, device=dev))
-                     for n, inp in zip(names, inps)]
-            # the quantizer also writes the token sums; the GEMMs take them
-            # (offset weights). `plain` is the same group without them.
-            G.append(dict(names=names, x=x, q=q, d=d, qs=qs,
-                          group=bl.GemmGroup(probs, q, d, qsum=qs),
-                          plain=bl.GemmGroup(probs, q, d),
-                          ops=sum(2 * M5 * by[n].N * by[n].K for n in names)))
-            del inps
-        torch.cuda.synchronize()
+        cfg5, M5, G = build_prefill(torch, bl, W, dev)
 
         def layer(gemm_only=False, plain=False):
             for e in G:
