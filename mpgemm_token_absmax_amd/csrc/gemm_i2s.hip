@@ -53,6 +53,7 @@ namespace bl {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int64_t kGemmMaxK = (int64_t)1 << 24;    // per-lane load offsets stay 32-bit
 constexpr int kBK = 128;                 // weights (k) per step
 constexpr int kXcds = 8;
 
@@ -150,31 +151,41 @@ struct GemmCfg {
   static_assert(kBBytes % (16 * kThreads) == 0, "activation tile must split over the block");
 };
 
-// Direct-to-LDS loads of step ks into its stage (see k_gemm_i2s).
-template <int NB, int NA, int kStage, int kBBytes, int BN>
-__device__ __forceinline__ void issue_step(int8_t* smem, int ks, int wv, int lane,
-                                           const int8_t* const (&bsrc)[NB], int bchunk,
-                                           const uint8_t* const (&asrc)[NA], int64_t K,
-                                           int64_t RB) {
+// Direct-to-LDS loads of step ks into its stage (see k_gemm_i2s). Each
+// address is a uniform base (the block's tile origin, advanced by the step)
+// plus a per-lane 32-bit offset that stays fixed for the whole loop.
+// The last step when K % 128 == 64 reaches past K: there a lane's activation
+// chunk is moved 64 weights back (valid memory; its weights are zeroed
+// before the MFMA) and its packed half 16 bytes back (bwrap, awrap).
+template <int NB, int NA, int kStage, int kBBytes, int BN, bool KFULL>
+__device__ __forceinline__ void issue_step(int8_t* smem, int ks, int wv, const int8_t* bbase,
+                                           const uint32_t (&boff)[NB], uint32_t bwrap,
+                                           const uint8_t* abase, const uint32_t (&aoff)[NA],
+                                           uint32_t awrap, int nfull) {
   int8_t* st = smem + (ks & 1) * kStage;
   const int64_t kb = (int64_t)ks * kBK;
-  // chunks past K (the last step when K % 128 == 64) re-read a chunk 64
-  // weights earlier in the same row: valid memory, products with zeroed weights
-  int64_t boff = kb + bchunk;
-  if (boff >= K) boff -= 64;
+  const int8_t* bb = bbase + kb;
+  const uint8_t* ab = abase + kb / 4;
+  if (KFULL || ks < nfull) {                          // a whole step
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
-    lds_dma16(bsrc[i] + boff, st + (i * 4 + wv) * 1024);
-  int64_t aoff = kb / 4 + 16 * (lane >> 4 & 1);
-  if (aoff >= RB) aoff -= 16;
+    for (int i = 0; i < NB; ++i) lds_dma16(bb + boff[i], st + (i * 4 + wv) * 1024);
 #pragma unroll
-  for (int i = 0; i < NA; ++i)
-    if ((i * 4 + wv) * 32 < BN)                       // wave-uniform: rows of the tile exist
-      lds_dma16(asrc[i] + aoff, st + kBBytes + (i * 4 + wv) * 1024);
+    for (int i = 0; i < NA; ++i)
+      if ((i * 4 + wv) * 32 < BN)                     // wave-uniform: rows of the tile exist
+        lds_dma16(ab + aoff[i], st + kBBytes + (i * 4 + wv) * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) lds_dma16(bb + (boff[i] - bwrap), st + (i * 4 + wv) * 1024);
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      if ((i * 4 + wv) * 32 < BN)
+        lds_dma16(ab + (aoff[i] - awrap), st + kBBytes + (i * 4 + wv) * 1024);
+  }
 }
 
 // OFF: offset weights (w + 1) and qs[t] subtracted in the epilogue.
-template <int RT, int TT, int WRW, bool OFF>
+// KFULL: K % 128 == 0, every step whole (no code for a partial last step).
+template <int RT, int TT, int WRW, bool OFF, bool KFULL>
 __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(const GemmArgs g, int64_t K,
                                                           const int8_t* __restrict__ q,
                                                           const float* __restrict__ d,
@@ -208,30 +219,37 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
   const int64_t n_blk = (int64_t)rb * C::BN;
   const int64_t m_blk = (int64_t)tb * C::BM;
   const int nks = (int)((K + kBK - 1) / kBK);
+  const int nfull = (int)(K / kBK);                   // steps with all 128 weights
 
   // ---- per-lane source addresses of the direct-to-LDS loads ---------------
   // activations: wave instruction i covers tile rows t = (i*4 + wv)*8 + l/8;
   // LDS chunk p = l%8 of row t holds global chunk p ^ swz(t), and swz(t)
   // depends on (t/2) % 8 == (4*(wv%2) + l/16) % 8 only, the same for every i
-  const int8_t* bsrc[C::kBLoads];
+  // (offsets from the tile origin: at most 256*K and 128*K/4, below 2^32 for
+  // K <= 2^24, which the launcher ensures)
+  const int8_t* bbase = q + m_blk * K;
+  uint32_t boff[C::kBLoads];
   const int bchunk = 16 * ((lane & 7) ^ swz(2 * (4 * (wv & 1) + (lane >> 4))));
 #pragma unroll
   for (int i = 0; i < C::kBLoads; ++i) {
     const int t = (i * 4 + wv) * 8 + (lane >> 3);
     int64_t tok = m_blk + t;
     tok = tok < M ? tok : M - 1;
-    bsrc[i] = q + tok * K;
+    boff[i] = (uint32_t)((tok - m_blk) * K + bchunk);
   }
+  const uint32_t bwrap = bchunk >= 64 ? 64u : 0u;
   // packed weights: 32 bytes per row per step; wave instruction i covers rows
   // (i*4 + wv)*32 + 16*(l/32) + l%16, byte half (l/16)%2
-  const uint8_t* asrc[C::kALoads];
+  const uint8_t* abase = packed + n_blk * RB;
+  uint32_t aoff[C::kALoads];
 #pragma unroll
   for (int i = 0; i < C::kALoads; ++i) {
     const int row = (i * 4 + wv) * 32 + 16 * (lane >> 5) + (lane & 15);
     int64_t n = n_blk + (row < C::BN ? row : C::BN - 1);
     n = n < N ? n : N - 1;
-    asrc[i] = packed + n * RB;
+    aoff[i] = (uint32_t)((n - n_blk) * RB + 16 * (lane >> 4 & 1));
   }
+  const uint32_t awrap = (lane >> 4 & 1) ? 16u : 0u;
   v4i acc[RT][TT];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
@@ -239,8 +257,9 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
     for (int j = 0; j < TT; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
   if (nks > 0)
-    issue_step<C::kBLoads, C::kALoads, C::kStage, C::kBBytes, C::BN>(smem, 0, wv, lane, bsrc,
-                                                                     bchunk, asrc, K, RB);
+    issue_step<C::kBLoads, C::kALoads, C::kStage, C::kBBytes, C::BN, KFULL>(smem, 0, wv, bbase, boff,
+                                                                     bwrap, abase, aoff, awrap,
+                                                                     nfull);
 
   for (int ks = 0; ks < nks; ++ks) {
     wait_vm<0>();             // this wave's loads of step ks have landed
@@ -270,17 +289,24 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
 
     // unconditional, so the wait counts stay exact across the loop: the last
     // step re-loads itself into the idle buffer, which nothing reads again
-    issue_step<C::kBLoads, C::kALoads, C::kStage, C::kBBytes, C::BN>(
-        smem, ks + 1 < nks ? ks + 1 : ks, wv, lane, bsrc, bchunk, asrc, K, RB);
+    issue_step<C::kBLoads, C::kALoads, C::kStage, C::kBBytes, C::BN, KFULL>(
+        smem, ks + 1 < nks ? ks + 1 : ks, wv, bbase, boff, bwrap, abase, aoff, awrap, nfull);
 
-    const bool kin = kb + 32 * h < K;                 // this lane's 32 weights exist
+    if (!KFULL && ks >= nfull) {    // the last step of a K % 128 == 64 shape
+      const bool kin = kb + 32 * h < K;               // this lane's 32 weights exist
+      constexpr uint32_t kZeroCodes = OFF ? 0xAAAAAAAAu : 0u;   // words that decode to 0
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        aw[rt].x = kin ? aw[rt].x : kZeroCodes;
+        aw[rt].y = kin ? aw[rt].y : kZeroCodes;
+      }
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const uint32_t word = s == 0 ? aw[rt].x : aw[rt].y;
-        v4i af = OFF ? decode_word_p1(word) : decode_word(word);
-        if (!kin) af = v4i{0, 0, 0, 0};
+        const v4i af = OFF ? decode_word_p1(word) : decode_word(word);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
           acc[rt][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[s][tt], acc[rt][tt], 0, 0, 0);
@@ -310,7 +336,7 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
   }
 }
 
-template <int RT, int TT, int WRW, bool OFF>
+template <int RT, int TT, int WRW, bool OFF, bool KFULL>
 hipError_t launch_cfg(const GemmProblem* const* p, int count, int64_t K, const int8_t* q,
                       const float* d, const int* qs, int64_t M, hipStream_t s) {
   using C = GemmCfg<RT, TT, WRW>;
@@ -328,13 +354,23 @@ hipError_t launch_cfg(const GemmProblem* const* p, int count, int64_t K, const i
   if (rb * ntb > INT32_MAX) return hipErrorInvalidValue;
   if (C::kLds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_gemm_i2s<RT, TT, WRW, OFF>),
+        reinterpret_cast<const void*>(&k_gemm_i2s<RT, TT, WRW, OFF, KFULL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW, OFF>), dim3((unsigned)(rb * ntb)), dim3(kThreads),
+  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW, OFF, KFULL>), dim3((unsigned)(rb * ntb)), dim3(kThreads),
                      C::kLds, s, a, K, q, d, qs, M, (int)ntb);
   return hipGetLastError();
+}
+
+template <int RT, int TT, int WRW>
+hipError_t launch_tiles(bool off, bool full, const GemmProblem* const* p, int count, int64_t K,
+                        const int8_t* q, const float* d, const int* qs, int64_t M, hipStream_t s) {
+  if (off)
+    return full ? launch_cfg<RT, TT, WRW, true, true>(p, count, K, q, d, qs, M, s)
+                : launch_cfg<RT, TT, WRW, true, false>(p, count, K, q, d, qs, M, s);
+  return full ? launch_cfg<RT, TT, WRW, false, true>(p, count, K, q, d, qs, M, s)
+              : launch_cfg<RT, TT, WRW, false, false>(p, count, K, q, d, qs, M, s);
 }
 
 }  // namespace
@@ -342,9 +378,9 @@ hipError_t launch_cfg(const GemmProblem* const* p, int count, int64_t K, const i
 hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const int8_t* q,
                              const float* d, const int* qs, int64_t M, hipStream_t s) {
   hipError_t e = hipSuccess;
-  if (K % 64 != 0 || M <= 16) {
+  if (K % 64 != 0 || M <= 16 || K > kGemmMaxK) {
     for (int i = 0; i < count && e == hipSuccess; ++i)
-      e = K % 64 != 0 ? launch_generic(p[i].packed, p[i].gamma, p[i].N, K, q, d, M, p[i].y,
+      e = K % 64 != 0 || K > kGemmMaxK ? launch_generic(p[i].packed, p[i].gamma, p[i].N, K, q, d, M, p[i].y,
                                        p[i].ytype, s)
                       : launch_gemv(p[i].packed, p[i].gamma, p[i].N, K, q, d, M, p[i].y,
                                     p[i].ytype, s);
@@ -362,12 +398,9 @@ hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const i
   }
   // offset weights need the token sums and |acc + qs[t]| <= 254*K in int32
   const bool off = qs != nullptr && 254 * K <= INT32_MAX;
-  if (nbig)
-    e = off ? launch_cfg<4, 8, 2, true>(big, nbig, K, q, d, qs, M, s)
-            : launch_cfg<4, 8, 2, false>(big, nbig, K, q, d, qs, M, s);
-  if (e == hipSuccess && nsmall)
-    e = off ? launch_cfg<2, 4, 2, true>(small, nsmall, K, q, d, qs, M, s)
-            : launch_cfg<2, 4, 2, false>(small, nsmall, K, q, d, qs, M, s);
+  const bool full = K % kBK == 0;
+  if (nbig) e = launch_tiles<4, 8, 2>(off, full, big, nbig, K, q, d, qs, M, s);
+  if (e == hipSuccess && nsmall) e = launch_tiles<2, 4, 2>(off, full, small, nsmall, K, q, d, qs, M, s);
   return e;
 }
 
