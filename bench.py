@@ -138,8 +138,9 @@ def measure_floors(torch, dev, stream, capture_fn, R, groups):
 
 def decode_more(torch, bl, W, dev, stream):
     """The 7B-class layer at 1, 4 and 16 tokens (4 group launches per layer,
-    16 rotating layer copies = 810 MB) and one-token GEMVs of the 100B-class
-    shapes (one launch, rotating copies), in GB/s of packed weights."""
+    a stream over 32 distinct layer copies = 1.62 GB) and one-token GEMVs of
+    the 100B-class shapes (one launch, rotating copies), in GB/s of packed
+    weights."""
     out = {}
     cfg = W.CONFIGS[4]
     layer_groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
@@ -148,7 +149,7 @@ def decode_more(torch, bl, W, dev, stream):
         inp = W.proj_inputs(cfg, proj, 1, with_acts=False)
         packed[proj.name] = bl.pack_i2s(torch.from_numpy(inp.w_f32).to(dev))
         del inp
-    R = 16
+    R = 32
     copies = [{n: (pg[0] if r == 0 else pg[0].clone(), pg[1]) for n, pg in packed.items()}
               for r in range(R)]
     for M in (1, 4, 16):
