@@ -32,7 +32,11 @@
 //    exactly the sum over those k.
 //  * Loads are unconditional with clamped addresses; out-of-range tokens and
 //    rows only reach outputs that are never stored, and weights past K are
-//    zeroed before the MFMA, so stale activations there add nothing.
+//    zeroed before the MFMA, so stale activations there add nothing. The
+//    vector ALU work of a step is kept to the decode (it does not hide under
+//    the other wave's MFMAs): load addresses are a uniform tile base plus a
+//    fixed per-lane 32-bit offset, and shapes with K % 128 == 0 (the kernel
+//    flag KFULL) compile no code for a partial last step.
 //  * Blocks are ordered so that consecutive blocks on one XCD (blocks are
 //    dealt to the 8 XCDs round robin) share a token tile, whose activations
 //    then stay in that XCD's L2.
@@ -43,9 +47,9 @@
 //    {-1, 0, +1}, so the accumulator holds acc + qs[t] exactly and the
 //    epilogue subtracts qs[t]. -1 is the byte 0xFF; operands of 0..2 switch
 //    far fewer multiplier bits, the matrix cores draw less power and the
-//    clock, which this GEMM holds well below its nominal value, rises:
-//    measured 3-7% more throughput on the 100B-class shapes. The decode is
-//    the same 9 ops with other tables.
+//    clock (power-limited under a full matrix load) rises: measured 3-7%
+//    more throughput on the 100B-class shapes. The decode is the same 9 ops
+//    with other tables.
 #include "common.hpp"
 #include "launch.hpp"
 
