@@ -239,32 +239,74 @@ def norm_layer_bench(torch, bl, W, dev, stream):
 
 def t3_bench(torch, bl, W, dev, stream):
     """Base-3 weights (five per byte, 1.6 bits per weight) against I2_S (2 bits
-    per weight) through the GEMV kernels of the same structure (int8 codes in,
-    one token): bl_gemv_t3 and bl_gemv, graph replays over copies of the
-    packed weights (>= 700 MB). Reported per format: microseconds per call,
-    GB/s of packed bytes and billions of weights per second."""
+    per weight), one token:
+      - through the GEMV kernels of the same structure (int8 codes in):
+        bl_gemv_t3 and bl_gemv ("t3", "i2s");
+      - through the fused one-token decode (bf16 x in, quantize in the
+        kernel): bl_decode_group_t3 and bl_decode_group ("t3_fused",
+        "i2s_fused");
+    graph replays over copies of the packed weights (>= 700 MB), microseconds
+    per call, GB/s of packed bytes and billions of weights per second; and the
+    BitNet-2B-like decode layer (4 fused launches, 32 rotating layer copies)
+    in both formats."""
     out = {}
     for N, K in ((2560, 2560), (6912, 2560), (2560, 6912), (28672, 8192), (8192, 28672)):
         t = torch.from_numpy(W.ternary_drawn(7 + N + K, N, K, 1.0 / 3.0)).to(dev)
         p2, p3 = bl.pack_i2s(t), bl.pack_t3(t)
         del t
         x = torch.from_numpy(W.activations_bf16(9 + K, 1, K, 0.005, 50.0).view(np.int16)).to(dev)
-        q, d = bl.quantize_act(x.view(torch.bfloat16))
+        xb = x.view(torch.bfloat16)
+        q, d = bl.quantize_act(xb)
         gam = torch.tensor([W.GAMMA_DRAWN], dtype=torch.float32, device=dev)
         R = max(2, -(-700_000_000 // p3.numel()))
         y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
         rec = {}
-        for name, p, fn in (("i2s", p2, bl.gemv), ("t3", p3, bl.gemv_t3)):
+        for name, p, fn in (("i2s", p2, bl.gemv), ("t3", p3, bl.gemv_t3),
+                            ("i2s_fused", p2, bl.DecodeGroup), ("t3_fused", p3, bl.DecodeGroupT3)):
             copies = [p] + [p.clone() for _ in range(R - 1)]
-            g = capture_fns(torch, stream, [(lambda c=c: fn(c, gam, q, d, out=y)) for c in copies])
+            if name.endswith("_fused"):
+                fns = [fn([dict(packed=c, gamma=gam, x=xb, y=y)]) for c in copies]
+                fns[0]()
+            else:
+                fns = [(lambda c=c: fn(c, gam, q, d, out=y)) for c in copies]
+            g = capture_fns(torch, stream, fns)
             us = replay_us(torch, stream, g, R, reps=10)
             rec[name] = {"us": round(us, 3), "packed_bytes": p.numel(),
                          "gbs": round(p.numel() / (us * 1e-6) / 1e9, 1),
                          "gweights_s": round(N * K / (us * 1e-6) / 1e9, 1)}
-            del g, copies
+            del g, copies, fns
         out[f"N{N}_K{K}"] = rec
         del p2, p3
         torch.cuda.empty_cache()
+    # the 2B decode layer, both formats
+    cfg = W.CONFIGS[2]
+    layer_groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    gam = torch.tensor([W.GAMMA_DRAWN], dtype=torch.float32, device=dev)
+    xs, tern = {}, {}
+    for proj in cfg.projs:
+        inp = W.proj_inputs(cfg, proj, 1)
+        tern[proj.name] = torch.from_numpy(inp.w_tern).to(dev)
+        xs[proj.name] = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+    R = 32
+    layer = {}
+    for name, pack, Grp in (("i2s_fused", bl.pack_i2s, bl.DecodeGroup),
+                            ("t3_fused", bl.pack_t3, bl.DecodeGroupT3)):
+        base = {n: pack(t) for n, t in tern.items()}
+        nbytes = sum(p.numel() for p in base.values())
+        copies = [{n: (p if r == 0 else p.clone()) for n, p in base.items()} for r in range(R)]
+        ys = {n: torch.empty((1, t.shape[0]), dtype=torch.bfloat16, device=dev) for n, t in tern.items()}
+        fns = [Grp([dict(packed=c[n], gamma=gam, x=xs[n], y=ys[n]) for n in names])
+               for c in copies for names in layer_groups]
+        for f in fns[:4]:
+            f()
+        g = capture_fns(torch, stream, fns)
+        us = replay_us(torch, stream, g, 1, reps=10) / R
+        layer[name] = {"us_per_layer": round(us, 3), "packed_bytes": nbytes,
+                       "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del g, fns, copies, base
+    out["bitnet2b_decode_layer"] = layer
+    del tern, xs
+    torch.cuda.empty_cache()
     return out
 
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define BL_ABI_VERSION 2
+#define BL_ABI_VERSION 3
 
 /* Status codes returned by every call. */
 enum {
@@ -332,6 +332,25 @@ typedef struct bl_decode_problem {
 } bl_decode_problem;
 
 int bl_decode_group(const bl_decode_problem *problems, int count, int64_t M, void *stream);
+
+/*
+ * bl_decode_group_t3 -- bl_decode_group over base-3 packed weights (five per
+ * byte, 1.6 bits per weight).
+ * Defines: the composition of bl_quantize_act and bl_gemv_t3 ([BN] Part A
+ * 2.3 / 4.1: the same exact contraction; the format table's sub-2-bit
+ * element-wise formats for the weight bytes), fused as in [FF] "融合内核设计".
+ * Results (y, and q and d when requested) are bit-identical to
+ * bl_quantize_act followed by bl_gemv_t3, and to bl_decode_group on the I2_S
+ * packing of the same weights.
+ *   problems, count, M: as bl_decode_group, except that packed is uint8
+ *     [N][bl_pack_t3_row_bytes(K)] from bl_pack_t3 and K % 16 == 0
+ *     (K <= 65536; BL_ERR_SHAPE otherwise). At M == 1 one launch quantizes
+ *     and contracts every problem (q and d optional); at M > 1 q and d are
+ *     required and receive the codes from a quantize pass inside the call,
+ *     which bl_gemv_t3 then reads, one launch per problem.
+ * Outputs must not alias any input or each other.
+ */
+int bl_decode_group_t3(const bl_decode_problem *problems, int count, int64_t M, void *stream);
 
 /*
  * bl_decode_norm_group -- one token through the residual add, RMSNorm and the

@@ -32,6 +32,7 @@ from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I
 __all__ = ["quantize_act", "quantize_act_tensor", "rmsnorm_quant", "pack_i2s", "pack_i2s_workspace",
            "pack_t3", "gemv_t3", "gemv", "gemm",
            "gemm_workspace", "gemm_group", "GemmGroup", "decode_group", "DecodeGroup",
+           "decode_group_t3", "DecodeGroupT3",
            "NormDecodeGroup",
            "BitLinearError", "status_string",
            "lib", "OUT_TYPES"]
@@ -357,6 +358,11 @@ class DecodeGroup:
     x (bf16 [M][K]), and optional y (output), q (int8 [M][K]) and d (fp32 [M])
     buffers; out_dtype applies to every y that is allocated here."""
 
+    _fn = "bl_decode_group"
+
+    def _row_bytes(self, K: int) -> int:
+        return K // 4
+
     def __init__(self, problems, out_dtype: str = "bf16"):
         if not 1 <= len(problems) <= MAX_GROUP:
             raise ValueError(f"1..{MAX_GROUP} problems per group")
@@ -371,7 +377,7 @@ class DecodeGroup:
                 raise ValueError("x rows must be contiguous")
             N, KB = packed.shape
             Mi, K = x.shape
-            if KB * 4 != K:
+            if KB != self._row_bytes(K):
                 raise ValueError("packed does not match x")
             M = Mi if M is None else M
             if Mi != M:
@@ -398,9 +404,19 @@ class DecodeGroup:
         return [p["y"] for p in self.problems]
 
     def __call__(self):
-        check("bl_decode_group", lib().bl_decode_group(self._arr, len(self.problems), self.M,
-                                                       _stream(self._device)))
+        check(self._fn, getattr(lib(), self._fn)(self._arr, len(self.problems), self.M,
+                                                 _stream(self._device)))
         return self.outputs
+
+
+class DecodeGroupT3(DecodeGroup):
+    """A prepared bl_decode_group_t3 call: DecodeGroup over base-3 packed
+    weights (packed: uint8 [N][64*ceil(K/320)] from pack_t3; K % 16 == 0)."""
+
+    _fn = "bl_decode_group_t3"
+
+    def _row_bytes(self, K: int) -> int:
+        return 64 * ((K + 319) // 320) if K > 0 else 0
 
 
 class NormDecodeGroup(DecodeGroup):
@@ -441,3 +457,8 @@ def decode_group(problems, out_dtype: str = "bf16"):
     """One fused launch: quantize each problem's bf16 x per token, GEMV, dequant.
     Returns the list of outputs y."""
     return DecodeGroup(problems, out_dtype)()
+
+
+def decode_group_t3(problems, out_dtype: str = "bf16"):
+    """decode_group over base-3 packed weights (pack_t3). Returns the outputs y."""
+    return DecodeGroupT3(problems, out_dtype)()

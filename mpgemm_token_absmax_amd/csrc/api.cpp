@@ -280,16 +280,23 @@ int bl_decode_norm_group(const bl_decode_problem* problems, int count, const uin
   return hip_status(bl::launch_decode_norm_group(gr, as_stream(stream)));
 }
 
-int bl_decode_group(const bl_decode_problem* problems, int count, int64_t M, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the I2_S and base-3 decode groups (kmod: required
+// divisor of K; t3: base-3 row bytes); fills g on success.
+int check_decode_group(const bl_decode_problem* problems, int count, int64_t M, int kmod,
+                       bool t3, bl::DecodeGroup& g) {
   if (count < 0 || count > bl::kMaxGroup || M < 0 || M > kGemvMaxM) return BL_ERR_SHAPE;
   if (count == 0 || M == 0) return BL_OK;
   if (!problems) return BL_ERR_NULL;
-  bl::DecodeGroup g{};
   g.M = (int)M;
   for (int i = 0; i < count; ++i) {
     const bl_decode_problem& p = problems[i];
-    if (p.N < 0 || p.K < 0 || p.K % 64 != 0 || p.ldx < p.K || p.K > kDecodeMaxK)
+    if (p.N < 0 || p.K < 0 || p.K % kmod != 0 || p.ldx < p.K || p.K > kDecodeMaxK)
       return BL_ERR_SHAPE;
+    if (t3 && p.N * 64 * ((p.K + 319) / 320) > ((int64_t)1 << 40)) return BL_ERR_SHAPE;
     if (p.ytype < BL_OUT_I32 || p.ytype > BL_OUT_BF16) return BL_ERR_DTYPE;
     if (p.ytype != BL_OUT_I32 && p.K > kFp32ExactK) return BL_ERR_SHAPE;
     if (127 * p.K > INT32_MAX) return BL_ERR_SHAPE;
@@ -297,7 +304,7 @@ int bl_decode_group(const bl_decode_problem* problems, int count, int64_t M, voi
     if (!p.y || (p.K > 0 && (!p.packed || !p.x)) || (p.ytype != BL_OUT_I32 && !p.gamma))
       return BL_ERR_NULL;
     if (M > 1 && p.K > 0 && (!p.q || !p.d)) return BL_ERR_NULL;   // staging of the codes
-    if (p.ldx % 4 != 0 || !aligned(p.y, 16)) return BL_ERR_ALIGN;
+    if ((p.K > 0 && p.ldx % 4 != 0) || !aligned(p.y, 16)) return BL_ERR_ALIGN;   // K == 0 reads no x
     if (p.K > 0 && (!aligned(p.packed, 16) || !aligned(p.x, 16))) return BL_ERR_ALIGN;
     if ((p.q && !aligned(p.q, 16)) || (p.d && !aligned(p.d, 4)) ||
         (p.gamma && !aligned(p.gamma, 4)))
@@ -314,8 +321,25 @@ int bl_decode_group(const bl_decode_problem* problems, int count, int64_t M, voi
     d.y = p.y;
     d.ytype = p.ytype;
   }
-  if (g.count == 0) return BL_OK;
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bl_decode_group(const bl_decode_problem* problems, int count, int64_t M, void* stream) {
+  bl::DecodeGroup g{};
+  const int st = check_decode_group(problems, count, M, 64, false, g);
+  if (st != BL_OK || g.count == 0) return st;
   return hip_status(bl::launch_decode_group(g, as_stream(stream)));
+}
+
+int bl_decode_group_t3(const bl_decode_problem* problems, int count, int64_t M, void* stream) {
+  bl::DecodeGroup g{};
+  const int st = check_decode_group(problems, count, M, 16, true, g);
+  if (st != BL_OK || g.count == 0) return st;
+  return hip_status(bl::launch_decode_group_t3(g, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -74,6 +74,9 @@ hipError_t launch_pack_t3(const void* w, bool f32, int64_t N, int64_t K, uint8_t
 hipError_t launch_gemv_t3(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                           const int8_t* q, const float* d, int64_t M, void* y, int ytype,
                           hipStream_t s);
+// One token: quantize in the kernel (K % 16 == 0, K <= 65536); several tokens:
+// quantize every problem's x into its q and d, then launch_gemv_t3 per problem.
+hipError_t launch_decode_group_t3(DecodeGroup& g, hipStream_t s);
 // Exponent bins and gamma of an fp32 matrix (the first two launches of the
 // fp32 I2_S packing): gamma[0] = fl32(exact sum |w| / (N*K)).
 hipError_t launch_absmean_gamma(const float* w, int64_t N, int64_t K, float* gamma, void* ws,

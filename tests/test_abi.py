@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bl_abi_version() == 2
+    assert lib.bl_abi_version() == 3
     for s in (L.BL_OK, L.BL_ERR_NULL, L.BL_ERR_SHAPE, L.BL_ERR_ALIGN, L.BL_ERR_DTYPE,
               L.BL_ERR_WORKSPACE, L.BL_ERR_HIP, L.BL_ERR_ALIAS):
         assert lib.bl_status_string(s)
@@ -159,6 +159,39 @@ def test_decode_group_validation(lib):
     assert call([prob()], M=0) == L.BL_OK
     assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK      # nothing to compute
     assert lib.bl_decode_group(None, 1, 1, None) == L.BL_ERR_NULL
+
+
+def test_decode_group_t3_validation(lib):
+    """The base-3 group takes the I2_S group's rules except K % 16 (not 64)."""
+    P = L.DecodeProblem
+
+    def prob(**kw):
+        base = dict(packed=A16, gamma=B16, N=64, K=336, x=C16, ldx=336, q=None, d=None, y=E16,
+                    ytype=2)
+        base.update(kw)
+        return P(**base)
+
+    def call(probs, M=1):
+        arr = (P * max(1, len(probs)))(*probs)
+        return lib.bl_decode_group_t3(arr, len(probs), M, None)
+
+    assert call([prob()] * 9) == L.BL_ERR_SHAPE
+    assert call([prob()], M=17) == L.BL_ERR_SHAPE
+    assert call([prob(K=344, ldx=344)]) == L.BL_ERR_SHAPE   # K % 16
+    assert call([prob(ldx=320)]) == L.BL_ERR_SHAPE          # ldx < K
+    assert call([prob(K=65552, ldx=65552, ytype=0)]) == L.BL_ERR_SHAPE   # K <= 65536
+    assert call([prob(N=1 << 33, K=65536, ldx=65536, ytype=0)]) == L.BL_ERR_SHAPE   # 2^40 bytes
+    assert call([prob(ytype=3)]) == L.BL_ERR_DTYPE
+    assert call([prob(packed=None)]) == L.BL_ERR_NULL
+    assert call([prob(x=None)]) == L.BL_ERR_NULL
+    assert call([prob(), prob(gamma=None)]) == L.BL_ERR_NULL
+    assert call([prob()], M=3) == L.BL_ERR_NULL             # several tokens need q and d
+    assert call([prob(packed=A16 + 4)]) == L.BL_ERR_ALIGN
+    assert call([prob(y=E16 + 8)]) == L.BL_ERR_ALIGN
+    assert call([prob(ldx=338)]) == L.BL_ERR_ALIGN
+    assert call([], M=1) == L.BL_OK
+    assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK
+    assert lib.bl_decode_group_t3(None, 1, 1, None) == L.BL_ERR_NULL
 
 
 def test_gemm_group_validation(lib):

@@ -774,6 +774,95 @@ def test_gemv_t3_empty_and_zero_k():
     assert y0.shape == (1, 0)
 
 
+def _decode_group_t3_case(bl, M, shapes, seed, with_qd=True, out_types=None, zero_x=False):
+    say(f"decode_group_t3 M={M} shapes={shapes} with_qd={with_qd}")
+    ots = out_types or ["bf16", "f32", "i32"]
+    probs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x = W.activations_bf16(seed + 10 * i, M, K, outlier_frac=0.01, outlier_scale=20.0)
+        if zero_x or M > 2:
+            x[M - 1] = 0                                  # an all-zero token
+        t = W.ternary_drawn(seed + 10 * i + 1, N, K, 0.4)
+        ot = ots[i % len(ots)]
+        p = dict(packed=bl.pack_t3(dev(t)), gamma=dev(np.array([GAMMA], np.float32)),
+                 x=dev_bf16(x), out_dtype=ot)
+        if with_qd:
+            p["q"] = torch.full((M, K), 99, dtype=torch.int8, device="cuda")
+            p["d"] = torch.full((M,), -1.0, dtype=torch.float32, device="cuda")
+        probs.append(p)
+        refs.append((x, t, ot))
+    ys = bl.DecodeGroupT3(probs)()
+    torch.cuda.synchronize()
+    for p, y, (x, t, ot) in zip(probs, ys, refs):
+        q_ref, d_ref = oracle.quantize_act_absmax(x)
+        acc = oracle.mpgemm_acc(q_ref, t)
+        if with_qd:
+            assert np.array_equal(host(p["q"]), q_ref)
+            assert np.array_equal(host(p["d"]).view(np.uint32), d_ref.view(np.uint32))
+        kw = {"i32": "y_i32", "f32": "y_f32", "bf16": "y_bf16"}[ot]
+        check_outputs(acc, GAMMA, d_ref, **{kw: host(y)})
+        # identical to quantize + the base-3 GEMV, and to the I2_S decode group
+        q, d = bl.quantize_act(p["x"])
+        y2 = bl.gemv_t3(p["packed"], p["gamma"], q, d, out_dtype=ot)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y2).view(np.uint8), host(y).view(np.uint8))
+        K = x.shape[1]
+        if K % 64 == 0:
+            (y3,) = bl.decode_group([dict(packed=bl.pack_i2s(dev(t)), gamma=p["gamma"], x=p["x"],
+                                          out_dtype=ot)])
+            torch.cuda.synchronize()
+            assert np.array_equal(host(y3).view(np.uint8), host(y).view(np.uint8))
+
+
+def test_decode_group_t3_one_token():
+    """One launch per group at M == 1, through every block configuration:
+    one segment per wave (K = 16 with a single step, 336, 2560), 2-4 segments
+    (6912, 4160 with an odd step count), 8 waves (12800) and two load batches
+    (28672), small problems riding with large ones, ragged row blocks, and
+    every output type."""
+    bl = _bl()
+    _decode_group_t3_case(bl, 1, [(2560, 2560), (640, 2560), (640, 2560)], seed=1200)
+    _decode_group_t3_case(bl, 1, [(17, 336), (1, 16), (33, 1296)], seed=1210)
+    _decode_group_t3_case(bl, 1, [(2560, 6912), (1000, 4160)], seed=1220,
+                          out_types=["bf16", "i32"])
+    _decode_group_t3_case(bl, 1, [(100, 12800), (16, 320)], seed=1230, out_types=["f32"])
+    _decode_group_t3_case(bl, 1, [(8192, 28672)], seed=1240, with_qd=False)
+    _decode_group_t3_case(bl, 1, [(129, 8192)], seed=1250, zero_x=True)
+
+
+def test_decode_group_t3_longest_k():
+    """The 16-wave block (more than 64 KB of LDS) at K = 65536 and 61456."""
+    bl = _bl()
+    _decode_group_t3_case(bl, 1, [(24, 65536), (9, 61456)], seed=1260, out_types=["f32", "bf16"])
+
+
+@pytest.mark.parametrize("M", [2, 3, 16])
+def test_decode_group_t3_tokens(M):
+    """Several tokens: quantize pass, then the base-3 GEMV per problem."""
+    bl = _bl()
+    _decode_group_t3_case(bl, M, [(100, 320), (33, 1296), (640, 2560)], seed=1270 + M)
+
+
+def test_decode_group_t3_zero_k():
+    """A K == 0 problem gives zeros (and a zero scale) next to a normal one."""
+    bl = _bl()
+    say("decode_group_t3 K = 0")
+    x0 = torch.zeros((1, 0), dtype=torch.bfloat16, device="cuda")
+    d0 = torch.full((1,), 5.0, dtype=torch.float32, device="cuda")
+    y0 = torch.full((1, 7), 3.0, dtype=torch.float32, device="cuda")
+    t = W.ternary_drawn(1290, 40, 336, 0.4)
+    x = W.activations_bf16(1291, 1, 336)
+    gamma = dev(np.array([GAMMA], np.float32))
+    ys = bl.decode_group_t3([dict(packed=torch.zeros((7, 0), dtype=torch.uint8, device="cuda"),
+                                  gamma=gamma, x=x0, y=y0, d=d0, out_dtype="f32"),
+                             dict(packed=bl.pack_t3(dev(t)), gamma=gamma, x=dev_bf16(x),
+                                  out_dtype="f32")])
+    torch.cuda.synchronize()
+    assert not host(ys[0]).any() and host(d0)[0] == 0.0
+    q_ref, d_ref = oracle.quantize_act_absmax(x)
+    check_outputs(oracle.mpgemm_acc(q_ref, t), GAMMA, d_ref, y_f32=host(ys[1]))
+
+
 NORM_GROUP_CASES = [
     ("qkv_2b", [(2560, 2560), (640, 2560), (640, 2560)], True, 1e-5),
     ("gate_up_2b", [(6912, 2560), (6912, 2560)], True, 1e-6),

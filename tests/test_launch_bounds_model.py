@@ -591,3 +591,120 @@ def test_decodet_group_len_max():
         for kmax in (7168, 28672, 32768):
             for buf, lo, hi, size in decodet_ranges(20, K, 4, K, group_kmax=kmax):
                 assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+# ---- one-token fused decode over base-3 weights ----------------------------
+
+def t3_segs_per_wave(K, wpb):
+    nseg = ((K + 319) // 320 + 1) // 2
+    return (nseg + wpb - 1) // wpb
+
+
+def decode1_t3_config(K):
+    """(WPB, XR, U, SINGLE, len) that launch_decode_group_t3 picks at M == 1."""
+    w4 = t3_segs_per_wave(K, 4)
+    if w4 <= 1:
+        return 4, 2, 1, True, w4
+    if w4 == 2:
+        return 4, 3, 2, True, w4
+    if w4 <= 4:
+        return 4, 5, 4, True, w4
+    w8 = t3_segs_per_wave(K, 8)
+    if w8 <= 4:
+        return 8, 5, 4, True, w8
+    if w8 <= 8:
+        return 8, 10, 4, False, w8
+    w16 = t3_segs_per_wave(K, 16)
+    return 16, 10, 4, False, w16
+
+
+def decode1_t3_ranges(N, K, group_kmax=None):
+    """Yield (buffer, lo, hi, size) of every global load and LDS access of
+    k_decode1_t3 for one problem of a group whose largest K is group_kmax,
+    and check that every LDS byte a fragment read covers was written."""
+    assert K % 16 == 0 and K >= 16
+    WPB, XR, U, single, len_max = decode1_t3_config(K if group_kmax is None else group_kmax)
+    nsteps = (K + 319) // 320
+    RBt = 64 * nsteps
+    nseg = (nsteps + 1) // 2
+    length = (nseg + WPB - 1) // WPB
+    assert length <= len_max
+    assert XR * WAVE >= length * 80                   # the x chunks cover the part
+    if single:
+        assert U >= length
+    region = len_max * 640
+    assert WPB * region + (WPB - 1) * 2 * WAVE * 16 + 4 * WPB <= 160 * 1024   # LDS per block
+    for b, wk in itertools.product(range((N + 15) // 16), range(WPB)):
+        n0 = b * 16
+        ja = min(wk * length, nseg)
+        jb = min(ja + length, nseg)
+        klo, khi = min(ja * 640, K), min(jb * 640, K)
+        assert (khi - klo) % 16 == 0
+        nch = (khi - klo) // 8
+        cbase = klo // 8 if nch > 0 else 0
+        clast = nch - 1 if nch > 0 else 0
+        for u in range(XR):
+            c = cbase + np.minimum(LANES + u * WAVE, clast)
+            yield "x", (16 * c).min(), (16 * c + 16).max(), 2 * K
+        rows = [np.minimum(n0 + R8_OF, N - 1), np.minimum(n0 + 8 + R8_OF, N - 1)]
+        bases = [ja] if single else sorted({bb for j in (range(ja, jb, 2 * U) or [ja])
+                                            for bb in (j, j + U, j + 2 * U)})
+        for base in bases:
+            for u in range(U):
+                seg = max(min(base + u, jb - 1), 0)
+                off = np.minimum(seg * 128 + 16 * C_OF, RBt - 16)
+                for r in rows:
+                    lo = r * RBt + off
+                    yield "packed", lo.min(), (lo + 16).max(), N * RBt
+        written = np.zeros(region, bool)
+        written[:8 * nch] = True                       # codes
+        zb = np.arange(khi - klo, (jb - ja) * 640, 16)
+        for z in zb:
+            written[z:z + 16] = True                   # zeros past K
+        if nch > 0:
+            yield "lds", 0, 8 * nch, region
+        if len(zb):
+            yield "lds", int(zb.min()), int(zb.max()) + 16, region
+        for seg in range(ja, jb):
+            for p in range(5):
+                lo = 80 * (2 * H_OF + (LANES & 1)) + (seg - ja) * 640 + 16 * p
+                yield "lds", lo.min(), (lo + 16).max(), region
+                for a in np.unique(lo):
+                    assert written[a:a + 16].all(), (seg, p, a)
+
+
+DECODE1_T3_SHAPES = [(16, 16), (17, 336), (2560, 2560), (640, 2560), (6912, 2560), (2560, 6912),
+                     (1000, 4160), (28672, 8192), (8192, 28672), (40, 65536), (33, 61456),
+                     (24, 12800), (8, 1296)]
+
+
+@pytest.mark.parametrize("N,K", DECODE1_T3_SHAPES, ids=[f"N{n}K{k}" for n, k in DECODE1_T3_SHAPES])
+def test_decode1_t3_loads_in_bounds(N, K):
+    for buf, lo, hi, size in decode1_t3_ranges(min(N, 64), K):
+        assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_decode1_t3_group_len_max():
+    for K in (16, 336, 2560, 8192):
+        for kmax in (2560, 8192, 28672, 65536):
+            if kmax < K:                              # the group's largest K
+                continue
+            for buf, lo, hi, size in decode1_t3_ranges(20, K, group_kmax=kmax):
+                assert 0 <= lo and hi <= size, (buf, lo, hi, size)
+
+
+def test_decode1_t3_unit_pairing():
+    """The unit a lane loads (c) is the unit whose codes its kept MFMA column
+    reads: column n of k-group h reads unit 2h + (n & 1) of the segment."""
+    for lane in range(WAVE):
+        r8, c = lane & 7, lane >> 3
+        m, h = lane & 15, lane >> 4
+        assert m == r8 + 8 * (c & 1) and h == c // 2
+        col = 0 if m < 8 else 1
+        assert 2 * h + (col & 1) == c
+    # row r of half i: D[r][0] (lane 16*(r//4), comp r%4) + D[8+r][1] (lane 33 + 16*(r//4))
+    for r in range(8):
+        lane0 = 16 * (r // 4)
+        assert (lane0 & 15) == 0 and 4 * (lane0 >> 4) + r % 4 == r
+        lane1 = lane0 + 33
+        assert (lane1 & 15) == 1 and 4 * (lane1 >> 4) + r % 4 == 8 + r
