@@ -140,7 +140,22 @@ def decode_more(torch, bl, W, dev, stream):
     """The 7B-class layer at 1, 4 and 16 tokens (4 group launches per layer,
     a stream over 32 distinct layer copies = 1.62 GB) and one-token GEMVs of
     the 100B-class shapes (one launch, rotating copies), in GB/s of packed
-    weights."""
+    weights; next to each 100B-class GEMV, a streaming read of the same bytes
+    (libblprobe.so) in the same setting."""
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "mpgemm_token_absmax_amd", "libblprobe.so"))
+    probe.blp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+
+    def stream_read(buf, nbytes, blocks):
+        def f():
+            rc = probe.blp_stream_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream)
+            if rc:
+                raise RuntimeError(f"blp_stream_read failed ({rc})")
+        return f
+
     out = {}
     cfg = W.CONFIGS[4]
     layer_groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
@@ -179,9 +194,19 @@ def decode_more(torch, bl, W, dev, stream):
         launches[0]()
         g = capture_fns(torch, stream, launches)
         us = replay_us(torch, stream, g, R, reps=10)
+        del g
+        # floor: a streaming read of the same bytes by as many threads as the
+        # decode launch has (16 rows per block, 256 or 512 threads), R copies
+        nbytes = N * K // 4
+        blocks = (N + 15) // 16 * (2 if K > 16384 else 1)
+        bufs = [c.problems[0]["packed"] for c in launches]
+        g = capture_fns(torch, stream, [stream_read(b, nbytes, blocks) for b in bufs])
+        floor = replay_us(torch, stream, g, R, reps=10)
         out[f"one_token_gemv_N{N}_K{K}"] = {"us": round(us, 3),
-                                           "gbs": round(N * K / 4 / (us * 1e-6) / 1e9, 1)}
-        del g, launches
+                                           "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                           "stream_floor_us": round(floor, 3),
+                                           "frac_of_floor": round(floor / us, 3)}
+        del g, launches, bufs
         torch.cuda.empty_cache()
     return out
 
