@@ -408,7 +408,8 @@ hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const i
   }
   // Problems big enough to fill the chip with 128x256 tiles share one launch
   // of those (their blocks then fill whole rounds together); the rest share
-  // one launch of 64x128 tiles.
+  // one launch of 64x128 tiles, or of 32x128 tiles when 64x128 would give
+  // fewer blocks than CUs.
   const GemmProblem* big[kMaxGroup];
   const GemmProblem* small[kMaxGroup];
   int nbig = 0, nsmall = 0;
@@ -420,7 +421,13 @@ hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const i
   const bool off = qs != nullptr && 254 * K <= INT32_MAX;
   const bool full = K % kBK == 0;
   if (nbig) e = launch_tiles<4, 8, 2>(off, full, big, nbig, K, q, d, qs, M, s);
-  if (e == hipSuccess && nsmall) e = launch_tiles<2, 4, 2>(off, full, small, nsmall, K, q, d, qs, M, s);
+  if (e == hipSuccess && nsmall) {
+    // 64x128 tiles, or 32x128 when those would leave CUs without a block
+    int64_t b64 = 0;
+    for (int i = 0; i < nsmall; ++i) b64 += ((small[i]->N + 63) / 64) * ((M + 127) / 128);
+    e = b64 < 256 ? launch_tiles<1, 4, 2>(off, full, small, nsmall, K, q, d, qs, M, s)
+                  : launch_tiles<2, 4, 2>(off, full, small, nsmall, K, q, d, qs, M, s);
+  }
   return e;
 }
 

@@ -523,7 +523,7 @@ def test_gemv_parity(M, N, K):
 
 GEMM_CASES = [(17, 1, 64), (17, 130, 256), (33, 17, 4), (64, 64, 2560), (100, 640, 320),
               (128, 128, 256), (129, 257, 576), (300, 100, 1024), (512, 640, 2560),
-              (65, 48, 6912), (1, 40, 256), (16, 40, 256), (200, 33, 260)]
+              (65, 48, 6912), (1, 40, 256), (16, 40, 256), (200, 33, 260), (2048, 1100, 320)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES, ids=[f"M{m}N{n}K{k}" for m, n, k in GEMM_CASES])

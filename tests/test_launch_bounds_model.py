@@ -205,8 +205,8 @@ GEMM_SHAPES = [(1, 64, 17), (130, 256, 17), (64, 2560, 64), (640, 320, 100), (25
 
 
 @pytest.mark.parametrize("N,K,M", GEMM_SHAPES, ids=[f"N{n}K{k}M{m}" for n, k, m in GEMM_SHAPES])
-@pytest.mark.parametrize("tile", [(8, 4, 2), (4, 8, 2), (2, 4, 2), (2, 2, 2)],
-                         ids=["256x128", "128x256", "64x128", "64x64"])
+@pytest.mark.parametrize("tile", [(8, 4, 2), (4, 8, 2), (2, 4, 2), (1, 4, 2), (2, 2, 2)],
+                         ids=["256x128", "128x256", "64x128", "32x128", "64x64"])
 def test_gemm_loads_in_bounds(N, K, M, tile):
     for buf, lo, hi, size in gemm_ranges(N, K, M, *tile):
         assert 0 <= lo and hi <= size, (buf, lo, hi, size)
@@ -279,7 +279,7 @@ def test_lds_cycle_model_matches_measurements():
     assert not banks_conflict_free(R_OF * 32 + 8 * H_OF, 8)
 
 
-@pytest.mark.parametrize("tile", [(4, 8, 2), (2, 4, 2), (8, 4, 2), (2, 2, 2)])
+@pytest.mark.parametrize("tile", [(4, 8, 2), (2, 4, 2), (1, 4, 2), (8, 4, 2), (2, 2, 2)])
 def test_gemm_lds_fragments(tile):
     """Every MFMA fragment read of a step returns the intended operand bytes
     and every read instruction is free of bank conflicts."""
