@@ -954,7 +954,7 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
       if (w4 == 4) return launch_one_token_w<4, 4, 4, true>(g, w4, s);
       const int w8 = wide_steps_per_wave(g, 8);
       if (w8 <= 4) return launch_one_token_w<8, 4, 4, true>(g, w8, s);
-      if (w8 <= 8) return launch_one_token_w<8, 8, 4, false>(g, w8, s);
+      if (w8 <= 8) return launch_one_token_w<8, 8, 2, false>(g, w8, s);   // batches of 2: measured 10% faster than 4 at K = 28672
       const int w16 = wide_steps_per_wave(g, 16);  // <= 8 for K <= 65536
       return launch_one_token_w<16, 8, 4, false>(g, w16, s);
     }

@@ -378,7 +378,7 @@ def decode1w_config(K):
     if w8 <= 4:
         return 8, 4, 4, True, w8
     if w8 <= 8:
-        return 8, 8, 4, False, w8
+        return 8, 8, 2, False, w8
     w16 = wide_steps_per_wave(K, 16)
     assert w16 <= 8, "K above 65536 is rejected at the boundary"
     return 16, 8, 4, False, w16
