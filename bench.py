@@ -157,7 +157,7 @@ def decode_more(torch, bl, W, dev, stream):
         return f
 
     out = {}
-    cfg = W.CONFIGS[4]
+    cfg = W.LAYERS[4]
     layer_groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
     packed = {}
     for proj in cfg.projs:
@@ -217,7 +217,7 @@ def norm_layer_bench(torch, bl, W, dev, stream):
     bl_decode_norm_group, two bl_decode_group), against unfused, 9 launches
     (bl_rmsnorm_quant, then one bl_gemv per projection of the normed input).
     32 rotating layer copies, graph replays; us per layer and packed GB/s."""
-    cfg = W.CONFIGS[2]
+    cfg = W.LAYERS[2]
     by = {p.name: p for p in cfg.projs}
     K = 2560
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -304,7 +304,7 @@ def t3_bench(torch, bl, W, dev, stream):
         del p2, p3
         torch.cuda.empty_cache()
     # the 2B decode layer, both formats
-    cfg = W.CONFIGS[2]
+    cfg = W.LAYERS[2]
     layer_groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
     gam = torch.tensor([W.GAMMA_DRAWN], dtype=torch.float32, device=dev)
     xs, tern = {}, {}
@@ -345,7 +345,7 @@ def norm_bench(torch, bl, W, dev, stream):
     out = {}
     for name, cid, M in (("100b-prefill-2048", 5, 2048), ("2b-prefill-512", 3, 512),
                          ("100b-decode-1", 5, 1), ("2b-decode-1", 3, 1)):
-        cfg = W.CONFIGS[cid]
+        cfg = W.LAYERS[cid]
         K = cfg.projs[0].K
         xb, rb, gb = W.norm_inputs(4242 + cid, M, K, cfg.outlier_frac, cfg.outlier_scale)
         t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -419,7 +419,7 @@ def build_prefill(torch, bl, W, dev):
     bl_gemm_group call on its quantized codes. The quantizer also writes the
     token sums and `group` takes them (offset weights); `plain` is the same
     group without them."""
-    cfg5 = W.CONFIGS[5]
+    cfg5 = W.LAYERS[5]
     M5 = 2048
     log(f"setup prefill: {cfg5.name}")
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -448,7 +448,7 @@ def build_prefill(torch, bl, W, dev):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
@@ -475,7 +475,7 @@ def main():
 
 
     # ----------------------------------------------------------------- decode
-    cfg = W.CONFIGS[2]
+    cfg = W.LAYERS[2]
     M = 1
     R = max(1, args.rotate)
     log(f"setup decode: {cfg.name}, {R} layer copies")
@@ -520,7 +520,7 @@ def main():
             step(r)
         torch.cuda.synchronize()
         if not args.no_extras:                # 4 fused norm launches, 100B prefill shape
-            cfg5 = W.CONFIGS[5]
+            cfg5 = W.LAYERS[5]
             K5 = cfg5.projs[0].K
             xb, rb, gb = W.norm_inputs(4247, 2048, K5, cfg5.outlier_frac, cfg5.outlier_scale)
             t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)

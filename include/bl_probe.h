@@ -2,7 +2,7 @@
  * bl_probe.h -- measurement aids of the benchmark (libblprobe.so).
  *
  * Not part of the BitLinear method: two trivial gfx950 kernels that give the
- * floors the decode GEMV is judged against on the same machine and in the
+ * floors the decode GEMV is measured against on the same machine and in the
  * same launch setting (HIP graphs, cold buffers).
  *
  * Conventions: device pointers owned by the caller; `stream` is a

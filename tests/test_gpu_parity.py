@@ -201,7 +201,7 @@ def test_config3_prefill_per_tensor_scale():
     """2B-layer prefill (512 tokens) with one activation scale per layer input:
     per-tensor quantize then bl_gemm_group, every output against the oracle."""
     bl = _bl()
-    cfg = W.CONFIGS[3]
+    cfg = W.LAYERS[3]
     by = {p.name: p for p in cfg.projs}
     for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
         inps = [W.proj_inputs(cfg, by[n], 512) for n in names]
@@ -381,7 +381,7 @@ def test_rmsnorm_quant_prefill_sampled(cid, M, n_rows):
     place, as in a decoder layer: sampled tokens against the oracle, and the
     whole h against the residual add done once on the CPU."""
     bl = _bl()
-    cfg = W.CONFIGS[cid]
+    cfg = W.LAYERS[cid]
     K = cfg.projs[0].K
     say(f"rmsnorm_quant config {cid}: M={M} K={K}")
     x, r, g = W.norm_inputs(5000 + cid, M, K, cfg.outlier_frac, cfg.outlier_scale)
@@ -1023,7 +1023,7 @@ def test_config2_layer_decode_groups():
     """BitNet-2B-like layer at batch 1 through the fused decode groups of a real
     decoder layer: {q, k, v}, {o}, {gate, up}, {down}."""
     bl = _bl()
-    cfg = W.CONFIGS[2]
+    cfg = W.LAYERS[2]
     groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
     by_name = {p.name: p for p in cfg.projs}
     for names in groups:
@@ -1092,7 +1092,7 @@ def _pipeline(bl, cfg, proj, M, p_zero_override=None, sample=None):
 @pytest.mark.parametrize("cid,M", [(1, 1), (2, 1), (4, 1), (4, 4), (4, 16), (3, 512)])
 def test_layer_configs(cid, M):
     bl = _bl()
-    cfg = W.CONFIGS[cid]
+    cfg = W.LAYERS[cid]
     for proj in cfg.projs:
         _pipeline(bl, cfg, proj, M)
 
@@ -1100,7 +1100,7 @@ def test_layer_configs(cid, M):
 def test_config4_sparse_variant():
     """7B layer with ternary weights drawn at P(0) = 0.65."""
     bl = _bl()
-    cfg = W.CONFIGS[4]
+    cfg = W.LAYERS[4]
     for proj in cfg.projs:
         _pipeline(bl, cfg, proj, 1, p_zero_override=0.65)
 
@@ -1110,7 +1110,7 @@ def test_config5_grouped_sampled():
     {gate, up} share one quantized input; sampled entries against the oracle,
     full outputs equal to the per-projection bl_gemm."""
     bl = _bl()
-    cfg = W.CONFIGS[5]
+    cfg = W.LAYERS[5]
     by = {p.name: p for p in cfg.projs}
     for names in (("q", "k", "v"), ("gate", "up")):
         K = by[names[0]].K
@@ -1143,6 +1143,6 @@ def test_config5_sampled():
     """100B-class layer at 2048 tokens: every stage at full size; the GEMM checked
     on sampled entries, two full tokens and two full output features."""
     bl = _bl()
-    cfg = W.CONFIGS[5]
+    cfg = W.LAYERS[5]
     for proj in cfg.projs:
         _pipeline(bl, cfg, proj, 2048, sample=5000 + proj.index)

@@ -68,7 +68,7 @@ def _layer(h: int, kv: int, ffn: int):
     return tuple(Proj(n, i, K, N) for i, (n, (K, N)) in enumerate(zip(PROJ_NAMES, shapes)))
 
 
-CONFIGS = {
+LAYERS = {
     1: LayerConfig(1, "single-1024x1024-decode", (Proj("single", 0, 1024, 1024),), (1,),
                    "f32_normal"),
     2: LayerConfig(2, "bitnet-2b-layer-decode", _layer(2560, 640, 6912), (1,),
