@@ -843,6 +843,34 @@ def test_decode_group_t3_tokens(M):
     _decode_group_t3_case(bl, M, [(100, 320), (33, 1296), (640, 2560)], seed=1270 + M)
 
 
+@pytest.mark.parametrize("M", [1, 3])
+def test_decode_group_t3_graph_replay(M):
+    """HIP-graph replays of the base-3 decode group (one fused launch at one
+    token; quantize + GEMV launches at three) give the eager result every time."""
+    bl = _bl()
+    say(f"decode_group_t3 graph replay M={M}")
+    probs = []
+    for i, (N, K) in enumerate([(2560, 2560), (640, 2560), (33, 1296)]):
+        x = W.activations_bf16(1400 + 10 * i + M, M, K, outlier_frac=0.01, outlier_scale=20.0)
+        t = W.ternary_drawn(1401 + 10 * i, N, K, 0.4)
+        probs.append(dict(packed=bl.pack_t3(dev(t)), gamma=dev(np.array([GAMMA], np.float32)),
+                          x=dev_bf16(x), out_dtype="bf16"))
+    grp = bl.DecodeGroupT3(probs)
+    ref = [host(y).copy() for y in grp()]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        grp()
+    for _ in range(3):
+        for y in grp.outputs:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, r in zip(grp.outputs, ref):
+            assert np.array_equal(host(y), r)
+
+
 def test_decode_group_t3_zero_k():
     """A K == 0 problem gives zeros (and a zero scale) next to a normal one."""
     bl = _bl()
