@@ -413,14 +413,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_prefill(torch, bl, W, dev):
-    """The 100B-class layer at 2048 tokens: one bf16 input per group of
-    projections that read it; each group's GEMMs run through one
-    bl_gemm_group call on its quantized codes. The quantizer also writes the
-    token sums and `group` takes them (offset weights); `plain` is the same
-    group without them."""
-    cfg5 = W.LAYERS[5]
-    M5 = 2048
+def build_prefill(torch, bl, W, dev, cid=5, M5=2048):
+    """A prefill layer (by default the 100B-class layer at 2048 tokens): one
+    bf16 input per group of projections that read it; each group's GEMMs run
+    through one bl_gemm_group call on its quantized codes. The quantizer also
+    writes the token sums and `group` takes them (offset weights); `plain` is
+    the same group without them."""
+    cfg5 = W.LAYERS[cid]
     log(f"setup prefill: {cfg5.name}")
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     by = {proj.name: proj for proj in cfg5.projs}
@@ -443,6 +442,35 @@ def build_prefill(torch, bl, W, dev):
         del inps
     torch.cuda.synchronize()
     return cfg5, M5, G
+
+
+def prefill_2b(torch, bl, W, dev, stream):
+    """The BitNet-2B-like layer at 512 tokens (small matrices on the int8
+    MFMA path): per input one bl_quantize_act, then one bl_gemm_group per
+    {q,k,v}, {o}, {gate,up}, {down}, as graph replays over 32 layer copies
+    (17.4 MB of packed weights each, so the weights come from HBM). TOPS of
+    the GEMMs alone and of the layer with its quantize launches."""
+    cfg, M, G = build_prefill(torch, bl, W, dev, cid=3, M5=512)
+    R = 32
+    copies = []
+    for r in range(R):
+        copies.append([e["group"] if r == 0 else
+                       bl.GemmGroup([dict(p, packed=p["packed"].clone()) for p in e["group"].problems],
+                                    e["q"], e["d"], qsum=e["qs"]) for e in G])
+    quant = [(lambda e=e: bl.quantize_act(e["x"], e["q"], e["d"], qsum=e["qs"])) for e in G]
+    gemm_only = [grp for layer in copies for grp in layer]
+    with_q = [f for layer in copies for pair in zip(quant, layer) for f in pair]
+    for f in with_q[:2 * len(G)]:
+        f()
+    out = {"workload": cfg.name, "tokens": M, "ops_per_layer": cfg.ops(M)}
+    for name, fns in (("gemm_only", gemm_only), ("with_quantize", with_q)):
+        g = capture_fns(torch, stream, fns)
+        us = replay_us(torch, stream, g, 1, reps=10) / R
+        out[name] = {"us_per_layer": round(us, 2), "tops": round(cfg.ops(M) / (us * 1e-6) / 1e12, 1)}
+        del g
+    del copies, G
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -793,6 +821,8 @@ def main():
         log(f"decode layer with norms: {result['decode_layer_with_norms']}")
         result["t3_gemv"] = t3_bench(torch, bl, W, dev, stream)
         log(f"t3_gemv: {result['t3_gemv']}")
+        result["gemm_2b_prefill_512"] = prefill_2b(torch, bl, W, dev, stream)
+        log(f"gemm_2b_prefill_512: {result['gemm_2b_prefill_512']}")
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
