@@ -151,9 +151,9 @@ int bl_quantize_act_tensor(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  *   then q, d of y exactly as bl_quantize_act (m = max|y|, s = fl32(127/m),
  *   q = rne(fl32(y*s)), d = fl32(m/127)); q = 0 and d[t] = 0 when m = 0 or
  *   fl32(ms_t + eps) = 0.
- * The sum of squares runs in fp64 (each square exact): ms_t is the correctly
- * rounded value unless the exact mean square lies within ~2^-40 (relative) of
- * a midpoint between two fp32 numbers, where either neighbour may result.
+ * ms_t is the correctly rounded fp32 value of the exact mean square (an fp64
+ * sum decides it when its error bound allows; otherwise the squares are
+ * summed exactly as integers binned by exponent).
  * x, r: bf16 [M][K] row stride ldx (r may be NULL); g: bf16 [K];
  * h_out: bf16 [M][K] row stride ldx, or NULL (not written); it may be r or x
  * itself (in-place update of the residual stream) but must not otherwise
@@ -365,9 +365,8 @@ int bl_decode_group_t3(const bl_decode_problem *problems, int count, int64_t M, 
  * codes and scale; h_out (bf16 [K] or NULL) receives h. h_out must not
  * overlap x or r (other blocks still read them while it is written).
  * M is 1. K % 64 == 0 and K <= 32768; N, ytype, gamma and alignment as in
- * bl_decode_group; g, r and h_out 16-byte aligned. The sum of squares runs in
- * fp64 per K part, so as for bl_rmsnorm_quant a mean square within ~2^-40 of
- * an fp32 rounding midpoint may round either way.
+ * bl_decode_group; g, r and h_out 16-byte aligned. The mean square is the
+ * correctly rounded one, as in bl_rmsnorm_quant.
  */
 int bl_decode_norm_group(const bl_decode_problem *problems, int count, const uint16_t *r,
                          const uint16_t *g, float eps, uint16_t *h_out, void *stream);

@@ -127,8 +127,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // ---- residual add + RMSNorm + quantize arithmetic, shared by the fused norm
 // kernel and the one-token decode kernel with the norm folded in. Per token:
-//   h = bf16_rne(fl32(x + r)); ms = fl32(sum h^2 / K) (fp64 sum of exact
-//   squares); rinv = fl32(1/fl32(sqrt(fl32(ms + eps)))); y = fl32(fl32(h*rinv)*g).
+//   h = bf16_rne(fl32(x + r)); ms = fl32(S / K) with S = sum h^2 exactly (one
+//   rounding); rinv = fl32(1/fl32(sqrt(fl32(ms + eps)))); y = fl32(fl32(h*rinv)*g).
 
 // Two packed bf16 sums: bf16_rne(fl32(x + r)) per half.
 __device__ __forceinline__ uint32_t add2_bf16(uint32_t x, uint32_t r) {
@@ -144,10 +144,135 @@ __device__ __forceinline__ double sumsq2_bf16(uint32_t w, double acc) {
   return acc;
 }
 
-// The mean square of a row from its fp64 sum of squares, and the factor
-// rinv = fl32(1/fl32(sqrt(fl32(ms + eps)))) (0 when ms + eps is 0).
-__device__ __forceinline__ float norm_factor(double sumsq, int64_t K, float eps) {
-  const float ms = (float)(sumsq / (double)K);
+// The mean square ms = fl32(S / K), fast path. tot is an fp64 sum of the exact
+// squares in any order, so |tot - S| <= (K-1) * 2^-53 * S (every term is >= 0);
+// qv = fl64(tot / K) adds one rounding, so qv is within (K+1) * 2^-53 * qv of
+// S / K (to first order). When qv lies farther than (K+2) * 2^-52 * qv from
+// both fp32 rounding midpoints next to fl32(qv), S / K is on the same side of
+// them and rounds to the same fp32 value: returns true with *ms = fl32(qv).
+// Otherwise (about K * 2^-27 of random tokens) the caller computes ms from the
+// exact bins below. tot == 0 means S == 0 (no square of a nonzero bf16
+// underflows fp64).
+__device__ __forceinline__ bool ms_fast(double tot, int64_t K, float* ms) {
+  const double qv = tot / (double)K;
+  const float f = (float)qv;
+  *ms = f;
+  if (tot == 0.0) return true;
+  const uint32_t u = __float_as_uint(f);
+  const double fd = (double)f;
+  const double flo = u ? (double)__uint_as_float(u - 1u) : -(double)__uint_as_float(1u);
+  const double fhi = (double)__uint_as_float(u + 1u);
+  const double tol = (double)(K + 2) * 0x1p-52 * qv;
+  return qv - 0.5 * (fd + flo) > tol && 0.5 * (fd + fhi) - qv > tol;
+}
+
+// Exact path: bins[b] (256 uint64 in LDS, zeroed) collects s^2 of every h =
+// s * 2^(b - 134) of the row, with b the bf16 exponent field (1 for
+// subnormals) and s the significand with its hidden bit (s < 256), so that
+// S = 2^-268 * sum_b bins[b] * 4^b exactly. Two bf16 values per call.
+__device__ __forceinline__ void sq_bins_add2(uint32_t w, unsigned long long* bins) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t v = i ? (w >> 16) : (w & 0xFFFFu);
+    const uint32_t e = (v >> 7) & 0xFFu, m = v & 0x7Fu;
+    if (e | m) {
+      const uint32_t s = e ? (m | 0x80u) : m;
+      atomicAdd(&bins[e ? e : 1u], (unsigned long long)(s * s));
+    }
+  }
+}
+
+// fl32(S / K) from the bins (one thread; the rare exact path). T = sum_b
+// bins[b] * 4^b is built as a 640-bit integer; A = its top 64 bits (T =
+// A * 2^L + rest), X = floor(A / K); S / K = X * 2^(L - 268) plus a positive
+// part below one unit of X exactly when rest or A mod K is nonzero (the
+// sticky bit). X has at least 46 significant bits, so one round to nearest
+// even at the fp32 position (subnormals included) with that sticky bit gives
+// the correctly rounded quotient.
+__device__ __noinline__ float ms_from_bins(const unsigned long long* bins, int64_t K) {
+  uint32_t W[20];
+#pragma unroll
+  for (int j = 0; j < 20; ++j) W[j] = 0u;
+  for (int b = 1; b < 256; ++b) {
+    const unsigned long long v = bins[b];
+    if (!v) continue;
+    const int w = b >> 4, sh = 2 * (b & 15);           // bit offset 2b = 32w + sh
+    const unsigned long long lo = v << sh;
+    const uint32_t hi = sh ? (uint32_t)(v >> (64 - sh)) : 0u;
+    unsigned long long c = (unsigned long long)W[w] + (uint32_t)lo;
+    W[w] = (uint32_t)c;
+    c = (c >> 32) + W[w + 1] + (uint32_t)(lo >> 32);
+    W[w + 1] = (uint32_t)c;
+    c = (c >> 32) + W[w + 2] + hi;
+    W[w + 2] = (uint32_t)c;
+    c >>= 32;
+    for (int j = w + 3; c != 0 && j < 20; ++j) {
+      c += W[j];
+      W[j] = (uint32_t)c;
+      c >>= 32;
+    }
+  }
+  int top = 19;
+  while (top >= 0 && W[top] == 0u) --top;
+  if (top < 0) return 0.0f;
+  const int P = 32 * top + 31 - __builtin_clz(W[top]);      // top set bit of T
+  const int L = P - 63;
+  unsigned long long A;
+  bool sticky = false;
+  if (L <= 0) {                                              // T < 2^64: exact
+    const unsigned long long T = ((unsigned long long)W[1] << 32) | W[0];
+    A = T << (-L);
+  } else {
+    const int j0 = L >> 5, sh = L & 31;
+    const unsigned __int128 win = ((unsigned __int128)(j0 + 2 < 20 ? W[j0 + 2] : 0u) << 64) |
+                                  ((unsigned __int128)W[j0 + 1] << 32) | W[j0];
+    A = (unsigned long long)(win >> sh);
+    sticky = (W[j0] & ((1u << sh) - 1u)) != 0u;
+    for (int j = 0; j < j0; ++j) sticky = sticky || W[j] != 0u;
+  }
+  const unsigned long long Ku = (unsigned long long)K;
+  const unsigned long long X = A / Ku;
+  sticky = sticky || (A % Ku) != 0u;
+  const int ex = 63 - __builtin_clzll(X);                    // X >= 2^63 / K > 0
+  int lsb = ex + L - 268 - 23;                               // fp32 unit of a normal result
+  if (lsb < -149) lsb = -149;
+  const int sh2 = lsb - (L - 268);                           // bits of X below that unit
+  unsigned long long keep;
+  if (sh2 > 64) {
+    keep = 0;                                                // below half the smallest unit
+  } else if (sh2 == 64) {
+    const unsigned long long half = 1ull << 63;
+    keep = (X > half || (X == half && sticky)) ? 1u : 0u;
+  } else {
+    keep = X >> sh2;
+    const unsigned long long rem = X & ((1ull << sh2) - 1ull), half = 1ull << (sh2 - 1);
+    if (rem > half || (rem == half && (sticky || (keep & 1u)))) ++keep;
+  }
+  return (float)ldexp((double)keep, lsb);
+}
+
+// ms of a row from its fp64 sum of squares tot: the fast path when it is
+// certain, else the exact bins (bins: 256 words of LDS, ms_sh: one LDS float;
+// add_own(bins) adds the calling thread's values with sq_bins_add2). Every
+// thread of the block must call it with the same tot (the branch is uniform).
+template <int NT, class F>
+__device__ __forceinline__ float mean_square(double tot, int64_t K, unsigned long long* bins,
+                                             float* ms_sh, F add_own) {
+  float ms;
+  if (ms_fast(tot, K, &ms)) return ms;
+  for (int i = (int)threadIdx.x; i < 256; i += NT) bins[i] = 0ull;
+  __syncthreads();
+  add_own(bins);
+  __syncthreads();
+  if (threadIdx.x == 0) *ms_sh = ms_from_bins(bins, K);
+  __syncthreads();
+  return *ms_sh;
+}
+
+// rinv = fl32(1/fl32(sqrt(fl32(ms + eps)))), 0 when ms + eps is 0. sqrt and
+// 1/x run in fp64 and are rounded once to fp32, which is the correctly rounded
+// fp32 result (fp64 carries more than 2*24 + 2 bits).
+__device__ __forceinline__ float norm_rinv(float ms, float eps) {
   const float v = __fadd_rn(ms, eps);
   if (!(v > 0.0f)) return 0.0f;
   const float root = (float)__dsqrt_rn((double)v);

@@ -104,6 +104,8 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   __shared__ v4i red[WPB - 1][RTW][kWave];
   __shared__ uint32_t wmax[WPB];
   __shared__ double wss[NORM ? WPB : 1];
+  __shared__ unsigned long long bins[NORM ? 256 : 1];
+  __shared__ float ms_sh;
 
   const DecodeProblem& P = grp.p[blockIdx.y];
   const int64_t N = P.N;
@@ -216,7 +218,18 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
     double tot = wss[0];
 #pragma unroll
     for (int w = 1; w < WPB; ++w) tot += wss[w];
-    rinv = norm_factor(tot, K, eps);
+    const float ms = mean_square<WPB * kWave>(tot, K, bins, &ms_sh, [&](unsigned long long* b) {
+#pragma unroll
+      for (int u = 0; u < XR; ++u) {
+        if (lane + u * kWave < nch) {
+          sq_bins_add2(xv[u].x, b);
+          sq_bins_add2(xv[u].y, b);
+          sq_bins_add2(xv[u].z, b);
+          sq_bins_add2(xv[u].w, b);
+        }
+      }
+    });
+    rinv = norm_rinv(ms, eps);
     uint32_t mb = 0u;
 #pragma unroll
     for (int u = 0; u < XR; ++u) {
@@ -280,27 +293,22 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) acc0[rt] = acc1[rt] = v4i{0, 0, 0, 0};
   const int8_t* arow = wact + 64 * h;
-  auto read_b = [&](v4i (&b)[4], int j) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      b[s] = *reinterpret_cast<const v4i*>(arow + (j - ja) * 256 + 16 * s);
-  };
+  // each activation fragment is read from LDS next to its MFMA (the other
+  // waves of the SIMD hide the latency): no fragment is held across steps
   auto compute = [&](const v4i (&w)[U][RTW], int j) {
-    v4i bn[4];
-    read_b(bn, j);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j + u < jb) {
-        v4i b[4] = {bn[0], bn[1], bn[2], bn[3]};
-        if (u + 1 < U && j + u + 1 < jb) read_b(bn, j + u + 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+          const v4i b = *reinterpret_cast<const v4i*>(arow + (j + u - ja) * 256 + 16 * s);
 #pragma unroll
           for (int rt = 0; rt < RTW; ++rt) {
             v4i& a = (s & 1) ? acc1[rt] : acc0[rt];
-            a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]), b[s], a,
+            a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]), b, a,
                                                       0, 0, 0);
           }
+        }
       }
     }
   };
@@ -600,25 +608,25 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int l
   __builtin_amdgcn_wave_barrier();
 
   // ---- 4. MFMA over this part's steps ----------------------------------
-  v4i acc[2][2];                                       // [half][chain]
-#pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = v4i{0, 0, 0, 0};
+  // one accumulator per row half: the halves alternate, so an MFMA never
+  // waits on the one just issued; each activation fragment is read from LDS
+  // next to its two MFMAs (registers: 7 waves per SIMD at 4 steps per wave)
+  v4i acc[2];
+  acc[0] = acc[1] = v4i{0, 0, 0, 0};
   const int8_t* arow = wact + 64 * (2 * h + (lane & 1));
   auto compute = [&](const auto& w, int j) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j + u < jb) {
         const uint32_t kmask = (j + u) * 512 + 64 * c < K ? 0xFFFFFFFFu : 0u;
-        v4i b[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          b[s] = *reinterpret_cast<const v4i*>(arow + (j + u - ja) * 512 + 16 * s);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+          const v4i b = *reinterpret_cast<const v4i*>(arow + (j + u - ja) * 512 + 16 * s);
 #pragma unroll
           for (int i = 0; i < 2; ++i)
-            acc[i][s & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                decode_word((uint32_t)w[u][i][s] & kmask), b[s], acc[i][s & 1], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                decode_word((uint32_t)w[u][i][s] & kmask), b, acc[i], 0, 0, 0);
+        }
       }
     }
   };
@@ -632,7 +640,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int l
       if (j + U < jb) compute(wb, j + U);
     }
   }
-  v4i a2[2] = {acc[0][0] + acc[0][1], acc[1][0] + acc[1][1]};
+  v4i a2[2] = {acc[0], acc[1]};
 
   // ---- 5. sum of the parts, even + odd chunks, dequant, store -----------
   if (wk > 0) {

@@ -10,11 +10,13 @@
 //   y  = fl32(fl32(h * rinv) * g)         (g: bf16 norm weight, one per feature)
 //   m = max |y|, s = fl32(127 / m), q = rne(fl32(y * s)), d = fl32(m / 127);
 //   q = 0 and d = 0 when m = 0 or fl32(ms + eps) = 0.
-// Rounding: every h^2 is exact in fp64 and the sum runs in fp64, so ms is the
-// correctly rounded fp32 mean square except when the exact value lies within
-// about (K/256 + 8) * 2^-53 (relative) of a midpoint between two fp32 values.
-// sqrt and 1/x run in fp64 and are rounded once to fp32, which gives the
-// correctly rounded fp32 result (fp64 carries more than 2*24 + 2 bits).
+// Rounding: ms is the correctly rounded fp32 value of the exact mean square.
+// The fp64 sum of the exact squares settles it when its error bound keeps it
+// away from every fp32 rounding midpoint (all but about K * 2^-27 of random
+// tokens); otherwise the block sums the squares exactly, as integers binned by
+// exponent, and rounds that sum divided by K once. sqrt and 1/x run in fp64
+// and are rounded once to fp32, which gives the correctly rounded fp32 result
+// (fp64 carries more than 2*24 + 2 bits).
 //
 // One workgroup per token. Fast path (K % 8 == 0, ldx % 8 == 0, K <= 32768):
 // each thread holds NC 16-byte chunks of the row in registers, so x, r and g
@@ -62,6 +64,8 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
   __shared__ double red_s[NT / kWave];
   __shared__ uint32_t red_m[NT / kWave];
   __shared__ int red_q[NT / kWave];
+  __shared__ unsigned long long bins[256];
+  __shared__ float ms_sh;
   const int64_t t = blockIdx.x;
   const int nchunk = (int)(K / 8);
   const uint16_t* xrow = x + t * ldx;
@@ -103,7 +107,19 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
   // g (the same for every token, an L2 hit) is in flight during the sum.
 #pragma unroll
   for (int i = 0; i < NC; ++i) gv[i] = ld16(g, off[i]);
-  const float rinv = norm_factor(block_sum_f64<NT>(ss, red_s), K, eps);
+  const float ms = mean_square<NT>(block_sum_f64<NT>(ss, red_s), K, bins, &ms_sh,
+                                   [&](unsigned long long* b) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if ((int)threadIdx.x + i * NT < nchunk) {
+        sq_bins_add2(hv[i].x, b);
+        sq_bins_add2(hv[i].y, b);
+        sq_bins_add2(hv[i].z, b);
+        sq_bins_add2(hv[i].w, b);
+      }
+    }
+  });
+  const float rinv = norm_rinv(ms, eps);
   uint32_t mb = 0;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
@@ -167,6 +183,8 @@ __global__ __launch_bounds__(kGenThreads) void k_rmsnorm_quant_any(
   __shared__ double red_s[kGenThreads / kWave];
   __shared__ uint32_t red_m[kGenThreads / kWave];
   __shared__ int red_q[kGenThreads / kWave];
+  __shared__ unsigned long long bins[256];
+  __shared__ float ms_sh;
   const int64_t t = blockIdx.x;
   const int64_t nchunk = K / 4;
   const uint2* xr = reinterpret_cast<const uint2*>(x + t * ldx);
@@ -179,7 +197,15 @@ __global__ __launch_bounds__(kGenThreads) void k_rmsnorm_quant_any(
     ss = sumsq2_bf16(h.y, sumsq2_bf16(h.x, ss));
     if (hr) hr[c] = h;
   }
-  const float rinv = norm_factor(block_sum_f64<kGenThreads>(ss, red_s), K, eps);
+  const float ms = mean_square<kGenThreads>(
+      block_sum_f64<kGenThreads>(ss, red_s), K, bins, &ms_sh, [&](unsigned long long* b) {
+        for (int64_t c = threadIdx.x; c < nchunk; c += kGenThreads) {
+          const uint2 h = hr ? hr[c] : load_h4(xr, rr, c);
+          sq_bins_add2(h.x, b);
+          sq_bins_add2(h.y, b);
+        }
+      });
+  const float rinv = norm_rinv(ms, eps);
   uint32_t mb = 0;
   for (int64_t c = threadIdx.x; c < nchunk; c += kGenThreads) {
     float y[4];

@@ -238,47 +238,90 @@ def test_quantize_empty():
 # residual add + RMSNorm + quantize
 # ---------------------------------------------------------------------------
 
-MS_AMBIGUOUS_REL = 2.0 ** -40    # the kernel's fp64 sum of squares is this close
-
-
-def _near_f32_midpoint(ms):
-    """True where the exact mean square lies within MS_AMBIGUOUS_REL of a
-    midpoint between two fp32 values (either rounding of it is correct for
-    the kernel's fp64 sum; everything downstream then follows that choice)."""
-    from fractions import Fraction
-    out = []
-    for v in ms:
-        if v == 0:
-            out.append(False)
-            continue
-        f = oracle.round_fraction_to_f32(v)
-        lo, hi = np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(np.inf))
-        mids = ((Fraction(float(lo)) + Fraction(float(f))) / 2,
-                (Fraction(float(f)) + Fraction(float(hi))) / 2)
-        out.append(min(abs(v - m) for m in mids) <= v * Fraction(MS_AMBIGUOUS_REL))
-    return np.array(out, dtype=bool)
-
-
 def check_norm(x, r, g, eps, h, q, d, rows=None):
     """GPU h, q, d (full [M] arrays) against the oracle on `rows` (all by
-    default): h bit-exact; q and d bit-exact except on tokens whose mean
-    square sits on an fp32 rounding midpoint, where q is within 1 and d
-    within 2^-22 relative. Returns the number of such tokens."""
+    default), every one bit-exact: the mean square is the correctly rounded
+    one on both sides."""
     rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
-    h_ref, q_ref, d_ref, ms = oracle.rmsnorm_quant(x[rows], None if r is None else r[rows], g,
-                                                   eps, return_ms=True)
+    h_ref, q_ref, d_ref = oracle.rmsnorm_quant(x[rows], None if r is None else r[rows], g, eps)
     if h is not None:
         assert np.array_equal(h[rows], h_ref), "h differs"
-    amb = _near_f32_midpoint(ms)
-    ok = ~amb
-    assert np.array_equal(q[rows][ok], q_ref[ok]), "codes differ"
-    assert np.array_equal(d[rows][ok].view(np.uint32), d_ref[ok].view(np.uint32)), "scales differ"
-    if amb.any():
-        dq = np.abs(q[rows][amb].astype(np.int32) - q_ref[amb].astype(np.int32))
-        assert dq.max() <= 1
-        rel = np.abs(d[rows][amb].astype(np.float64) - d_ref[amb]) / np.maximum(d_ref[amb], 1e-38)
-        assert rel.max() <= 2.0 ** -22
-    return int(amb.sum())
+    assert np.array_equal(q[rows], q_ref), "codes differ"
+    assert np.array_equal(d[rows].view(np.uint32), d_ref.view(np.uint32)), "scales differ"
+
+
+def midpoint_batch(seed, K, n_per_kind=2, scales=(0, -50, 40)):
+    """Rows of K bf16 values whose exact mean square is an fp32 rounding
+    midpoint ("tie") or lies 2^-80 (relative) above or below one, at several
+    magnitudes (tests/midpoint_rows.py), each checked here to be what it
+    claims against the oracle's exact mean square."""
+    from fractions import Fraction
+    import midpoint_rows as MR
+    rng = np.random.default_rng(seed)
+    rows, kinds = [], []
+    for kind in ("tie", "above", "below"):
+        for se in scales:
+            got = 0
+            for _ in range(8):
+                row = MR.midpoint_row(rng, K, kind, se, background=got % 2 == 0)
+                if row is None:
+                    continue
+                ms = oracle.norm._mean_square(oracle.widen_bf16(row))
+                f = oracle.round_fraction_to_f32(ms)
+                lo, hi = np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(np.inf))
+                mids = [(Fraction(float(lo)) + Fraction(float(f))) / 2,
+                        (Fraction(float(f)) + Fraction(float(hi))) / 2]
+                dist = min(abs(ms - m) for m in mids)
+                assert (dist == 0) == (kind == "tie") and dist <= ms * Fraction(1, 2 ** 70)
+                rows.append(row)
+                kinds.append(kind)
+                got += 1
+                if got == n_per_kind:
+                    break
+    return np.stack(rows), kinds
+
+
+@pytest.mark.parametrize("K,ldx", [(64, 64), (2560, 2560), (8192, 8192), (4100, 4100),
+                                   (2560, 2564), (40000, 40000)])
+def test_rmsnorm_quant_midpoints(K, ldx):
+    """Tokens whose exact mean square sits on an fp32 rounding midpoint or
+    2^-80 beside one, where an fp64 sum of squares alone would round the
+    wrong way: every code and scale bit-exact, through the register-row
+    kernel (K % 8 == 0, K <= 32768) and the generic one, with and without a
+    residual (a zero residual keeps h = x)."""
+    bl = _bl()
+    x, kinds = midpoint_batch(4000 + K, K)
+    M = x.shape[0]
+    say(f"rmsnorm_quant midpoints K={K} ldx={ldx} rows={M} kinds={kinds}")
+    g = W.f32_to_bf16_bits((1.0 + 0.1 * W.rng(K).standard_normal(K)).astype(np.float32))
+    for r in (None, np.zeros_like(x)):
+        h, q, d = _norm_run(bl, x, r, g, 0.0 if r is None else 1e-30, ldx,
+                            "none" if r is None else "new")
+        check_norm(x, r, g, 0.0 if r is None else 1e-30, h, q, d)
+
+
+@pytest.mark.parametrize("K", [2560, 4096, 8192])
+def test_decode_norm_group_midpoints(K):
+    """The one-token decode launch with the norm folded in, on midpoint
+    tokens: each token's q, d and outputs bit-exact against the oracle."""
+    bl = _bl()
+    x, kinds = midpoint_batch(4100 + K, K, n_per_kind=1, scales=(0, -40))
+    g = W.f32_to_bf16_bits((1.0 + 0.1 * W.rng(K + 1).standard_normal(K)).astype(np.float32))
+    t = W.ternary_drawn(K + 7, 96, K, 0.4)
+    packed = bl.pack_i2s(dev(t))
+    gam = dev(np.array([GAMMA], np.float32))
+    say(f"decode_norm_group midpoints K={K} tokens={x.shape[0]}")
+    for i in range(x.shape[0]):
+        xi = x[i:i + 1]
+        q = torch.empty((1, K), dtype=torch.int8, device="cuda")
+        d = torch.empty((1,), dtype=torch.float32, device="cuda")
+        (y,) = bl.NormDecodeGroup([dict(packed=packed, gamma=gam, q=q, d=d, out_dtype="f32")],
+                                  dev_bf16(xi), dev_bf16(g), 0.0)()
+        torch.cuda.synchronize()
+        _, q_ref, d_ref = oracle.rmsnorm_quant(xi, None, g, 0.0)
+        assert np.array_equal(host(q), q_ref), (i, kinds[i])
+        assert host(d).view(np.uint32)[0] == d_ref.view(np.uint32)[0], (i, kinds[i])
+        check_outputs(oracle.mpgemm_acc(q_ref, t), GAMMA, d_ref, y_f32=host(y))
 
 
 # (M, K, ldx, residual, h mode, eps): h mode "new" (a fresh h_out), "none"
@@ -325,8 +368,7 @@ def test_rmsnorm_quant_parity(M, K, ldx, res, mode, eps):
     if not res:
         r = None
     h, q, d = _norm_run(bl, x, r, g, eps, ldx, mode)
-    n_amb = check_norm(x, r, g, eps, h if mode != "none" else None, q, d)
-    assert n_amb <= 1
+    check_norm(x, r, g, eps, h if mode != "none" else None, q, d)
 
 
 def test_rmsnorm_quant_golden_and_special():
@@ -388,7 +430,7 @@ def test_rmsnorm_quant_prefill_sampled(cid, M, n_rows):
     h, q, d = _norm_run(bl, x, r, g, 1e-5, K, "in_r")
     rows = np.sort(W.rng(77 + cid).permutation(M)[:n_rows])
     rows[0], rows[-1] = 0, M - 1
-    assert check_norm(x, r, g, 1e-5, None, q, d, rows=rows) <= 1
+    check_norm(x, r, g, 1e-5, None, q, d, rows=rows)
     xs = oracle.widen_bf16(x)
     rs = oracle.widen_bf16(r)
     h_all = oracle.norm._bf16_rne_from_f32((xs + rs).astype(np.float32))
@@ -907,8 +949,7 @@ NORM_GROUP_CASES = [
 def test_decode_norm_group_parity(name, shapes, res, eps):
     """Residual add + RMSNorm + quantize + GEMV in one launch: h, q, d and
     every output against the oracle, and byte-identical to bl_rmsnorm_quant
-    followed by bl_gemv (tokens whose mean square sits on an fp32 rounding
-    midpoint excepted, as for the fused norm)."""
+    followed by bl_gemv."""
     bl = _bl()
     K = shapes[0][1]
     say(f"decode_norm_group {name}: shapes={shapes} residual={res} eps={eps}")
@@ -928,25 +969,22 @@ def test_decode_norm_group_parity(name, shapes, res, eps):
                           out_dtype=("bf16", "f32", "i32")[i % 3]))
     grp = bl.NormDecodeGroup(probs, xd, gd, eps, residual=rd, h_out=hd)
     ys = grp()
-    h_ref, q_ref, d_ref, ms = oracle.rmsnorm_quant(x, r, g, eps, return_ms=True)
+    h_ref, q_ref, d_ref = oracle.rmsnorm_quant(x, r, g, eps)
     # the unfused path: fused norm kernel, then the GEMV over its codes
     h2, q2, d2 = bl.rmsnorm_quant(xd, gd, eps, residual=rd)
     torch.cuda.synchronize()
     if res:
         assert np.array_equal(host(hd), h_ref)
-    amb = bool(_near_f32_midpoint(ms)[0])
-    say(f"  near-midpoint mean square: {amb}")
     for p, y, t in zip(grp.problems, ys, ts):
         ot = p["out_dtype"]
-        if not amb:
-            assert np.array_equal(host(p["q"]), q_ref)
-            assert host(p["d"]).view(np.uint32)[0] == d_ref.view(np.uint32)[0]
-            acc = oracle.mpgemm_acc(q_ref, t)
-            kw = {"i32": "y_i32", "f32": "y_f32", "bf16": "y_bf16"}[ot]
-            check_outputs(acc, GAMMA, d_ref, **{kw: host(y)})
-            y2 = bl.gemv(p["packed"], p["gamma"], q2, d2, out_dtype=ot)
-            torch.cuda.synchronize()
-            assert np.array_equal(host(y2).view(np.uint8), host(y).view(np.uint8))
+        assert np.array_equal(host(p["q"]), q_ref)
+        assert host(p["d"]).view(np.uint32)[0] == d_ref.view(np.uint32)[0]
+        acc = oracle.mpgemm_acc(q_ref, t)
+        kw = {"i32": "y_i32", "f32": "y_f32", "bf16": "y_bf16"}[ot]
+        check_outputs(acc, GAMMA, d_ref, **{kw: host(y)})
+        y2 = bl.gemv(p["packed"], p["gamma"], q2, d2, out_dtype=ot)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y2).view(np.uint8), host(y).view(np.uint8))
 
 
 def test_decode_norm_group_graph_replay():
