@@ -2,26 +2,35 @@
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
-Headline (the JSON `value`): decode GEMV packed-weight GB/s on the
-BitNet-2B-like layer at batch 1 (hidden 2560, k/v 640, FFN 6912). One step =
-one pass of the per-token hot path over that layer: for each of the 7
-projections (q, k, v, o, gate, up, down) the per-token absmax int8
-quantization of its bf16 input and the I2_S GEMV with the bf16 dequant fused
-into the store, issued as one fused launch per group of projections that do
-not depend on each other in a decoder layer: {q,k,v}, {o}, {gate,up}, {down}.
-Weight packing is the offline conversion and is done once before timing. Steps rotate over R distinct copies of the layer's packed
-weights (R * 17.4 MB > the 256 MB Infinity Cache), so every step streams its
-weights from HBM. Steps are replayed from HIP graphs (captured through
-torch.cuda.CUDAGraph) so host launch cost is not timed.
+Headline (the JSON `value`): decode GEMV packed-weight GB/s on a stream of 32
+distinct 7B-class layers (hidden 4096, FFN 11008, 32 heads; ternary weights
+from fp32 N(0, 0.02) by the absmean rule) at batch 1. One step = one layer:
+for each of its 7 projections (q, k, v, o, gate, up, down) the per-token
+absmax int8 quantization of the bf16 input and the I2_S GEMV with the bf16
+dequant fused into the store, issued as one fused launch per group of
+projections that do not depend on each other in a decoder layer: {q,k,v},
+{o}, {gate,up}, {down}. Step i runs layer copy i mod 32 (32 * 50.6 MB =
+1.62 GB, six times the 256 MB Infinity Cache), so every step streams its
+weights from HBM, as decoding one token through a 32-layer model does.
+Weight packing is the offline conversion and is done before timing; inputs
+are resident in HBM. Exactly --steps steps are timed: the --warmup steps and
+then the --steps steps are each captured into one HIP graph (the rotation
+continues across them) and replayed once, between two synchronizations.
 
-Also reported on the same JSON line:
-  roofline      the fused decode kernel: algorithmic packed bytes per launch
-                over its average launch duration (HIP events around graph
-                replays on the replay stream), against 8 TB/s;
-  gemm          prefill on the 100B-class layer (2048 tokens, hidden 8192,
-                FFN 28672, k/v 1024): 2*M*N*K int8 ops per second over the 7
-                projections (quantize + GEMM), against 5.0 POP/s dense int8;
-  cpu_baseline  the CPU oracle on a bounded sample of the decode workload.
+Also on the same JSON line:
+  roofline       the fused one-token decode kernels of that step: packed bytes
+                 per launch over the mean launch interval of the timed steps
+                 (HIP events on the replay stream), against 8 TB/s; `traffic`
+                 from rocprofv3 counters while the kernel sources are unchanged;
+  roofline_gemm  the prefill GEMM (k_gemm_i2s) on the 100B-class layer at 2048
+                 tokens, int8 ops per second against 5.0 POP/s;
+  configs        every workload: the 1024 x 1024 GEMV, the BitNet-2B-like
+                 layer at batch 1 and at 512 tokens, the 7B-class layer at 1,
+                 4 and 16 tokens (and with 65% zero weights), the 100B-class
+                 layer at 2048 tokens;
+  cpu_baseline   the CPU oracle timed per workload on this host, on one core
+                 and on all cores (row shards in worker processes), with the
+                 GPU / oracle ratio.
 """
 from __future__ import annotations
 
@@ -37,19 +46,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PREFILL_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode1_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_7b_stream_traffic.json")
 DECODE_SOURCES = ("mpgemm_token_absmax_amd/csrc/gemv_i2s.hip",
                   "mpgemm_token_absmax_amd/csrc/common.hpp",
                   "mpgemm_token_absmax_amd/csrc/launch.hpp")
+ROTATE = 32                       # distinct layer copies of a decode stream
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
 
 
 def measured_traffic():
     """HBM bytes per decode launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a plain-kernel calibration), or
-    None when the decode kernel's sources changed since the counters were taken."""
+    None when the decode kernels' sources changed since the counters were taken."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
@@ -65,6 +78,8 @@ def measured_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+# ------------------------------------------------------------- graph helpers
+
 def capture_fns(torch, stream, fns):
     """HIP graph of the given launch callables, captured on `stream`."""
     g = torch.cuda.CUDAGraph()
@@ -74,8 +89,9 @@ def capture_fns(torch, stream, fns):
     return g
 
 
-def replay_us(torch, stream, g, launches, reps=20):
-    """Mean microseconds per launch over `reps` replays of graph g."""
+def replay_us(torch, stream, g, units, reps=10):
+    """Mean microseconds per unit over `reps` replays of graph g (one warm
+    replay first)."""
     with torch.cuda.stream(stream):
         g.replay()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -85,15 +101,103 @@ def replay_us(torch, stream, g, launches, reps=20):
             g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * launches)
+    return e0.elapsed_time(e1) * 1e3 / (reps * units)
 
 
-def measure_floors(torch, dev, stream, capture_fn, R, groups):
-    """Floors of a decode launch on this machine, with the measurement aids of
-    libblprobe.so in the same setting as the decode step (graph replays over R
-    cold buffer copies): an empty kernel, a streaming read of each group's
-    packed bytes by as many 256-thread blocks as its decode launch has, and a
-    1 GiB streaming read (practical HBM peak)."""
+def time_steps(torch, stream, layers, steps, warmup, spread_reps=None):
+    """Exactly `steps` steps timed: layers[r] is the list of launch callables
+    of layer copy r; step i runs copy i mod len(layers). The warmup steps and
+    the timed steps are captured as two graphs (the rotation continues from
+    one to the other); the timed graph is replayed once between two
+    synchronizations. Returns (ms per step, [p10, p50, p90] us per step over
+    further replays of the timed graph)."""
+    R = len(layers)
+    fw = [f for i in range(warmup) for f in layers[i % R]]
+    ft = [f for i in range(warmup, warmup + steps) for f in layers[i % R]]
+    g_warm = capture_fns(torch, stream, fw) if fw else None
+    g_timed = capture_fns(torch, stream, ft)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        if g_warm is not None:
+            g_warm.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g_timed.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    n = spread_reps or max(8, min(64, 2000 // steps))
+    marks = []
+    with torch.cuda.stream(stream):
+        for _ in range(n):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            g_timed.replay()
+            a1.record(stream)
+            marks.append((a0, a1))
+    torch.cuda.synchronize()
+    per = np.array([x0.elapsed_time(x1) * 1e3 / steps for x0, x1 in marks])
+    spread = [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)]
+    del g_warm, g_timed
+    return ms_step, spread
+
+
+# ------------------------------------------------------------ decode layers
+
+def to_dev(torch, a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def bf16_dev(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def packed_layer(torch, bl, W, dev, cfg, p_zero_override=None):
+    """{proj: (packed, gamma)} of one layer: fp32 master weights are
+    ternarized and packed by bl_pack_i2s (absmean gamma), drawn ternary
+    weights packed with the configuration's gamma."""
+    out = {}
+    for proj in cfg.projs:
+        inp = W.proj_inputs(cfg, proj, 1, with_acts=False, p_zero_override=p_zero_override)
+        if inp.w_f32 is not None:
+            out[proj.name] = bl.pack_i2s(to_dev(torch, inp.w_f32, dev))
+        else:
+            out[proj.name] = (bl.pack_i2s(to_dev(torch, inp.w_tern, dev)),
+                              to_dev(torch, np.array([inp.gamma], np.float32), dev))
+        del inp
+    return out
+
+
+def decode_layers(torch, bl, W, dev, cfg, M, R=ROTATE, p_zero_override=None):
+    """R distinct copies of a layer's packed weights and, per copy, the fused
+    decode launches of W.LAYER_GROUPS over seeded bf16 activations [M][K]
+    (one input per projection). Returns (layers, outputs by projection)."""
+    base = packed_layer(torch, bl, W, dev, cfg, p_zero_override)
+    xs = {p.name: bf16_dev(torch, W.activations_bf16(W.seed_for(cfg.cid, p.index, 1), M, p.K,
+                                                     cfg.outlier_frac, cfg.outlier_scale), dev)
+          for p in cfg.projs}
+    ys = {p.name: torch.empty((M, p.N), dtype=torch.bfloat16, device=dev) for p in cfg.projs}
+    layers = []
+    for r in range(R):
+        launches = []
+        for names in W.LAYER_GROUPS:
+            probs = [dict(packed=base[n][0] if r == 0 else base[n][0].clone(), gamma=base[n][1],
+                          x=xs[n], y=ys[n]) for n in names]
+            launches.append(bl.DecodeGroup(probs))
+        layers.append(launches)
+    torch.cuda.synchronize()
+    return layers, ys
+
+
+def stream_floors(torch, dev, stream, R, groups):
+    """Floors of a decode launch on this machine with the measurement aids of
+    libblprobe.so, in the same setting as the decode step (graph replays over
+    R cold buffer copies): an empty kernel, a streaming read of each group's
+    packed bytes by as many 256-thread blocks as its decode launch has 16-row
+    tiles, and a 1 GiB streaming read (practical HBM peak)."""
     import ctypes
     probe = ctypes.CDLL(os.path.join(ROOT, "mpgemm_token_absmax_amd", "libblprobe.so"))
     probe.blp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
@@ -114,12 +218,12 @@ def measure_floors(torch, dev, stream, capture_fn, R, groups):
             raise RuntimeError("blp_empty failed")
 
     out = {}
-    g = capture_fn(torch, stream, [empty] * 128)
+    g = capture_fns(torch, stream, [empty] * 128)
     out["empty_launch_us"] = round(replay_us(torch, stream, g, 128), 3)
     stream_us = {}
     for names, nbytes, blocks in groups:
         bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
-        g = capture_fn(torch, stream, [read(b, nbytes, blocks) for b in bufs])
+        g = capture_fns(torch, stream, [read(b, nbytes, blocks) for b in bufs])
         stream_us["+".join(names)] = round(replay_us(torch, stream, g, R), 3)
         del g, bufs
     out["stream_read_us"] = stream_us
@@ -128,7 +232,7 @@ def measure_floors(torch, dev, stream, capture_fn, R, groups):
     out["layer_floor_gbs"] = round(total / (out["layer_floor_us"] * 1e-6) / 1e9, 1)
     big = 1 << 30
     bufs = [torch.ones(big, dtype=torch.uint8, device=dev) for _ in range(2)]
-    g = capture_fn(torch, stream, [read(b, big, 2048) for b in bufs])
+    g = capture_fns(torch, stream, [read(b, big, 2048) for b in bufs])
     out["practical_peak_gbs"] = round(big / (replay_us(torch, stream, g, 2, reps=5) * 1e-6) / 1e9,
                                       1)
     del g, bufs
@@ -136,12 +240,56 @@ def measure_floors(torch, dev, stream, capture_fn, R, groups):
     return out
 
 
-def decode_more(torch, bl, W, dev, stream):
-    """The 7B-class layer at 1, 4 and 16 tokens (4 group launches per layer,
-    a stream over 32 distinct layer copies = 1.62 GB) and one-token GEMVs of
-    the 100B-class shapes (one launch, rotating copies), in GB/s of packed
-    weights; next to each 100B-class GEMV, a streaming read of the same bytes
-    (libblprobe.so) in the same setting."""
+def decode_workload(torch, bl, W, dev, stream, cid, M, p_zero_override=None):
+    """A decode stream over ROTATE layer copies (graph replays): microseconds
+    per layer and packed GB/s."""
+    cfg = W.LAYERS[cid]
+    layers, _ = decode_layers(torch, bl, W, dev, cfg, M, p_zero_override=p_zero_override)
+    for f in layers[0]:
+        f()
+    g = capture_fns(torch, stream, [f for layer in layers for f in layer])
+    us = replay_us(torch, stream, g, len(layers), reps=10)
+    del g, layers
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "tokens": M, "us_per_layer": round(us, 3),
+            "packed_bytes": cfg.packed_bytes,
+            "gbs": round(cfg.packed_bytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(cfg.packed_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "launches_per_layer": len(W.LAYER_GROUPS), "layer_copies": ROTATE}
+
+
+def single_gemv_workload(torch, bl, W, dev, stream):
+    """The 1024 x 1024 BitLinear GEMV at batch 1 (fp32 N(0, 0.02) weights,
+    absmean-ternarized), one fused decode launch per call, rotating over 2048
+    weight copies (537 MB, twice the Infinity Cache) so every call reads from
+    HBM; and the same launch on one copy (L2-resident weights)."""
+    cfg = W.LAYERS[1]
+    proj = cfg.projs[0]
+    inp = W.proj_inputs(cfg, proj, 1)
+    packed, gamma = bl.pack_i2s(to_dev(torch, inp.w_f32, dev))
+    x = bf16_dev(torch, inp.x_bf16, dev)
+    y = torch.empty((1, proj.N), dtype=torch.bfloat16, device=dev)
+    R = 2048
+    copies = [packed] + [packed.clone() for _ in range(R - 1)]
+    fns = [bl.DecodeGroup([dict(packed=c, gamma=gamma, x=x, y=y)]) for c in copies]
+    fns[0]()
+    g = capture_fns(torch, stream, fns)
+    us = replay_us(torch, stream, g, R, reps=5)
+    del g
+    g = capture_fns(torch, stream, [fns[0]] * 256)
+    us_warm = replay_us(torch, stream, g, 256, reps=10)
+    del g, fns, copies
+    torch.cuda.empty_cache()
+    nbytes = proj.N * proj.K // 4
+    return {"workload": cfg.name, "tokens": 1, "us_per_call": round(us, 3),
+            "packed_bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "warm_us_per_call": round(us_warm, 3), "weight_copies": R}
+
+
+def one_token_gemv_100b(torch, bl, dev, stream):
+    """One-token GEMVs of the 100B-class shapes (one fused launch each,
+    rotating copies), and next to each a streaming read of the same bytes
+    (libblprobe.so) by as many threads, in the same setting."""
     import ctypes
     probe = ctypes.CDLL(os.path.join(ROOT, "mpgemm_token_absmax_amd", "libblprobe.so"))
     probe.blp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
@@ -157,33 +305,6 @@ def decode_more(torch, bl, W, dev, stream):
         return f
 
     out = {}
-    cfg = W.LAYERS[4]
-    layer_groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
-    packed = {}
-    for proj in cfg.projs:
-        inp = W.proj_inputs(cfg, proj, 1, with_acts=False)
-        packed[proj.name] = bl.pack_i2s(torch.from_numpy(inp.w_f32).to(dev))
-        del inp
-    R = 32
-    copies = [{n: (pg[0] if r == 0 else pg[0].clone(), pg[1]) for n, pg in packed.items()}
-              for r in range(R)]
-    for M in (1, 4, 16):
-        xs = {}
-        for proj in cfg.projs:
-            bits = W.activations_bf16(W.seed_for(cfg.cid, proj.index, 1), M, proj.K,
-                                      cfg.outlier_frac, cfg.outlier_scale)
-            xs[proj.name] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-        launches = [bl.DecodeGroup([dict(packed=copies[r][n][0], gamma=copies[r][n][1], x=xs[n])
-                                    for n in names]) for r in range(R) for names in layer_groups]
-        for f in launches[:len(layer_groups)]:
-            f()
-        g = capture_fns(torch, stream, launches)
-        us = replay_us(torch, stream, g, 1, reps=10) / R
-        out[f"7b_layer_M{M}"] = {"us_per_layer": round(us, 3),
-                                 "gbs": round(cfg.packed_bytes / (us * 1e-6) / 1e9, 1)}
-        del g, launches
-    del copies, packed
-    torch.cuda.empty_cache()
     for N, K in ((28672, 8192), (8192, 28672)):
         t = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev)
         x = torch.randn(1, K, device=dev).to(torch.bfloat16)
@@ -195,17 +316,15 @@ def decode_more(torch, bl, W, dev, stream):
         g = capture_fns(torch, stream, launches)
         us = replay_us(torch, stream, g, R, reps=10)
         del g
-        # floor: a streaming read of the same bytes by as many threads as the
-        # decode launch has (16 rows per block, 256 or 512 threads), R copies
         nbytes = N * K // 4
         blocks = (N + 15) // 16 * (2 if K > 16384 else 1)
         bufs = [c.problems[0]["packed"] for c in launches]
         g = capture_fns(torch, stream, [stream_read(b, nbytes, blocks) for b in bufs])
         floor = replay_us(torch, stream, g, R, reps=10)
-        out[f"one_token_gemv_N{N}_K{K}"] = {"us": round(us, 3),
-                                           "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
-                                           "stream_floor_us": round(floor, 3),
-                                           "frac_of_floor": round(floor / us, 3)}
+        out[f"N{N}_K{K}"] = {"us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "stream_floor_us": round(floor, 3),
+                             "frac_of_floor": round(floor / us, 3)}
         del g, launches, bufs
         torch.cuda.empty_cache()
     return out
@@ -220,7 +339,7 @@ def norm_layer_bench(torch, bl, W, dev, stream):
     cfg = W.LAYERS[2]
     by = {p.name: p for p in cfg.projs}
     K = 2560
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    t = lambda a: bf16_dev(torch, a, dev)
     x1, r1, g1 = W.norm_inputs(2001, 1, K, cfg.outlier_frac, cfg.outlier_scale)
     x2, r2, g2 = W.norm_inputs(2002, 1, K, cfg.outlier_frac, cfg.outlier_scale)
     xo = W.activations_bf16(2003, 1, K, cfg.outlier_frac, cfg.outlier_scale)
@@ -228,9 +347,9 @@ def norm_layer_bench(torch, bl, W, dev, stream):
     X1, R1, G1, X2, R2, G2, XO, XD = (t(a) for a in (x1, r1, g1, x2, r2, g2, xo, xd))
     H1, H2 = torch.empty_like(X1), torch.empty_like(X2)
     gam = torch.tensor([W.GAMMA_DRAWN], dtype=torch.float32, device=dev)
-    base = {n: bl.pack_i2s(torch.from_numpy(W.proj_inputs(cfg, by[n], 1, with_acts=False).w_tern).to(dev))
+    base = {n: bl.pack_i2s(to_dev(torch, W.proj_inputs(cfg, by[n], 1, with_acts=False).w_tern, dev))
             for n in by}
-    R = 32
+    R = ROTATE
     copies = [{n: (p if r == 0 else p.clone()) for n, p in base.items()} for r in range(R)]
     fused, unfused = [], []
     q1 = torch.empty((1, K), dtype=torch.int8, device=dev)
@@ -254,7 +373,7 @@ def norm_layer_bench(torch, bl, W, dev, stream):
         for f in fns[:9]:
             f()
         g = capture_fns(torch, stream, fns)
-        us = replay_us(torch, stream, g, 1, reps=10) / R
+        us = replay_us(torch, stream, g, R, reps=10)
         out[name] = {"us_per_layer": round(us, 3), "gbs": round(cfg.packed_bytes / (us * 1e-6) / 1e9, 1)}
         del g
     del copies, fused, unfused
@@ -264,36 +383,24 @@ def norm_layer_bench(torch, bl, W, dev, stream):
 
 def t3_bench(torch, bl, W, dev, stream):
     """Base-3 weights (five per byte, 1.6 bits per weight) against I2_S (2 bits
-    per weight), one token:
-      - through the GEMV kernels of the same structure (int8 codes in):
-        bl_gemv_t3 and bl_gemv ("t3", "i2s");
-      - through the fused one-token decode (bf16 x in, quantize in the
-        kernel): bl_decode_group_t3 and bl_decode_group ("t3_fused",
-        "i2s_fused");
-    graph replays over copies of the packed weights (>= 700 MB), microseconds
-    per call, GB/s of packed bytes and billions of weights per second; and the
-    BitNet-2B-like decode layer (4 fused launches, 32 rotating layer copies)
-    in both formats."""
+    per weight), one token, through the fused one-token decode (bf16 x in,
+    quantize in the kernel): bl_decode_group_t3 against bl_decode_group, graph
+    replays over copies of the packed weights (>= 700 MB), microseconds per
+    call, GB/s of packed bytes and billions of weights per second."""
     out = {}
-    for N, K in ((2560, 2560), (6912, 2560), (2560, 6912), (28672, 8192), (8192, 28672)):
-        t = torch.from_numpy(W.ternary_drawn(7 + N + K, N, K, 1.0 / 3.0)).to(dev)
+    for N, K in ((2560, 2560), (6912, 2560), (28672, 8192), (8192, 28672)):
+        t = to_dev(torch, W.ternary_drawn(7 + N + K, N, K, 1.0 / 3.0), dev)
         p2, p3 = bl.pack_i2s(t), bl.pack_t3(t)
         del t
-        x = torch.from_numpy(W.activations_bf16(9 + K, 1, K, 0.005, 50.0).view(np.int16)).to(dev)
-        xb = x.view(torch.bfloat16)
-        q, d = bl.quantize_act(xb)
+        xb = bf16_dev(torch, W.activations_bf16(9 + K, 1, K, 0.005, 50.0), dev)
         gam = torch.tensor([W.GAMMA_DRAWN], dtype=torch.float32, device=dev)
         R = max(2, -(-700_000_000 // p3.numel()))
         y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
         rec = {}
-        for name, p, fn in (("i2s", p2, bl.gemv), ("t3", p3, bl.gemv_t3),
-                            ("i2s_fused", p2, bl.DecodeGroup), ("t3_fused", p3, bl.DecodeGroupT3)):
+        for name, p, fn in (("i2s_fused", p2, bl.DecodeGroup), ("t3_fused", p3, bl.DecodeGroupT3)):
             copies = [p] + [p.clone() for _ in range(R - 1)]
-            if name.endswith("_fused"):
-                fns = [fn([dict(packed=c, gamma=gam, x=xb, y=y)]) for c in copies]
-                fns[0]()
-            else:
-                fns = [(lambda c=c: fn(c, gam, q, d, out=y)) for c in copies]
+            fns = [fn([dict(packed=c, gamma=gam, x=xb, y=y)]) for c in copies]
+            fns[0]()
             g = capture_fns(torch, stream, fns)
             us = replay_us(torch, stream, g, R, reps=10)
             rec[name] = {"us": round(us, 3), "packed_bytes": p.numel(),
@@ -303,35 +410,6 @@ def t3_bench(torch, bl, W, dev, stream):
         out[f"N{N}_K{K}"] = rec
         del p2, p3
         torch.cuda.empty_cache()
-    # the 2B decode layer, both formats
-    cfg = W.LAYERS[2]
-    layer_groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
-    gam = torch.tensor([W.GAMMA_DRAWN], dtype=torch.float32, device=dev)
-    xs, tern = {}, {}
-    for proj in cfg.projs:
-        inp = W.proj_inputs(cfg, proj, 1)
-        tern[proj.name] = torch.from_numpy(inp.w_tern).to(dev)
-        xs[proj.name] = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
-    R = 32
-    layer = {}
-    for name, pack, Grp in (("i2s_fused", bl.pack_i2s, bl.DecodeGroup),
-                            ("t3_fused", bl.pack_t3, bl.DecodeGroupT3)):
-        base = {n: pack(t) for n, t in tern.items()}
-        nbytes = sum(p.numel() for p in base.values())
-        copies = [{n: (p if r == 0 else p.clone()) for n, p in base.items()} for r in range(R)]
-        ys = {n: torch.empty((1, t.shape[0]), dtype=torch.bfloat16, device=dev) for n, t in tern.items()}
-        fns = [Grp([dict(packed=c[n], gamma=gam, x=xs[n], y=ys[n]) for n in names])
-               for c in copies for names in layer_groups]
-        for f in fns[:4]:
-            f()
-        g = capture_fns(torch, stream, fns)
-        us = replay_us(torch, stream, g, 1, reps=10) / R
-        layer[name] = {"us_per_layer": round(us, 3), "packed_bytes": nbytes,
-                       "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
-        del g, fns, copies, base
-    out["bitnet2b_decode_layer"] = layer
-    del tern, xs
-    torch.cuda.empty_cache()
     return out
 
 
@@ -348,11 +426,11 @@ def norm_bench(torch, bl, W, dev, stream):
         cfg = W.LAYERS[cid]
         K = cfg.projs[0].K
         xb, rb, gb = W.norm_inputs(4242 + cid, M, K, cfg.outlier_frac, cfg.outlier_scale)
-        t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        g = t(gb)
+        g = bf16_dev(torch, gb, dev)
         nbytes = M * (7 * K + 4) + 2 * K
         R = max(1, min(64, -(-600_000_000 // nbytes)))
-        bufs = [dict(x=t(xb), r=t(rb), h=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+        bufs = [dict(x=bf16_dev(torch, xb, dev), r=bf16_dev(torch, rb, dev),
+                     h=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
                      q=torch.empty((M, K), dtype=torch.int8, device=dev),
                      d=torch.empty((M,), dtype=torch.float32, device=dev)) for _ in range(R)]
 
@@ -373,7 +451,6 @@ def norm_bench(torch, bl, W, dev, stream):
         gr = capture_fns(torch, stream, [unfused(b) for b in bufs])
         us_unf = replay_us(torch, stream, gr, R)
         del gr, bufs
-        # floor: a plain device copy moving the same bytes (half read, half written)
         half = nbytes // 2
         cbufs = [(torch.empty(half, dtype=torch.uint8, device=dev),
                   torch.ones(half, dtype=torch.uint8, device=dev)) for _ in range(R)]
@@ -389,69 +466,110 @@ def norm_bench(torch, bl, W, dev, stream):
     return out
 
 
-def parse():
-    p = argparse.ArgumentParser()
-    p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=640)
-    p.add_argument("--warmup", type=int, default=64)
-    p.add_argument("--rotate", type=int, default=32, help="distinct layer copies")
-    p.add_argument("--gemm-steps", type=int, default=5)
-    p.add_argument("--no-gemm", action="store_true")
-    p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-extras", action="store_true",
-                   help="skip the 7B-layer and 100B-shape decode measurements")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--mfma-counters", action="store_true",
-                   help="counter-collection mode: only the prefill GEMM layers (eager), no JSON line")
-    p.add_argument("--traffic", action="store_true",
-                   help="counter-collection mode: a 256 MiB plain copy (calibration) and "
-                        "eager decode launches over distinct weight copies; no JSON line")
-    return p.parse_args()
+# ------------------------------------------------------------------ prefill
 
-
-def log(*a):
-    print(*a, file=sys.stderr, flush=True)
-
-
-def build_prefill(torch, bl, W, dev, cid=5, M5=2048):
+def build_prefill(torch, bl, W, dev, cid=5, M=2048):
     """A prefill layer (by default the 100B-class layer at 2048 tokens): one
-    bf16 input per group of projections that read it; each group's GEMMs run
-    through one bl_gemm_group call on its quantized codes. The quantizer also
-    writes the token sums and `group` takes them (offset weights); `plain` is
-    the same group without them."""
-    cfg5 = W.LAYERS[cid]
-    log(f"setup prefill: {cfg5.name}")
-    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    by = {proj.name: proj for proj in cfg5.projs}
+    bf16 input per group of W.LAYER_GROUPS; each group's GEMMs run through
+    one bl_gemm_group call on its quantized codes. The quantizer also writes
+    the token sums and `group` takes them (offset weights); `plain` is the
+    same group without them."""
+    cfg = W.LAYERS[cid]
+    log(f"setup prefill: {cfg.name}")
+    by = {proj.name: proj for proj in cfg.projs}
     G = []
-    for names in PREFILL_GROUPS:
-        inps = [W.proj_inputs(cfg5, by[n], M5) for n in names]
+    for names in W.LAYER_GROUPS:
+        inps = [W.proj_inputs(cfg, by[n], M) for n in names]
         K = by[names[0]].K
-        x = to_dev(inps[0].x_bf16.view(np.int16)).view(torch.bfloat16)
-        q = torch.empty((M5, K), dtype=torch.int8, device=dev)
-        d = torch.empty((M5,), dtype=torch.float32, device=dev)
-        qs = torch.empty((M5,), dtype=torch.int32, device=dev)
-        probs = [dict(packed=bl.pack_i2s(to_dev(inp.w_tern)),
-                      gamma=to_dev(np.array([inp.gamma], np.float32)),
-                      y=torch.empty((M5, by[n].N), dtype=torch.bfloat16, device=dev))
+        x = bf16_dev(torch, inps[0].x_bf16, dev)
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        d = torch.empty((M,), dtype=torch.float32, device=dev)
+        qs = torch.empty((M,), dtype=torch.int32, device=dev)
+        probs = [dict(packed=bl.pack_i2s(to_dev(torch, inp.w_tern, dev)),
+                      gamma=to_dev(torch, np.array([inp.gamma], np.float32), dev),
+                      y=torch.empty((M, by[n].N), dtype=torch.bfloat16, device=dev))
                  for n, inp in zip(names, inps)]
         G.append(dict(names=names, x=x, q=q, d=d, qs=qs,
                       group=bl.GemmGroup(probs, q, d, qsum=qs),
                       plain=bl.GemmGroup(probs, q, d),
-                      ops=sum(2 * M5 * by[n].N * by[n].K for n in names)))
+                      ops=sum(2 * M * by[n].N * by[n].K for n in names)))
         del inps
     torch.cuda.synchronize()
-    return cfg5, M5, G
+    return cfg, M, G
+
+
+def prefill_100b(torch, bl, W, dev, gemm_steps):
+    """The 100B-class layer at 2048 tokens: per input one bl_quantize_act
+    (codes, scales, token sums), then one bl_gemm_group per group (offset
+    weights). TOPS with and without the quantize launches, without the token
+    sums (interleaved rounds), per group, and with one scale per tensor."""
+    cfg5, M5, G = build_prefill(torch, bl, W, dev)
+
+    def layer(gemm_only=False, plain=False):
+        for e in G:
+            if not gemm_only:
+                bl.quantize_act(e["x"], e["q"], e["d"], qsum=e["qs"])
+            e["plain" if plain else "group"]()
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    layer()
+    ms_layer = timed(layer, gemm_steps)
+    ops = cfg5.ops(M5)
+    # GEMMs only, with and without the token sums, interleaved (the clock
+    # drifts with the power state): medians over 3 rounds
+    ms_by = {False: [], True: []}
+    for rnd in range(3):
+        for plain in ((False, True) if rnd % 2 == 0 else (True, False)):
+            ms_by[plain].append(timed(lambda: layer(gemm_only=True, plain=plain), gemm_steps))
+    ms_gemm = float(np.median(ms_by[False]))
+    ws_t = torch.empty((max(16, int(bl.lib().bl_quantize_act_tensor_workspace(M5))),),
+                       dtype=torch.uint8, device=dev)
+
+    def layer_pt():
+        for e in G:
+            bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t, qsum=e["qs"])
+            e["group"]()
+
+    ms_layer_pt = timed(layer_pt, gemm_steps)
+    per_group = {}
+    for e in G:
+        ms = timed(e["group"], 3)
+        per_group["+".join(e["names"])] = {"us": round(ms * 1e3, 2),
+                                           "tops": round(e["ops"] / (ms * 1e-3) / 1e12, 1)}
+    del G
+    torch.cuda.empty_cache()
+    return {"workload": cfg5.name, "tokens": M5, "ops_per_layer": ops,
+            "ms_per_layer": round(ms_layer, 4), "tops": round(ops / (ms_layer * 1e-3) / 1e12, 1),
+            "gemm_only_ms": round(ms_gemm, 4),
+            "gemm_only_tops": round(ops / (ms_gemm * 1e-3) / 1e12, 1),
+            "frac": round(ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "gemm_only_tops_without_token_sums":
+                round(ops / (float(np.median(ms_by[True])) * 1e-3) / 1e12, 1),
+            "step": "per input: bl_quantize_act (codes, scales, token sums), then one "
+                    "bl_gemm_group for {q,k,v}, {o}, {gate,up}, {down} (offset weights)",
+            "per_group": per_group,
+            "tops_per_tensor_scale": round(ops / (ms_layer_pt * 1e-3) / 1e12, 1)}
 
 
 def prefill_2b(torch, bl, W, dev, stream):
     """The BitNet-2B-like layer at 512 tokens (small matrices on the int8
     MFMA path): per input one bl_quantize_act, then one bl_gemm_group per
-    {q,k,v}, {o}, {gate,up}, {down}, as graph replays over 32 layer copies
-    (17.4 MB of packed weights each, so the weights come from HBM). TOPS of
-    the GEMMs alone and of the layer with its quantize launches."""
-    cfg, M, G = build_prefill(torch, bl, W, dev, cid=3, M5=512)
-    R = 32
+    group, as graph replays over 32 layer copies (17.4 MB of packed weights
+    each, so the weights come from HBM). TOPS of the GEMMs alone and of the
+    layer with its quantize launches."""
+    cfg, M, G = build_prefill(torch, bl, W, dev, cid=3, M=512)
+    R = ROTATE
     copies = []
     for r in range(R):
         copies.append([e["group"] if r == 0 else
@@ -465,12 +583,154 @@ def prefill_2b(torch, bl, W, dev, stream):
     out = {"workload": cfg.name, "tokens": M, "ops_per_layer": cfg.ops(M)}
     for name, fns in (("gemm_only", gemm_only), ("with_quantize", with_q)):
         g = capture_fns(torch, stream, fns)
-        us = replay_us(torch, stream, g, 1, reps=10) / R
-        out[name] = {"us_per_layer": round(us, 2), "tops": round(cfg.ops(M) / (us * 1e-6) / 1e12, 1)}
+        us = replay_us(torch, stream, g, R, reps=10)
+        out[name] = {"us_per_layer": round(us, 2), "tops": round(cfg.ops(M) / (us * 1e-6) / 1e12, 1),
+                     "frac": round(cfg.ops(M) / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)}
         del g
     del copies, G
     torch.cuda.empty_cache()
     return out
+
+
+# --------------------------------------------------------------- CPU oracle
+
+# Each workload's oracle step: per projection, the bf16 input quantized per
+# token, the packed rows unpacked, the int64 dot and the dequant to bf16; the
+# packing itself is the offline conversion and is not timed. The oracle's
+# speed does not depend on the weight values (a dense integer matmul), so the
+# packed rows are drawn ternary at the workload's zero fraction.
+CPU_PLAN = {
+    # cid: (tokens, workload name, row fraction on one core, row fraction on all cores)
+    1: (1, "single-1024x1024-decode", 1, 1),
+    2: (1, "bitnet-2b-layer-decode", 1, 1),
+    3: (512, "bitnet-2b-layer-prefill-512", 16, 1),
+    4: (1, "7b-layer-decode", 1, 1),
+    5: (2048, "100b-layer-prefill-2048", 512, 16),
+}
+
+
+def _cpu_inputs(cid, rows_div, shard, nshard):
+    """Seeded inputs of one shard of a workload's row sample: per projection
+    (x bf16 [M][K], packed rows, gamma, K). The sample is N/rows_div output
+    rows of every projection; shard s of n takes its s-th part."""
+    import oracle
+    import workloads as W
+    cfg = W.LAYERS[cid]
+    M = CPU_PLAN[cid][0]
+    p0 = 0.31 if cfg.weights == "f32_normal" else cfg.p_zero
+    out = []
+    for proj in cfg.projs:
+        n_rows = max(1, proj.N // rows_div)
+        lo, hi = n_rows * shard // nshard, n_rows * (shard + 1) // nshard
+        if hi <= lo:
+            continue
+        x = W.activations_bf16(W.seed_for(cid, proj.index, 1), M, proj.K,
+                               cfg.outlier_frac, cfg.outlier_scale)
+        w = W.ternary_drawn(W.seed_for(cid, proj.index, 0) + 7 * shard + 1, hi - lo, proj.K, p0)
+        out.append((x, oracle.pack_i2s(w), np.float32(W.GAMMA_DRAWN), proj.K))
+    return out
+
+
+def _cpu_step(data):
+    """One oracle step over the given inputs; returns the seconds it took."""
+    import oracle
+    t0 = time.perf_counter()
+    for x, packed, gamma, K in data:
+        q, d = oracle.quantize_act_absmax(x)
+        t = oracle.unpack_i2s(packed, K)
+        acc = oracle.mpgemm_acc(q, t)
+        oracle.round_f64_to_bf16_bits(oracle.dequant_f64(acc, gamma, d))
+    return time.perf_counter() - t0
+
+
+def _cpu_worker(cid, rows_div, shard, nshard, ready, go, results):
+    """One worker process: builds its shard's inputs, waits until every worker
+    has, runs one oracle step when the parent says go, reports its time."""
+    data = _cpu_inputs(cid, rows_div, shard, nshard)
+    if data:
+        _cpu_step(data[:1])                              # warm the code paths
+    ready.wait()
+    go.wait()
+    results.put((shard, _cpu_step(data)))
+
+
+def cpu_baseline(gpu_us, headline_cid=4):
+    """The oracle timed per workload on this host: on one core (this process)
+    over a row sample, and on all cores (one spawned worker process per core,
+    each a contiguous shard of a row sample, all started together) as the wall
+    time until the last worker finishes; both extrapolated to the whole
+    workload by the row fraction. gpu_us: the GPU time of each workload's step
+    in microseconds."""
+    import multiprocessing as mp
+    import workloads as W
+    ncores = min(16, len(os.sched_getaffinity(0)))
+    out = {"host_cores": len(os.sched_getaffinity(0)), "worker_processes": ncores, "per_config": {}}
+    ctx = mp.get_context("spawn")
+    for cid, (M, name, div1, divn) in CPU_PLAN.items():
+        data = _cpu_inputs(cid, div1, 0, 1)
+        _cpu_step(data[:1])
+        t1 = _cpu_step(data) * div1
+        del data
+        ready, go, results = ctx.Barrier(ncores + 1), ctx.Event(), ctx.Queue()
+        procs = [ctx.Process(target=_cpu_worker, args=(cid, divn, s, ncores, ready, go, results))
+                 for s in range(ncores)]
+        for pr in procs:
+            pr.start()
+        ready.wait(timeout=600)
+        t0 = time.perf_counter()
+        go.set()
+        shards = [results.get(timeout=600) for _ in range(ncores)]
+        tn = (time.perf_counter() - t0) * divn
+        for pr in procs:
+            pr.join(timeout=60)
+        if sorted(s for s, _ in shards) != list(range(ncores)):
+            raise RuntimeError("cpu baseline: missing worker results")
+        cfg = W.LAYERS[cid]
+        rec = {"workload": name, "tokens": M,
+               "one_core_s": round(t1, 4), "one_core_row_fraction": f"1/{div1}",
+               "all_cores_s": round(tn, 4), "all_cores_row_fraction": f"1/{divn}",
+               "extrapolated": div1 > 1 or divn > 1,
+               "slowest_worker_s": round(max(t for _, t in shards) * divn, 4)}
+        if M == 1:
+            rec["one_core_gbs"] = round(cfg.packed_bytes / t1 / 1e9, 4)
+            rec["all_cores_gbs"] = round(cfg.packed_bytes / tn / 1e9, 4)
+        else:
+            rec["one_core_tops"] = round(cfg.ops(M) / t1 / 1e12, 6)
+            rec["all_cores_tops"] = round(cfg.ops(M) / tn / 1e12, 6)
+        if gpu_us.get(cid):
+            rec["gpu_us"] = round(gpu_us[cid], 3)
+            rec["gpu_speedup_vs_all_cores"] = round(tn / (gpu_us[cid] * 1e-6), 1)
+            rec["gpu_speedup_vs_one_core"] = round(t1 / (gpu_us[cid] * 1e-6), 1)
+        out["per_config"][str(cid)] = rec
+        log(f"cpu oracle config {cid}: one core {t1:.3f} s, {ncores} cores {tn:.3f} s")
+    h = out["per_config"][str(headline_cid)]
+    out.update({"value": h["all_cores_gbs"], "unit": "GB/s", "cores": ncores, "kind": "oracle",
+                "sample": f"the 7B-class decode layer at batch 1 (7 projections, 50.6 MB "
+                          f"packed): quantize, unpack, int64 dot, dequant, bf16 (numpy), row "
+                          f"shards in {ncores} worker processes on a {out['host_cores']}-core "
+                          f"host; one core: {h['one_core_gbs']} GB/s; every workload in "
+                          f"per_config (configs 3 and 5 on row samples, extrapolated)"})
+    return out
+
+
+# --------------------------------------------------------------------- main
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=640)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--gemm-steps", type=int, default=5)
+    p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="only the headline stream (and the prefill unless --no-gemm)")
+    p.add_argument("--mfma-counters", action="store_true",
+                   help="counter-collection mode: only the prefill GEMM layers (eager), no JSON line")
+    p.add_argument("--traffic", action="store_true",
+                   help="counter-collection mode: a 256 MiB plain copy (calibration) and "
+                        "eager decode launches of the headline stream; no JSON line")
+    return p.parse_args()
 
 
 def main():
@@ -478,6 +738,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -487,11 +750,8 @@ def main():
     bl.lib()
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     if args.mfma_counters:
-        # counter-collection mode for the prefill GEMMs: quantize (with token
-        # sums) and bl_gemm_group per input, --gemm-steps layers, eager
         _, _, G = build_prefill(torch, bl, W, dev)
         for _ in range(args.gemm_steps):
             for e in G:
@@ -501,176 +761,47 @@ def main():
         log(f"mfma-counters mode: {args.gemm_steps} prefill layers ({len(G)} groups each)")
         return
 
-
-    # ----------------------------------------------------------------- decode
-    cfg = W.LAYERS[2]
-    M = 1
-    R = max(1, args.rotate)
-    log(f"setup decode: {cfg.name}, {R} layer copies")
-    inputs = {}
-    for proj in cfg.projs:
-        inp = W.proj_inputs(cfg, proj, M)
-        inputs[proj.name] = dict(
-            packed=bl.pack_i2s(to_dev(inp.w_tern)),
-            gamma=to_dev(np.array([inp.gamma], np.float32)),
-            x=to_dev(inp.x_bf16.view(np.int16)).view(torch.bfloat16),
-            y=torch.empty((M, proj.N), dtype=torch.bfloat16, device=dev),
-            q=torch.empty((M, proj.K), dtype=torch.int8, device=dev),
-            d=torch.empty((M,), dtype=torch.float32, device=dev))
-    torch.cuda.synchronize()
+    # ----------------------------------------------- headline: 7B decode stream
+    cfg = W.LAYERS[4]
+    log(f"setup decode stream: {cfg.name}, {ROTATE} layer copies")
+    layers, _ = decode_layers(torch, bl, W, dev, cfg, 1)
     step_bytes = cfg.packed_bytes
-    # the projections of a decoder layer that do not depend on each other
-    GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
-    layers = []            # layers[r] = fused decode launches of layer copy r
-    for r in range(R):
-        launches = []
-        for names in GROUPS:
-            probs = []
-            for nm in names:
-                e = inputs[nm]
-                packed = e["packed"] if r == 0 else e["packed"].clone()
-                probs.append(dict(packed=packed, gamma=e["gamma"], x=e["x"], y=e["y"], name=nm))
-            launches.append(bl.DecodeGroup(probs))
-        layers.append(launches)
-    torch.cuda.synchronize()
-
-    def step(r):
-        for launch in layers[r]:
-            launch()
-
     if args.traffic:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src).fill_(0)
         torch.cuda.synchronize()
         torch.bitwise_not(src, out=dst)       # calibration kernel: 256 MiB read, 256 MiB written
         torch.cuda.synchronize()
-        for r in range(R):                    # each launch reads weights no earlier launch read
-            step(r)
+        for layer in layers:                  # each launch reads weights no earlier launch read
+            for f in layer:
+                f()
         torch.cuda.synchronize()
-        if not args.no_extras:                # 4 fused norm launches, 100B prefill shape
-            cfg5 = W.LAYERS[5]
-            K5 = cfg5.projs[0].K
-            xb, rb, gb = W.norm_inputs(4247, 2048, K5, cfg5.outlier_frac, cfg5.outlier_scale)
-            t = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-            gn = t(gb)
-            for _ in range(4):
-                xn, rn = t(xb), t(rb)
-                bl.rmsnorm_quant(xn, gn, 1e-5, residual=rn, h_out=rn)
-            torch.cuda.synchronize()
-        log(f"traffic mode: 1 calibration kernel over {src.numel()} B, {R * len(GROUPS)} decode launches "
-            f"({step_bytes // len(GROUPS)} packed bytes per launch on average)")
+        log(f"traffic mode: 1 calibration kernel over {src.numel()} B, "
+            f"{len(layers) * len(W.LAYER_GROUPS)} decode launches "
+            f"({step_bytes // len(W.LAYER_GROUPS)} packed bytes per launch on average)")
         return
-
-    def step_unfused(r):        # 7 x (bl_quantize_act + bl_gemv), for comparison
-        for launch in layers[r]:
-            for p in launch.problems:
-                e = inputs[p["name"]]
-                bl.quantize_act(p["x"], e["q"], e["d"])
-                bl.gemv(p["packed"], p["gamma"], e["q"], e["d"], out_dtype="bf16", out=p["y"])
-
-    for r in range(R):          # eager warm-up (loads the code objects) before capture
-        step(r)
-        step_unfused(r)
+    for layer in layers:                      # eager pass: loads the code objects
+        for f in layer:
+            f()
     torch.cuda.synchronize()
-
     stream = torch.cuda.Stream()
-
-    def capture(fn, rs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for r in rs:
-                fn(r)
-        return g
-
-    g_all = capture(step, range(R))
-    g_one = [capture(step, [r]) for r in range(R)]
-    g_unfused = capture(step_unfused, range(R))
-    torch.cuda.synchronize()
-
-    def run_steps(n):
-        full, rem = divmod(n, R)
-        for _ in range(full):
-            g_all.replay()
-        for r in range(rem):
-            g_one[r].replay()
-
-    log(f"warmup {args.warmup} steps")
-    run_steps(args.warmup)
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    run_steps(args.steps)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
+    log(f"timing {args.steps} steps after {args.warmup} warmup steps")
+    ms_step, spread = time_steps(torch, stream, layers, args.steps, args.warmup)
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"decode: {ms_step * 1e3:.2f} us/step, {gbs:.1f} GB/s packed")
-
-    # The dominant kernel is the fused decode kernel itself (the step is made of
-    # its launches): average launch duration from events on the replay stream.
-    reps = max(4, args.steps // R)
-    with torch.cuda.stream(stream):
-        g_all.replay()
-        k0 = torch.cuda.Event(enable_timing=True)
-        k1 = torch.cuda.Event(enable_timing=True)
-        k0.record(stream)
-        for _ in range(reps):
-            g_all.replay()
-        k1.record(stream)
-        u0 = torch.cuda.Event(enable_timing=True)
-        u1 = torch.cuda.Event(enable_timing=True)
-        g_unfused.replay()
-        u0.record(stream)
-        for _ in range(reps):
-            g_unfused.replay()
-        u1.record(stream)
-    torch.cuda.synchronize()
-    launches = reps * R * len(GROUPS)
-    us_launch = k0.elapsed_time(k1) * 1e3 / launches
-    bytes_launch = step_bytes / len(GROUPS)
-    gemv_gbs = bytes_launch / (us_launch * 1e-6) / 1e9
-    us_unfused = u0.elapsed_time(u1) * 1e3 / (reps * R)
-    log(f"fused decode kernel: {us_launch:.2f} us/launch avg, {gemv_gbs:.1f} GB/s; "
-        f"unfused 7x(quantize+gemv): {us_unfused:.2f} us/step")
-
-    # per-replay spread: each replay of g_all is R steps
-    marks = []
-    with torch.cuda.stream(stream):
-        for _ in range(max(8, min(64, args.steps // R))):
-            a0 = torch.cuda.Event(enable_timing=True)
-            a1 = torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            g_all.replay()
-            a1.record(stream)
-            marks.append((a0, a1))
-    torch.cuda.synchronize()
-    per_step = np.array([x0.elapsed_time(x1) * 1e3 / R for x0, x1 in marks])
-    spread = [round(float(np.percentile(per_step, q)), 3) for q in (10, 50, 90)]
-
-    # warm mode: every step reuses layer copy 0 (weights stay in the Infinity Cache)
-    g_warm = capture(step, [0] * R)
-    with torch.cuda.stream(stream):
-        g_warm.replay()
-        w0 = torch.cuda.Event(enable_timing=True)
-        w1 = torch.cuda.Event(enable_timing=True)
-        w0.record(stream)
-        for _ in range(reps):
-            g_warm.replay()
-        w1.record(stream)
-    torch.cuda.synchronize()
-    us_warm = w0.elapsed_time(w1) * 1e3 / (reps * R)
-
-    floors = measure_floors(torch, dev, stream, capture_fn=capture_fns, R=R,
-                            groups=[(names, sum(inputs[n]["packed"].numel() for n in names),
-                                     sum((inputs[n]["packed"].shape[0] + 15) // 16 for n in names))
-                                    for names in GROUPS])
-    log(f"decode spread p10/p50/p90 {spread} us/step; warm (cache-resident weights) "
-        f"{us_warm:.2f} us/step; floors {floors}")
+    launches = len(W.LAYER_GROUPS)
+    us_launch = ms_step * 1e3 / launches
+    log(f"7B decode stream: {ms_step * 1e3:.2f} us/step, {gbs:.1f} GB/s packed; p10/p50/p90 {spread}")
+    # warm: every step reuses layer copy 0 (weights resident in the Infinity Cache)
+    g_warm = capture_fns(torch, stream, [f for _ in range(ROTATE) for f in layers[0]])
+    us_warm = replay_us(torch, stream, g_warm, ROTATE)
     del g_warm
+    blocks16 = lambda names: sum((next(p.N for p in cfg.projs if p.name == n) + 15) // 16 for n in names)
+    floors = stream_floors(torch, dev, stream, ROTATE,
+                           [(names, sum(p.N * p.K // 4 for p in cfg.projs if p.name in names),
+                             blocks16(names)) for names in W.LAYER_GROUPS])
+    log(f"floors {floors}")
+    del layers
+    torch.cuda.empty_cache()
 
     result = {
         "metric": "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM int8 TOPS (% peak)",
@@ -685,135 +816,60 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": M, "hidden": 2560, "ffn": 6912, "kv": 640,
-                   "layer_copies": R, "packed_bytes_per_step": step_bytes,
-                   "step": "4 fused launches {q,k,v},{o},{gate,up},{down}: per-token absmax "
-                           "int8 quantize + I2_S GEMV + bf16 dequant",
+        "config": {"workload": "7b-layer-decode-stream", "tokens": 1, "hidden": 4096,
+                   "ffn": 11008, "heads": 32, "layer_copies": ROTATE,
+                   "packed_bytes_per_step": step_bytes,
+                   "step": "one layer: 4 fused launches {q,k,v},{o},{gate,up},{down}, each "
+                           "per-token absmax int8 quantize + I2_S GEMV + bf16 dequant; step i "
+                           "on layer copy i mod 32",
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                   "unfused_us_per_step": round(us_unfused, 3),
                    "us_per_step_p10_p50_p90": spread,
                    "warm_us_per_step": round(us_warm, 3),
                    "floors": floors,
                    "frac_of_layer_floor": round(floors["layer_floor_us"] / (ms_step * 1e3), 4)},
-        "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "k_decode1 (one-token fused decode group)",
-                     "us_per_launch": round(us_launch, 3), "bytes_per_launch": bytes_launch},
+                     "kernel": "k_decode1 / k_decode1w (one-token fused decode launches)",
+                     "us_per_launch": round(us_launch, 3),
+                     "bytes_per_launch": step_bytes / launches},
     }
-    del layers, g_all, g_one, g_unfused
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    gpu_us = {4: ms_step * 1e3}
+    configs = {"4": {"M1": {"us_per_layer": round(ms_step * 1e3, 3), "gbs": round(gbs, 1),
+                            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}}}
 
-    # ------------------------------------------------ more decode workloads
     if not args.no_extras:
-        result["decode_more"] = decode_more(torch, bl, W, dev, stream)
-        log(f"more decode: {result['decode_more']}")
+        for M in (4, 16):
+            configs["4"][f"M{M}"] = decode_workload(torch, bl, W, dev, stream, 4, M)
+            log(f"7B decode M={M}: {configs['4'][f'M{M}']}")
+        configs["4"]["M1_p_zero_0.65"] = decode_workload(torch, bl, W, dev, stream, 4, 1,
+                                                         p_zero_override=0.65)
+        log(f"7B decode, 65% zeros: {configs['4']['M1_p_zero_0.65']}")
+        configs["2"] = decode_workload(torch, bl, W, dev, stream, 2, 1)
+        gpu_us[2] = configs["2"]["us_per_layer"]
+        log(f"2B decode: {configs['2']}")
+        configs["1"] = single_gemv_workload(torch, bl, W, dev, stream)
+        gpu_us[1] = configs["1"]["us_per_call"]
+        log(f"1024x1024 GEMV: {configs['1']}")
+        result["one_token_gemv_100b"] = one_token_gemv_100b(torch, bl, dev, stream)
+        log(f"100B one-token GEMVs: {result['one_token_gemv_100b']}")
 
-    # ----------------------------------------------------------------- prefill
     if not args.no_gemm:
-        cfg5, M5, G = build_prefill(torch, bl, W, dev)
+        g5 = prefill_100b(torch, bl, W, dev, args.gemm_steps)
+        configs["5"] = g5
+        gpu_us[5] = g5["ms_per_layer"] * 1e3
+        log(f"prefill 100B: {g5}")
+        tops = g5["gemm_only_tops"]
+        result["roofline_gemm"] = {"bound": "mfma", "achieved": tops, "peak": INT8_PEAK_TOPS,
+                                   "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
+                                   "kernel": "k_gemm_i2s", "workload": g5["workload"],
+                                   "us_per_layer": round(g5["gemm_only_ms"] * 1e3, 2)}
+        if not args.no_extras:
+            configs["3"] = prefill_2b(torch, bl, W, dev, stream)
+            gpu_us[3] = configs["3"]["with_quantize"]["us_per_layer"]
+            log(f"prefill 2B: {configs['3']}")
+    result["configs"] = configs
 
-        def layer(gemm_only=False, plain=False):
-            for e in G:
-                if not gemm_only:
-                    bl.quantize_act(e["x"], e["q"], e["d"], qsum=e["qs"])
-                e["plain" if plain else "group"]()
-
-        layer()
-        layer()
-        torch.cuda.synchronize()
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        a0.record()
-        for _ in range(args.gemm_steps):
-            layer()
-        a1.record()
-        torch.cuda.synchronize()
-        ms_layer = a0.elapsed_time(a1) / args.gemm_steps
-        ops = cfg5.ops(M5)
-        tops = ops / (ms_layer * 1e-3) / 1e12
-        # GEMMs only, with and without the token sums, interleaved (the clock
-        # drifts with the power state, so back-to-back blocks would favour
-        # whichever runs second): medians over 3 rounds of gemm_steps layers
-        b0 = torch.cuda.Event(enable_timing=True)
-        b1 = torch.cuda.Event(enable_timing=True)
-        ms_by = {False: [], True: []}
-        for rnd in range(3):
-            for plain in ((False, True) if rnd % 2 == 0 else (True, False)):
-                b0.record()
-                for _ in range(args.gemm_steps):
-                    layer(gemm_only=True, plain=plain)
-                b1.record()
-                torch.cuda.synchronize()
-                ms_by[plain].append(b0.elapsed_time(b1) / args.gemm_steps)
-        ms_gemm = float(np.median(ms_by[False]))
-        gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
-        gemm_tops_plain = ops / (float(np.median(ms_by[True])) * 1e-3) / 1e12
-        # one activation scale per layer input (per tensor) instead of per token
-        ws_t = torch.empty((max(16, int(bl.lib().bl_quantize_act_tensor_workspace(M5))),),
-                           dtype=torch.uint8, device=dev)
-
-        def quantize_all(per_tensor):
-            for e in G:
-                if per_tensor:
-                    bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t, qsum=e["qs"])
-                else:
-                    bl.quantize_act(e["x"], e["q"], e["d"], qsum=e["qs"])
-
-        def layer_pt():
-            for e in G:
-                bl.quantize_act_tensor(e["x"], e["q"], e["d"], workspace=ws_t, qsum=e["qs"])
-                e["group"]()
-
-        def timed(fn, n):
-            fn()
-            torch.cuda.synchronize()
-            t0 = torch.cuda.Event(enable_timing=True)
-            t1 = torch.cuda.Event(enable_timing=True)
-            t0.record()
-            for _ in range(n):
-                fn()
-            t1.record()
-            torch.cuda.synchronize()
-            return t0.elapsed_time(t1) / n
-
-        ms_layer_pt = timed(layer_pt, args.gemm_steps)
-        tops_pt = ops / (ms_layer_pt * 1e-3) / 1e12
-        us_q_tok = timed(lambda: quantize_all(False), 10) * 1e3
-        us_q_ten = timed(lambda: quantize_all(True), 10) * 1e3
-        per_group = {}
-        for e in G:
-            c0 = torch.cuda.Event(enable_timing=True)
-            c1 = torch.cuda.Event(enable_timing=True)
-            c0.record()
-            for _ in range(3):
-                e["group"]()
-            c1.record()
-            torch.cuda.synchronize()
-            ms = c0.elapsed_time(c1) / 3
-            per_group["+".join(e["names"])] = round(e["ops"] / (ms * 1e-3) / 1e12, 1)
-        log(f"prefill: {ms_layer:.3f} ms/layer ({tops:.1f} TOPS incl. quantize), "
-            f"GEMM only {gemm_tops:.1f} TOPS ({gemm_tops_plain:.1f} without token sums); "
-            f"per group {per_group}; per-tensor scale "
-            f"{tops_pt:.1f} TOPS; quantize per layer {us_q_tok:.1f} us per token, "
-            f"{us_q_ten:.1f} us per tensor")
-        result["gemm"] = {"workload": cfg5.name, "tokens": M5, "ops_per_layer": ops,
-                          "ms_per_layer": round(ms_layer, 4), "tops": round(tops, 1),
-                          "gemm_only_tops": round(gemm_tops, 1), "peak_tops": INT8_PEAK_TOPS,
-                          "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                          "gemm_only_tops_without_token_sums": round(gemm_tops_plain, 1),
-                          "step": "per input: bl_quantize_act (codes, scales and token sums), "
-                                  "then one bl_gemm_group for {q,k,v}, {o}, {gate,up}, {down} "
-                                  "(offset weights)",
-                          "tops_per_group": per_group,
-                          "tops_per_tensor_scale": round(tops_pt, 1),
-                          "quantize_us_per_layer": {"per_token": round(us_q_tok, 1),
-                                                    "per_tensor": round(us_q_ten, 1)}}
-        del G
-        torch.cuda.empty_cache()
-
-    # ------------------------------------- residual add + RMSNorm + quantize
     if not args.no_extras:
         result["rmsnorm_quant"] = norm_bench(torch, bl, W, dev, stream)
         log(f"rmsnorm_quant: {result['rmsnorm_quant']}")
@@ -821,40 +877,10 @@ def main():
         log(f"decode layer with norms: {result['decode_layer_with_norms']}")
         result["t3_gemv"] = t3_bench(torch, bl, W, dev, stream)
         log(f"t3_gemv: {result['t3_gemv']}")
-        result["gemm_2b_prefill_512"] = prefill_2b(torch, bl, W, dev, stream)
-        log(f"gemm_2b_prefill_512: {result['gemm_2b_prefill_512']}")
 
-    # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu_baseline:
-        import oracle
-        log("cpu baseline: oracle on the decode layer")
-        host_inputs = []
-        for proj in cfg.projs:
-            inp = W.proj_inputs(cfg, proj, M)
-            host_inputs.append((inp, oracle.pack_i2s(inp.w_tern)))
-
-        def oracle_step():
-            for inp, packed in host_inputs:
-                q, d = oracle.quantize_act_absmax(inp.x_bf16)
-                t = oracle.unpack_i2s(packed, inp.proj.K)
-                acc = oracle.mpgemm_acc(q, t)
-                oracle.round_f64_to_bf16_bits(oracle.dequant_f64(acc, inp.gamma, d))
-
-        n = 0
-        t0 = time.perf_counter()
-        while True:
-            oracle_step()
-            n += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-        dt = time.perf_counter() - t0
-        cpu_gbs = step_bytes * n / dt / 1e9
-        result["cpu_baseline"] = {
-            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} decode steps of the same layer (7 projections: quantize, unpack, "
-                      f"int64 dot, dequant, bf16) in {dt:.1f} s; numpy, single thread; "
-                      f"host has {len(os.sched_getaffinity(0))} cores"}
-        log(f"cpu oracle: {cpu_gbs:.4f} GB/s ({n} steps in {dt:.1f} s)")
+        log("cpu baseline: oracle per workload")
+        result["cpu_baseline"] = cpu_baseline(gpu_us)
 
     print(json.dumps(result), flush=True)
 

