@@ -468,17 +468,17 @@ def norm_bench(torch, bl, W, dev, stream):
 
 # ------------------------------------------------------------------ prefill
 
-def build_prefill(torch, bl, W, dev, cid=5, M=2048):
+def build_prefill(torch, bl, W, dev, cid=5, M=2048, groups=None):
     """A prefill layer (by default the 100B-class layer at 2048 tokens): one
-    bf16 input per group of W.LAYER_GROUPS; each group's GEMMs run through
-    one bl_gemm_group call on its quantized codes. The quantizer also writes
-    the token sums and `group` takes them (offset weights); `plain` is the
-    same group without them."""
+    bf16 input per group of W.LAYER_GROUPS (or of `groups`); each group's
+    GEMMs run through one bl_gemm_group call on its quantized codes. The
+    quantizer also writes the token sums and `group` takes them (offset
+    weights); `plain` is the same group without them."""
     cfg = W.LAYERS[cid]
     log(f"setup prefill: {cfg.name}")
     by = {proj.name: proj for proj in cfg.projs}
     G = []
-    for names in W.LAYER_GROUPS:
+    for names in (groups or W.LAYER_GROUPS):
         inps = [W.proj_inputs(cfg, by[n], M) for n in names]
         K = by[names[0]].K
         x = bf16_dev(torch, inps[0].x_bf16, dev)
@@ -574,7 +574,8 @@ def prefill_2b(torch, bl, W, dev, stream):
     for r in range(R):
         copies.append([e["group"] if r == 0 else
                        bl.GemmGroup([dict(p, packed=p["packed"].clone()) for p in e["group"].problems],
-                                    e["q"], e["d"], qsum=e["qs"]) for e in G])
+                                    e["q"], e["d"], qsum=e["qs"], workspace=e["group"].workspace)
+                       for e in G])
     quant = [(lambda e=e: bl.quantize_act(e["x"], e["q"], e["d"], qsum=e["qs"])) for e in G]
     gemm_only = [grp for layer in copies for grp in layer]
     with_q = [f for layer in copies for pair in zip(quant, layer) for f in pair]

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define BL_ABI_VERSION 3
+#define BL_ABI_VERSION 4
 
 /* Status codes returned by every call. */
 enum {
@@ -246,15 +246,27 @@ int bl_gemv_t3(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
                const int8_t *q, const float *d, int64_t M, void *y, int ytype,
                void *stream);
 
-/* bl_gemm_workspace -- bytes of workspace bl_gemm needs (currently 0). */
+/*
+ * bl_gemm_workspace -- bytes of workspace with which bl_gemm splits K for
+ * this shape (0: the call does not split). A launch with fewer output tiles
+ * than about four per compute unit splits its K steps into up to 8 ranges
+ * of at least 512 weights; each range's exact int32 partial sums go to the
+ * workspace ([splits][M][N] int32) and a second launch adds them, subtracts
+ * the token sums and dequantizes. Integer sums are exact, so the results are
+ * bit-identical with and without the split.
+ */
 size_t bl_gemm_workspace(int64_t M, int64_t N, int64_t K);
 
 /*
  * bl_gemm -- prefill BitLinear for any M >= 1 (int8 MFMA path).
  * Defines: as bl_gemv ([BN] Part A 2.3 / 4.1); the pages leave prefill
  * unoptimized ([BN] 4.4), so this is the dense contraction on matrix cores.
- * Same arguments and results as bl_gemv, plus a workspace of ws_bytes
- * (>= bl_gemm_workspace(M, N, K); may be NULL when that is 0) and qsum:
+ * Same arguments and results as bl_gemv, plus a workspace and qsum:
+ *   ws: NULL (the launch runs unsplit), or device memory of ws_bytes >=
+ *     bl_gemm_workspace(M, N, K), 16-byte aligned (BL_ERR_WORKSPACE /
+ *     BL_ERR_ALIGN otherwise), overlapping no other argument; it receives
+ *     the split-K partial sums. Calls that share a workspace must not
+ *     overlap in time (it is not needed after the call's work ends).
  *   qsum: NULL, or int32 [M] (4-byte aligned) holding the token sums
  *     qsum[t] = sum_k q[t][k] of exactly this q (as bl_quantize_act or
  *     bl_rmsnorm_quant write them; they are not checked). With them the
@@ -277,7 +289,8 @@ int bl_gemm(const uint8_t *packed, const float *gamma, int64_t N, int64_t K,
  *   per problem: packed uint8 [N][K/4], gamma (device, 1 float), y [M][N] of
  *     type ytype (see the output enum), row stride N; N == 0 is skipped.
  *   shared: K (K % 4 == 0), q int8 [M][K], d fp32 [M], qsum (NULL or the
- *     token sums of q, as in bl_gemm), M >= 0 tokens.
+ *     token sums of q, as in bl_gemm), M >= 0 tokens; ws, ws_bytes: NULL or
+ *     a workspace of >= bl_gemm_group_workspace(...) bytes, as in bl_gemm.
  * Each y is bit-identical to what bl_gemm gives for that problem alone.
  * Validation is bl_gemm's, problem by problem; nothing is launched when any
  * problem fails it. Outputs must not alias any input or each other.
@@ -290,8 +303,16 @@ typedef struct bl_gemm_problem {
   int ytype;
 } bl_gemm_problem;
 
+/*
+ * bl_gemm_group_workspace -- bytes of workspace with which bl_gemm_group
+ * splits K for problems of these output sizes (Ns: HOST array of `count`
+ * N values; N == 0 problems count for nothing), as bl_gemm_workspace.
+ */
+size_t bl_gemm_group_workspace(const int64_t *Ns, int count, int64_t K, int64_t M);
+
 int bl_gemm_group(const bl_gemm_problem *problems, int count, int64_t K, const int8_t *q,
-                  const float *d, const int32_t *qsum, int64_t M, void *stream);
+                  const float *d, const int32_t *qsum, int64_t M, void *ws, size_t ws_bytes,
+                  void *stream);
 
 /*
  * bl_decode_problem / bl_decode_group -- fused decode BitLinear for a group

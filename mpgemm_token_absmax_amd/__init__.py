@@ -24,6 +24,8 @@ and streams only.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from ._lib import (BL_OUT_BF16, BL_OUT_F32, BL_OUT_I32, BL_W_F32, BL_W_TERNARY_I8, MAX_GROUP,
@@ -277,14 +279,18 @@ def _qsum_in(qsum, M):
 
 def gemm(packed: torch.Tensor, gamma: torch.Tensor, q: torch.Tensor, d: torch.Tensor,
          out_dtype: str = "bf16", out: torch.Tensor | None = None,
-         workspace: torch.Tensor | None = None, qsum: torch.Tensor | None = None) -> torch.Tensor:
+         workspace: torch.Tensor | None = None, qsum: torch.Tensor | None = None,
+         split: bool = True) -> torch.Tensor:
     """y[M][N] for any M (prefill path, int8 MFMA). qsum: the token sums of q
     (from quantize_act(..., with_sums=True)); with them the kernel runs on
-    offset weights, same results."""
+    offset weights, same results. split: give the call a workspace (the one
+    passed, or a new one) so that small launches split K; same results."""
     N, K, M, ytype, out = _matmul_args(packed, gamma, q, d, out, out_dtype)
     qsum = _qsum_in(qsum, M)
     nws = gemm_workspace(M, N, K)
-    if nws and workspace is None:
+    if not split:
+        workspace = None
+    elif nws and workspace is None:
         workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
     check("bl_gemm", lib().bl_gemm(_ptr(packed), _ptr(gamma), N, K, _ptr(q), _ptr(d), _ptr(qsum), M,
                                    _ptr(out), ytype, _ptr(workspace),
@@ -299,10 +305,14 @@ class GemmGroup:
     graph capture) only pass pointers.
 
     problems: list of dicts with keys packed (uint8 [N][K/4]), gamma (fp32 [1])
-    and optional y (output [M][N]) and out_dtype."""
+    and optional y (output [M][N]) and out_dtype. split: give the calls the
+    workspace with which small launches split K (the outputs are the same
+    without it): `workspace` when given (uint8, large enough; groups whose
+    calls run one after another on one stream may share one), else a new one."""
 
     def __init__(self, problems, q: torch.Tensor, d: torch.Tensor, out_dtype: str = "bf16",
-                 qsum: torch.Tensor | None = None):
+                 qsum: torch.Tensor | None = None, split: bool = True,
+                 workspace: torch.Tensor | None = None):
         if not 1 <= len(problems) <= MAX_GROUP:
             raise ValueError(f"1..{MAX_GROUP} problems per group")
         _need(q, "q", torch.int8, 2)
@@ -330,24 +340,36 @@ class GemmGroup:
             self.problems.append(dict(p, y=y))
         self.q, self.d, self.M, self.K = q, d, M, K
         self._arr = arr
+        Ns = (ctypes.c_int64 * len(problems))(*[p["packed"].shape[0] for p in self.problems])
+        nws = int(lib().bl_gemm_group_workspace(Ns, len(problems), K, M)) if split else 0
+        if nws and workspace is not None:
+            _need(workspace, "workspace", torch.uint8, 1)
+            if workspace.numel() < nws:
+                raise ValueError(f"workspace holds {workspace.numel()} bytes, {nws} needed")
+        elif nws:
+            workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
+        self.workspace = workspace if nws else None
 
     @property
     def outputs(self):
         return [p["y"] for p in self.problems]
 
     def __call__(self):
+        ws = self.workspace
         check("bl_gemm_group", lib().bl_gemm_group(self._arr, len(self.problems), self.K,
                                                    self.q.data_ptr(), self.d.data_ptr(),
-                                                   _ptr(self.qsum), self.M,
+                                                   _ptr(self.qsum), self.M, _ptr(ws),
+                                                   0 if ws is None else ws.numel(),
                                                    _stream(self.q.device)))
         return self.outputs
 
 
 def gemm_group(problems, q: torch.Tensor, d: torch.Tensor, out_dtype: str = "bf16",
-               qsum: torch.Tensor | None = None):
+               qsum: torch.Tensor | None = None, split: bool = True):
     """GEMMs of several projections over the same quantized input q, d
-    (qsum: optional token sums of q, as in gemm). Returns the list of outputs y."""
-    return GemmGroup(problems, q, d, out_dtype, qsum)()
+    (qsum: optional token sums of q, as in gemm; split: as in GemmGroup).
+    Returns the list of outputs y."""
+    return GemmGroup(problems, q, d, out_dtype, qsum, split)()
 
 
 class DecodeGroup:

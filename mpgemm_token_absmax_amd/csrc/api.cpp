@@ -2,7 +2,7 @@
 // Declarations, argument meaning, layouts, ownership and errors: the public
 // header bitlinear.h. Validation touches no HIP API, so every error path runs
 // (and is tested) on a machine without a GPU.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include "../../include/bitlinear.h"
 #include "launch.hpp"
@@ -191,11 +191,42 @@ int bl_gemv(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, con
   return hip_status(bl::launch_gemv(packed, gamma, N, K, q, d, M, y, ytype, as_stream(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of a grouped GEMM over the problems with these N (N == 0 ones
+// left out, as the call skips them): the split-K partial sums of its plan.
+size_t gemm_ws_bytes(const int64_t* Ns, int count, int64_t K, int64_t M) {
+  int64_t kept[bl::kMaxGroup];
+  int n = 0;
+  for (int i = 0; i < count; ++i)
+    if (Ns[i] > 0) kept[n++] = Ns[i];
+  if (n == 0 || M <= 0 || K <= 0) return 0;
+  return bl::plan_gemm_group(kept, n, K, M).ws_bytes;
+}
+
+// The workspace rule shared by bl_gemm and bl_gemm_group: NULL runs unsplit;
+// otherwise it must hold `need` bytes and be 16-byte aligned.
+int check_gemm_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return BL_OK;
+  if (ws_bytes < need) return BL_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return BL_ERR_ALIGN;
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t bl_gemm_workspace(int64_t M, int64_t N, int64_t K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 4 != 0) return 0;
+  return gemm_ws_bytes(&N, 1, K, M);
+}
+
+size_t bl_gemm_group_workspace(const int64_t* Ns, int count, int64_t K, int64_t M) {
+  if (!Ns || count <= 0 || count > bl::kMaxGroup || K <= 0 || K % 4 != 0 || M <= 0) return 0;
+  return gemm_ws_bytes(Ns, count, K, M);
 }
 
 int bl_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, const int8_t* q,
@@ -204,32 +235,55 @@ int bl_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K, con
   const int st = check_matmul(packed, gamma, N, K, q, d, M, y, ytype);
   if (st != BL_OK || M == 0 || N == 0) return st;
   if (!aligned(qsum, 4)) return BL_ERR_ALIGN;
-  if (ws_bytes < bl_gemm_workspace(M, N, K)) return BL_ERR_WORKSPACE;
-  (void)ws;
   if (N > (int64_t)UINT32_MAX * 64 || M > (int64_t)65535 * 128) return BL_ERR_SHAPE;
-  return hip_status(bl::launch_gemm(packed, gamma, N, K, q, d, qsum, M, y, ytype,
+  const int wst = check_gemm_ws(ws, ws_bytes, bl_gemm_workspace(M, N, K));
+  if (wst != BL_OK) return wst;
+  return hip_status(bl::launch_gemm(packed, gamma, N, K, q, d, qsum, M, y, ytype, ws,
                                     as_stream(stream)));
 }
 
-int bl_gemm_group(const bl_gemm_problem* problems, int count, int64_t K, const int8_t* q,
-                  const float* d, const int32_t* qsum, int64_t M, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation of a grouped GEMM (every problem, before anything is launched);
+// on BL_OK, g[0..n) are the problems with N > 0 and Ns their sizes.
+int check_gemm_group(const bl_gemm_problem* problems, int count, int64_t K, const int8_t* q,
+                     const float* d, const int32_t* qsum, int64_t M, bl::GemmProblem* g,
+                     int64_t* Ns, int* n) {
+  *n = 0;
   if (count < 0 || count > bl::kMaxGroup || M < 0 || K < 0 || K % 4 != 0) return BL_ERR_SHAPE;
   if (count == 0 || M == 0) return BL_OK;
   if (!problems) return BL_ERR_NULL;
   if (!aligned(qsum, 4)) return BL_ERR_ALIGN;
   if (M > (int64_t)65535 * 256) return BL_ERR_SHAPE;
-  bl::GemmProblem g[bl::kMaxGroup];
-  int n = 0;
   for (int i = 0; i < count; ++i) {
     const bl_gemm_problem& p = problems[i];
     const int st = check_matmul(p.packed, p.gamma, p.N, K, q, d, M, p.y, p.ytype);
     if (st != BL_OK) return st;
     if (p.N > (int64_t)UINT32_MAX * 64) return BL_ERR_SHAPE;
     if (p.N == 0) continue;
-    g[n++] = bl::GemmProblem{p.packed, p.gamma, p.y, p.N, p.ytype};
+    Ns[*n] = p.N;
+    g[(*n)++] = bl::GemmProblem{p.packed, p.gamma, p.y, p.N, p.ytype};
   }
-  if (n == 0) return BL_OK;
-  return hip_status(bl::launch_gemm_group(g, n, K, q, d, qsum, M, as_stream(stream)));
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bl_gemm_group(const bl_gemm_problem* problems, int count, int64_t K, const int8_t* q,
+                  const float* d, const int32_t* qsum, int64_t M, void* ws, size_t ws_bytes,
+                  void* stream) {
+  bl::GemmProblem g[bl::kMaxGroup];
+  int64_t Ns[bl::kMaxGroup];
+  int n = 0;
+  const int st = check_gemm_group(problems, count, K, q, d, qsum, M, g, Ns, &n);
+  if (st != BL_OK || n == 0) return st;
+  const int wst = check_gemm_ws(ws, ws_bytes, gemm_ws_bytes(Ns, n, K, M));
+  if (wst != BL_OK) return wst;
+  return hip_status(bl::launch_gemm_group(g, n, K, q, d, qsum, M, ws, as_stream(stream)));
 }
 
 int bl_decode_norm_group(const bl_decode_problem* problems, int count, const uint16_t* r,

@@ -35,6 +35,24 @@ __device__ __forceinline__ v4i decode_word(uint32_t word) {
   return r;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l
+// writes dst + 16*l, dst is wave-uniform. A plain function, so that no kernel
+// template instantiates the device-only builtin itself (clang's host pass
+// rejects a second template instantiation that reaches it).
+__device__ __forceinline__ void lds_dma16(const void* src, int8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] (15) | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
 // Ternary value of weight o of a group of b bytes starting at p (generic,
 // byte-wise; used only on shapes off the fast paths).
 __device__ __forceinline__ int decode_one(const uint8_t* p, int b, int o) {
@@ -183,15 +201,15 @@ __device__ __forceinline__ void sq_bins_add2(uint32_t w, unsigned long long* bin
 }
 
 // fl32(S / K) from the bins (one thread; the rare exact path). T = sum_b
-// bins[b] * 4^b is built as a 640-bit integer; A = its top 64 bits (T =
-// A * 2^L + rest), X = floor(A / K); S / K = X * 2^(L - 268) plus a positive
-// part below one unit of X exactly when rest or A mod K is nonzero (the
-// sticky bit). X has at least 46 significant bits, so one round to nearest
-// even at the fp32 position (subnormals included) with that sticky bit gives
-// the correctly rounded quotient.
-__device__ __noinline__ float ms_from_bins(const unsigned long long* bins, int64_t K) {
-  uint32_t W[20];
-#pragma unroll
+// bins[b] * 4^b is built as a 640-bit integer in W (20 words of LDS, so the
+// hot kernels keep no private array); A = its top 64 bits (T = A * 2^L +
+// rest), X = floor(A / K); S / K = X * 2^(L - 268) plus a positive part below
+// one unit of X exactly when rest or A mod K is nonzero (the sticky bit). X
+// has at least 46 significant bits, so one round to nearest even at the fp32
+// position (subnormals included) with that sticky bit gives the correctly
+// rounded quotient.
+__device__ __forceinline__ float ms_from_bins(const unsigned long long* bins, uint32_t* W,
+                                              int64_t K) {
   for (int j = 0; j < 20; ++j) W[j] = 0u;
   for (int b = 1; b < 256; ++b) {
     const unsigned long long v = bins[b];
@@ -224,15 +242,25 @@ __device__ __noinline__ float ms_from_bins(const unsigned long long* bins, int64
     A = T << (-L);
   } else {
     const int j0 = L >> 5, sh = L & 31;
-    const unsigned __int128 win = ((unsigned __int128)(j0 + 2 < 20 ? W[j0 + 2] : 0u) << 64) |
-                                  ((unsigned __int128)W[j0 + 1] << 32) | W[j0];
-    A = (unsigned long long)(win >> sh);
+    const uint32_t w2 = j0 + 2 < 20 ? W[j0 + 2] : 0u;
+    const unsigned long long lo64 = ((unsigned long long)W[j0 + 1] << 32) | W[j0];
+    A = sh ? ((lo64 >> sh) | ((unsigned long long)w2 << (64 - sh))) : lo64;
     sticky = (W[j0] & ((1u << sh) - 1u)) != 0u;
     for (int j = 0; j < j0; ++j) sticky = sticky || W[j] != 0u;
   }
+  // X = A / K and the remainder by binary long division (few registers: this
+  // path shares its kernel's register budget)
   const unsigned long long Ku = (unsigned long long)K;
-  const unsigned long long X = A / Ku;
-  sticky = sticky || (A % Ku) != 0u;
+  unsigned long long X = 0, rem = 0;
+  for (int i = 63; i >= 0; --i) {
+    rem = (rem << 1) | ((A >> i) & 1u);
+    X <<= 1;
+    if (rem >= Ku) {
+      rem -= Ku;
+      X |= 1u;
+    }
+  }
+  sticky = sticky || rem != 0u;
   const int ex = 63 - __builtin_clzll(X);                    // X >= 2^63 / K > 0
   int lsb = ex + L - 268 - 23;                               // fp32 unit of a normal result
   if (lsb < -149) lsb = -149;
@@ -251,22 +279,28 @@ __device__ __noinline__ float ms_from_bins(const unsigned long long* bins, int64
   return (float)ldexp((double)keep, lsb);
 }
 
+// LDS of the exact path: the exponent bins, the 640-bit sum and the result.
+struct MsScratch {
+  unsigned long long bins[256];
+  uint32_t words[20];
+  float ms;
+};
+
 // ms of a row from its fp64 sum of squares tot: the fast path when it is
-// certain, else the exact bins (bins: 256 words of LDS, ms_sh: one LDS float;
-// add_own(bins) adds the calling thread's values with sq_bins_add2). Every
-// thread of the block must call it with the same tot (the branch is uniform).
+// certain, else the exact bins (sc: LDS; add_own(bins) adds the calling
+// thread's values with sq_bins_add2). Every thread of the block must call it
+// with the same tot (the branch is uniform).
 template <int NT, class F>
-__device__ __forceinline__ float mean_square(double tot, int64_t K, unsigned long long* bins,
-                                             float* ms_sh, F add_own) {
+__device__ __forceinline__ float mean_square(double tot, int64_t K, MsScratch* sc, F add_own) {
   float ms;
   if (ms_fast(tot, K, &ms)) return ms;
-  for (int i = (int)threadIdx.x; i < 256; i += NT) bins[i] = 0ull;
+  for (int i = (int)threadIdx.x; i < 256; i += NT) sc->bins[i] = 0ull;
   __syncthreads();
-  add_own(bins);
+  add_own(sc->bins);
   __syncthreads();
-  if (threadIdx.x == 0) *ms_sh = ms_from_bins(bins, K);
+  if (threadIdx.x == 0) sc->ms = ms_from_bins(sc->bins, sc->words, K);
   __syncthreads();
-  return *ms_sh;
+  return sc->ms;
 }
 
 // rinv = fl32(1/fl32(sqrt(fl32(ms + eps)))), 0 when ms + eps is 0. sqrt and

@@ -57,19 +57,8 @@ namespace bl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int64_t kGemmMaxK = (int64_t)1 << 24;    // per-lane load offsets stay 32-bit
-constexpr int kBK = 128;                 // weights (k) per step
+constexpr int kBK = kGemmBK;             // weights (k) per step
 constexpr int kXcds = 8;
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l
-// writes dst + 16*l, dst is wave-uniform. A plain function, so that no kernel
-// template instantiates the device-only builtin itself (clang's host pass
-// rejects a second template instantiation that reaches it).
-__device__ __forceinline__ void lds_dma16(const void* src, int8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-}
 
 __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_t t, int64_t n,
                                            v4i acc, float c) {
@@ -124,22 +113,31 @@ __device__ __forceinline__ v4i decode_word_p1(uint32_t word) {
   return r;
 }
 
-// Wait until at most n vector-memory operations of this wave are outstanding.
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] (15) | vmcnt[5:4] at [15:14]
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
 // Kernel argument of a GEMM launch: the problems that share q, each owning
-// a contiguous range of row blocks [rb0[i], rb0[i+1]).
+// a contiguous range of row blocks [rb0[i], rb0[i+1]). With splits > 1 the K
+// steps of every tile are cut into `splits` contiguous ranges, one block per
+// range, and each block stores its exact int32 partial tile at ws + wsoff[i]
+// + split * M * N (layout [split][M][N]); k_gemm_finalize adds them.
 struct GemmArgs {
   int count;
   int total_rb;
+  int splits;
   int rb0[kMaxGroup + 1];
+  int64_t wsoff[kMaxGroup];
+  int* ws;
   GemmProblem p[kMaxGroup];
 };
+
+// Store 4 int32 partial sums ws[t][n .. n+3] of an [M][N] partial tile.
+__device__ __forceinline__ void store_partial(int* ws, int64_t N, int64_t t, int64_t n, v4i a) {
+  const int64_t base = t * N + n;
+  if (n + 3 < N && (N & 3) == 0) {
+    *reinterpret_cast<v4i*>(ws + base) = a;
+    return;
+  }
+  const int v[4] = {a.x, a.y, a.z, a.w};
+  for (int i = 0; i < 4 && n + i < N; ++i) ws[base + i] = v[i];
+}
 
 template <int RT, int TT, int WRW>
 struct GemmCfg {
@@ -200,10 +198,15 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
 
   // XCD-aware order: block b runs on XCD b % 8; give each XCD a contiguous run
   // of the tile sequence (token-tile major) so its blocks share activations.
+  // The splits of a tile are consecutive in this order (they read the same
+  // rows of packed weights and tokens, at different K).
   const int n_row_blocks = g.total_rb;
-  const int nb = n_row_blocks * n_tok_blocks;
+  const int S = g.splits;
+  const int nb = n_row_blocks * n_tok_blocks * S;
   int lin = blockIdx.x;
   if (nb % kXcds == 0) lin = (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds;
+  const int split = lin % S;
+  lin /= S;
   const int tb = lin / n_row_blocks;
   int rb = lin % n_row_blocks;
   int pi = 0;                                         // problem of this block (uniform)
@@ -222,8 +225,11 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
   const int64_t RB = K / 4;
   const int64_t n_blk = (int64_t)rb * C::BN;
   const int64_t m_blk = (int64_t)tb * C::BM;
-  const int nks = (int)((K + kBK - 1) / kBK);
+  const int nks_all = (int)((K + kBK - 1) / kBK);
   const int nfull = (int)(K / kBK);                   // steps with all 128 weights
+  // this block's steps [ks0, nks): split s of S takes a contiguous share
+  const int ks0 = (int)((int64_t)nks_all * split / S);
+  const int nks = (int)((int64_t)nks_all * (split + 1) / S);
 
   // ---- per-lane source addresses of the direct-to-LDS loads ---------------
   // activations: wave instruction i covers tile rows t = (i*4 + wv)*8 + l/8;
@@ -260,12 +266,12 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
 #pragma unroll
     for (int j = 0; j < TT; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  if (nks > 0)
-    issue_step<C::kBLoads, C::kALoads, C::kStage, C::kBBytes, C::BN, KFULL>(smem, 0, wv, bbase, boff,
-                                                                     bwrap, abase, aoff, awrap,
-                                                                     nfull);
+  if (ks0 < nks)
+    issue_step<C::kBLoads, C::kALoads, C::kStage, C::kBBytes, C::BN, KFULL>(smem, ks0, wv, bbase,
+                                                                     boff, bwrap, abase, aoff,
+                                                                     awrap, nfull);
 
-  for (int ks = 0; ks < nks; ++ks) {
+  for (int ks = ks0; ks < nks; ++ks) {
     wait_vm<0>();             // this wave's loads of step ks have landed
     __syncthreads();          // every wave's have; every wave is done reading step ks-1
 
@@ -337,6 +343,20 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
   wait_vm<0>();                // no LDS write may still be in flight when the block ends
 
   // D layout: lane holds token (column) lane%16 and features 4*(lane/16) + v.
+  if (S > 1) {                 // raw partial sums (offset form included): finalized later
+    int* wsp = g.ws + g.wsoff[pi] + (int64_t)split * M * N;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int64_t tok = m_blk + wt * TT * 16 + tt * 16 + r;
+      if (tok >= M) continue;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int64_t n = n_blk + wr * RT * 16 + rt * 16 + 4 * h;
+        if (n < N) store_partial(wsp, N, tok, n, acc[rt][tt]);
+      }
+    }
+    return;
+  }
   const int ytype = g.p[pi].ytype;
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
@@ -356,49 +376,106 @@ __global__ __launch_bounds__(kThreads, (RT * TT >= 64 ? 1 : 2)) void k_gemm_i2s(
   }
 }
 
-template <int RT, int TT, int WRW, bool OFF, bool KFULL>
-hipError_t launch_cfg(const GemmProblem* const* p, int count, int64_t K, const int8_t* q,
-                      const float* d, const int* qs, int64_t M, hipStream_t s) {
+// The partial tiles of a split launch, added in split order (int32 sums are
+// exact, so the order does not change them), the token sums subtracted for
+// offset weights, and the same dequant and store as the unsplit epilogue:
+// the outputs are bit-identical. Grid: x = 256-thread blocks over the
+// [M][ceil(N/4)] quads of the largest problem, y = problem.
+__global__ __launch_bounds__(256) void k_gemm_finalize(const GemmArgs g, const float* __restrict__ d,
+                                                       const int* __restrict__ qs, int64_t M,
+                                                       bool off) {
+  const GemmProblem& P = g.p[blockIdx.y];
+  const int64_t N = P.N;
+  const int64_t qpr = (N + 3) / 4;                    // quads per row
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * qpr) return;
+  const int64_t t = i / qpr, n = 4 * (i % qpr);
+  const int* wsp = g.ws + g.wsoff[blockIdx.y] + t * N + n;
+  const bool vec = n + 3 < N && (N & 3) == 0;
+  v4i acc = v4i{0, 0, 0, 0};
+  for (int sp = 0; sp < g.splits; ++sp) {
+    const int* src = wsp + (int64_t)sp * M * N;
+    if (vec) {
+      acc += *reinterpret_cast<const v4i*>(src);
+    } else {
+      acc.x += src[0];
+      if (n + 1 < N) acc.y += src[1];
+      if (n + 2 < N) acc.z += src[2];
+      if (n + 3 < N) acc.w += src[3];
+    }
+  }
+  if (off) acc -= v4i{qs[t], qs[t], qs[t], qs[t]};
+  const float c = P.ytype ? P.gamma[0] * d[t] : 0.0f;
+  store_quad(P.y, P.ytype, N, t, n, acc, c);
+}
+
+template <int RT, int TT, int WRW>
+GemmArgs make_args(const GemmProblem* const* p, int count, int splits, int* ws, int64_t M) {
   using C = GemmCfg<RT, TT, WRW>;
   GemmArgs a{};
-  int64_t rb = 0;
+  int64_t rb = 0, off = 0;
   for (int i = 0; i < count; ++i) {
     a.rb0[i] = (int)rb;
     a.p[i] = *p[i];
+    a.wsoff[i] = off;
     rb += (p[i]->N + C::BN - 1) / C::BN;
+    off += (int64_t)splits * M * p[i]->N;
   }
   a.count = count;
   a.rb0[count] = (int)rb;
   a.total_rb = (int)rb;
+  a.splits = splits;
+  a.ws = ws;
+  return a;
+}
+
+template <int RT, int TT, int WRW, bool OFF, bool KFULL>
+hipError_t launch_cfg(const GemmProblem* const* p, int count, int64_t K, const int8_t* q,
+                      const float* d, const int* qs, int64_t M, int splits, int* ws,
+                      hipStream_t s) {
+  using C = GemmCfg<RT, TT, WRW>;
+  const GemmArgs a = make_args<RT, TT, WRW>(p, count, splits, ws, M);
   const int64_t ntb = (M + C::BM - 1) / C::BM;
-  if (rb * ntb > INT32_MAX) return hipErrorInvalidValue;
+  if ((int64_t)a.total_rb * ntb * splits > INT32_MAX) return hipErrorInvalidValue;
   if (C::kLds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&k_gemm_i2s<RT, TT, WRW, OFF, KFULL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW, OFF, KFULL>), dim3((unsigned)(rb * ntb)), dim3(kThreads),
-                     C::kLds, s, a, K, q, d, qs, M, (int)ntb);
+  hipLaunchKernelGGL((k_gemm_i2s<RT, TT, WRW, OFF, KFULL>),
+                     dim3((unsigned)(a.total_rb * ntb * splits)), dim3(kThreads), C::kLds, s, a, K,
+                     q, d, qs, M, (int)ntb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  int64_t nmax = 0;
+  for (int i = 0; i < count; ++i) nmax = p[i]->N > nmax ? p[i]->N : nmax;
+  const int64_t quads = M * ((nmax + 3) / 4);
+  hipLaunchKernelGGL(k_gemm_finalize, dim3((unsigned)((quads + 255) / 256), (unsigned)count),
+                     dim3(256), 0, s, a, d, qs, M, OFF);
   return hipGetLastError();
 }
 
 template <int RT, int TT, int WRW>
 hipError_t launch_tiles(bool off, bool full, const GemmProblem* const* p, int count, int64_t K,
-                        const int8_t* q, const float* d, const int* qs, int64_t M, hipStream_t s) {
+                        const int8_t* q, const float* d, const int* qs, int64_t M, int splits,
+                        int* ws, hipStream_t s) {
   if (off)
-    return full ? launch_cfg<RT, TT, WRW, true, true>(p, count, K, q, d, qs, M, s)
-                : launch_cfg<RT, TT, WRW, true, false>(p, count, K, q, d, qs, M, s);
-  return full ? launch_cfg<RT, TT, WRW, false, true>(p, count, K, q, d, qs, M, s)
-              : launch_cfg<RT, TT, WRW, false, false>(p, count, K, q, d, qs, M, s);
+    return full ? launch_cfg<RT, TT, WRW, true, true>(p, count, K, q, d, qs, M, splits, ws, s)
+                : launch_cfg<RT, TT, WRW, true, false>(p, count, K, q, d, qs, M, splits, ws, s);
+  return full ? launch_cfg<RT, TT, WRW, false, true>(p, count, K, q, d, qs, M, splits, ws, s)
+              : launch_cfg<RT, TT, WRW, false, false>(p, count, K, q, d, qs, M, splits, ws, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const int8_t* q,
-                             const float* d, const int* qs, int64_t M, hipStream_t s) {
+                             const float* d, const int* qs, int64_t M, void* ws, hipStream_t s) {
   hipError_t e = hipSuccess;
-  if (K % 64 != 0 || M <= 16 || K > kGemmMaxK) {
+  int64_t Ns[kMaxGroup];
+  for (int i = 0; i < count; ++i) Ns[i] = p[i].N;
+  const GemmPlan pl = plan_gemm_group(Ns, count, K, M);
+  if (!pl.mfma) {
     for (int i = 0; i < count && e == hipSuccess; ++i)
       e = K % 64 != 0 || K > kGemmMaxK ? launch_generic(p[i].packed, p[i].gamma, p[i].N, K, q, d, M, p[i].y,
                                        p[i].ytype, s)
@@ -406,36 +483,29 @@ hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const i
                                     p[i].ytype, s);
     return e;
   }
-  // Problems big enough to fill the chip with 128x256 tiles share one launch
-  // of those (their blocks then fill whole rounds together); the rest share
-  // one launch of 64x128 tiles, or of 32x128 tiles when 64x128 would give
-  // fewer blocks than CUs.
   const GemmProblem* big[kMaxGroup];
   const GemmProblem* small[kMaxGroup];
-  int nbig = 0, nsmall = 0;
-  for (int i = 0; i < count; ++i) {
-    if (((p[i].N + 127) / 128) * ((M + 255) / 256) >= 256) big[nbig++] = &p[i];
-    else small[nsmall++] = &p[i];
-  }
+  for (int j = 0; j < pl.nbig; ++j) big[j] = &p[pl.big[j]];
+  for (int j = 0; j < pl.nsmall; ++j) small[j] = &p[pl.small[j]];
   // offset weights need the token sums and |acc + qs[t]| <= 254*K in int32
   const bool off = qs != nullptr && 254 * K <= INT32_MAX;
   const bool full = K % kBK == 0;
-  if (nbig) e = launch_tiles<4, 8, 2>(off, full, big, nbig, K, q, d, qs, M, s);
-  if (e == hipSuccess && nsmall) {
-    // 64x128 tiles, or 32x128 when those would leave CUs without a block
-    int64_t b64 = 0;
-    for (int i = 0; i < nsmall; ++i) b64 += ((small[i]->N + 63) / 64) * ((M + 127) / 128);
-    e = b64 < 256 ? launch_tiles<1, 4, 2>(off, full, small, nsmall, K, q, d, qs, M, s)
-                  : launch_tiles<2, 4, 2>(off, full, small, nsmall, K, q, d, qs, M, s);
+  if (pl.nbig) e = launch_tiles<4, 8, 2>(off, full, big, pl.nbig, K, q, d, qs, M, 1, nullptr, s);
+  if (e == hipSuccess && pl.nsmall) {
+    // without a workspace the launch runs unsplit (same results)
+    const int sp = ws ? pl.splits : 1;
+    int* w = static_cast<int*>(ws);
+    e = pl.small32 ? launch_tiles<1, 4, 2>(off, full, small, pl.nsmall, K, q, d, qs, M, sp, w, s)
+                   : launch_tiles<2, 4, 2>(off, full, small, pl.nsmall, K, q, d, qs, M, sp, w, s);
   }
   return e;
 }
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                        const int8_t* q, const float* d, const int* qs, int64_t M, void* y,
-                       int ytype, hipStream_t s) {
+                       int ytype, void* ws, hipStream_t s) {
   const GemmProblem p{packed, gamma, y, N, ytype};
-  return launch_gemm_group(&p, 1, K, q, d, qs, M, s);
+  return launch_gemm_group(&p, 1, K, q, d, qs, M, ws, s);
 }
 
 }  // namespace bl

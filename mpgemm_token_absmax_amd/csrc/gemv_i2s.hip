@@ -27,6 +27,8 @@
 //    adds;
 //  * the waves add their int32 tiles through LDS (exact, order free) and the
 //    dequant acc * fl32(gamma * d_t) is fused into the store.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -104,8 +106,8 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
   __shared__ v4i red[WPB - 1][RTW][kWave];
   __shared__ uint32_t wmax[WPB];
   __shared__ double wss[NORM ? WPB : 1];
-  __shared__ unsigned long long bins[NORM ? 256 : 1];
-  __shared__ float ms_sh;
+  // LDS of the exact mean-square path (norm launches only)
+  __shared__ typename std::conditional<NORM, MsScratch, char>::type msx_lds;
 
   const DecodeProblem& P = grp.p[blockIdx.y];
   const int64_t N = P.N;
@@ -199,6 +201,8 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
         xv[u].y = add2_bf16(xv[u].y, rv[u].y);
         xv[u].z = add2_bf16(xv[u].z, rv[u].z);
         xv[u].w = add2_bf16(xv[u].w, rv[u].w);
+        // h as opaque values (not recomputed later from x and r)
+        asm volatile("" : "+v"(xv[u].x), "+v"(xv[u].y), "+v"(xv[u].z), "+v"(xv[u].w));
       }
     }
     double ss = 0.0;
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
     double tot = wss[0];
 #pragma unroll
     for (int w = 1; w < WPB; ++w) tot += wss[w];
-    const float ms = mean_square<WPB * kWave>(tot, K, bins, &ms_sh, [&](unsigned long long* b) {
+    const float ms = mean_square<WPB * kWave>(tot, K, reinterpret_cast<MsScratch*>(&msx_lds), [&](unsigned long long* b) {
 #pragma unroll
       for (int u = 0; u < XR; ++u) {
         if (lane + u * kWave < nch) {
@@ -227,6 +231,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
           sq_bins_add2(xv[u].z, b);
           sq_bins_add2(xv[u].w, b);
         }
+        __builtin_amdgcn_sched_barrier(0);    // one chunk at a time: few registers
       }
     });
     rinv = norm_rinv(ms, eps);
@@ -515,10 +520,16 @@ __global__ __launch_bounds__(WPB * kWave) void k_decodeT(DecodeGroup grp, int le
 // of half i is D[r][0] + D[8 + r][1] (lanes 0/16 and 33/49 of the result).
 // The WPB waves split K into runs of 512-weight steps; SINGLE: every step of
 // a wave's run is in one load batch (U >= run length), so no second buffer
-// is held.
-template <int WPB, int XR, int U, bool SINGLE>
+// is held. XDMA: x goes to the wave's LDS region by direct-to-LDS loads (no
+// registers while the weights are in flight: 7 waves per SIMD at 4 steps
+// per wave, which puts the 1792 blocks of a 28672-row problem in one round),
+// and each chunk's codes are written in place over the bf16 values, which by
+// then are read (chunk c of step u is read before step u writes chunks below
+// 32(u + 1), and every chunk below that was read at step u/2 or earlier).
+template <int WPB, int XR, int U, bool SINGLE, bool XDMA = false>
 __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int len_max) {
-  extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][len_max*512]
+  // [wave][len_max*512] codes; [wave][len_max*1024] with XDMA (the bf16 x first)
+  extern __shared__ __attribute__((aligned(16))) int8_t act[];
   __shared__ v4i red[WPB - 1][2][kWave];
   __shared__ uint32_t wmax[WPB];
 
@@ -549,14 +560,19 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int l
   const int klo = min(ja * 512, K);
   const int khi = min(jb * 512, K);
   const int nch = (khi - klo) / 8;
-  int8_t* wact = act + wk * len_max * 512;
+  int8_t* wact = act + wk * len_max * (XDMA ? 1024 : 512);
 
   // ---- 1. loads: this wave's part of x, then the first weight batch -----
   const uint4* xs = reinterpret_cast<const uint4*>(xg) + (nch > 0 ? klo / 8 : 0);
   const int clast = nch > 0 ? nch - 1 : 0;
-  uint4 xv[XR];
+  uint4 xv[XDMA ? 1 : XR];
+  if constexpr (XDMA) {
 #pragma unroll
-  for (int u = 0; u < XR; ++u) xv[u] = xs[min(lane + u * kWave, clast)];
+    for (int u = 0; u < XR; ++u) lds_dma16(xs + min(lane + u * kWave, clast), wact + 1024 * u);
+  } else {
+#pragma unroll
+    for (int u = 0; u < XR; ++u) xv[u] = xs[min(lane + u * kWave, clast)];
+  }
   const float gam = ytype ? __builtin_nontemporal_load(gptr) : 0.0f;
   int64_t ra = n0 + r8, rb = n0 + 8 + r8;
   ra = ra < N ? ra : N - 1;
@@ -579,9 +595,17 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int l
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. absmax of the row: part maxima, one barrier -------------------
+  // XDMA: only the 2U weight loads are younger than the x loads (gamma's, if
+  // any, sits between them), so this wait retires x and leaves the weights in
+  // flight; the compiler's own wait for direct-to-LDS loads is a full one.
+  if constexpr (XDMA) wait_vm<2 * U>();
+  const uint4* xl = reinterpret_cast<const uint4*>(wact) + lane;   // XDMA: chunk lane + 64u
   uint32_t m = 0u;
 #pragma unroll
-  for (int u = 0; u < XR; ++u) m = max(m, lane + u * kWave < nch ? absmax8_bf16(xv[u]) : 0u);
+  for (int u = 0; u < XR; ++u) {
+    const uint4 v = XDMA ? xl[kWave * u] : xv[u];
+    m = max(m, lane + u * kWave < nch ? absmax8_bf16(v) : 0u);
+  }
   m = wave_max_u32(m);
   if (lane == 0) wmax[wk] = m;
   __syncthreads();
@@ -597,8 +621,9 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int l
 #pragma unroll
   for (int u = 0; u < XR; ++u) {
     const int cc = lane + u * kWave;
+    const uint4 v = XDMA ? xl[kWave * u] : xv[u];
     if (cc < nch) {
-      const uint2 qv = quant8_bf16(xv[u], sq);
+      const uint2 qv = quant8_bf16(v, sq);
       *reinterpret_cast<uint2*>(wact + 8 * cc) = qv;
       if (write_q) *reinterpret_cast<uint2*>(qp + klo + 8 * cc) = qv;
     }
@@ -818,16 +843,17 @@ hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int WPB, int XR, int U, bool SINGLE>
+template <int WPB, int XR, int U, bool SINGLE, bool XDMA = false>
 hipError_t launch_one_token_w(DecodeGroup& g, int len_max, hipStream_t s) {
+  static_assert(!XDMA || XR <= U, "the x staging must fit the wave's LDS region");
   int64_t blocks = 0;
   for (int i = 0; i < g.count; ++i) {
     const int64_t b = (g.p[i].N + 15) / 16;
     blocks = b > blocks ? b : blocks;
   }
   if (blocks == 0) return hipSuccess;
-  const size_t lds = (size_t)WPB * len_max * 512;
-  hipLaunchKernelGGL((k_decode1w<WPB, XR, U, SINGLE>), dim3((unsigned)blocks, (unsigned)g.count),
+  const size_t lds = (size_t)WPB * len_max * (XDMA ? 1024 : 512);
+  hipLaunchKernelGGL((k_decode1w<WPB, XR, U, SINGLE, XDMA>), dim3((unsigned)blocks, (unsigned)g.count),
                      dim3(WPB * kWave), lds, s, g, len_max);
   return hipGetLastError();
 }
@@ -959,7 +985,7 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
       if (w4 <= 1) return launch_one_token_w<4, 1, 1, true>(g, w4, s);
       if (w4 == 2) return launch_one_token_w<4, 2, 2, true>(g, w4, s);
       if (w4 == 3) return launch_one_token_w<4, 3, 3, true>(g, w4, s);
-      if (w4 == 4) return launch_one_token_w<4, 4, 4, true>(g, w4, s);
+      if (w4 == 4) return launch_one_token_w<4, 4, 4, true, true>(g, w4, s);
       const int w8 = wide_steps_per_wave(g, 8);
       if (w8 <= 4) return launch_one_token_w<8, 4, 4, true>(g, w8, s);
       if (w8 <= 8) return launch_one_token_w<8, 8, 2, false>(g, w8, s);   // batches of 2: measured 10% faster than 4 at K = 28672

@@ -2,7 +2,7 @@
 // already validated by api.cpp; each launcher only enqueues work on `s`.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -10,6 +10,21 @@ namespace bl {
 
 constexpr int kMaxGroup = 8;        // problems per decode-group launch
 constexpr int kMaxDecodeM = 16;     // tokens of the decode kernels
+
+// Prefill GEMM: weights per K step, the largest K of the MFMA path (per-lane
+// load offsets stay 32-bit), and the split-K rule (plan_gemm_group).
+constexpr int kGemmBK = 128;
+constexpr int64_t kGemmMaxK = (int64_t)1 << 24;
+constexpr int64_t kSplitBlocks = 1024;   // split-K aims at about this many blocks
+constexpr int64_t kSplitMinSteps = 4;    // K steps per split, at least
+constexpr int64_t kMaxSplits = 8;
+
+// fp32 packing: exponent bins of |w| per workgroup (kBins of them, one
+// thread each) over at most kMaxBinBlocks workgroups.
+constexpr int kBinThreads = 256;
+constexpr int kBins = 256;
+constexpr int kMaxBinBlocks = 1024;
+int64_t bin_blocks(int64_t n);
 
 // One GEMV of a decode launch. Activations come either as bf16 x (quantized
 // in-kernel; q and d, when not NULL, receive the codes and scales) or as
@@ -93,10 +108,12 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, int64_t N, int
                        const int8_t* q, const float* d, int64_t M, void* y, int ytype,
                        hipStream_t s);
 // qs (may be NULL): the token sums of q; with them the GEMM runs on offset
-// weights (w + 1) and subtracts qs[t] in the epilogue.
+// weights (w + 1) and subtracts qs[t] in the epilogue. ws (may be NULL: no
+// split): int32 partial sums of a split-K launch, plan_gemm_group's
+// ws_bytes at least.
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                        const int8_t* q, const float* d, const int* qs, int64_t M, void* y,
-                       int ytype, hipStream_t s);
+                       int ytype, void* ws, hipStream_t s);
 // Several GEMMs over the same int8 activations q [M][K] (scales d): problem i
 // has its own packed [N_i][K/4], gamma, y [M][N_i] and output type.
 struct GemmProblem {
@@ -107,7 +124,21 @@ struct GemmProblem {
   int ytype;
 };
 hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const int8_t* q,
-                             const float* d, const int* qs, int64_t M, hipStream_t s);
+                             const float* d, const int* qs, int64_t M, void* ws, hipStream_t s);
+
+// How a grouped GEMM is launched: which problems take 128x256 tiles (big),
+// the tile of the rest (32x128 or 64x128), and the K split of that launch
+// with the workspace it needs (0 when it does not split or mfma is false:
+// then the GEMV or the generic kernel runs).
+struct GemmPlan {
+  bool mfma;
+  int nbig, nsmall;
+  int big[kMaxGroup], small[kMaxGroup];
+  bool small32;
+  int splits;
+  size_t ws_bytes;
+};
+GemmPlan plan_gemm_group(const int64_t* Ns, int count, int64_t K, int64_t M);
 
 // Shapes off the fast paths (K % 64 != 0): one thread per output element.
 hipError_t launch_generic(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,

@@ -64,8 +64,7 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
   __shared__ double red_s[NT / kWave];
   __shared__ uint32_t red_m[NT / kWave];
   __shared__ int red_q[NT / kWave];
-  __shared__ unsigned long long bins[256];
-  __shared__ float ms_sh;
+  __shared__ MsScratch msx;
   const int64_t t = blockIdx.x;
   const int nchunk = (int)(K / 8);
   const uint16_t* xrow = x + t * ldx;
@@ -95,6 +94,9 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
       hv[i].y = add2_bf16(hv[i].y, rv[i].y);
       hv[i].z = add2_bf16(hv[i].z, rv[i].z);
       hv[i].w = add2_bf16(hv[i].w, rv[i].w);
+      // h as opaque values: the compiler keeps these 4 registers instead of
+      // x and r (8) to recompute them later
+      asm volatile("" : "+v"(hv[i].x), "+v"(hv[i].y), "+v"(hv[i].z), "+v"(hv[i].w));
     }
     if (c < nchunk) {
       ss = sumsq2_bf16(hv[i].x, ss);
@@ -104,10 +106,7 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
       if (h_out) reinterpret_cast<uint4*>(h_out + t * ldx)[c] = hv[i];
     }
   }
-  // g (the same for every token, an L2 hit) is in flight during the sum.
-#pragma unroll
-  for (int i = 0; i < NC; ++i) gv[i] = ld16(g, off[i]);
-  const float ms = mean_square<NT>(block_sum_f64<NT>(ss, red_s), K, bins, &ms_sh,
+  const float ms = mean_square<NT>(block_sum_f64<NT>(ss, red_s), K, &msx,
                                    [&](unsigned long long* b) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
@@ -117,8 +116,13 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant16(
         sq_bins_add2(hv[i].z, b);
         sq_bins_add2(hv[i].w, b);
       }
+      __builtin_amdgcn_sched_barrier(0);    // one chunk at a time: few registers
     }
   });
+  // g (the same for every token: an L2 hit) is loaded once the mean square
+  // is known, so it holds no registers across the sum
+#pragma unroll
+  for (int i = 0; i < NC; ++i) gv[i] = ld16(g, off[i]);
   const float rinv = norm_rinv(ms, eps);
   uint32_t mb = 0;
 #pragma unroll
@@ -183,8 +187,7 @@ __global__ __launch_bounds__(kGenThreads) void k_rmsnorm_quant_any(
   __shared__ double red_s[kGenThreads / kWave];
   __shared__ uint32_t red_m[kGenThreads / kWave];
   __shared__ int red_q[kGenThreads / kWave];
-  __shared__ unsigned long long bins[256];
-  __shared__ float ms_sh;
+  __shared__ MsScratch msx;
   const int64_t t = blockIdx.x;
   const int64_t nchunk = K / 4;
   const uint2* xr = reinterpret_cast<const uint2*>(x + t * ldx);
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(kGenThreads) void k_rmsnorm_quant_any(
     if (hr) hr[c] = h;
   }
   const float ms = mean_square<kGenThreads>(
-      block_sum_f64<kGenThreads>(ss, red_s), K, bins, &ms_sh, [&](unsigned long long* b) {
+      block_sum_f64<kGenThreads>(ss, red_s), K, &msx, [&](unsigned long long* b) {
         for (int64_t c = threadIdx.x; c < nchunk; c += kGenThreads) {
           const uint2 h = hr ? hr[c] : load_h4(xr, rr, c);
           sq_bins_add2(h.x, b);

@@ -25,17 +25,7 @@
 namespace bl {
 namespace {
 
-constexpr int kBinThreads = 256;
-constexpr int kBins = 256;
-constexpr int kMaxBinBlocks = 1024;
 constexpr int kLimbs = 6;
-
-int64_t bin_blocks(int64_t n) {
-  int64_t b = (n + (int64_t)kBinThreads * 64 - 1) / ((int64_t)kBinThreads * 64);
-  if (b < 1) b = 1;
-  if (b > kMaxBinBlocks) b = kMaxBinBlocks;
-  return b;
-}
 
 __device__ __forceinline__ void add_bin(unsigned long long* bins, uint32_t bits) {
   const uint32_t u = bits & 0x7FFFFFFFu;
@@ -191,10 +181,6 @@ __global__ void k_pack_bytes(const void* __restrict__ wv, int64_t N, int64_t K,
 unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
 }  // namespace
-
-size_t pack_workspace_bytes(int64_t N, int64_t K) {
-  return (size_t)bin_blocks(N * K) * kBins * sizeof(unsigned long long);
-}
 
 hipError_t launch_absmean_gamma(const float* w, int64_t N, int64_t K, float* gamma, void* ws,
                                 hipStream_t s) {

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bl_abi_version() == 3
+    assert lib.bl_abi_version() == 4
     for s in (L.BL_OK, L.BL_ERR_NULL, L.BL_ERR_SHAPE, L.BL_ERR_ALIGN, L.BL_ERR_DTYPE,
               L.BL_ERR_WORKSPACE, L.BL_ERR_HIP, L.BL_ERR_ALIAS):
         assert lib.bl_status_string(s)
@@ -202,9 +202,9 @@ def test_gemm_group_validation(lib):
         base.update(kw)
         return P(**base)
 
-    def call(probs, K=256, q=C16, d=D16, M=32, qsum=None):
+    def call(probs, K=256, q=C16, d=D16, M=32, qsum=None, ws=None, ws_bytes=0):
         arr = (P * max(1, len(probs)))(*probs)
-        return lib.bl_gemm_group(arr, len(probs), K, q, d, qsum, M, None)
+        return lib.bl_gemm_group(arr, len(probs), K, q, d, qsum, M, ws, ws_bytes, None)
 
     assert call([prob()] * 9) == L.BL_ERR_SHAPE            # more than 8 problems
     assert call([prob()], K=6) == L.BL_ERR_SHAPE
@@ -224,7 +224,44 @@ def test_gemm_group_validation(lib):
     assert call([], M=4) == L.BL_OK
     assert call([prob()], M=0) == L.BL_OK
     assert call([prob(N=0, packed=None, y=None)]) == L.BL_OK
-    assert lib.bl_gemm_group(None, 1, 256, C16, D16, None, 4, None) == L.BL_ERR_NULL
+    assert lib.bl_gemm_group(None, 1, 256, C16, D16, None, 4, None, 0, None) == L.BL_ERR_NULL
+    # a workspace, when given, must hold the split's partial sums and be aligned
+    Ns = (ctypes.c_int64 * 2)(2560, 640)
+    need = lib.bl_gemm_group_workspace(Ns, 2, 2560, 512)
+    assert need > 0
+    two = [prob(N=2560), prob(N=640)]
+    assert call(two, K=2560, M=512, ws=A16, ws_bytes=need - 1) == L.BL_ERR_WORKSPACE
+    assert call(two, K=2560, M=512, ws=A16 + 8, ws_bytes=need) == L.BL_ERR_ALIGN
+
+
+def test_gemm_workspace_sizes(lib):
+    """bl_gemm_workspace / bl_gemm_group_workspace: the split-K partial sums
+    ([splits][M][N] int32) of launches with fewer tiles than about four per
+    compute unit; 0 where the call runs unsplit (big problems, the GEMV path
+    at M <= 16, the generic path at K % 64 != 0, empty shapes)."""
+    ws = lib.bl_gemm_workspace
+    for M, N, K in ((512, 2560, 2560), (512, 2560, 6912), (2048, 1024, 8192), (17, 40, 256 * 16)):
+        b = ws(M, N, K)
+        assert b > 0 and b % (4 * M * N) == 0, (M, N, K, b)
+        assert 2 <= b // (4 * M * N) <= 8
+    assert ws(2048, 28672, 8192) == 0          # fills the chip unsplit
+    assert ws(16, 2560, 2560) == 0             # GEMV path
+    assert ws(512, 2560, 2600) == 0            # K % 64 != 0: generic kernel
+    assert ws(512, 2560, 256) == 0             # 2 K steps: too short to split
+    assert ws(0, 2560, 2560) == 0 and ws(512, 0, 2560) == 0 and ws(512, 2560, 0) == 0
+    G = lib.bl_gemm_group_workspace
+    N1 = (ctypes.c_int64 * 1)(2560)
+    assert G(N1, 1, 2560, 512) == ws(512, 2560, 2560)
+    N3 = (ctypes.c_int64 * 3)(2560, 0, 640)     # N == 0 problems add nothing
+    N2 = (ctypes.c_int64 * 2)(2560, 640)
+    assert G(N3, 3, 2560, 512) == G(N2, 2, 2560, 512)
+    assert G(None, 1, 2560, 512) == 0 and G(N1, 9, 2560, 512) == 0
+    # bl_gemm: a given workspace must be large enough and aligned (NULL: unsplit)
+    need = ws(512, 2560, 2560)
+    f = lib.bl_gemm
+    args = (A16, B16, 2560, 2560, C16, D16, None, 512, E16, 2)
+    assert f(*args, A16, need - 16, None) == L.BL_ERR_WORKSPACE
+    assert f(*args, A16 + 4, need, None) == L.BL_ERR_ALIGN
 
 
 def test_probe_library_exports_and_validation():

@@ -620,23 +620,90 @@ def test_gemm_group_parity(M, K, Ns, outs):
         check_outputs(acc, g, d, **{f"y_{o}": host(y)})
 
 
-def test_gemv_equals_gemm_and_deterministic():
+@pytest.mark.parametrize("M,N,K", [(17, 640, 2560), (31, 300, 320), (33, 2560, 6912),
+                                   (33, 1024, 8192)])
+def test_gemv_equals_gemm(M, N, K):
+    """The MFMA GEMM at its smallest token counts (M > 16, so bl_gemm runs
+    k_gemm_i2s) against bl_gemv over the same tokens in slices of at most 16:
+    byte-identical for every output type, with and without the token sums,
+    and both equal to the oracle; a repeated GEMM gives the same bytes."""
     bl = _bl()
-    say("gemv == gemm, repeat determinism")
-    for M in (1, 4, 16):
-        q, t, d = _mm_case(M, 333, 1024, 77)
-        packed = bl.pack_i2s(dev(t))
-        gd = dev(np.array([GAMMA], np.float32))
-        a = host(bl.gemv(packed, gd, dev(q), dev(d), out_dtype="f32"))
-        b = host(bl.gemm(packed, gd, dev(q), dev(d), out_dtype="f32"))
-        torch.cuda.synchronize()
-        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    q, t, d = _mm_case(300, 700, 2560, 78)
+    say(f"gemv == gemm M={M} N={N} K={K}")
+    q, t, d = _mm_case(M, N, K, 79 + M)
+    acc = oracle.mpgemm_acc(q, t)
     packed = bl.pack_i2s(dev(t))
     gd = dev(np.array([GAMMA], np.float32))
-    y1 = host(bl.gemm(packed, gd, dev(q), dev(d), out_dtype="bf16"))
-    y2 = host(bl.gemm(packed, gd, dev(q), dev(d), out_dtype="bf16"))
-    assert np.array_equal(y1, y2)
+    qd, dd = dev(q), dev(d)
+    qs = dev(oracle.token_sums(q).astype(np.int32))
+    for name in ("i32", "f32", "bf16"):
+        y_mm = host(bl.gemm(packed, gd, qd, dd, out_dtype=name))
+        y_off = host(bl.gemm(packed, gd, qd, dd, out_dtype=name, qsum=qs))
+        y_again = host(bl.gemm(packed, gd, qd, dd, out_dtype=name, qsum=qs))
+        parts = [host(bl.gemv(packed, gd, qd[t0:t0 + 16], dd[t0:t0 + 16], out_dtype=name))
+                 for t0 in range(0, M, 16)]
+        torch.cuda.synchronize()
+        y_mv = np.concatenate(parts, axis=0)
+        assert np.array_equal(y_mm.view(np.uint8), y_mv.view(np.uint8)), name
+        assert np.array_equal(y_off.view(np.uint8), y_mv.view(np.uint8)), name
+        assert np.array_equal(y_again.view(np.uint8), y_off.view(np.uint8)), name
+        kw = {"i32": "y_i32", "f32": "y_f32", "bf16": "y_bf16"}[name]
+        check_outputs(acc, GAMMA, d, **{kw: y_mm})
+
+
+SPLIT_CASES = [(512, 2560, 2560), (512, 2560, 6912), (17, 40, 4096), (100, 300, 2624),
+               (300, 1000, 1088), (2048, 1024, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_CASES, ids=[f"M{m}N{n}K{k}" for m, n, k in SPLIT_CASES])
+def test_gemm_split_k(M, N, K):
+    """Launches with fewer tiles than about four per CU split K over the
+    workspace and add the int32 partials in a second launch: byte-identical to
+    the unsplit launch (no workspace) for every output type, with and without
+    the token sums (K % 128 == 64 tails included), and equal to the oracle."""
+    bl = _bl()
+    nws = bl.gemm_workspace(M, N, K)
+    say(f"gemm split-K M={M} N={N} K={K} workspace={nws}")
+    assert nws > 0
+    q, t, d = _mm_case(M, N, K, 301 + M)
+    acc = oracle.mpgemm_acc(q, t) if M * N * K < 4e8 else oracle.mpgemm_acc_f64blas(q, t)
+    packed = bl.pack_i2s(dev(t))
+    gd = dev(np.array([GAMMA], np.float32))
+    qd, dd = dev(q), dev(d)
+    qs = dev(oracle.token_sums(q).astype(np.int32))
+    ws = torch.full((nws,), 0x5A, dtype=torch.uint8, device="cuda")   # stale bytes in it
+    for name in ("i32", "f32", "bf16"):
+        for qsum in (None, qs):
+            y_split = host(bl.gemm(packed, gd, qd, dd, out_dtype=name, qsum=qsum, workspace=ws))
+            y_plain = host(bl.gemm(packed, gd, qd, dd, out_dtype=name, qsum=qsum, split=False))
+            torch.cuda.synchronize()
+            assert np.array_equal(y_split.view(np.uint8), y_plain.view(np.uint8)), name
+        kw = {"i32": "y_i32", "f32": "y_f32", "bf16": "y_bf16"}[name]
+        check_outputs(acc, GAMMA, d, **{kw: y_split})
+
+
+def test_gemm_group_split_k():
+    """A group whose small problems split K next to one that fills the chip
+    unsplit (the 100B-class {q,k,v} shapes at 256 tokens, and the 2B-class
+    {q,k,v} at 512 tokens): byte-identical to the group without a workspace
+    and to bl_gemm per problem."""
+    bl = _bl()
+    for M, K, Ns in ((256, 8192, (8192, 1024, 1024)), (512, 2560, (2560, 640, 640))):
+        say(f"gemm_group split-K M={M} K={K} Ns={Ns}")
+        q, _, d = _mm_case(M, 8, K, 400 + M)
+        qd, dd = dev(q), dev(d)
+        qs = dev(oracle.token_sums(q).astype(np.int32))
+        probs = [dict(packed=bl.pack_i2s(dev(W.ternary_drawn(410 + i, n, K, 0.35))),
+                      gamma=dev(np.array([GAMMA], np.float32)), out_dtype=ot)
+                 for i, (n, ot) in enumerate(zip(Ns, ("bf16", "i32", "f32")))]
+        g_split = bl.GemmGroup(probs, qd, dd, qsum=qs)
+        assert g_split.workspace is not None
+        ys = [host(y) for y in g_split()]
+        ys_plain = [host(y) for y in bl.GemmGroup(probs, qd, dd, qsum=qs, split=False)()]
+        torch.cuda.synchronize()
+        for p, a, b in zip(probs, ys, ys_plain):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+            one = host(bl.gemm(p["packed"], p["gamma"], qd, dd, out_dtype=p["out_dtype"]))
+            assert np.array_equal(a.view(np.uint8), one.view(np.uint8))
 
 
 def test_k_zero_and_empty():
@@ -722,6 +789,10 @@ def test_decode_group_wide():
                        out_types=["bf16", "i32", "f32"])
     _decode_group_case(bl, 1, [(9000, 512), (16, 64)], seed=93)
     _decode_group_case(bl, 1, [(8193, 28672)], seed=94, out_types=["i32"])
+    # four steps per wave with x staged by direct-to-LDS loads: the 100B-class
+    # shape, and a ragged last step (K % 512 != 0) with a ragged row block
+    _decode_group_case(bl, 1, [(28672, 8192)], seed=98, out_types=["i32"])
+    _decode_group_case(bl, 1, [(8200, 7936), (300, 7936)], seed=99, out_types=["f32", "bf16"])
 
 
 def test_decode_group_wide_longest_k():
