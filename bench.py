@@ -110,25 +110,33 @@ def time_steps(torch, stream, layers, steps, warmup, spread_reps=None):
     the timed steps are captured as two graphs (the rotation continues from
     one to the other); the timed graph is replayed once between two
     synchronizations. Returns (ms per step, [p10, p50, p90] us per step over
-    further replays of the timed graph)."""
+    further replays of the timed graph each between two synchronizations,
+    i.e. measured exactly as the timed one, and the p50 of back-to-back
+    replays, where each replay's launch overlaps the previous one's work)."""
     R = len(layers)
     fw = [f for i in range(warmup) for f in layers[i % R]]
     ft = [f for i in range(warmup, warmup + steps) for f in layers[i % R]]
     g_warm = capture_fns(torch, stream, fw) if fw else None
     g_timed = capture_fns(torch, stream, ft)
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        if g_warm is not None:
-            g_warm.replay()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+
+    def one(pre=None):
+        with torch.cuda.stream(stream):
+            if pre is not None:
+                pre.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g_timed.replay()
+            e1.record(stream)
         torch.cuda.synchronize()
-        e0.record(stream)
-        g_timed.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
+        return e0.elapsed_time(e1) / steps
+
+    ms_step = one(g_warm)
     n = spread_reps or max(8, min(64, 2000 // steps))
+    per = np.array([one() * 1e3 for _ in range(n)])
+    spread = [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)]
     marks = []
     with torch.cuda.stream(stream):
         for _ in range(n):
@@ -139,10 +147,9 @@ def time_steps(torch, stream, layers, steps, warmup, spread_reps=None):
             a1.record(stream)
             marks.append((a0, a1))
     torch.cuda.synchronize()
-    per = np.array([x0.elapsed_time(x1) * 1e3 / steps for x0, x1 in marks])
-    spread = [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)]
+    piped = np.array([x0.elapsed_time(x1) * 1e3 / steps for x0, x1 in marks])
     del g_warm, g_timed
-    return ms_step, spread
+    return ms_step, spread, round(float(np.percentile(piped, 50)), 3)
 
 
 # ------------------------------------------------------------ decode layers
@@ -787,7 +794,7 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     log(f"timing {args.steps} steps after {args.warmup} warmup steps")
-    ms_step, spread = time_steps(torch, stream, layers, args.steps, args.warmup)
+    ms_step, spread, piped_p50 = time_steps(torch, stream, layers, args.steps, args.warmup)
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     launches = len(W.LAYER_GROUPS)
     us_launch = ms_step * 1e3 / launches
@@ -825,6 +832,7 @@ def main():
                            "on layer copy i mod 32",
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                    "us_per_step_p10_p50_p90": spread,
+                   "us_per_step_back_to_back_p50": piped_p50,
                    "warm_us_per_step": round(us_warm, 3),
                    "floors": floors,
                    "frac_of_layer_floor": round(floors["layer_floor_us"] / (ms_step * 1e3), 4)},

@@ -17,6 +17,8 @@ constexpr int kGemmBK = 128;
 constexpr int64_t kGemmMaxK = (int64_t)1 << 24;
 constexpr int64_t kSplitBlocks = 1024;   // split-K aims at about this many blocks
 constexpr int64_t kSplitMinSteps = 4;    // K steps per split, at least
+constexpr int64_t kSplitMaxBlocks = 256; // launches with at least this many tiles run unsplit
+constexpr int64_t kSplitMinK = 32;       // K steps of a launch worth splitting, at least
 constexpr int64_t kMaxSplits = 8;
 
 // fp32 packing: exponent bins of |w| per workgroup (kBins of them, one

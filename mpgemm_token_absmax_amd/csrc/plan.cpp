@@ -21,9 +21,14 @@ size_t pack_workspace_bytes(int64_t N, int64_t K) {
 // problems big enough to fill the chip with 128x256 tiles share one launch of
 // those (their blocks then fill whole rounds together); the rest share one
 // launch of 64x128 tiles, or of 32x128 tiles when 64x128 would give fewer
-// blocks than CUs. That second launch splits K when it has fewer blocks
-// than four per CU: S = min(8, 1024 / blocks, steps / 4) ranges of at least
-// four 128-weight steps, so more blocks share the latency of the K loop.
+// blocks than CUs. That second launch splits K when its tiles leave CUs
+// idle (fewer than 256 blocks) and K is long (at least 32 steps of 128
+// weights): S = min(8, 1024 / blocks, steps / 4) ranges of at least four
+// steps, so more blocks share the K loop. Measured on MI355X: the 2B {down}
+// projection (K = 6912) at 64 tokens 24.7 -> 13.4 us, at 128 tokens 25.1 ->
+// 15.8 us; at K = 2560, or with 256 blocks or more, the partial sums' traffic
+// and the second launch cost as much as the split saves or more (2B {q,k,v}
+// at 512 tokens 14.5 -> 22.7 us with 2 splits), so those run unsplit.
 GemmPlan plan_gemm_group(const int64_t* Ns, int count, int64_t K, int64_t M) {
   GemmPlan pl{};
   pl.mfma = K % 64 == 0 && M > 16 && K <= kGemmMaxK;
@@ -47,6 +52,7 @@ GemmPlan plan_gemm_group(const int64_t* Ns, int count, int64_t K, int64_t M) {
     nsum += Ns[pl.small[j]];
   }
   const int64_t steps = (K + kGemmBK - 1) / kGemmBK;
+  if (blocks >= kSplitMaxBlocks || steps < kSplitMinK) return pl;
   int64_t sp = blocks > 0 ? kSplitBlocks / blocks : 1;
   sp = sp < steps / kSplitMinSteps ? sp : steps / kSplitMinSteps;
   sp = sp < kMaxSplits ? sp : kMaxSplits;

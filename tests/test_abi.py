@@ -227,39 +227,42 @@ def test_gemm_group_validation(lib):
     assert lib.bl_gemm_group(None, 1, 256, C16, D16, None, 4, None, 0, None) == L.BL_ERR_NULL
     # a workspace, when given, must hold the split's partial sums and be aligned
     Ns = (ctypes.c_int64 * 2)(2560, 640)
-    need = lib.bl_gemm_group_workspace(Ns, 2, 2560, 512)
+    need = lib.bl_gemm_group_workspace(Ns, 2, 6912, 64)
     assert need > 0
     two = [prob(N=2560), prob(N=640)]
-    assert call(two, K=2560, M=512, ws=A16, ws_bytes=need - 1) == L.BL_ERR_WORKSPACE
-    assert call(two, K=2560, M=512, ws=A16 + 8, ws_bytes=need) == L.BL_ERR_ALIGN
+    assert call(two, K=6912, M=64, ws=A16, ws_bytes=need - 1) == L.BL_ERR_WORKSPACE
+    assert call(two, K=6912, M=64, ws=A16 + 8, ws_bytes=need) == L.BL_ERR_ALIGN
 
 
 def test_gemm_workspace_sizes(lib):
     """bl_gemm_workspace / bl_gemm_group_workspace: the split-K partial sums
-    ([splits][M][N] int32) of launches with fewer tiles than about four per
-    compute unit; 0 where the call runs unsplit (big problems, the GEMV path
-    at M <= 16, the generic path at K % 64 != 0, empty shapes)."""
+    ([splits][M][N] int32) of launches whose tiles leave CUs idle (fewer than
+    256 blocks) and whose K is at least 32 steps of 128; 0 where the call runs
+    unsplit (enough tiles, short K, the GEMV path at M <= 16, the generic path
+    at K % 64 != 0, empty shapes)."""
     ws = lib.bl_gemm_workspace
-    for M, N, K in ((512, 2560, 2560), (512, 2560, 6912), (2048, 1024, 8192), (17, 40, 256 * 16)):
+    for M, N, K in ((64, 2560, 6912), (300, 1000, 8192), (512, 640, 8192), (17, 40, 256 * 16)):
         b = ws(M, N, K)
         assert b > 0 and b % (4 * M * N) == 0, (M, N, K, b)
         assert 2 <= b // (4 * M * N) <= 8
     assert ws(2048, 28672, 8192) == 0          # fills the chip unsplit
+    assert ws(2048, 1024, 8192) == 0           # 256 blocks of 64 x 128
+    assert ws(512, 2560, 2560) == 0            # 20 K steps: not worth splitting
     assert ws(16, 2560, 2560) == 0             # GEMV path
     assert ws(512, 2560, 2600) == 0            # K % 64 != 0: generic kernel
     assert ws(512, 2560, 256) == 0             # 2 K steps: too short to split
     assert ws(0, 2560, 2560) == 0 and ws(512, 0, 2560) == 0 and ws(512, 2560, 0) == 0
     G = lib.bl_gemm_group_workspace
     N1 = (ctypes.c_int64 * 1)(2560)
-    assert G(N1, 1, 2560, 512) == ws(512, 2560, 2560)
+    assert G(N1, 1, 6912, 64) == ws(64, 2560, 6912) > 0
     N3 = (ctypes.c_int64 * 3)(2560, 0, 640)     # N == 0 problems add nothing
     N2 = (ctypes.c_int64 * 2)(2560, 640)
-    assert G(N3, 3, 2560, 512) == G(N2, 2, 2560, 512)
-    assert G(None, 1, 2560, 512) == 0 and G(N1, 9, 2560, 512) == 0
+    assert G(N3, 3, 6912, 64) == G(N2, 2, 6912, 64) > 0
+    assert G(None, 1, 6912, 64) == 0 and G(N1, 9, 6912, 64) == 0
     # bl_gemm: a given workspace must be large enough and aligned (NULL: unsplit)
-    need = ws(512, 2560, 2560)
+    need = ws(64, 2560, 6912)
     f = lib.bl_gemm
-    args = (A16, B16, 2560, 2560, C16, D16, None, 512, E16, 2)
+    args = (A16, B16, 2560, 6912, C16, D16, None, 64, E16, 2)
     assert f(*args, A16, need - 16, None) == L.BL_ERR_WORKSPACE
     assert f(*args, A16 + 4, need, None) == L.BL_ERR_ALIGN
 

@@ -109,20 +109,21 @@ def test_valid_calls_reach_the_launchers(asan_lib):
         assert lib.bl_gemv(A, B, 640, 2560, C, D, 4, E, L.BL_OUT_BF16, None) == ok
         assert last("gemv")[0][:3] == [4, 640, 2560]
         # the GEMM: with a workspace of exactly the size asked for, and without one
-        need = lib.bl_gemm_workspace(512, 2560, 2560)
+        need = lib.bl_gemm_workspace(64, 2560, 6912)
         assert need > 0
-        assert lib.bl_gemm(A, B, 2560, 2560, C, D, None, 512, E, L.BL_OUT_BF16, F, need, None) == ok
+        assert lib.bl_gemm(A, B, 2560, 6912, C, D, None, 64, E, L.BL_OUT_BF16, F, need, None) == ok
         v, wsp = last("gemm")
-        assert v[:3] == [512, 2560, 2560] and wsp == F
-        assert lib.bl_gemm(A, B, 2560, 2560, C, D, None, 512, E, L.BL_OUT_BF16, None, 0, None) == ok
+        assert v[:3] == [64, 2560, 6912] and wsp == F
+        assert lib.bl_gemm(A, B, 2560, 6912, C, D, None, 64, E, L.BL_OUT_BF16, None, 0, None) == ok
         assert last("gemm")[1] is None
         P = L.GemmProblem
         arr = (P * 3)(P(A, B, 2560, E, 2), P(A, B, 0, None, 2), P(A, B, 640, F, 1))
         Ns = (ctypes.c_int64 * 3)(2560, 0, 640)
-        need = lib.bl_gemm_group_workspace(Ns, 3, 2560, 512)
-        assert lib.bl_gemm_group(arr, 3, 2560, C, D, None, 512, A, need, None) == ok
+        need = lib.bl_gemm_group_workspace(Ns, 3, 6912, 64)
+        assert need > 0
+        assert lib.bl_gemm_group(arr, 3, 6912, C, D, None, 64, A, need, None) == ok
         v, wsp = last("gemm_group")
-        assert v == [512, 2560, 2560, 2] and wsp == A       # the N == 0 problem is dropped
+        assert v == [64, 2560, 6912, 2] and wsp == A        # the N == 0 problem is dropped
         D_ = L.DecodeProblem
         darr = (D_ * 2)(D_(A, B, 640, 2560, C, 2560, None, None, E, 2),
                         D_(A, B, 2560, 2560, C, 2560, None, None, F, 2))

@@ -103,9 +103,11 @@ def test_step_count_is_exact():
     R = 32
     layers = [[(lambda r=r, j=j: FakeTorch._capturing.fns.append((r, j))) for j in range(4)]
               for r in range(R)]
-    ms, spread = bench.time_steps(FakeTorch, None, layers, steps=20, warmup=5, spread_reps=2)
-    assert len(calls) >= 2
-    warm, timed = calls[0], calls[1]
-    assert warm == tuple((i % R, j) for i in range(5) for j in range(4))
-    assert timed == tuple((i % R, j) for i in range(5, 25) for j in range(4))
-    assert ms == 1.0 / 20 and len(spread) == 3
+    ms, spread, piped = bench.time_steps(FakeTorch, None, layers, steps=20, warmup=5,
+                                         spread_reps=2)
+    warm = tuple((i % R, j) for i in range(5) for j in range(4))
+    timed = tuple((i % R, j) for i in range(5, 25) for j in range(4))
+    # the warmup graph, the timed graph, then only further replays of the timed graph
+    assert calls[0] == warm and len(calls) == 1 + 1 + 2 + 2
+    assert all(c == timed for c in calls[1:])
+    assert ms == 1.0 / 20 and len(spread) == 3 and piped == round(1e3 / 20, 3)

@@ -650,13 +650,13 @@ def test_gemv_equals_gemm(M, N, K):
         check_outputs(acc, GAMMA, d, **{kw: y_mm})
 
 
-SPLIT_CASES = [(512, 2560, 2560), (512, 2560, 6912), (17, 40, 4096), (100, 300, 2624),
-               (300, 1000, 1088), (2048, 1024, 8192)]
+SPLIT_CASES = [(64, 2560, 6912), (17, 40, 4096), (100, 300, 4160), (300, 1000, 8192),
+               (512, 640, 8192), (33, 4000, 6912)]
 
 
 @pytest.mark.parametrize("M,N,K", SPLIT_CASES, ids=[f"M{m}N{n}K{k}" for m, n, k in SPLIT_CASES])
 def test_gemm_split_k(M, N, K):
-    """Launches with fewer tiles than about four per CU split K over the
+    """Launches whose tiles leave CUs idle and whose K is long split K over the
     workspace and add the int32 partials in a second launch: byte-identical to
     the unsplit launch (no workspace) for every output type, with and without
     the token sums (K % 128 == 64 tails included), and equal to the oracle."""
@@ -683,11 +683,11 @@ def test_gemm_split_k(M, N, K):
 
 def test_gemm_group_split_k():
     """A group whose small problems split K next to one that fills the chip
-    unsplit (the 100B-class {q,k,v} shapes at 256 tokens, and the 2B-class
-    {q,k,v} at 512 tokens): byte-identical to the group without a workspace
-    and to bl_gemm per problem."""
+    unsplit, and a group of small problems that split together (the 2B-class
+    {q,k,v} shapes at 128 tokens and K = 6912): byte-identical to the group
+    without a workspace and to bl_gemm per problem."""
     bl = _bl()
-    for M, K, Ns in ((256, 8192, (8192, 1024, 1024)), (512, 2560, (2560, 640, 640))):
+    for M, K, Ns in ((1024, 4096, (16384, 64, 256)), (128, 6912, (2560, 640, 640))):
         say(f"gemm_group split-K M={M} K={K} Ns={Ns}")
         q, _, d = _mm_case(M, 8, K, 400 + M)
         qd, dd = dev(q), dev(d)
