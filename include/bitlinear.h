@@ -315,6 +315,27 @@ int bl_gemm_group(const bl_gemm_problem *problems, int count, int64_t K, const i
                   void *stream);
 
 /*
+ * bl_gemm_group_noalloc -- bl_gemm_group for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. Same arguments (minus the workspace),
+ * validation and results as bl_gemm_group with a workspace of
+ * bl_gemm_group_workspace(...) bytes; it calls no allocating routine.
+ * The split-K partial sums go to a workspace inside the library: a
+ * file-scope device array of BL_GEMM_NOALLOC_SCRATCH_BYTES (32 MiB, the
+ * most any launch plan needs) that each GPU the library runs on holds until
+ * the process ends; its address on a device is looked up on the first call
+ * there. BL_ERR_WORKSPACE if a plan ever needed more; BL_ERR_HIP if the
+ * lookup fails. Every call on one GPU shares that array: calls that overlap
+ * in time on one GPU (two streams, two threads) race and may give wrong
+ * results; calls ordered on one stream do not (each launch writes every
+ * partial sum it later reads).
+ */
+#define BL_GEMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int bl_gemm_group_noalloc(const bl_gemm_problem *problems, int count, int64_t K,
+                          const int8_t *q, const float *d, const int32_t *qsum, int64_t M,
+                          void *stream);
+
+/*
  * bl_decode_problem / bl_decode_group -- fused decode BitLinear for a group
  * of independent projections in ONE launch: per-token absmax int8
  * quantization of bf16 activations, the I2_S GEMV and the dequant.

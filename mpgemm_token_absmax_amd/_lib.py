@@ -32,10 +32,11 @@ EXPORTS = ("bl_abi_version", "bl_status_string", "bl_quantize_act",
            "bl_quantize_act_tensor_workspace", "bl_quantize_act_tensor", "bl_rmsnorm_quant",
            "bl_pack_i2s_workspace", "bl_pack_i2s", "bl_pack_t3_row_bytes", "bl_pack_t3",
            "bl_gemv", "bl_gemv_t3", "bl_gemm_workspace", "bl_gemm", "bl_gemm_group_workspace",
-           "bl_gemm_group",
+           "bl_gemm_group", "bl_gemm_group_noalloc",
            "bl_decode_group", "bl_decode_group_t3", "bl_decode_norm_group")
 
 MAX_GROUP = 8
+BL_GEMM_NOALLOC_SCRATCH_BYTES = 32 << 20     # include/bitlinear.h
 
 
 class DecodeProblem(ctypes.Structure):
@@ -99,6 +100,8 @@ def _declare(lib):
     lib.bl_gemm_group_workspace.argtypes = [ctypes.POINTER(ctypes.c_int64), INT, I64, I64]
     lib.bl_gemm_group.restype = INT
     lib.bl_gemm_group.argtypes = [ctypes.POINTER(GemmProblem), INT, I64, P, P, P, I64, P, SZ, P]
+    lib.bl_gemm_group_noalloc.restype = INT
+    lib.bl_gemm_group_noalloc.argtypes = [ctypes.POINTER(GemmProblem), INT, I64, P, P, P, I64, P]
     lib.bl_decode_group.restype = INT
     lib.bl_decode_group.argtypes = [ctypes.POINTER(DecodeProblem), INT, I64, P]
     lib.bl_decode_group_t3.restype = INT

@@ -12,6 +12,8 @@ namespace {
 constexpr int64_t kGemvMaxM = 16;
 constexpr int64_t kFp32ExactK = ((int64_t)1 << 24) / 127;   // 127*K < 2^24
 constexpr int64_t kDecodeMaxK = 65536;                       // fused decode: K per problem
+static_assert(bl::kNoAllocScratchBytes == BL_GEMM_NOALLOC_SCRATCH_BYTES,
+              "the header states the allocation-free workspace size");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -283,6 +285,20 @@ int bl_gemm_group(const bl_gemm_problem* problems, int count, int64_t K, const i
   if (st != BL_OK || n == 0) return st;
   const int wst = check_gemm_ws(ws, ws_bytes, gemm_ws_bytes(Ns, n, K, M));
   if (wst != BL_OK) return wst;
+  return hip_status(bl::launch_gemm_group(g, n, K, q, d, qsum, M, ws, as_stream(stream)));
+}
+
+int bl_gemm_group_noalloc(const bl_gemm_problem* problems, int count, int64_t K, const int8_t* q,
+                          const float* d, const int32_t* qsum, int64_t M, void* stream) {
+  bl::GemmProblem g[bl::kMaxGroup];
+  int64_t Ns[bl::kMaxGroup];
+  int n = 0;
+  const int st = check_gemm_group(problems, count, K, q, d, qsum, M, g, Ns, &n);
+  if (st != BL_OK || n == 0) return st;
+  const size_t need = gemm_ws_bytes(Ns, n, K, M);
+  if (need > bl::kNoAllocScratchBytes) return BL_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && bl::noalloc_scratch(&ws) != hipSuccess) return BL_ERR_HIP;
   return hip_status(bl::launch_gemm_group(g, n, K, q, d, qsum, M, ws, as_stream(stream)));
 }
 

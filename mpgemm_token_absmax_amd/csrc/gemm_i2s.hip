@@ -50,6 +50,8 @@
 //    clock (power-limited under a full matrix load) rises: measured 3-7%
 //    more throughput on the 100B-class shapes. The decode is the same 9 ops
 //    with other tables.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -499,6 +501,37 @@ hipError_t launch_gemm_group(const GemmProblem* p, int count, int64_t K, const i
                    : launch_tiles<2, 4, 2>(off, full, small, pl.nsmall, K, q, d, qs, M, sp, w, s);
   }
   return e;
+}
+
+// ---- the workspace of the allocation-free grouped GEMM ----------------------
+// A split plan holds at most kSplitBlocks blocks of at most 64 x 128 outputs
+// (splits * blocks <= kSplitBlocks), so its partial sums never exceed
+// kSplitBlocks * 64 * 128 * 4 bytes = kNoAllocScratchBytes. The array lives on
+// every device the library runs on until the process ends. In host code its
+// name is a host-side stand-in, never a device address: only the pointer
+// hipGetSymbolAddress returns (per device) reaches kernels.
+static __device__ __align__(256) int scratch[kNoAllocScratchBytes / sizeof(int)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];            // device address of `scratch`, per device
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {                 // first call on this device (it is current)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_dev[dev] = p;
+  }
+  *ptr = scratch_dev[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,

@@ -142,6 +142,14 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm_group(const int64_t* Ns, int count, int64_t K, int64_t M);
 
+// The allocation-free grouped GEMM's workspace: a file-scope device array of
+// this many bytes (the most a split plan needs); *ptr = its address on the
+// current device (looked up on the first call on each device).
+constexpr size_t kNoAllocScratchBytes = (size_t)1024 * 64 * 128 * 4;
+static_assert(kSplitBlocks * 64 * 128 * sizeof(int) <= kNoAllocScratchBytes,
+              "a split plan's partial sums fit the allocation-free workspace");
+hipError_t noalloc_scratch(void** ptr);
+
 // Shapes off the fast paths (K % 64 != 0): one thread per output element.
 hipError_t launch_generic(const uint8_t* packed, const float* gamma, int64_t N, int64_t K,
                           const int8_t* q, const float* d, int64_t M, void* y, int ytype,

@@ -6,7 +6,8 @@ record each call. In a child process with the sanitizer runtime preloaded:
   * every case of tests/test_abi.py runs against that library (a sanitizer
     report aborts the child, so the test fails), and
   * valid calls of every entry point reach their launcher with the arguments
-    they were given (the workspace pointer included).
+    they were given (the workspace pointer included; the allocation-free
+    grouped GEMM gets the library's own array).
 Skipped where g++ or its sanitizer runtime is missing, or where another
 library is already preloaded into this process tree."""
 import os
@@ -124,6 +125,9 @@ def test_valid_calls_reach_the_launchers(asan_lib):
         assert lib.bl_gemm_group(arr, 3, 6912, C, D, None, 64, A, need, None) == ok
         v, wsp = last("gemm_group")
         assert v == [64, 2560, 6912, 2] and wsp == A        # the N == 0 problem is dropped
+        assert lib.bl_gemm_group_noalloc(arr, 3, 6912, C, D, None, 64, None) == ok
+        v, wsp = last("gemm_group")
+        assert v == [64, 2560, 6912, 2] and wsp not in (None, 0)
         D_ = L.DecodeProblem
         darr = (D_ * 2)(D_(A, B, 640, 2560, C, 2560, None, None, E, 2),
                         D_(A, B, 2560, 2560, C, 2560, None, None, F, 2))
