@@ -200,35 +200,40 @@ __device__ __forceinline__ void sq_bins_add2(uint32_t w, unsigned long long* bin
   }
 }
 
-// fl32(S / K) from the bins (one thread; the rare exact path). T = sum_b
-// bins[b] * 4^b is built as a 640-bit integer in W (20 words of LDS, so the
-// hot kernels keep no private array); A = its top 64 bits (T = A * 2^L +
-// rest), X = floor(A / K); S / K = X * 2^(L - 268) plus a positive part below
-// one unit of X exactly when rest or A mod K is nonzero (the sticky bit). X
-// has at least 46 significant bits, so one round to nearest even at the fp32
-// position (subnormals included) with that sticky bit gives the correctly
-// rounded quotient.
-__device__ __forceinline__ float ms_from_bins(const unsigned long long* bins, uint32_t* W,
-                                              int64_t K) {
-  for (int j = 0; j < 20; ++j) W[j] = 0u;
-  for (int b = 1; b < 256; ++b) {
+// The rare exact path in two parts. First every thread of the block takes
+// whole bins b (tid, tid + NT, ...) and adds bins[b] * 4^b, a value below
+// 2^(2b + 64), into 64-bit column sums of 32-bit words: cols[j] collects bits
+// 32j .. 32j+31 of each term (at most 3 words per term, each word < 2^32, at
+// most 256 terms a column: no overflow). Then one thread propagates the
+// carries, so that W holds T = sum_b bins[b] * 4^b as a 640-bit integer.
+__device__ __forceinline__ void bins_to_cols(const unsigned long long* bins,
+                                             unsigned long long* cols, int tid, int nt) {
+  for (int b = tid; b < 256; b += nt) {
     const unsigned long long v = bins[b];
-    if (!v) continue;
+    if (b == 0 || !v) continue;
     const int w = b >> 4, sh = 2 * (b & 15);           // bit offset 2b = 32w + sh
     const unsigned long long lo = v << sh;
     const uint32_t hi = sh ? (uint32_t)(v >> (64 - sh)) : 0u;
-    unsigned long long c = (unsigned long long)W[w] + (uint32_t)lo;
-    W[w] = (uint32_t)c;
-    c = (c >> 32) + W[w + 1] + (uint32_t)(lo >> 32);
-    W[w + 1] = (uint32_t)c;
-    c = (c >> 32) + W[w + 2] + hi;
-    W[w + 2] = (uint32_t)c;
+    atomicAdd(&cols[w], (unsigned long long)(uint32_t)lo);
+    atomicAdd(&cols[w + 1], lo >> 32);
+    if (hi) atomicAdd(&cols[w + 2], (unsigned long long)hi);
+  }
+}
+
+// fl32(S / K) from the column sums (one thread). W (20 words of LDS, so the
+// hot kernels keep no private array) receives T with its carries; A = the
+// top 64 bits of T (T = A * 2^L + rest), X = floor(A / K); S / K = X *
+// 2^(L - 268) plus a positive part below one unit of X exactly when rest or
+// A mod K is nonzero (the sticky bit). X has at least 46 significant bits, so
+// one round to nearest even at the fp32 position (subnormals included) with
+// that sticky bit gives the correctly rounded quotient.
+__device__ __forceinline__ float ms_from_cols(const unsigned long long* cols, uint32_t* W,
+                                              int64_t K) {
+  unsigned long long c = 0;
+  for (int j = 0; j < 20; ++j) {
+    c += cols[j];
+    W[j] = (uint32_t)c;
     c >>= 32;
-    for (int j = w + 3; c != 0 && j < 20; ++j) {
-      c += W[j];
-      W[j] = (uint32_t)c;
-      c >>= 32;
-    }
   }
   int top = 19;
   while (top >= 0 && W[top] == 0u) --top;
@@ -282,6 +287,7 @@ __device__ __forceinline__ float ms_from_bins(const unsigned long long* bins, ui
 // LDS of the exact path: the exponent bins, the 640-bit sum and the result.
 struct MsScratch {
   unsigned long long bins[256];
+  unsigned long long cols[20];
   uint32_t words[20];
   float ms;
 };
@@ -295,10 +301,13 @@ __device__ __forceinline__ float mean_square(double tot, int64_t K, MsScratch* s
   float ms;
   if (ms_fast(tot, K, &ms)) return ms;
   for (int i = (int)threadIdx.x; i < 256; i += NT) sc->bins[i] = 0ull;
+  for (int i = (int)threadIdx.x; i < 20; i += NT) sc->cols[i] = 0ull;
   __syncthreads();
   add_own(sc->bins);
   __syncthreads();
-  if (threadIdx.x == 0) sc->ms = ms_from_bins(sc->bins, sc->words, K);
+  bins_to_cols(sc->bins, sc->cols, (int)threadIdx.x, NT);
+  __syncthreads();
+  if (threadIdx.x == 0) sc->ms = ms_from_cols(sc->cols, sc->words, K);
   __syncthreads();
   return sc->ms;
 }
