@@ -107,7 +107,8 @@ def test_step_count_is_exact():
                                          spread_reps=2)
     warm = tuple((i % R, j) for i in range(5) for j in range(4))
     timed = tuple((i % R, j) for i in range(5, 25) for j in range(4))
-    # the warmup graph, the timed graph, then only further replays of the timed graph
-    assert calls[0] == warm and len(calls) == 1 + 1 + 2 + 2
-    assert all(c == timed for c in calls[1:])
+    # one untimed launch of the timed graph, then (warmup graph, timed graph)
+    # for the timed step and each spread repetition, then back-to-back replays
+    assert calls[0] == timed and len(calls) == 1 + 2 * (1 + 2) + 2
+    assert calls[1:7] == [warm, timed] * 3 and calls[7:] == [timed, timed]
     assert ms == 1.0 / 20 and len(spread) == 3 and piped == round(1e3 / 20, 3)
