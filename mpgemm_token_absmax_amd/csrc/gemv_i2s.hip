@@ -999,12 +999,22 @@ hipError_t launch_decode_group(DecodeGroup& g, hipStream_t s) {
     if (len4 == 2) return launch_one_token<4, 1, 1, 2>(g, len4, s);
     if (len4 == 3) return launch_one_token<4, 1, 2, 3>(g, len4, s);
     if (len4 == 4) return launch_one_token<4, 1, 2, 4>(g, len4, s);
+    // up to 8 steps per wave: all of them in one load batch (a batch that
+    // does not divide the steps issues clamped extra loads, which still cost
+    // requests: the 7B-class {down} launch, 6 steps a wave, ran 6.35 us in
+    // batches of 4 and 5.89 us in one batch of 6)
     const int len8 = steps_per_wave(g, 8);
     if (len8 == 3) return launch_one_token<8, 1, 2, 3>(g, len8, s);
     if (len8 == 4) return launch_one_token<8, 1, 2, 4>(g, len8, s);
-    if (len8 <= 8) return launch_one_token<8, 1, 4, 4>(g, len8, s);
+    if (len8 == 5) return launch_one_token<8, 1, 4, 5>(g, len8, s);
+    if (len8 == 6) return launch_one_token<8, 1, 4, 6>(g, len8, s);
+    if (len8 == 7) return launch_one_token<8, 1, 4, 7>(g, len8, s);
+    if (len8 == 8) return launch_one_token<8, 1, 4, 8>(g, len8, s);
     const int len16 = steps_per_wave(g, 16);       // <= 16 for K <= 65536
-    if (len16 <= 8) return launch_one_token<16, 1, 4, 4>(g, len16, s);
+    if (len16 == 5) return launch_one_token<16, 1, 4, 5>(g, len16, s);
+    if (len16 == 6) return launch_one_token<16, 1, 4, 6>(g, len16, s);
+    if (len16 == 7) return launch_one_token<16, 1, 4, 7>(g, len16, s);
+    if (len16 == 8) return launch_one_token<16, 1, 4, 8>(g, len16, s);
     return launch_one_token<16, 1, 8, 4>(g, len16, s);
   }
   bool tokens_ok = fused && g.M <= kFusedTokens;

@@ -777,6 +777,16 @@ def test_decode_group_one_token_long_k():
     _decode_group_case(bl, 1, [(3, 65536), (9, 40960)], seed=78, out_types=["f32", "bf16"])
 
 
+@pytest.mark.parametrize("K", [9024, 11008, 13824, 16384, 20032, 24576, 27648, 32768])
+def test_decode_group_one_token_batches(K):
+    """One-token groups whose waves walk 5 to 8 steps in a single load batch:
+    8 waves per block at K = 9024, 11008 (the 7B-class {down}), 13824 and
+    16384, 16 waves at K = 20032, 24576, 27648 and 32768 (ragged last steps
+    included)."""
+    bl = _bl()
+    _decode_group_case(bl, 1, [(33, K), (17, K)], seed=700 + K % 97)
+
+
 def test_decode_group_wide():
     """One-token groups with a problem of >= 8192 rows take the whole-line
     kernel: one batch per wave at K = 512, 2560, 4160 (K % 512 != 0) and 8192
