@@ -298,22 +298,34 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) acc0[rt] = acc1[rt] = v4i{0, 0, 0, 0};
   const int8_t* arow = wact + 64 * h;
-  // each activation fragment is read from LDS next to its MFMA (the other
-  // waves of the SIMD hide the latency): no fragment is held across steps
+  // the four activation fragments of a step are read from LDS one step ahead
+  // of their MFMAs (with one or two waves per SIMD nothing else hides the
+  // read latency); steps past the wave's last read its last step's bytes
+  auto read_b = [&](v4i (&b)[4], int j) {
+    const int8_t* p = arow + (min(j, jb - 1) - ja) * 256;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const v4i*>(p + 16 * s);
+  };
   auto compute = [&](const v4i (&w)[U][RTW], int j) {
+    v4i bc[4], bn[4];
+    read_b(bc, j);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (u + 1 < U) read_b(bn, j + u + 1);
       if (j + u < jb) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const v4i b = *reinterpret_cast<const v4i*>(arow + (j + u - ja) * 256 + 16 * s);
 #pragma unroll
           for (int rt = 0; rt < RTW; ++rt) {
             v4i& a = (s & 1) ? acc1[rt] : acc0[rt];
-            a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]), b, a,
-                                                      0, 0, 0);
+            a = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_word((uint32_t)w[u][rt][s]), bc[s],
+                                                      a, 0, 0, 0);
           }
         }
+      }
+      if (u + 1 < U) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bc[s] = bn[s];
       }
     }
   };

@@ -805,6 +805,31 @@ def test_decode_group_wide():
     _decode_group_case(bl, 1, [(8200, 7936), (300, 7936)], seed=99, out_types=["f32", "bf16"])
 
 
+def test_decode_group_one_token_large_groups():
+    """One-token groups of at least 256 16-row tiles, as the layers stream
+    them: three problems whose row counts are not multiples of 16 (ragged
+    last row blocks in every problem), partial last steps (K % 512 != 0 and
+    K % 256 != 0), eight problems in one launch, the 7B-class groups, the
+    x chunks of a 24576-long row, no q and d outputs, and an i32 output
+    without gamma."""
+    bl = _bl()
+    _decode_group_case(bl, 1, [(4100, 1088), (2000, 1088), (100, 1088)], seed=130)
+    _decode_group_case(bl, 1, [(4096, 4096)] * 3, seed=131, out_types=["bf16"])
+    _decode_group_case(bl, 1, [(11008, 4096), (11008, 4096)], seed=132, out_types=["bf16"])
+    _decode_group_case(bl, 1, [(4096, 11008)], seed=133, out_types=["f32"])
+    _decode_group_case(bl, 1, [(520, 512)] * 8, seed=134)
+    _decode_group_case(bl, 1, [(5000, 320), (3001, 320)], seed=135, with_qd=False)
+    _decode_group_case(bl, 1, [(4100, 24576)], seed=136, out_types=["i32"])
+    N, K = 4111, 2112
+    say(f"decode_group i32 without gamma N={N} K={K}")
+    x = W.activations_bf16(137, 1, K, outlier_frac=0.01, outlier_scale=20.0)
+    t = W.ternary_drawn(138, N, K, 0.4)
+    (y,) = bl.decode_group([dict(packed=bl.pack_i2s(dev(t)), x=dev_bf16(x))], out_dtype="i32")
+    torch.cuda.synchronize()
+    q_ref, _ = oracle.quantize_act_absmax(x)
+    assert np.array_equal(host(y), oracle.mpgemm_acc(q_ref, t).astype(np.int32))
+
+
 def test_decode_group_wide_longest_k():
     """The 16-wave whole-line block at the largest K the call takes (65536):
     byte-identical to quantize + bl_gemv, sampled rows against the oracle."""
