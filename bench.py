@@ -767,8 +767,9 @@ def parse():
                    help="counter-collection mode: only the prefill GEMM layers (eager) of the "
                         "100B-class layer at 2048 tokens and the 2B-class layer at 512; no JSON line")
     p.add_argument("--traffic", action="store_true",
-                   help="counter-collection mode: a 256 MiB plain copy (calibration) and "
-                        "eager decode launches of the headline stream; no JSON line")
+                   help="counter-collection mode: a 256 MiB plain copy (calibration), "
+                        "eager decode launches of the headline stream and 4 fused norm launches "
+                        "on the 100B-class prefill shape; no JSON line")
     return p.parse_args()
 
 
@@ -820,9 +821,21 @@ def main():
             for f in layer:
                 f()
         torch.cuda.synchronize()
+        # the fused norm on the 100B-class prefill shape, 4 launches on fresh buffers
+        cfg5 = W.LAYERS[5]
+        K5 = cfg5.projs[0].K
+        xb, rb, gb = W.norm_inputs(4242 + 5, 2048, K5, cfg5.outlier_frac, cfg5.outlier_scale)
+        g5 = bf16_dev(torch, gb, dev)
+        for _ in range(4):
+            bl.rmsnorm_quant(bf16_dev(torch, xb, dev), g5, 1e-5, residual=bf16_dev(torch, rb, dev),
+                             h_out=torch.empty((2048, K5), dtype=torch.bfloat16, device=dev),
+                             q=torch.empty((2048, K5), dtype=torch.int8, device=dev),
+                             d=torch.empty((2048,), dtype=torch.float32, device=dev))
+        torch.cuda.synchronize()
         log(f"traffic mode: 1 calibration kernel over {src.numel()} B, "
             f"{len(layers) * len(W.LAYER_GROUPS)} decode launches "
-            f"({step_bytes // len(W.LAYER_GROUPS)} packed bytes per launch on average)")
+            f"({step_bytes // len(W.LAYER_GROUPS)} packed bytes per launch on average), "
+            f"4 bl_rmsnorm_quant launches of 2048 x {K5}")
         return
     for layer in layers:                      # eager pass: loads the code objects
         for f in layer:
