@@ -342,9 +342,10 @@ def one_token_gemv_100b(torch, bl, dev, stream):
         return f
 
     out = {}
+    gen = torch.Generator(device=dev).manual_seed(2048)
     for N, K in ((28672, 8192), (8192, 28672)):
-        t = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev)
-        x = torch.randn(1, K, device=dev).to(torch.bfloat16)
+        t = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev, generator=gen)
+        x = torch.randn(1, K, device=dev, generator=gen).to(torch.bfloat16)
         gam = torch.tensor([0.01], device=dev)
         R = 8
         launches = [bl.DecodeGroup([dict(packed=bl.pack_i2s(t), gamma=gam, x=x)]) for _ in range(R)]
@@ -768,8 +769,9 @@ def parse():
                         "100B-class layer at 2048 tokens and the 2B-class layer at 512; no JSON line")
     p.add_argument("--traffic", action="store_true",
                    help="counter-collection mode: a 256 MiB plain copy (calibration), "
-                        "eager decode launches of the headline stream and 4 fused norm launches "
-                        "on the 100B-class prefill shape; no JSON line")
+                        "eager decode launches of the headline stream, 4 fused norm launches "
+                        "on the 100B-class prefill shape and 4 one-token GEMVs of 28672 x 8192; "
+                        "no JSON line")
     return p.parse_args()
 
 
@@ -832,10 +834,21 @@ def main():
                              q=torch.empty((2048, K5), dtype=torch.int8, device=dev),
                              d=torch.empty((2048,), dtype=torch.float32, device=dev))
         torch.cuda.synchronize()
+        # the one-token GEMV of the 100B-class 28672 x 8192 shape, 4 launches on fresh weights
+        gen = torch.Generator(device=dev).manual_seed(2048)
+        t = torch.randint(-1, 2, (28672, 8192), dtype=torch.int8, device=dev, generator=gen)
+        x1 = torch.randn(1, 8192, device=dev, generator=gen).to(torch.bfloat16)
+        gam = torch.tensor([0.01], device=dev)
+        gemvs = [bl.DecodeGroup([dict(packed=bl.pack_i2s(t), gamma=gam, x=x1)]) for _ in range(4)]
+        del t
+        torch.cuda.synchronize()
+        for f in gemvs:
+            f()
+        torch.cuda.synchronize()
         log(f"traffic mode: 1 calibration kernel over {src.numel()} B, "
             f"{len(layers) * len(W.LAYER_GROUPS)} decode launches "
             f"({step_bytes // len(W.LAYER_GROUPS)} packed bytes per launch on average), "
-            f"4 bl_rmsnorm_quant launches of 2048 x {K5}")
+            f"4 bl_rmsnorm_quant launches of 2048 x {K5}, 4 one-token GEMVs of 28672 x 8192")
         return
     for layer in layers:                      # eager pass: loads the code objects
         for f in layer:
