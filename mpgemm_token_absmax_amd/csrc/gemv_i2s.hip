@@ -43,6 +43,18 @@ constexpr int64_t kWideN = 8192;
 // One-token-style fused decode (quantize in the kernel) up to this many tokens.
 constexpr int kFusedTokens = 4;
 
+// One-token launches with at least this many 16-row blocks (two per compute
+// unit on MI355X) issue a wave's weight loads only once the block has the
+// activation row's maximum (k_decode1), or once the wave's codes are written
+// (k_decode1w, from kLateWeightsAfterCodes blocks): x then reaches each
+// wave ahead of the weight traffic of the blocks beside it, while those
+// blocks keep HBM busy. Measured per launch on the 7B-class layer: {q,k,v}
+// (768 blocks) 5.66 -> 5.25 us; on 28672 x 8192 (1792 blocks) 14.7 -> 13.5
+// us; with one block per compute unit the delay idles the memory system
+// ({o}: 3.54 -> 3.82 us), so those launches load the weights first.
+constexpr int64_t kLateWeightsBlocks = 512;
+constexpr int64_t kLateWeightsAfterCodes = 1024;
+
 // Two row tiles per wave in k_gemvq from this many 32-row blocks per launch.
 constexpr int64_t kGemvqTwoTileBlocks = 256;
 
@@ -100,7 +112,9 @@ __device__ __forceinline__ void store_quad(void* y, int ytype, int64_t N, int64_
 // sums the parts' fp64 sums of squares (one barrier), each wave normalizes
 // its part and the block takes the absmax of y (a second barrier); the codes
 // are those of y. The first block writes h (and q, d when asked).
-template <int WPB, int RTW, int XR, int U, bool NORM = false>
+// LATE: the first weight batch is issued after the row maximum is known
+// instead of right after x (launches with several blocks per compute unit).
+template <int WPB, int RTW, int XR, int U, bool NORM = false, bool LATE = false>
 __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int len_max) {
   extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][len_max*256]
   __shared__ v4i red[WPB - 1][RTW][kWave];
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
     }
   };
   __builtin_amdgcn_sched_barrier(0);
-  load_w(wa, ja);
+  if constexpr (!LATE) load_w(wa, ja);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. absmax of the row: quarter maxima, one barrier ----------------
@@ -267,6 +281,11 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
     dv = m ? mf / 127.0f : 0.0f;
   }
   if (first_block && wk == 0 && lane == 0 && dp) dp[0] = dv;
+  if constexpr (LATE) {                     // the row maximum is known: now the weights
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wa, ja);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // ---- 3. int8 codes of this quarter -> the wave's LDS region -----------
   const bool write_q = first_block && qp;
@@ -538,7 +557,9 @@ __global__ __launch_bounds__(WPB * kWave) void k_decodeT(DecodeGroup grp, int le
 // and each chunk's codes are written in place over the bf16 values, which by
 // then are read (chunk c of step u is read before step u writes chunks below
 // 32(u + 1), and every chunk below that was read at step u/2 or earlier).
-template <int WPB, int XR, int U, bool SINGLE, bool XDMA = false>
+// LATE: the first weight batch is issued after the wave's codes are written
+// instead of right after x (launches with many blocks per compute unit).
+template <int WPB, int XR, int U, bool SINGLE, bool XDMA = false, bool LATE = false>
 __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int len_max) {
   // [wave][len_max*512] codes; [wave][len_max*1024] with XDMA (the bf16 x first)
   extern __shared__ __attribute__((aligned(16))) int8_t act[];
@@ -603,14 +624,15 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int l
     }
   };
   __builtin_amdgcn_sched_barrier(0);
-  load_w(wa, ja);
+  if constexpr (!LATE) load_w(wa, ja);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. absmax of the row: part maxima, one barrier -------------------
   // XDMA: only the 2U weight loads are younger than the x loads (gamma's, if
   // any, sits between them), so this wait retires x and leaves the weights in
   // flight; the compiler's own wait for direct-to-LDS loads is a full one.
-  if constexpr (XDMA) wait_vm<2 * U>();
+  // LATE: no weight load is in flight yet.
+  if constexpr (XDMA) wait_vm<LATE ? 0 : 2 * U>();
   const uint4* xl = reinterpret_cast<const uint4*>(wact) + lane;   // XDMA: chunk lane + 64u
   uint32_t m = 0u;
 #pragma unroll
@@ -643,6 +665,11 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1w(DecodeGroup grp, int l
   // (activation bytes past K in a partial last step are never paired with a
   // weight: those weights are masked to 0)
   __builtin_amdgcn_wave_barrier();
+  if constexpr (LATE) {                     // the wave's codes are written: now the weights
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wa, ja);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // ---- 4. MFMA over this part's steps ----------------------------------
   // one accumulator per row half: the halves alternate, so an MFMA never
@@ -843,30 +870,44 @@ __global__ void k_generic(const uint8_t* __restrict__ packed, const float* __res
 
 template <int WPB, int RTW, int XR, int U, bool NORM = false>
 hipError_t launch_one_token(DecodeGroup& g, int len_max, hipStream_t s) {
-  int64_t blocks = 0;
+  int64_t blocks = 0, total = 0;
   for (int i = 0; i < g.count; ++i) {
     const int64_t b = (g.p[i].N + 16 * RTW - 1) / (16 * RTW);
     blocks = b > blocks ? b : blocks;
+    total += b;
   }
   if (blocks == 0) return hipSuccess;
   const size_t lds = (size_t)WPB * len_max * 256;
-  hipLaunchKernelGGL((k_decode1<WPB, RTW, XR, U, NORM>), dim3((unsigned)blocks, (unsigned)g.count),
-                     dim3(WPB * kWave), lds, s, g, len_max);
+  if (!NORM && total >= kLateWeightsBlocks)
+    hipLaunchKernelGGL((k_decode1<WPB, RTW, XR, U, NORM, true>),
+                       dim3((unsigned)blocks, (unsigned)g.count), dim3(WPB * kWave), lds, s, g,
+                       len_max);
+  else
+    hipLaunchKernelGGL((k_decode1<WPB, RTW, XR, U, NORM, false>),
+                       dim3((unsigned)blocks, (unsigned)g.count), dim3(WPB * kWave), lds, s, g,
+                       len_max);
   return hipGetLastError();
 }
 
 template <int WPB, int XR, int U, bool SINGLE, bool XDMA = false>
 hipError_t launch_one_token_w(DecodeGroup& g, int len_max, hipStream_t s) {
   static_assert(!XDMA || XR <= U, "the x staging must fit the wave's LDS region");
-  int64_t blocks = 0;
+  int64_t blocks = 0, total = 0;
   for (int i = 0; i < g.count; ++i) {
     const int64_t b = (g.p[i].N + 15) / 16;
     blocks = b > blocks ? b : blocks;
+    total += b;
   }
   if (blocks == 0) return hipSuccess;
   const size_t lds = (size_t)WPB * len_max * (XDMA ? 1024 : 512);
-  hipLaunchKernelGGL((k_decode1w<WPB, XR, U, SINGLE, XDMA>), dim3((unsigned)blocks, (unsigned)g.count),
-                     dim3(WPB * kWave), lds, s, g, len_max);
+  if (total >= kLateWeightsAfterCodes)
+    hipLaunchKernelGGL((k_decode1w<WPB, XR, U, SINGLE, XDMA, true>),
+                       dim3((unsigned)blocks, (unsigned)g.count), dim3(WPB * kWave), lds, s, g,
+                       len_max);
+  else
+    hipLaunchKernelGGL((k_decode1w<WPB, XR, U, SINGLE, XDMA, false>),
+                       dim3((unsigned)blocks, (unsigned)g.count), dim3(WPB * kWave), lds, s, g,
+                       len_max);
   return hipGetLastError();
 }
 

@@ -810,8 +810,9 @@ def test_decode_group_one_token_large_groups():
     them: three problems whose row counts are not multiples of 16 (ragged
     last row blocks in every problem), partial last steps (K % 512 != 0 and
     K % 256 != 0), eight problems in one launch, the 7B-class groups, the
-    x chunks of a 24576-long row, no q and d outputs, and an i32 output
-    without gamma."""
+    x chunks of a 24576-long row, launches that issue their weights after
+    the activation row (several load batches per wave), no q and d outputs,
+    and an i32 output without gamma."""
     bl = _bl()
     _decode_group_case(bl, 1, [(4100, 1088), (2000, 1088), (100, 1088)], seed=130)
     _decode_group_case(bl, 1, [(4096, 4096)] * 3, seed=131, out_types=["bf16"])
@@ -820,6 +821,10 @@ def test_decode_group_one_token_large_groups():
     _decode_group_case(bl, 1, [(520, 512)] * 8, seed=134)
     _decode_group_case(bl, 1, [(5000, 320), (3001, 320)], seed=135, with_qd=False)
     _decode_group_case(bl, 1, [(4100, 24576)], seed=136, out_types=["i32"])
+    # weights issued after the row maximum or the codes (launches of >= 512
+    # and >= 1024 blocks), with several load batches per wave
+    _decode_group_case(bl, 1, [(4096, 36864)] * 2, seed=139, out_types=["i32", "f32"])
+    _decode_group_case(bl, 1, [(16384, 16896)], seed=140, out_types=["bf16"])
     N, K = 4111, 2112
     say(f"decode_group i32 without gamma N={N} K={K}")
     x = W.activations_bf16(137, 1, K, outlier_frac=0.01, outlier_scale=20.0)
