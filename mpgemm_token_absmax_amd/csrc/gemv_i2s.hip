@@ -48,10 +48,11 @@ constexpr int kFusedTokens = 4;
 // activation row's maximum (k_decode1), or once the wave's codes are written
 // (k_decode1w, from kLateWeightsAfterCodes blocks): x then reaches each
 // wave ahead of the weight traffic of the blocks beside it, while those
-// blocks keep HBM busy. Measured per launch on the 7B-class layer: {q,k,v}
-// (768 blocks) 5.66 -> 5.25 us; on 28672 x 8192 (1792 blocks) 14.7 -> 13.5
-// us; with one block per compute unit the delay idles the memory system
-// ({o}: 3.54 -> 3.82 us), so those launches load the weights first.
+// blocks keep HBM busy. Measured with a distinct x per launch: 28672 x 8192
+// (1792 blocks) 14.8 -> 13.4 us, the 7B-class {q,k,v} (768 blocks) 5.79 ->
+// 5.72 us; with one block per compute unit the delay idles the memory system
+// (the 7B-class {o}: 3.54 -> 3.82 us), so those launches load the weights
+// first.
 constexpr int64_t kLateWeightsBlocks = 512;
 constexpr int64_t kLateWeightsAfterCodes = 1024;
 
