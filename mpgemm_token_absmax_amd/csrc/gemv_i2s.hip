@@ -386,7 +386,9 @@ __global__ __launch_bounds__(WPB * kWave) void k_decode1(DecodeGroup grp, int le
 // 16 lanes of a fragment read spread over the banks; lane (n, h) reads token
 // n's fragments (token MT-1 for n >= MT: those output columns are dropped).
 // Tokens M..MT-1 repeat token M-1 (read, quantized, never stored).
-template <int WPB, int XR, int U, int MT>
+// LATE: the first weight batch is issued after the row maxima are known, as
+// in k_decode1 (on the 7B-class layer at 4 tokens: 35.5 -> 33.6 us).
+template <int WPB, int XR, int U, int MT, bool LATE = false>
 __global__ __launch_bounds__(WPB * kWave) void k_decodeT(DecodeGroup grp, int len_max) {
   extern __shared__ __attribute__((aligned(16))) int8_t act[];   // [wave][MT][tstride]
   __shared__ v4i red[WPB - 1][kWave];
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_decodeT(DecodeGroup grp, int le
     }
   };
   __builtin_amdgcn_sched_barrier(0);
-  load_w(wa, ja);
+  if constexpr (!LATE) load_w(wa, ja);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. per-token absmax: part maxima, one barrier ---------------------
@@ -478,6 +480,11 @@ __global__ __launch_bounds__(WPB * kWave) void k_decodeT(DecodeGroup grp, int le
     dp[lane] = dl;
   }
 
+  if constexpr (LATE) {                     // the row maxima are known: now the weights
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wa, ja);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // ---- 3. int8 codes of this part of every token -> LDS ------------------
   const bool write_q = first_block && qp;
 #pragma unroll
@@ -915,21 +922,28 @@ hipError_t launch_one_token_w(DecodeGroup& g, int len_max, hipStream_t s) {
 template <int WPB, int XR, int U>
 hipError_t launch_tokens(DecodeGroup& g, int len_max, hipStream_t s) {
   constexpr int MT = kFusedTokens;
-  int64_t blocks = 0;
+  int64_t blocks = 0, total = 0;
   for (int i = 0; i < g.count; ++i) {
     const int64_t b = (g.p[i].N + 15) / 16;
     blocks = b > blocks ? b : blocks;
+    total += b;
   }
   if (blocks == 0) return hipSuccess;
   const size_t lds = (size_t)WPB * MT * (len_max * 256 + 16);
+  const bool late = total >= kLateWeightsBlocks;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_decodeT<WPB, XR, U, MT>),
+        late ? reinterpret_cast<const void*>(&k_decodeT<WPB, XR, U, MT, true>)
+             : reinterpret_cast<const void*>(&k_decodeT<WPB, XR, U, MT, false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_decodeT<WPB, XR, U, MT>), dim3((unsigned)blocks, (unsigned)g.count),
-                     dim3(WPB * kWave), lds, s, g, len_max);
+  if (late)
+    hipLaunchKernelGGL((k_decodeT<WPB, XR, U, MT, true>), dim3((unsigned)blocks, (unsigned)g.count),
+                       dim3(WPB * kWave), lds, s, g, len_max);
+  else
+    hipLaunchKernelGGL((k_decodeT<WPB, XR, U, MT, false>), dim3((unsigned)blocks, (unsigned)g.count),
+                       dim3(WPB * kWave), lds, s, g, len_max);
   return hipGetLastError();
 }
 

@@ -835,6 +835,16 @@ def test_decode_group_one_token_large_groups():
     assert np.array_equal(host(y), oracle.mpgemm_acc(q_ref, t).astype(np.int32))
 
 
+def test_decode_group_tokens_large_groups():
+    """2-4-token groups of at least 512 16-row blocks, whose weights are
+    issued after the row maxima: the 7B-class {q,k,v} at 4 tokens (one load
+    batch), and 3 tokens over two 24576-long problems (two batches per wave,
+    more than 64 KB of LDS)."""
+    bl = _bl()
+    _decode_group_case(bl, 4, [(4096, 4096)] * 3, seed=141, out_types=["bf16"])
+    _decode_group_case(bl, 3, [(4096, 24576)] * 2, seed=142, out_types=["f32", "i32"])
+
+
 def test_decode_group_wide_longest_k():
     """The 16-wave whole-line block at the largest K the call takes (65536):
     byte-identical to quantize + bl_gemv, sampled rows against the oracle."""
