@@ -24,7 +24,8 @@ def steps_per_wave(K, wpb):
 
 def decode1_config(K):
     """(WPB, XR, U, len) that launch_decode_group picks for a one-token group
-    whose largest K is K."""
+    whose largest K is K: up to 8 steps a wave, one load batch of exactly the
+    wave's steps."""
     len4 = steps_per_wave(K, 4)
     if len4 <= 4:
         return 4, (1 if len4 <= 2 else 2), max(len4, 1), len4
@@ -32,10 +33,10 @@ def decode1_config(K):
     if len8 <= 4:
         return 8, 2, len8, len8
     if len8 <= 8:
-        return 8, 4, 4, len8
+        return 8, 4, len8, len8
     len16 = steps_per_wave(K, 16)
     assert len16 <= 16, "K above 65536 is rejected at the boundary"
-    return (16, 4, 4, len16) if len16 <= 8 else (16, 8, 4, len16)
+    return (16, 4, len16, len16) if len16 <= 8 else (16, 8, 4, len16)
 
 
 def gemvq_config(K, blocks32=0):
@@ -708,3 +709,53 @@ def test_decode1_t3_unit_pairing():
         assert (lane0 & 15) == 0 and 4 * (lane0 >> 4) + r % 4 == r
         lane1 = lane0 + 33
         assert (lane1 & 15) == 1 and 4 * (lane1 >> 4) + r % 4 == 8 + r
+
+
+# ---- the models follow the launchers --------------------------------------
+
+def _dispatch_rules():
+    """The one-token and 2..4-token launch choices of launch_decode_group,
+    read from gemv_i2s.hip: {launcher: [(var, op, bound or None, template
+    args, len var)]} in source order, and the step-count variables."""
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(__file__), "..", "mpgemm_token_absmax_amd", "csrc",
+                            "gemv_i2s.hip")).read()
+    body = src[src.index("hipError_t launch_decode_group(DecodeGroup"):]
+    body = body[:body.index("\n}\n")]
+    vars_ = {}
+    for m in re.finditer(r"const int (\w+) = (wide_steps_per_wave|steps_per_wave)\(g, (\d+)\);",
+                         body):
+        vars_[m.group(1)] = (512 if m.group(2).startswith("wide") else 256, int(m.group(3)))
+    rules = {}
+    pat = (r"(?:if \((\w+) (<=|==) (\d+)\) )?return (launch_one_token_w|launch_one_token|"
+           r"launch_tokens)<([^>]*)>\(g, (\w+), s\);")
+    for m in re.finditer(pat, body):
+        args = tuple(a.strip() for a in m.group(5).split(","))
+        rules.setdefault(m.group(4), []).append(
+            (m.group(1), m.group(2), int(m.group(3)) if m.group(3) else None, args, m.group(6)))
+    return rules, vars_
+
+
+def _pick(rules, vars_, K):
+    vals = {v: ((K + sz - 1) // sz + w - 1) // w for v, (sz, w) in vars_.items()}
+    for var, op, bound, args, lenvar in rules:
+        if var is None or (op == "<=" and vals[var] <= bound) or (op == "==" and vals[var] == bound):
+            return args, vals[lenvar]
+    raise AssertionError(f"no launch for K = {K}")
+
+
+def test_models_follow_the_launchers():
+    """decode1_config, decode1w_config and decodet_config give the launch
+    configuration that gemv_i2s.hip's dispatch picks, for every K."""
+    rules, vars_ = _dispatch_rules()
+    assert set(rules) == {"launch_one_token_w", "launch_one_token", "launch_tokens"}
+    for K in range(64, 65536 + 1, 64):
+        (wpb, rtw, xr, u), length = _pick(rules["launch_one_token"], vars_, K)
+        assert rtw == "1"
+        assert decode1_config(K) == (int(wpb), int(xr), int(u), length), K
+        a, length = _pick(rules["launch_one_token_w"], vars_, K)
+        assert decode1w_config(K) == (int(a[0]), int(a[1]), int(a[2]), a[3] == "true", length), K
+        if K <= 32768:
+            a, length = _pick(rules["launch_tokens"], vars_, K)
+            assert decodet_config(K) == (int(a[0]), int(a[1]), int(a[2]), length), K
